@@ -1,0 +1,105 @@
+"""The oracle pins must reject plausible mistakes (CPU only).
+
+Each case plants one mistake in a temporary copy of the oracle's C source (a
+wrong index, a dropped factor, a swapped operand, a wrong boundary rule),
+compiles it with gcc, and checks that the brute-force / closed-form pins used
+by test_oracle_pins fail against it.  Nothing here touches the GPU path.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_recurrence_scan_reverse_amd import synth
+from tests import direct_sums as ds
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "rlscan_oracle.c")
+
+# (name, original text, planted mistake)
+MUTATIONS = [
+    ("gae_value_index", "v_next = (double)v[i + 1];\n        carry = A_next;",
+     "v_next = (double)v[i];\n        carry = A_next;"),
+    ("gae_dropped_gamma", "(double)r[i] + gamma * v_next - (double)v[i];\n      const double A",
+     "(double)r[i] + v_next - (double)v[i];\n      const double A"),
+    ("trunc_before_term", "if (term && term[i]) return STEP_TERM;\n  if (trunc && trunc[i]) return STEP_TRUNC;",
+     "if (trunc && trunc[i]) return STEP_TRUNC;\n  if (term && term[i]) return STEP_TERM;"),
+    ("trunc_uses_row_bootstrap",
+     "if (kind == STEP_TRUNC) return trunc_bootstrap ? (double)trunc_bootstrap[i] : 0.0;",
+     "if (kind == STEP_TRUNC) return bootstrap_value ? (double)bootstrap_value[e] : 0.0;"),
+    ("end_ignores_bootstrap", "return bootstrap_value ? (double)bootstrap_value[e] : 0.0;\n}",
+     "return 0.0;\n}"),
+    ("td_lambda_weights_swapped", "(1.0 - lambda) * (double)v[i + 1] + lambda * G_next",
+     "lambda * (double)v[i + 1] + (1.0 - lambda) * G_next"),
+    ("vtrace_trace_without_lambda", "const double c = lambda * fmin(c_bar, ratio);",
+     "const double c = fmin(c_bar, ratio);"),
+    ("vtrace_pg_uses_value", "pg_advantages[i] = rho * ((double)r[i] + gamma * vs_succ",
+     "pg_advantages[i] = rho * ((double)r[i] + gamma * v_next"),
+    ("vtrace_rho_uses_cbar", "const double rho = fmin(rho_bar, ratio);",
+     "const double rho = fmin(c_bar, ratio);"),
+    ("retrace_ratio_inverted", "(double)pi_prob[i + 1] / (double)mu_prob[i + 1]",
+     "(double)mu_prob[i + 1] / (double)pi_prob[i + 1]"),
+    ("retrace_trace_of_current_step", "(double)pi_prob[i + 1] / (double)mu_prob[i + 1]",
+     "(double)pi_prob[i] / (double)mu_prob[i]"),
+    ("retrace_uses_q_not_expected_q", "target = (double)exp_q[i + 1] + c_next",
+     "target = (double)q[i + 1] + c_next"),
+    ("traces_reset_off_by_one", "if (t > 0 && step_done(term, trunc, i - 1)) prev = 0.0;\n      const double cur = decay",
+     "if (step_done(term, trunc, i)) prev = 0.0;\n      const double cur = decay"),
+    ("prefix_ignores_init", "double prev = init ? (double)init[e] : 0.0;\n    for (int64_t t = 0; t < T; ++t) {\n      const int64_t i = e * T + t;\n      if (t > 0 && step_done(term, trunc, i - 1)) prev = 0.0;\n      const double cur = prev +",
+     "double prev = 0.0;\n    for (int64_t t = 0; t < T; ++t) {\n      const int64_t i = e * T + t;\n      if (t > 0 && step_done(term, trunc, i - 1)) prev = 0.0;\n      const double cur = prev +"),
+    ("scan_direction_flipped", "const int64_t t = reverse ? (T - 1 - k) : k;",
+     "const int64_t t = reverse ? k : (T - 1 - k);"),
+]
+
+
+def _err(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    return float(np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref))))
+
+
+def _pins_pass() -> bool:
+    """The brute-force pins of test_oracle_pins, condensed: True iff all agree."""
+    term, trunc = synth.flag_patterns(4)
+    E, T = term.shape[0], 4
+    d = synth.draw(E, T, seed=9)
+    d["terminated"], d["truncated"] = term, trunc
+    te, tr, bv, tb = term, trunc, d["bootstrap_value"], d["trunc_bootstrap"]
+    checks = [
+        (oracle.discounted_returns(d["r"], te, tr, bv, tb), ds.discounted_returns(d["r"], te, tr, bv, tb)),
+        (oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb), ds.td_lambda(d["r"], d["v"], te, tr, bv, tb)),
+        (oracle.gae(d["r"], d["v"], te, tr, bv, tb), ds.gae(d["r"], d["v"], te, tr, bv, tb)),
+        (oracle.retrace(d["r"], d["q"], d["exp_q"], d["pi"], d["mu"], te, tr, bv, tb),
+         ds.retrace(d["r"], d["q"], d["exp_q"], d["pi"], d["mu"], te, tr, bv, tb)),
+        (oracle.eligibility_traces(d["r"], te, tr, bv), ds.eligibility_traces(d["r"], te, tr, bv)),
+        (oracle.episodic_prefix_sum(d["r"], te, tr, bv), ds.episodic_prefix_sum(d["r"], te, tr, bv)),
+    ]
+    vs, pg = oracle.vtrace(d["r"], d["v"], d["log_rhos"], te, tr, bv, tb, lam=0.9, rho_bar=0.8, c_bar=1.2)
+    rvs, rpg = ds.vtrace(d["r"], d["v"], d["log_rhos"], te, tr, bv, tb, lam=0.9, rho_bar=0.8, c_bar=1.2)
+    checks += [(vs, rvs), (pg, rpg)]
+    rng = np.random.default_rng(4)
+    a = rng.uniform(-1, 1, (5, 9)).astype(np.float32)
+    b = rng.standard_normal((5, 9)).astype(np.float32)
+    for rev in (True, False):
+        checks.append((oracle.linear_scan(a, b, None, reverse=rev), ds.linear_scan(a, b, None, reverse=rev)))
+    return all(_err(g, r) < 1e-12 for g, r in checks)
+
+
+def test_unmutated_oracle_passes():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, orig, bad):
+    src = open(SRC).read()
+    assert src.count(orig) >= 1, "mutation anchor not found: %s" % name
+    mutated = src.replace(orig, bad, 1)
+    c_path = tmp_path / "mut.c"
+    so_path = tmp_path / "libmut.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(so_path), str(c_path), "-lm"],
+                   check=True)
+    with oracle.use_library(str(so_path)):
+        assert not _pins_pass(), "planted mistake %s went unnoticed" % name

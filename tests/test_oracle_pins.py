@@ -1,0 +1,479 @@
+"""Pins for the fp64 CPU oracle (CPU only).
+
+The rl-triton pages print no worked example, so the oracle is pinned by:
+  * brute-force direct sums (tests/direct_sums.py) on every terminated /
+    truncated flag pattern of length T <= 6 and on random longer rows;
+  * closed forms (constant reward, unit signal, prefix counts);
+  * reductions between estimators (GAE at lambda 0 and 1, TD(1), V-trace at
+    rho = c = 1, Retrace at lambda 0 and on-policy);
+  * exact-rational algebra of the affine scan operator (gist.science summary,
+    Methodologie section 1) and the identity "fold of the per-step (a_t, b_t)
+    pairs == the estimator", which ties every coefficient table the GPU kernels
+    use to the textbook recursions.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_recurrence_scan_reverse_amd import synth
+from tests import direct_sums as ds
+
+TOL = 1e-12
+
+
+def err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref))))
+
+
+def rand_inputs(E, T, seed, p=0.15):
+    d = synth.draw(E, T, seed=seed, p_term=p, p_trunc=p)
+    return d
+
+
+# ------------------------------------------------------------------ brute force
+def _exhaustive(T, seed):
+    term, trunc = synth.flag_patterns(T)
+    E = term.shape[0]
+    d = synth.draw(E, T, seed=seed)
+    d["terminated"], d["truncated"] = term, trunc
+    return d
+
+
+def _check_all(d, gamma=0.99, lam=0.95, use_null_boot=False):
+    bv = None if use_null_boot else d["bootstrap_value"]
+    tb = None if use_null_boot else d["trunc_bootstrap"]
+    te, tr = d["terminated"], d["truncated"]
+    got = oracle.discounted_returns(d["r"], te, tr, bv, tb, gamma=gamma)
+    assert err(got, ds.discounted_returns(d["r"], te, tr, bv, tb, gamma=gamma)) < TOL
+    got = oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=gamma, lam=lam)
+    assert err(got, ds.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=gamma, lam=lam)) < TOL
+    adv, ret = oracle.gae(d["r"], d["v"], te, tr, bv, tb, gamma=gamma, lam=lam, with_returns=True)
+    ref = ds.gae(d["r"], d["v"], te, tr, bv, tb, gamma=gamma, lam=lam)
+    assert err(adv, ref) < TOL
+    assert err(ret, ref + d["v"].astype(np.float64)) < TOL
+    vs, pg = oracle.vtrace(d["r"], d["v"], d["log_rhos"], te, tr, bv, tb, gamma=gamma, lam=lam,
+                           rho_bar=1.0, c_bar=0.9)
+    rvs, rpg = ds.vtrace(d["r"], d["v"], d["log_rhos"], te, tr, bv, tb, gamma=gamma, lam=lam,
+                         rho_bar=1.0, c_bar=0.9)
+    assert err(vs, rvs) < TOL
+    assert err(pg, rpg) < TOL
+    got = oracle.retrace(d["r"], d["q"], d["exp_q"], d["pi"], d["mu"], te, tr, bv, tb,
+                         gamma=gamma, lam=lam)
+    ref = ds.retrace(d["r"], d["q"], d["exp_q"], d["pi"], d["mu"], te, tr, bv, tb,
+                     gamma=gamma, lam=lam)
+    assert err(got, ref) < TOL
+    init = None if use_null_boot else d["bootstrap_value"]
+    got = oracle.eligibility_traces(d["r"], te, tr, init, gamma=gamma, lam=lam)
+    assert err(got, ds.eligibility_traces(d["r"], te, tr, init, gamma=gamma, lam=lam)) < TOL
+    got = oracle.episodic_prefix_sum(d["r"], te, tr, init)
+    assert err(got, ds.episodic_prefix_sum(d["r"], te, tr, init)) < TOL
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6])
+def test_exhaustive_flag_patterns(T):
+    """Every (terminated, truncated) pattern of length T, all seven estimators."""
+    d = _exhaustive(T, seed=100 + T)
+    _check_all(d)
+
+
+@pytest.mark.parametrize("T", [3, 5])
+def test_exhaustive_flag_patterns_null_bootstraps(T):
+    d = _exhaustive(T, seed=200 + T)
+    _check_all(d, use_null_boot=True)
+
+
+@pytest.mark.parametrize("gamma,lam", [(0.99, 0.95), (0.5, 0.0), (1.0, 1.0), (0.0, 0.7), (0.9, 0.3)])
+def test_random_rows_against_direct_sums(gamma, lam):
+    d = rand_inputs(12, 29, seed=7, p=0.12)
+    _check_all(d, gamma=gamma, lam=lam)
+
+
+def test_null_flags_mean_no_flags():
+    d = rand_inputs(6, 17, seed=3, p=0.0)
+    z = np.zeros_like(d["terminated"])
+    a = oracle.gae(d["r"], d["v"], None, None, d["bootstrap_value"], None)
+    b = oracle.gae(d["r"], d["v"], z, z, d["bootstrap_value"], None)
+    assert np.array_equal(a, b)
+    a = oracle.episodic_prefix_sum(d["r"], None, None)
+    b = oracle.episodic_prefix_sum(d["r"], z, z)
+    assert np.array_equal(a, b)
+
+
+def test_generic_scan_against_direct_sums():
+    rng = np.random.default_rng(5)
+    a = rng.uniform(-1.2, 1.2, size=(9, 13)).astype(np.float32)
+    b = rng.standard_normal((9, 13)).astype(np.float32)
+    c = rng.standard_normal(9).astype(np.float32)
+    for rev in (True, False):
+        for carry in (None, c):
+            assert err(oracle.linear_scan(a, b, carry, reverse=rev),
+                       ds.linear_scan(a, b, carry, reverse=rev)) < TOL
+
+
+# ------------------------------------------------------------------ closed forms
+def test_discounted_constant_reward_closed_form():
+    """Constant reward c, no flags, zero bootstrap: G_t = c (1 - g^(T-t)) / (1 - g)."""
+    E, T, c = 3, 300, 0.75
+    r = np.full((E, T), c, dtype=np.float32)
+    g = ds.f32(0.99)
+    got = oracle.discounted_returns(r, gamma=0.99)
+    t = np.arange(T)
+    ref = c * (1.0 - g ** (T - t)) / (1.0 - g)
+    assert err(got, np.broadcast_to(ref, (E, T))) < 1e-12
+
+
+def test_discounted_terminal_closed_form():
+    """A terminal at step j: G_t = c (1 - g^(j-t+1)) / (1 - g) for t <= j; bootstrap ignored."""
+    E, T, c, j = 2, 40, 2.0, 17
+    r = np.full((E, T), c, dtype=np.float32)
+    term = np.zeros((E, T), np.uint8)
+    term[:, j] = 1
+    bv = np.array([5.0, -3.0], np.float32)
+    g = ds.f32(0.9)
+    got = oracle.discounted_returns(r, term, None, bv, gamma=0.9)
+    t = np.arange(j + 1)
+    assert err(got[:, : j + 1], np.broadcast_to(c * (1 - g ** (j - t + 1)) / (1 - g), (E, j + 1))) < 1e-12
+    # after the terminal, the window-end bootstrap enters: G_t = c(1-g^n)/(1-g) + g^n * bv
+    t2 = np.arange(j + 1, T)
+    n = T - t2
+    ref2 = c * (1 - g ** n) / (1 - g) + np.outer(bv.astype(np.float64), g ** n)
+    assert err(got[:, j + 1:], ref2) < 1e-12
+
+
+def test_hand_worked_gae_example():
+    """Four steps, gamma = lambda = 1/2 (exact in binary), terminal at t = 1.
+
+    r = [1, 2, 0, 4], V = [1, 1, 2, 2], bootstrap = 4, term = [0, 1, 0, 0].
+      t=3 (window end): delta = 4 + .5*4 - 2 = 4;            A = 4
+      t=2:              delta = 0 + .5*2 - 2 = -1;           A = -1 + .25*4 = 0
+      t=1 (terminal):   delta = 2 + 0 - 1 = 1;               A = 1
+      t=0:              delta = 1 + .5*1 - 1 = 0.5;          A = 0.5 + .25*1 = 0.75
+    """
+    r = np.array([[1, 2, 0, 4]], np.float32)
+    v = np.array([[1, 1, 2, 2]], np.float32)
+    term = np.array([[0, 1, 0, 0]], np.uint8)
+    bv = np.array([4], np.float32)
+    adv = oracle.gae(r, v, term, None, bv, None, gamma=0.5, lam=0.5)
+    assert adv.tolist() == [[0.75, 1.0, 0.0, 4.0]]
+    ret = oracle.td_lambda(r, v, term, None, bv, None, gamma=0.5, lam=0.5)
+    assert ret.tolist() == [[1.75, 2.0, 2.0, 6.0]]
+
+
+def test_hand_worked_truncation_example():
+    """Truncation uses its own bootstrap; termination wins over truncation.
+
+    gamma = 1/2, r = [1, 1, 1], trunc = [1, 0, 1], term = [0, 0, 1],
+    trunc_bootstrap = [8, *, 16], row bootstrap 32 (never used: t=2 is terminal).
+      t=2: terminal -> G = 1
+      t=1: G = 1 + .5*1 = 1.5
+      t=0: truncated -> G = 1 + .5*8 = 5
+    """
+    r = np.ones((1, 3), np.float32)
+    trunc = np.array([[1, 0, 1]], np.uint8)
+    term = np.array([[0, 0, 1]], np.uint8)
+    tb = np.array([[8, 99, 16]], np.float32)
+    bv = np.array([32], np.float32)
+    got = oracle.discounted_returns(r, term, trunc, bv, tb, gamma=0.5)
+    assert got.tolist() == [[5.0, 1.5, 1.0]]
+
+
+def test_traces_unit_signal_closed_form():
+    """x = 1, no flags, init 0: e_t = (1 - d^(t+1)) / (1 - d)."""
+    T = 200
+    x = np.ones((2, T), np.float32)
+    d = ds.f32(0.99) * ds.f32(0.95)
+    got = oracle.eligibility_traces(x, gamma=0.99, lam=0.95)
+    t = np.arange(T)
+    assert err(got, np.broadcast_to((1 - d ** (t + 1)) / (1 - d), (2, T))) < 1e-12
+
+
+def test_prefix_sum_counts_exactly():
+    """x = 1, no flags: S_t = t + 1 exactly; with a done at j the count restarts."""
+    T = 1000
+    x = np.ones((2, T), np.float32)
+    got = oracle.episodic_prefix_sum(x)
+    assert np.array_equal(got, np.broadcast_to(np.arange(1, T + 1, dtype=np.float64), (2, T)))
+    trunc = np.zeros((2, T), np.uint8)
+    trunc[1, 9] = 1
+    got = oracle.episodic_prefix_sum(x, None, trunc, np.array([5, 5], np.float32))
+    assert got[0, 0] == 6 and got[0, -1] == T + 5
+    assert got[1, 9] == 15 and got[1, 10] == 1 and got[1, -1] == T - 10
+
+
+def test_generic_scan_special_cases():
+    rng = np.random.default_rng(11)
+    b = rng.standard_normal((4, 50)).astype(np.float32)
+    c = rng.standard_normal(4).astype(np.float32)
+    zeros = np.zeros_like(b)
+    ones = np.ones_like(b)
+    for rev in (True, False):
+        assert np.array_equal(oracle.linear_scan(zeros, b, c, reverse=rev), b.astype(np.float64))
+        assert np.array_equal(oracle.linear_scan(ones, zeros, c, reverse=rev),
+                              np.broadcast_to(c.astype(np.float64)[:, None], b.shape))
+    suffix = np.cumsum(b[:, ::-1].astype(np.float64), axis=1)[:, ::-1]
+    assert err(oracle.linear_scan(ones, b, None, reverse=True), suffix) < 1e-13
+    prefix = np.cumsum(b.astype(np.float64), axis=1)
+    assert err(oracle.linear_scan(ones, b, None, reverse=False), prefix) < 1e-13
+
+
+# ------------------------------------------------------------------ reductions
+@pytest.fixture(scope="module")
+def mid():
+    return rand_inputs(40, 64, seed=21, p=0.05)
+
+
+def _args(d):
+    return d["terminated"], d["truncated"], d["bootstrap_value"], d["trunc_bootstrap"]
+
+
+def test_gae_lambda0_is_td_error(mid):
+    d = mid
+    te, tr, bv, tb = _args(d)
+    adv = oracle.gae(d["r"], d["v"], te, tr, bv, tb, gamma=0.97, lam=0.0)
+    ret1 = oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=0.97, lam=0.0)
+    # TD(0) target is r + g * next value, so GAE(0) = TD(0) target - V
+    assert err(adv, ret1 - d["v"]) < 1e-13
+
+
+def test_gae_lambda1_is_return_minus_value(mid):
+    d = mid
+    te, tr, bv, tb = _args(d)
+    adv = oracle.gae(d["r"], d["v"], te, tr, bv, tb, gamma=0.97, lam=1.0)
+    G = oracle.discounted_returns(d["r"], te, tr, bv, tb, gamma=0.97)
+    assert err(adv, G - d["v"]) < 1e-12
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.3, 0.95, 1.0])
+def test_td_lambda_minus_value_is_gae(mid, lam):
+    d = mid
+    te, tr, bv, tb = _args(d)
+    adv = oracle.gae(d["r"], d["v"], te, tr, bv, tb, gamma=0.99, lam=lam)
+    ret = oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=0.99, lam=lam)
+    assert err(ret - d["v"], adv) < 1e-12
+
+
+def test_td1_is_discounted_return_and_td0_is_one_step(mid):
+    d = mid
+    te, tr, bv, tb = _args(d)
+    assert err(oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=0.99, lam=1.0),
+               oracle.discounted_returns(d["r"], te, tr, bv, tb, gamma=0.99)) < 1e-12
+    # TD(0): r_t + g * (V_{t+1} inside an episode, else the cut bootstrap)
+    got = oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=0.99, lam=0.0)
+    ref = ds.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=0.99, lam=0.0)
+    assert err(got, ref) < 1e-13
+
+
+def test_vtrace_on_policy_reduces_to_td_lambda(mid):
+    d = mid
+    te, tr, bv, tb = _args(d)
+    zero = np.zeros_like(d["r"])
+    for lam in (0.9, 1.0):
+        vs, pg = oracle.vtrace(d["r"], d["v"], zero, te, tr, bv, tb, gamma=0.99, lam=lam)
+        assert err(vs, oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=0.99, lam=lam)) < 1e-12
+    vs, _ = oracle.vtrace(d["r"], d["v"], zero, te, tr, bv, tb, gamma=0.99, lam=1.0)
+    assert err(vs, oracle.discounted_returns(d["r"], te, tr, bv, tb, gamma=0.99)) < 1e-12
+    # large positive log-ratios are clipped to rho_bar = c_bar = 1: same as on-policy
+    big = np.full_like(d["r"], 5.0)
+    vs5, pg5 = oracle.vtrace(d["r"], d["v"], big, te, tr, bv, tb, gamma=0.99, lam=1.0)
+    vs0, pg0 = oracle.vtrace(d["r"], d["v"], zero, te, tr, bv, tb, gamma=0.99, lam=1.0)
+    assert np.array_equal(vs5, vs0) and np.array_equal(pg5, pg0)
+    # vanishing importance ratios: vs -> V and pg -> 0
+    tiny = np.full_like(d["r"], -30.0)
+    vs, pg = oracle.vtrace(d["r"], d["v"], tiny, te, tr, bv, tb, gamma=0.99, lam=1.0)
+    assert err(vs, d["v"]) < 1e-10 and np.max(np.abs(pg)) < 1e-10
+
+
+def test_retrace_reductions(mid):
+    d = mid
+    te, tr, bv, tb = _args(d)
+    # lambda = 0: one-step expected-SARSA target r + g * (E_pi Q(s_{t+1}) or the cut bootstrap)
+    got = oracle.retrace(d["r"], d["q"], d["exp_q"], d["pi"], d["mu"], te, tr, bv, tb,
+                         gamma=0.99, lam=0.0)
+    ref = oracle.td_lambda(d["r"], d["exp_q"], te, tr, bv, tb, gamma=0.99, lam=0.0)
+    assert err(got, ref) < 1e-13
+    # on-policy (pi = mu), lambda = 1 and E_pi Q = Q: the discounted return
+    got = oracle.retrace(d["r"], d["q"], d["q"], d["pi"], d["pi"], te, tr, bv, tb,
+                         gamma=0.99, lam=1.0)
+    assert err(got, oracle.discounted_returns(d["r"], te, tr, bv, tb, gamma=0.99)) < 1e-12
+
+
+def test_episode_isolation_in_oracle(mid):
+    """Changing the inputs of one episode leaves every other step's output unchanged."""
+    d = {k: v.copy() for k, v in mid.items()}
+    te, tr, bv, tb = _args(d)
+    e = 3
+    te[e, :] = 0
+    tr[e, :] = 0
+    te[e, 20] = 1
+    base = oracle.gae(d["r"], d["v"], te, tr, bv, tb)
+    base_tr = oracle.eligibility_traces(d["r"], te, tr)
+    d["r"][e, :21] += 10.0    # rewards of the first episode only
+    d["v"][e, 1:21] -= 3.0    # its values (V_0 is read only by step 0 itself)
+    after = oracle.gae(d["r"], d["v"], te, tr, bv, tb)
+    after_tr = oracle.eligibility_traces(d["r"], te, tr)
+    assert np.array_equal(base[e, 21:], after[e, 21:])
+    assert np.array_equal(base_tr[e, 21:], after_tr[e, 21:])
+    mask = np.ones(base.shape[0], bool)
+    mask[e] = False
+    assert np.array_equal(base[mask], after[mask])
+
+
+# ------------------------------------------------------------------ scan operator algebra
+def oplus(outer, inner):
+    """(a_o, b_o) (+) (a_i, b_i): the affine map x -> a_o (a_i x + b_i) + b_o.
+
+    The outer element is the one further from the carry (earlier in time for the
+    backward recurrence): x_t = a_t x_{t+1} + b_t.
+    """
+    return (outer[0] * inner[0], outer[1] + outer[0] * inner[1])
+
+
+IDENT = (Fraction(1), Fraction(0))
+
+
+def _rand_pair(rng):
+    return (Fraction(rng.randint(-50, 50), rng.randint(1, 20)),
+            Fraction(rng.randint(-50, 50), rng.randint(1, 20)))
+
+
+def test_oplus_associative_exact():
+    rng = random.Random(0)
+    for _ in range(2000):
+        x, y, z = (_rand_pair(rng) for _ in range(3))
+        assert oplus(oplus(x, y), z) == oplus(x, oplus(y, z))
+
+
+def test_oplus_identity_and_noncommutative():
+    rng = random.Random(1)
+    for _ in range(200):
+        x = _rand_pair(rng)
+        assert oplus(x, IDENT) == x and oplus(IDENT, x) == x
+    a, b = (Fraction(2), Fraction(1)), (Fraction(3), Fraction(1))
+    assert oplus(a, b) == (6, 3) and oplus(b, a) == (6, 4)
+
+
+def _all_folds(seq):
+    if len(seq) == 1:
+        yield seq[0]
+        return
+    for k in range(1, len(seq)):
+        for left in _all_folds(seq[:k]):
+            for right in _all_folds(seq[k:]):
+                yield oplus(left, right)
+
+
+def test_every_parenthesization_agrees():
+    rng = random.Random(2)
+    seq = [_rand_pair(rng) for _ in range(8)]
+    results = set(_all_folds(seq))
+    assert len(results) == 1
+
+
+def _Fr(x):
+    return Fraction(float(x))
+
+
+def _fold_reverse(pairs, carry=Fraction(0)):
+    """x_t for all t by composing (a_t, b_t) from the window end: exact rationals."""
+    T = len(pairs)
+    out = [None] * T
+    acc = IDENT
+    for t in range(T - 1, -1, -1):
+        acc = oplus(pairs[t], acc)
+        out[t] = acc[0] * carry + acc[1]
+    return out
+
+
+def _fold_forward(pairs, carry=Fraction(0)):
+    T = len(pairs)
+    out = [None] * T
+    acc = IDENT
+    for t in range(T):
+        acc = oplus(pairs[t], acc)
+        out[t] = acc[0] * carry + acc[1]
+    return out
+
+
+def _kinds(te, tr, T):
+    return ds._kinds(te, tr, T)
+
+
+def _boot(kind, j, bv, tb):
+    return _Fr(ds._boot(kind, j, bv, tb))
+
+
+def test_coefficient_fold_equals_estimators():
+    """Each estimator is the affine scan of its on-chip (a_t, b_t) pairs.
+
+    The pairs below are the ones the GPU kernels build (with kappa_t = 1 for a
+    plain continuation, 0 at a cut, and nu_t the successor value); folding them
+    with (+) in exact rationals must give the oracle's recursion.
+    """
+    d = rand_inputs(10, 23, seed=31, p=0.15)
+    E, T = d["r"].shape
+    g, l = _Fr(np.float32(0.99)), _Fr(np.float32(0.95))
+    rb, cb = _Fr(np.float32(1.0)), _Fr(np.float32(0.8))
+    te, tr = d["terminated"], d["truncated"]
+    refs = {
+        "dr": oracle.discounted_returns(d["r"], te, tr, d["bootstrap_value"], d["trunc_bootstrap"]),
+        "td": oracle.td_lambda(d["r"], d["v"], te, tr, d["bootstrap_value"], d["trunc_bootstrap"]),
+        "gae": oracle.gae(d["r"], d["v"], te, tr, d["bootstrap_value"], d["trunc_bootstrap"]),
+        "vt": oracle.vtrace(d["r"], d["v"], d["log_rhos"], te, tr, d["bootstrap_value"],
+                            d["trunc_bootstrap"], lam=0.95, c_bar=0.8),
+        "rt": oracle.retrace(d["r"], d["q"], d["exp_q"], d["pi"], d["mu"], te, tr,
+                             d["bootstrap_value"], d["trunc_bootstrap"]),
+        "el": oracle.eligibility_traces(d["r"], te, tr, d["bootstrap_value"]),
+        "ps": oracle.episodic_prefix_sum(d["r"], te, tr, d["bootstrap_value"]),
+    }
+    for e in range(E):
+        r = [_Fr(x) for x in d["r"][e]]
+        v = [_Fr(x) for x in d["v"][e]]
+        q = [_Fr(x) for x in d["q"][e]]
+        eq = [_Fr(x) for x in d["exp_q"][e]]
+        bv = float(d["bootstrap_value"][e])
+        tb = [float(x) for x in d["trunc_bootstrap"][e]]
+        kinds = _kinds(te[e], tr[e], T)
+        kap = [Fraction(1 if k == ds.CONT else 0) for k in kinds]
+
+        def nu(t, nxt):
+            return nxt[t + 1] if kinds[t] == ds.CONT else _boot(kinds[t], t, bv, tb)
+
+        dr = [(g * kap[t], r[t] + g * (1 - kap[t]) * _boot(kinds[t], t, bv, tb)) for t in range(T)]
+        td = [(g * l * kap[t], r[t] + g * (1 - l * kap[t]) * nu(t, v)) for t in range(T)]
+        ga = [(g * l * kap[t], r[t] + g * nu(t, v) - v[t]) for t in range(T)]
+        ratio = [_Fr(math.exp(float(x))) for x in d["log_rhos"][e]]
+        rho = [min(rb, x) for x in ratio]
+        c = [l * min(cb, x) for x in ratio]
+        vt = [(g * c[t] * kap[t], rho[t] * (r[t] + g * nu(t, v) - v[t])) for t in range(T)]
+        cr = [l * min(Fraction(1), _Fr(d["pi"][e, t]) / _Fr(d["mu"][e, t])) for t in range(T)]
+        rt = [(g * kap[t] * (cr[t + 1] if kinds[t] == ds.CONT else 0), r[t] + g * nu(t, eq) - q[t])
+              for t in range(T)]
+        done = [bool(te[e, t] or tr[e, t]) for t in range(T)]
+        keep = [Fraction(1) if t == 0 else Fraction(0 if done[t - 1] else 1) for t in range(T)]
+        el = [(g * l * keep[t], r[t]) for t in range(T)]
+        ps = [(keep[t], r[t]) for t in range(T)]
+
+        checks = [
+            ("dr", _fold_reverse(dr), 0),
+            ("td", _fold_reverse(td), 0),
+            ("gae", _fold_reverse(ga), 0),
+            ("vt", [x + v[t] for t, x in enumerate(_fold_reverse(vt))], 0),
+            ("rt", [x + q[t] for t, x in enumerate(_fold_reverse(rt))], 0),
+            ("el", _fold_forward(el, _Fr(bv)), 0),
+            ("ps", _fold_forward(ps, _Fr(bv)), 0),
+        ]
+        for name, vals, _ in checks:
+            ref = refs[name][0][e] if name == "vt" else refs[name][e]
+            got = np.array([float(x) for x in vals])
+            assert err(got, ref) < 1e-13, name
