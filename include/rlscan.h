@@ -1,0 +1,185 @@
+/*
+ * rlscan.h -- C ABI of librlscan: RL credit-assignment estimators on MI355X
+ * (gfx950) as one-pass affine scans.
+ *
+ * Every estimator below is the first-order linear recurrence
+ *     x_t = a_t * x_{t+1} + b_t            (backward in time)
+ * or its forward-time mirror  x_t = a_t * x_{t-1} + b_t, with the per-step
+ * coefficients (a_t, b_t) built on-chip from the raw rollout inputs and the
+ * recurrence solved by an associative scan over (a, b) pairs.  Source: rl-triton
+ * (arxivlens.com paper view), Abstract; gist.science summary of rl-triton,
+ * "Technische Samenvatting" > "Methodologie" section 1 (Unified Algebraic
+ * Framework: the recurrence and the pair operator) and section 2 (Fused
+ * kernels: coefficients built in registers, one HBM read and one HBM write).
+ * The pages name the estimators but give no per-estimator formula; each
+ * function names the published definition it computes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout      All [E,T] arrays are row-major and contiguous: row e is
+ *             environment e, column t is time step t, element (e,t) sits at
+ *             index e*T + t.  [E] arrays hold one value per row.
+ * Memory      Every array pointer is a DEVICE pointer (memory the GPU can
+ *             read/write, e.g. from hipMalloc or a torch CUDA tensor).  float
+ *             pointers must be 4-byte aligned.  The caller owns and allocates
+ *             every buffer; the library allocates nothing, keeps no state
+ *             between calls and is safe to call from several host threads.
+ * Types       Values are IEEE float32; flags are uint8 with nonzero = true.
+ *             The scan runs in float64 on-chip and each output is rounded
+ *             once to float32 (round to nearest).
+ * Flags       terminated[e,t] / truncated[e,t] describe transition t (the same
+ *             index as reward t).  Terminated: the successor state's value is
+ *             0.  Truncated: the successor's value is trunc_bootstrap[e,t].  If
+ *             both are set, terminated wins.  At the window end t = T-1 of a
+ *             step that is neither, the successor's value is
+ *             bootstrap_value[e].  The bootstrap always enters the local term
+ *             b_t of the cut step and the scan carry beyond the window is 0,
+ *             so nothing is counted twice (gist.science summary, "Methodologie"
+ *             section 3, Explicit boundary semantics: termination vs
+ *             truncation, rollout windows).
+ * Optional    A NULL terminated/truncated array means "no such flags" and is
+ *             not read.  A NULL bootstrap_value, trunc_bootstrap, init or carry
+ *             means zeros.  Outputs documented as optional may be NULL.
+ * Streams     Each call validates its arguments on the host, then enqueues ONE
+ *             kernel on `stream` (NULL = the default stream) and returns; it
+ *             never synchronises.  Outputs are valid once the stream has
+ *             reached that point.
+ * Errors      Validation happens before any HIP call and returns:
+ *               RLSCAN_ERR_SHAPE  E < 0, T < 0, or E*T overflows int64;
+ *               RLSCAN_ERR_PARAM  a parameter is non-finite or out of range;
+ *               RLSCAN_ERR_NULL   a required pointer is NULL while E*T > 0;
+ *               RLSCAN_ERR_ALIGN  a float pointer is not 4-byte aligned;
+ *               RLSCAN_ERR_ALIAS  an output range overlaps an input range or
+ *                                 another output range;
+ *             E*T == 0 (after shape/parameter checks) is a no-op returning
+ *             RLSCAN_OK.  A failed launch returns RLSCAN_ERR_HIP.
+ *             Non-finite input values are outside the contract.
+ */
+#ifndef RLSCAN_H
+#define RLSCAN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rlscan_status {
+  RLSCAN_OK = 0,
+  RLSCAN_ERR_NULL = 1,
+  RLSCAN_ERR_SHAPE = 2,
+  RLSCAN_ERR_PARAM = 3,
+  RLSCAN_ERR_HIP = 4,
+  RLSCAN_ERR_ALIGN = 5,
+  RLSCAN_ERR_ALIAS = 6
+} rlscan_status;
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *rlscan_status_string(rlscan_status status);
+
+/* Static version string, e.g. "librlscan 0.1.0 gfx950". */
+const char *rlscan_version(void);
+
+/* Discounted return (Monte-Carlo return with bootstrap at cuts):
+ *   G_t = r_t + gamma * (G_{t+1} while the episode continues, else the
+ *         successor value of the cut).
+ * Recurrence: a_t = gamma*k_t, b_t = r_t + gamma*(1-k_t)*boot_t, with k_t = 1
+ * for a plain continuation and 0 at a cut.
+ * In:  rewards [E,T]; terminated, truncated [E,T] (optional);
+ *      bootstrap_value [E] (optional); trunc_bootstrap [E,T] (optional, read
+ *      only where a step is truncated and not terminated).
+ * Out: returns [E,T] (required).
+ * gamma in [0,1]. */
+rlscan_status rlscan_discounted_returns(const float *rewards, const uint8_t *terminated,
+                                        const uint8_t *truncated, const float *bootstrap_value,
+                                        const float *trunc_bootstrap, float *returns, int64_t E,
+                                        int64_t T, float gamma, hipStream_t stream);
+
+/* TD(lambda) return, recursive lambda-return (Sutton & Barto 2018, ch. 12):
+ *   G_t = r_t + gamma * ((1-lambda) V_{t+1} + lambda G_{t+1})  while continuing,
+ *   G_t = r_t + gamma * boot_t                                  at a cut.
+ * In:  rewards, values [E,T]; flags, bootstraps as for discounted returns.
+ * Out: returns [E,T] (required).  gamma, lambda in [0,1]. */
+rlscan_status rlscan_td_lambda(const float *rewards, const float *values,
+                               const uint8_t *terminated, const uint8_t *truncated,
+                               const float *bootstrap_value, const float *trunc_bootstrap,
+                               float *returns, int64_t E, int64_t T, float gamma, float lambda,
+                               hipStream_t stream);
+
+/* Generalized Advantage Estimation (Schulman et al. 2016):
+ *   delta_t = r_t + gamma * nu_t - V_t, nu_t = V_{t+1} while continuing, else
+ *             the cut's successor value;
+ *   A_t = delta_t + gamma*lambda*A_{t+1} (the A_{t+1} term only while continuing).
+ * Out: advantages [E,T] (required); returns [E,T] = A + V (optional, NULL =
+ * not written).  gamma, lambda in [0,1]. */
+rlscan_status rlscan_gae(const float *rewards, const float *values, const uint8_t *terminated,
+                         const uint8_t *truncated, const float *bootstrap_value,
+                         const float *trunc_bootstrap, float *advantages, float *returns,
+                         int64_t E, int64_t T, float gamma, float lambda, hipStream_t stream);
+
+/* V-trace (Espeholt et al. 2018, IMPALA, eq. 1 with lambda-weighted traces):
+ *   ratio_t = exp(log_rhos_t), rho_t = min(rho_bar, ratio_t),
+ *   c_t = lambda * min(c_bar, ratio_t),
+ *   delta_t = rho_t (r_t + gamma nu_t - V_t),
+ *   vs_t - V_t = delta_t + gamma c_t (vs_{t+1} - V_{t+1})  while continuing;
+ *   pg_t = rho_t (r_t + gamma * (vs_{t+1} while continuing, else the cut's
+ *          successor value) - V_t).
+ * In:  rewards, values, log_rhos = log(pi/mu) [E,T]; flags and bootstraps as
+ *      above.
+ * Out: vs [E,T] (required); pg_advantages [E,T] (optional).
+ * gamma, lambda in [0,1] (lambda = 1 is plain IMPALA); rho_bar, c_bar finite
+ * and > 0. */
+rlscan_status rlscan_vtrace(const float *rewards, const float *values, const float *log_rhos,
+                            const uint8_t *terminated, const uint8_t *truncated,
+                            const float *bootstrap_value, const float *trunc_bootstrap,
+                            float *vs, float *pg_advantages, int64_t E, int64_t T, float gamma,
+                            float lambda, float rho_bar, float c_bar, hipStream_t stream);
+
+/* Retrace(lambda) (Munos et al. 2016):
+ *   c_{t+1} = lambda * min(1, pi_{t+1} / mu_{t+1}),
+ *   Qret_t = r_t + gamma * (EQ_{t+1} + c_{t+1} (Qret_{t+1} - Q_{t+1}))  while continuing,
+ *   Qret_t = r_t + gamma * boot_t                                       at a cut.
+ * In:  rewards; q_values = Q(s_t, a_t); expected_q = E_pi Q(s_t, .);
+ *      pi_prob / mu_prob = target / behaviour probability of a_t (> 0) [E,T];
+ *      bootstrap_value [E] = E_pi Q(s_T, .) (optional); flags, trunc_bootstrap
+ *      as above.
+ * Out: q_ret [E,T] (required).  gamma, lambda in [0,1]. */
+rlscan_status rlscan_retrace(const float *rewards, const float *q_values, const float *expected_q,
+                             const float *pi_prob, const float *mu_prob, const uint8_t *terminated,
+                             const uint8_t *truncated, const float *bootstrap_value,
+                             const float *trunc_bootstrap, float *q_ret, int64_t E, int64_t T,
+                             float gamma, float lambda, hipStream_t stream);
+
+/* Accumulating eligibility trace, forward in time (the forward-time mirror of
+ * the recurrence in the gist.science summary, "Methodologie" section 1):
+ *   e_t = gamma*lambda * e_{t-1} + x_t, e_{-1} = init[e] (NULL -> 0), and the
+ *   trace restarts from 0 after any step that terminated or was truncated.
+ * Out: traces [E,T] (required).  gamma, lambda in [0,1]. */
+rlscan_status rlscan_eligibility_traces(const float *x, const uint8_t *terminated,
+                                        const uint8_t *truncated, const float *init, float *traces,
+                                        int64_t E, int64_t T, float gamma, float lambda,
+                                        hipStream_t stream);
+
+/* Episodic inclusive prefix sum, forward in time:
+ *   S_t = S_{t-1} + x_t, S_{-1} = init[e] (NULL -> 0), restarting from 0 after
+ *   any step that terminated or was truncated.
+ * Out: sums [E,T] (required). */
+rlscan_status rlscan_episodic_prefix_sum(const float *x, const uint8_t *terminated,
+                                         const uint8_t *truncated, const float *init, float *sums,
+                                         int64_t E, int64_t T, hipStream_t stream);
+
+/* The generic recurrence itself (gist.science summary, "Methodologie"
+ * section 1), with caller-supplied coefficients and no flags:
+ *   reverse != 0:  x_t = a_t x_{t+1} + b_t,  x_T    = carry[e]
+ *   reverse == 0:  x_t = a_t x_{t-1} + b_t,  x_{-1} = carry[e]
+ * In:  a, b [E,T] (required); carry [E] (optional, NULL -> 0).
+ * Out: x [E,T] (required). */
+rlscan_status rlscan_linear_scan(const float *a, const float *b, const float *carry, float *x,
+                                 int64_t E, int64_t T, int reverse, hipStream_t stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* RLSCAN_H */

@@ -1,1 +1,306 @@
-"""MI355X-native RL credit-assignment scans (binding is added with the HIP library)."""
+"""RL credit-assignment estimators as one-pass affine scans on MI355X (gfx950).
+
+Thin binding over the C ABI of ``librlscan.so`` (declared in include/rlscan.h).
+Every function here only checks and marshals torch tensors (device, dtype,
+contiguity, shape) and calls the matching ``rlscan_*`` entry point on the
+current HIP stream; all arithmetic runs in the library's HIP kernels.  There is
+no fallback: if the library is not built or cannot be loaded, every call raises.
+
+Estimators (rl-triton, arxivlens.com paper view, Abstract): discounted returns,
+TD(lambda) returns, GAE, V-trace, Retrace(lambda), eligibility traces and
+episodic prefix sums, plus the generic recurrence ``linear_scan``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "RlscanError", "lib", "library_path", "version",
+    "discounted_returns", "td_lambda", "gae", "vtrace", "retrace",
+    "eligibility_traces", "episodic_prefix_sum", "linear_scan",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librlscan.so")
+_lock = threading.Lock()
+_lib = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_int = ctypes.c_int
+
+# Argument types of every entry point, in include/rlscan.h order.
+_SIGNATURES = {
+    "rlscan_discounted_returns": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+    "rlscan_td_lambda": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _vp],
+    "rlscan_gae": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _vp],
+    "rlscan_vtrace": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _f32, _f32, _vp],
+    "rlscan_retrace": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _vp],
+    "rlscan_eligibility_traces": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _vp],
+    "rlscan_episodic_prefix_sum": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp],
+    "rlscan_linear_scan": [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp],
+}
+
+
+class RlscanError(RuntimeError):
+    """A librlscan call returned a non-OK status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, _status_string(status), status))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librlscan.so with argument types set (raises if not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                "librlscan.so is not built (%s); build it with "
+                "`python -m linear_recurrence_scan_reverse_amd.build`" % _LIB_PATH)
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        handle.rlscan_status_string.argtypes = [ctypes.c_int]
+        handle.rlscan_status_string.restype = ctypes.c_char_p
+        handle.rlscan_version.argtypes = []
+        handle.rlscan_version.restype = ctypes.c_char_p
+        _lib = handle
+        return handle
+
+
+def _status_string(status: int) -> str:
+    return lib().rlscan_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().rlscan_version().decode()
+
+
+# ----------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _rows(x, name):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.dim() != 2:
+        raise ValueError("%s must be [E, T], got shape %s" % (name, tuple(x.shape)))
+    return x
+
+
+def _check_f32(x, name, shape, device):
+    torch = _torch()
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, x.dtype))
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(x.shape)))
+    if x.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, x.device, device))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return x
+
+
+def _check_flags(x, name, shape, device):
+    torch = _torch()
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.dtype == torch.bool:
+        x = x.view(torch.uint8)
+    if x.dtype != torch.uint8:
+        raise TypeError("%s must be uint8 or bool, got %s" % (name, x.dtype))
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(x.shape)))
+    if x.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, x.device, device))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return x
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def _stream(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _out(x, name, shape, device):
+    torch = _torch()
+    if x is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    return _check_f32(x, name, shape, device)
+
+
+def _call(fname, *args):
+    st = getattr(lib(), fname)(*args)
+    if st != 0:
+        raise RlscanError(st, fname)
+
+
+def _prep(primary, name):
+    x = _rows(primary, name)
+    if x.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device, got %s" % (name, x.device))
+    return x.shape, x.device
+
+
+# ----------------------------------------------------------------- estimators
+def discounted_returns(rewards, terminated=None, truncated=None, bootstrap_value=None,
+                       trunc_bootstrap=None, *, gamma=0.99, out=None, stream=None):
+    """Discounted returns G_t = r_t + gamma * G_{t+1}, cut and bootstrapped at episode ends."""
+    shape, dev = _prep(rewards, "rewards")
+    E, T = shape
+    r = _check_f32(rewards, "rewards", shape, dev)
+    te = _check_flags(terminated, "terminated", shape, dev)
+    tr = _check_flags(truncated, "truncated", shape, dev)
+    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
+    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
+    out = _out(out, "out", shape, dev)
+    _call("rlscan_discounted_returns", _ptr(r), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(out),
+          E, T, float(gamma), _stream(dev, stream))
+    return out
+
+
+def td_lambda(rewards, values, terminated=None, truncated=None, bootstrap_value=None,
+              trunc_bootstrap=None, *, gamma=0.99, lam=0.95, out=None, stream=None):
+    """TD(lambda) returns (recursive lambda-return)."""
+    shape, dev = _prep(rewards, "rewards")
+    E, T = shape
+    r = _check_f32(rewards, "rewards", shape, dev)
+    v = _check_f32(values, "values", shape, dev)
+    te = _check_flags(terminated, "terminated", shape, dev)
+    tr = _check_flags(truncated, "truncated", shape, dev)
+    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
+    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
+    out = _out(out, "out", shape, dev)
+    _call("rlscan_td_lambda", _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(out),
+          E, T, float(gamma), float(lam), _stream(dev, stream))
+    return out
+
+
+def gae(rewards, values, terminated=None, truncated=None, bootstrap_value=None,
+        trunc_bootstrap=None, *, gamma=0.99, lam=0.95, with_returns=False, advantages=None,
+        returns=None, stream=None):
+    """Generalized advantage estimates; with_returns=True also returns A + V."""
+    shape, dev = _prep(rewards, "rewards")
+    E, T = shape
+    r = _check_f32(rewards, "rewards", shape, dev)
+    v = _check_f32(values, "values", shape, dev)
+    te = _check_flags(terminated, "terminated", shape, dev)
+    tr = _check_flags(truncated, "truncated", shape, dev)
+    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
+    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
+    adv = _out(advantages, "advantages", shape, dev)
+    ret = _out(returns, "returns", shape, dev) if (with_returns or returns is not None) else None
+    _call("rlscan_gae", _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(adv), _ptr(ret),
+          E, T, float(gamma), float(lam), _stream(dev, stream))
+    return (adv, ret) if ret is not None else adv
+
+
+def vtrace(rewards, values, log_rhos, terminated=None, truncated=None, bootstrap_value=None,
+           trunc_bootstrap=None, *, gamma=0.99, lam=1.0, rho_bar=1.0, c_bar=1.0, with_pg=True,
+           vs=None, pg_advantages=None, stream=None):
+    """V-trace targets vs (and policy-gradient advantages when with_pg)."""
+    shape, dev = _prep(rewards, "rewards")
+    E, T = shape
+    r = _check_f32(rewards, "rewards", shape, dev)
+    v = _check_f32(values, "values", shape, dev)
+    lr = _check_f32(log_rhos, "log_rhos", shape, dev)
+    te = _check_flags(terminated, "terminated", shape, dev)
+    tr = _check_flags(truncated, "truncated", shape, dev)
+    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
+    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
+    vs = _out(vs, "vs", shape, dev)
+    pg = _out(pg_advantages, "pg_advantages", shape, dev) if (with_pg or pg_advantages is not None) else None
+    _call("rlscan_vtrace", _ptr(r), _ptr(v), _ptr(lr), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb),
+          _ptr(vs), _ptr(pg), E, T, float(gamma), float(lam), float(rho_bar), float(c_bar),
+          _stream(dev, stream))
+    return (vs, pg) if pg is not None else vs
+
+
+def retrace(rewards, q_values, expected_q, pi_prob, mu_prob, terminated=None, truncated=None,
+            bootstrap_value=None, trunc_bootstrap=None, *, gamma=0.99, lam=0.95, out=None,
+            stream=None):
+    """Retrace(lambda) targets Q^ret."""
+    shape, dev = _prep(rewards, "rewards")
+    E, T = shape
+    r = _check_f32(rewards, "rewards", shape, dev)
+    q = _check_f32(q_values, "q_values", shape, dev)
+    eq = _check_f32(expected_q, "expected_q", shape, dev)
+    pi = _check_f32(pi_prob, "pi_prob", shape, dev)
+    mu = _check_f32(mu_prob, "mu_prob", shape, dev)
+    te = _check_flags(terminated, "terminated", shape, dev)
+    tr = _check_flags(truncated, "truncated", shape, dev)
+    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
+    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
+    out = _out(out, "out", shape, dev)
+    _call("rlscan_retrace", _ptr(r), _ptr(q), _ptr(eq), _ptr(pi), _ptr(mu), _ptr(te), _ptr(tr),
+          _ptr(bv), _ptr(tb), _ptr(out), E, T, float(gamma), float(lam), _stream(dev, stream))
+    return out
+
+
+def eligibility_traces(x, terminated=None, truncated=None, init=None, *, gamma=0.99, lam=0.95,
+                       out=None, stream=None):
+    """Accumulating eligibility traces of x, forward in time, reset after each episode end."""
+    shape, dev = _prep(x, "x")
+    E, T = shape
+    xx = _check_f32(x, "x", shape, dev)
+    te = _check_flags(terminated, "terminated", shape, dev)
+    tr = _check_flags(truncated, "truncated", shape, dev)
+    i0 = _check_f32(init, "init", (E,), dev)
+    out = _out(out, "out", shape, dev)
+    _call("rlscan_eligibility_traces", _ptr(xx), _ptr(te), _ptr(tr), _ptr(i0), _ptr(out), E, T,
+          float(gamma), float(lam), _stream(dev, stream))
+    return out
+
+
+def episodic_prefix_sum(x, terminated=None, truncated=None, init=None, *, out=None, stream=None):
+    """Inclusive prefix sums of x within each episode, forward in time."""
+    shape, dev = _prep(x, "x")
+    E, T = shape
+    xx = _check_f32(x, "x", shape, dev)
+    te = _check_flags(terminated, "terminated", shape, dev)
+    tr = _check_flags(truncated, "truncated", shape, dev)
+    i0 = _check_f32(init, "init", (E,), dev)
+    out = _out(out, "out", shape, dev)
+    _call("rlscan_episodic_prefix_sum", _ptr(xx), _ptr(te), _ptr(tr), _ptr(i0), _ptr(out), E, T,
+          _stream(dev, stream))
+    return out
+
+
+def linear_scan(a, b, carry=None, *, reverse=True, out=None, stream=None):
+    """The generic recurrence x_t = a_t x_{t+1} + b_t (reverse) or x_t = a_t x_{t-1} + b_t."""
+    shape, dev = _prep(a, "a")
+    E, T = shape
+    aa = _check_f32(a, "a", shape, dev)
+    bb = _check_f32(b, "b", shape, dev)
+    c0 = _check_f32(carry, "carry", (E,), dev)
+    out = _out(out, "out", shape, dev)
+    _call("rlscan_linear_scan", _ptr(aa), _ptr(bb), _ptr(c0), _ptr(out), E, T, 1 if reverse else 0,
+          _stream(dev, stream))
+    return out

@@ -1,0 +1,7 @@
+// Kernel instantiations for one estimator (compiled separately to keep
+// build times short; see rlscan_kernel.hpp for the algorithm).
+#include "rlscan_launch.hpp"
+
+namespace rlscan {
+template hipError_t launch<LinearScanReverse>(const KernelArgs&, hipStream_t);
+}  // namespace rlscan

@@ -1,0 +1,148 @@
+"""C-ABI surface of librlscan (CPU only: no kernel is ever launched here).
+
+* the library loads and exports every function include/rlscan.h declares;
+* host-side validation returns the documented status before any HIP call
+  (every call below fails validation, so no device is needed);
+* the Python binding fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import linear_recurrence_scan_reverse_amd as rl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlscan.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_HIP, ERR_ALIGN, ERR_ALIAS = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlscan_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rl.library_path()):
+        from linear_recurrence_scan_reverse_amd import build
+        build.build(verbose=False)
+    return rl.lib()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for n in ["rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_gae", "rlscan_vtrace",
+              "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum",
+              "rlscan_linear_scan", "rlscan_status_string", "rlscan_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), "librlscan.so does not export %s" % name
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in rl.version()
+    for s in range(7):
+        assert lib.rlscan_status_string(s)
+    assert lib.rlscan_status_string(99) == b"unknown status"
+
+
+# Fake, never-dereferenced device addresses (validation fails before any HIP call).
+A = 0x7F0000000000
+B = 0x7F0010000000
+C = 0x7F0020000000
+D = 0x7F0030000000
+F = 0x7F0040000000
+G = 0x7F0050000000
+S = None  # default stream
+
+
+def test_shape_errors(lib):
+    assert lib.rlscan_gae(A, B, None, None, None, None, C, None, -1, 4, 0.99, 0.95, S) == ERR_SHAPE
+    assert lib.rlscan_gae(A, B, None, None, None, None, C, None, 4, -1, 0.99, 0.95, S) == ERR_SHAPE
+    assert lib.rlscan_gae(A, B, None, None, None, None, C, None, 2 ** 40, 2 ** 40, 0.99, 0.95, S) == ERR_SHAPE
+    assert lib.rlscan_linear_scan(A, B, None, C, -3, 1, 1, S) == ERR_SHAPE
+
+
+@pytest.mark.parametrize("g,l", [(1.5, 0.9), (-0.1, 0.9), (0.9, 1.01), (math.nan, 0.5), (0.5, math.inf)])
+def test_parameter_errors(lib, g, l):
+    assert lib.rlscan_gae(A, B, None, None, None, None, C, None, 4, 4, g, l, S) == ERR_PARAM
+    assert lib.rlscan_td_lambda(A, B, None, None, None, None, C, 4, 4, g, l, S) == ERR_PARAM
+    assert lib.rlscan_eligibility_traces(A, None, None, None, C, 4, 4, g, l, S) == ERR_PARAM
+    assert lib.rlscan_retrace(A, B, C, D, F, None, None, None, None, G, 4, 4, g, l, S) == ERR_PARAM
+
+
+@pytest.mark.parametrize("rho,c", [(0.0, 1.0), (1.0, -1.0), (math.inf, 1.0), (1.0, math.nan)])
+def test_vtrace_clip_errors(lib, rho, c):
+    assert lib.rlscan_vtrace(A, B, C, None, None, None, None, D, None, 4, 4, 0.99, 1.0, rho, c, S) == ERR_PARAM
+
+
+def test_discounted_gamma_range(lib):
+    assert lib.rlscan_discounted_returns(A, None, None, None, None, C, 4, 4, 1.0001, S) == ERR_PARAM
+
+
+def test_null_required_pointers(lib):
+    assert lib.rlscan_discounted_returns(None, None, None, None, None, C, 4, 4, 0.99, S) == ERR_NULL
+    assert lib.rlscan_discounted_returns(A, None, None, None, None, None, 4, 4, 0.99, S) == ERR_NULL
+    assert lib.rlscan_td_lambda(A, None, None, None, None, None, C, 4, 4, 0.99, 0.9, S) == ERR_NULL
+    assert lib.rlscan_gae(A, B, None, None, None, None, None, None, 4, 4, 0.99, 0.95, S) == ERR_NULL
+    assert lib.rlscan_vtrace(A, B, None, None, None, None, None, D, None, 4, 4, 0.99, 1.0, 1.0, 1.0, S) == ERR_NULL
+    assert lib.rlscan_retrace(A, B, C, None, F, None, None, None, None, G, 4, 4, 0.99, 0.9, S) == ERR_NULL
+    assert lib.rlscan_eligibility_traces(None, None, None, None, C, 4, 4, 0.99, 0.9, S) == ERR_NULL
+    assert lib.rlscan_episodic_prefix_sum(A, None, None, None, None, 4, 4, S) == ERR_NULL
+    assert lib.rlscan_linear_scan(A, None, None, C, 4, 4, 1, S) == ERR_NULL
+
+
+def test_empty_shapes_are_noops(lib):
+    # E*T == 0: OK without touching any pointer (all NULL here)
+    assert lib.rlscan_gae(None, None, None, None, None, None, None, None, 0, 128, 0.99, 0.95, S) == OK
+    assert lib.rlscan_gae(None, None, None, None, None, None, None, None, 64, 0, 0.99, 0.95, S) == OK
+    assert lib.rlscan_retrace(None, None, None, None, None, None, None, None, None, None, 0, 0, 0.9, 0.9, S) == OK
+    assert lib.rlscan_episodic_prefix_sum(None, None, None, None, None, 0, 5, S) == OK
+    assert lib.rlscan_linear_scan(None, None, None, None, 3, 0, 0, S) == OK
+    # ...but shape and parameter checks still come first
+    assert lib.rlscan_gae(None, None, None, None, None, None, None, None, 0, 128, 2.0, 0.95, S) == ERR_PARAM
+
+
+def test_misaligned_float_pointers(lib):
+    assert lib.rlscan_gae(A + 2, B, None, None, None, None, C, None, 4, 4, 0.99, 0.95, S) == ERR_ALIGN
+    assert lib.rlscan_gae(A, B, None, None, None, None, C + 1, None, 4, 4, 0.99, 0.95, S) == ERR_ALIGN
+    assert lib.rlscan_gae(A, B, None, None, D + 3, None, C, None, 4, 4, 0.99, 0.95, S) == ERR_ALIGN
+    assert lib.rlscan_linear_scan(A, B, C + 2, D, 4, 4, 1, S) == ERR_ALIGN
+
+
+def test_overlapping_outputs_are_rejected(lib):
+    E, T = 8, 16
+    n = 4 * E * T
+    # output starts inside rewards
+    assert lib.rlscan_gae(A, B, None, None, None, None, A + n - 4, None, E, T, 0.99, 0.95, S) == ERR_ALIAS
+    # advantages and returns overlap each other
+    assert lib.rlscan_gae(A, B, None, None, None, None, C, C + 64, E, T, 0.99, 0.95, S) == ERR_ALIAS
+    # output overlaps a flag array (E*T bytes)
+    assert lib.rlscan_discounted_returns(A, D, None, None, None, D + E * T - 4, E, T, 0.9, S) == ERR_ALIAS
+    # output overlaps the per-row bootstrap
+    assert lib.rlscan_td_lambda(A, B, None, None, F, None, F, E, T, 0.9, 0.9, S) == ERR_ALIAS
+    assert lib.rlscan_linear_scan(A, B, None, B, E, T, 1, S) == ERR_ALIAS
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(rl, "_LIB_PATH", "/nonexistent/librlscan.so")
+    monkeypatch.setattr(rl, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        rl.lib()
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    r = torch.zeros(2, 3)
+    with pytest.raises(ValueError, match="GPU"):
+        rl.discounted_returns(r)

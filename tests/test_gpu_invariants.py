@@ -1,0 +1,165 @@
+"""GPU invariants that hold at any size (bitwise where the arithmetic allows).
+
+* run-to-run determinism (bitwise);
+* permuting env rows permutes outputs (bitwise);
+* episode isolation: changing the inputs of one episode leaves every output of
+  the other episodes bit-identical (a cut enters the scan as an exact zero);
+* chaining two windows of a forward estimator through `init` equals one call;
+* the generic recurrence: reverse scan == forward scan of flipped arrays, and
+  parity with the oracle;
+* calls on a side stream and inside a captured HIP graph (replayed several
+  times) match eager calls.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_recurrence_scan_reverse_amd import synth
+from tests.estimators import NAMES, TOL, parity_err, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(out):
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("T", [64, 256, 1000])
+def test_bitwise_determinism(T):
+    d = synth.draw(300, T, seed=21, p_term=0.01, p_trunc=0.01)
+    dd = to_dev(d)
+    for name in NAMES:
+        a = _np(run_gpu(name, dd))
+        b = _np(run_gpu(name, dd))
+        for k in a:
+            assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), (name, k)
+
+
+@pytest.mark.parametrize("T", [64, 128, 256, 777])
+def test_row_permutation_equivariance(T):
+    E = 97
+    d = synth.draw(E, T, seed=22, p_term=0.02, p_trunc=0.02)
+    perm = np.random.default_rng(5).permutation(E)
+    dp = {k: np.ascontiguousarray(v[perm]) for k, v in d.items()}
+    base = {n: _np(run_gpu(n, to_dev(d))) for n in NAMES}
+    moved = {n: _np(run_gpu(n, to_dev(dp))) for n in NAMES}
+    for n in NAMES:
+        for k in base[n]:
+            assert np.array_equal(base[n][k][perm].view(np.uint32), moved[n][k].view(np.uint32)), (n, k)
+
+
+@pytest.mark.parametrize("T,j", [(256, 100), (256, 3), (1024, 700), (64, 40)])
+def test_episode_isolation_bitwise(T, j):
+    """Row 5 terminates at step j: later inputs never reach earlier outputs and vice versa."""
+    E, e = 16, 5
+    d = synth.draw(E, T, seed=23, p_term=0.0, p_trunc=0.0)
+    d["terminated"][e, j] = 1
+    base = {n: _np(run_gpu(n, to_dev(d))) for n in NAMES}
+
+    later = {k: v.copy() for k, v in d.items()}
+    for k in ("r", "v", "log_rhos", "q", "exp_q", "trunc_bootstrap"):
+        later[k][e, j + 1:] += 3.5
+    later["pi"][e, j + 1:] *= 0.5
+    later["bootstrap_value"][e] += 2.0
+    after = {n: _np(run_gpu(n, to_dev(later))) for n in NAMES}
+    for n in NAMES:
+        for k in base[n]:
+            assert np.array_equal(base[n][k][e, :j + 1].view(np.uint32),
+                                  after[n][k][e, :j + 1].view(np.uint32)), ("later->earlier", n, k)
+            other = np.arange(E) != e
+            assert np.array_equal(base[n][k][other].view(np.uint32), after[n][k][other].view(np.uint32))
+
+    earlier = {k: v.copy() for k, v in d.items()}
+    for k in ("r", "v", "log_rhos", "q", "exp_q", "trunc_bootstrap"):
+        earlier[k][e, :j + 1] -= 1.25
+    earlier["mu"][e, :j + 1] *= 0.5
+    after = {n: _np(run_gpu(n, to_dev(earlier))) for n in NAMES}
+    for n in NAMES:
+        for k in base[n]:
+            assert np.array_equal(base[n][k][e, j + 1:].view(np.uint32),
+                                  after[n][k][e, j + 1:].view(np.uint32)), ("earlier->later", n, k)
+
+
+def test_forward_windows_chain_through_init():
+    """Two windows chained with init = last output (zeroed after a done) == one call."""
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    rng = np.random.default_rng(24)
+    E, T, T1 = 40, 600, 257
+    x = rng.integers(-20, 21, size=(E, T)).astype(np.float32)
+    term = (rng.random((E, T)) < 0.01).astype(np.uint8)
+    xd, td = torch.from_numpy(x).cuda(), torch.from_numpy(term).cuda()
+    full = rl.episodic_prefix_sum(xd, td)
+    first = rl.episodic_prefix_sum(xd[:, :T1].contiguous(), td[:, :T1].contiguous())
+    init = torch.where(td[:, T1 - 1] != 0, torch.zeros_like(first[:, -1]), first[:, -1]).contiguous()
+    second = rl.episodic_prefix_sum(xd[:, T1:].contiguous(), td[:, T1:].contiguous(), init)
+    assert torch.equal(torch.cat([first, second], 1), full)
+    tr_full = rl.eligibility_traces(xd, td, gamma=0.9, lam=0.8)
+    tr1 = rl.eligibility_traces(xd[:, :T1].contiguous(), td[:, :T1].contiguous(), gamma=0.9, lam=0.8)
+    init = torch.where(td[:, T1 - 1] != 0, torch.zeros_like(tr1[:, -1]), tr1[:, -1]).contiguous()
+    tr2 = rl.eligibility_traces(xd[:, T1:].contiguous(), td[:, T1:].contiguous(), init, gamma=0.9, lam=0.8)
+    # the chained result rounds the carry to fp32 once at the window edge
+    assert parity_err(torch.cat([tr1, tr2], 1).cpu().numpy(), tr_full.cpu().numpy()) <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 5, 64, 65, 256, 999, 4100])
+def test_generic_scan_parity_and_mirror(T):
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    rng = np.random.default_rng(25 + T)
+    E = 21
+    a = rng.uniform(-1.0, 1.0, size=(E, T)).astype(np.float32)
+    b = rng.standard_normal((E, T)).astype(np.float32)
+    c = rng.standard_normal(E).astype(np.float32)
+    ad, bd, cd = (torch.from_numpy(v).cuda() for v in (a, b, c))
+    for rev in (True, False):
+        got = rl.linear_scan(ad, bd, cd, reverse=rev).cpu().numpy()
+        assert parity_err(got, oracle.linear_scan(a, b, c, reverse=rev)) <= TOL
+    rev = rl.linear_scan(ad, bd, cd, reverse=True)
+    fwd_flipped = rl.linear_scan(ad.flip(1).contiguous(), bd.flip(1).contiguous(), cd, reverse=False)
+    assert parity_err(fwd_flipped.flip(1).cpu().numpy(), rev.cpu().numpy()) <= TOL
+
+
+def test_generic_scan_special_cases():
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    rng = np.random.default_rng(26)
+    E, T = 7, 300
+    b = torch.from_numpy(rng.standard_normal((E, T)).astype(np.float32)).cuda()
+    c = torch.from_numpy(rng.standard_normal(E).astype(np.float32)).cuda()
+    zeros, ones = torch.zeros_like(b), torch.ones_like(b)
+    for rev in (True, False):
+        assert torch.equal(rl.linear_scan(zeros, b, c, reverse=rev), b)
+        assert torch.equal(rl.linear_scan(ones, zeros, c, reverse=rev), c[:, None].expand(E, T))
+
+
+def test_side_stream_and_graph_capture():
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    d = synth.draw(512, 256, seed=27, p_term=0.01, p_trunc=0.01)
+    dd = to_dev(d)
+    eager = _np(run_gpu("gae", dd))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        side = _np(run_gpu("gae", dd))
+    torch.cuda.current_stream().wait_stream(s)
+    for k in eager:
+        assert np.array_equal(eager[k], side[k])
+
+    adv = torch.empty_like(dd["r"])
+    ret = torch.empty_like(dd["r"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rl.gae(dd["r"], dd["v"], dd["terminated"], dd["truncated"], dd["bootstrap_value"],
+               dd["trunc_bootstrap"], advantages=adv, returns=ret)
+    for rep in range(4):
+        adv.fill_(float("nan"))
+        ret.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(adv.cpu().numpy(), eager["out"]), rep
+        assert np.array_equal(ret.cpu().numpy(), eager["out1"]), rep

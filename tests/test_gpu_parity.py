@@ -1,0 +1,161 @@
+"""GPU parity: every estimator through the C ABI vs the fp64 oracle.
+
+Bar: max |gpu - oracle| / max(1, |oracle|) <= 1e-5 on every element (fp32
+outputs of a float64 on-chip scan vs the float64 sequential oracle).
+Covers the five rollout workloads at full size (the launch shapes the bench
+times), ragged and boundary row lengths, flag and NULL-input variants,
+parameter extremes and misaligned (scalar-path) rows.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+from linear_recurrence_scan_reverse_amd import synth
+from tests.estimators import NAMES, TOL, compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _assert_ok(name, res, what=""):
+    for k, (e, mx) in res.items():
+        assert e <= TOL, "%s %s %s: err %.3g (max|ref| %.3g)" % (name, k, what, e, mx)
+
+
+def _params_for(w):
+    return dict(gamma=w.gamma, lam=w.lam, vtrace_lam=w.vtrace_lam, rho_bar=w.rho_bar, c_bar=w.c_bar)
+
+
+@pytest.mark.parametrize("wname", list(synth.WORKLOADS))
+def test_workload_full_size(wname):
+    """Full-size workloads in the launch shapes the bench times."""
+    w = synth.WORKLOADS[wname]
+    _say("workload", wname, w.E, w.T)
+    d = synth.workload_inputs(w)
+    # The trace / prefix estimators take the rewards array as their signal and the
+    # per-row bootstrap array as their initial value.
+    for name in w.estimators:
+        res = compare(name, d, _params_for(w),
+                      term="terminated" in d, trunc="truncated" in d,
+                      boot="bootstrap_value" in d, tboot="trunc_bootstrap" in d)
+        _say("  ", name, {k: "%.2e" % v[0] for k, v in res.items()})
+        _assert_ok(name, res, wname)
+
+
+EDGE_T = [1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256,
+          257, 300, 511, 512, 513, 1000, 1023, 1024, 1025, 2047, 2048, 2049, 4096, 5000]
+
+
+@pytest.mark.parametrize("T", EDGE_T)
+def test_edge_lengths_all_estimators(T):
+    """Ragged tails, tile/wave/team boundaries and multi-tile rows."""
+    for E in (1, 3, 65):
+        d = synth.draw(E, T, seed=1000 + T + E, p_term=0.05, p_trunc=0.05)
+        for name in NAMES:
+            _assert_ok(name, compare(name, d), "E=%d T=%d" % (E, T))
+
+
+VARIANTS = {
+    "no_flags": dict(term=False, trunc=False),
+    "term_only": dict(trunc=False),
+    "trunc_only": dict(term=False),
+    "null_bootstraps": dict(boot=False, tboot=False),
+    "null_trunc_bootstrap": dict(tboot=False),
+}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("T", [64, 129, 256, 1024])
+def test_optional_inputs(variant, T):
+    d = synth.draw(37, T, seed=7, p_term=0.03, p_trunc=0.03)
+    for name in NAMES:
+        _assert_ok(name, compare(name, d, **VARIANTS[variant]), "%s T=%d" % (variant, T))
+
+
+@pytest.mark.parametrize("pattern", ["all_term", "all_trunc", "all_both", "dense_random"])
+def test_flag_patterns(pattern):
+    E, T = 20, 256
+    d = synth.draw(E, T, seed=11, p_term=0.5, p_trunc=0.5)
+    if pattern == "all_term":
+        d["terminated"][:] = 1
+        d["truncated"][:] = 0
+    elif pattern == "all_trunc":
+        d["terminated"][:] = 0
+        d["truncated"][:] = 1
+    elif pattern == "all_both":
+        d["terminated"][:] = 1
+        d["truncated"][:] = 1
+    for name in NAMES:
+        _assert_ok(name, compare(name, d), pattern)
+
+
+def test_nonbinary_flag_bytes():
+    """Any nonzero byte means true."""
+    d = synth.draw(9, 130, seed=12, p_term=0.1, p_trunc=0.1)
+    d2 = dict(d)
+    d2["terminated"] = (d["terminated"] * 7).astype(np.uint8)
+    d2["truncated"] = (d["truncated"] * 200).astype(np.uint8)
+    for name in NAMES:
+        _assert_ok(name, compare(name, d2), "nonbinary")
+
+
+@pytest.mark.parametrize("gamma,lam", [(0.0, 0.0), (1.0, 1.0), (0.0, 1.0), (1.0, 0.0), (0.5, 0.5)])
+def test_parameter_extremes(gamma, lam):
+    d = synth.draw(8, 300, seed=13, p_term=0.02, p_trunc=0.02)
+    P = dict(gamma=gamma, lam=lam, vtrace_lam=lam)
+    for name in NAMES:
+        _assert_ok(name, compare(name, d, P), "gamma=%g lam=%g" % (gamma, lam))
+
+
+@pytest.mark.parametrize("rho_bar,c_bar", [(1.0, 1.0), (0.5, 2.0), (3.0, 0.25)])
+def test_vtrace_clips(rho_bar, c_bar):
+    d = synth.draw(16, 256, seed=14, p_term=0.01, p_trunc=0.01, logrho_std=1.0)
+    P = dict(rho_bar=rho_bar, c_bar=c_bar, vtrace_lam=0.9)
+    _assert_ok("vtrace", compare("vtrace", d, P), "clips")
+
+
+def test_misaligned_rows_use_the_scalar_path():
+    """Tensors whose storage starts one element off a 16-byte boundary."""
+    import torch
+    from tests.estimators import run_gpu, run_oracle, parity_err
+    E, T = 33, 256
+    d = synth.draw(E, T, seed=15, p_term=0.02, p_trunc=0.02)
+    dd = {}
+    for k, v in d.items():
+        flat = torch.zeros(v.size + 1, dtype=torch.from_numpy(v).dtype, device="cuda")
+        view = flat[1:].view(v.shape)
+        view.copy_(torch.from_numpy(v))
+        dd[k] = view
+    for name in NAMES:
+        got = run_gpu(name, dd)
+        ref = run_oracle(name, d)
+        torch.cuda.synchronize()
+        for k in ref:
+            assert parity_err(got[k].cpu().numpy(), ref[k]) <= TOL, (name, k)
+
+
+def test_prefix_sum_of_integers_is_exact():
+    """Integer-valued signal with |S| < 2^24: the fp32 output is exact."""
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    import oracle
+    rng = np.random.default_rng(16)
+    E, T = 64, 1024
+    x = rng.integers(-50, 51, size=(E, T)).astype(np.float32)
+    term = (rng.random((E, T)) < 0.01).astype(np.uint8)
+    got = rl.episodic_prefix_sum(torch.from_numpy(x).cuda(), torch.from_numpy(term).cuda()).cpu().numpy()
+    ref = oracle.episodic_prefix_sum(x, term)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_large_rows_few_envs():
+    """Long rows (many tiles per row)."""
+    d = synth.draw(2, 20000, seed=17, p_term=0.001, p_trunc=0.001)
+    for name in NAMES:
+        _assert_ok(name, compare(name, d), "T=20000")
