@@ -6,32 +6,34 @@
 // or x_t = a_t x_{t-1} + b_t (forward); pairs compose associatively,
 //     outer (+) inner = (a_o a_i, b_o + a_o b_i),
 // where "inner" is the element nearer the scan's carry.  The pairs are built
-// in registers from the raw inputs and never written to memory.
+// in registers from the raw inputs and never written to memory; every input
+// element is read from HBM once and every output element written once.
 //
 // Work decomposition (ours, for 64-wide wavefronts):
-//   * A row (one environment) is owned by a team of L lanes (L = 16 or 32:
-//     several rows per wave; L = 64: one wave) or of W whole waves.
+//   * A row (one environment) is owned by a team: L = 16 or 32 lanes (several
+//     rows per wave), one wave (L = 64), or W whole waves.
 //   * The row is cut into tiles of SPAN = (lanes in team) * K steps; a lane
 //     owns K consecutive steps of a tile (one 16-byte load per input when
 //     K = 4).  Lanes are numbered in SCAN order: lane 0 holds the steps nearest
 //     the carry (the latest steps for a backward scan), so a backward suffix
-//     scan is an ordinary prefix scan over lane index, and a wave still reads
+//     scan is an ordinary prefix scan over lane index while a wave still reads
 //     one contiguous block of memory.
-//   * Per tile: (1) each lane folds its K pairs serially; (2) a log2(L)-step
-//     DPP prefix scan over lanes (row_shr 1,2,4,8, row_bcast 15, row_bcast 31);
-//     (3) with W > 1 waves, the wave totals go through LDS and every wave
-//     applies the totals of the waves nearer the carry; (4) each lane takes
-//     its incoming value from its lower neighbour (DPP wave_shr 1) and
-//     re-walks its K steps; (5) the epilogue forms the outputs and stores them.
-//     Tiles are visited from the carry side, the running value crossing tiles
-//     in registers.
-//   * Neighbour-step inputs (V_{t+1}, EQ_{t+1} and c_{t+1}, or the previous
-//     step's done flag) come from the adjacent lane by DPP; a lane whose
-//     neighbour sits in another team/tile reloads that one element (an L1/L2
-//     hit: the neighbouring lane's load brought in the line).
+//   * Per tile ("item"): (1) each lane folds its K pairs serially; (2) a
+//     log2(L)-step DPP prefix scan over lanes (row_shr 1,2,4,8, row_bcast 15,
+//     row_bcast 31); (3) with W > 1 waves, wave totals meet in LDS; (4) each
+//     lane takes its incoming value from its lower neighbour (DPP wave_shr 1)
+//     and re-walks its K steps; (5) the epilogue forms the outputs and stores
+//     them once.  The running value crosses tiles of a row in registers.
+//   * Teams are persistent: each walks a sequence of items (the tiles of its
+//     rows, in scan order) as a software pipeline -- flags are loaded two
+//     items ahead, inputs one item ahead, and the gather of truncation
+//     bootstraps (whose addresses depend on the flags) one item ahead, so
+//     HBM latency overlaps the scan of the current item.  Every load is
+//     branch-free: out-of-range elements read a clamped in-row address and
+//     are masked in registers, so the compiler can count outstanding loads
+//     exactly.
 // All scan arithmetic is float64; inputs are float32 and each output is
-// rounded once.  Each input element is read from HBM once and each output
-// written once.
+// rounded once.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,20 +42,23 @@
 namespace rlscan {
 
 // ----------------------------------------------------------------- arguments
+// Optional inputs are resolved on the host: a pointer below is never NULL when
+// the kernel dereferences it; the has_* switches say whether its values count.
 struct KernelArgs {
   const float* r;       // rewards; signal x (traces, prefix sums); a (generic scan)
   const float* v;       // values V; Q(s_t, a_t) (Retrace); b (generic scan)
   const float* aux;     // log_rhos (V-trace); E_pi Q(s_t, .) (Retrace)
   const float* pi;      // target-policy probability of a_t (Retrace)
   const float* mu;      // behaviour-policy probability of a_t (Retrace)
-  const uint8_t* term;  // terminated flags, NULL = none
-  const uint8_t* trunc; // truncated flags, NULL = none
-  const float* row;     // [E]: bootstrap_value, init or carry; NULL = zeros
-  const float* tboot;   // [E,T] successor value at truncated steps; NULL = zeros
+  const uint8_t* term;  // terminated flags (aliases `trunc` when absent)
+  const uint8_t* trunc; // truncated flags (aliases `term` when absent)
+  const float* row;     // [E]: bootstrap_value, init or carry (aliases r when absent)
+  const float* tboot;   // [E,T] successor value at truncated steps (aliases r when absent)
   float* out0;          // main output
-  float* out1;          // second output (GAE returns, V-trace pg), NULL = none
+  float* out1;          // second output (GAE returns, V-trace pg); NULL = none
   int64_t E, T;
   double gamma, lam, rho_bar, c_bar;
+  int has_term, has_trunc, has_row, has_tboot;
 };
 
 // Estimator tags (also make the kernel names readable in profiles).
@@ -73,15 +78,16 @@ template <class Est> struct Traits {
       __is_same(Est, Vtrace) || __is_same(Est, Retrace);
   static constexpr bool kForwardRl = __is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum);
   static constexpr bool kLinear = __is_same(Est, LinearScanReverse) || __is_same(Est, LinearScanForward);
-  static constexpr bool kUsesV = __is_same(Est, TdLambda) || __is_same(Est, Gae) ||
-                                 __is_same(Est, Vtrace) || __is_same(Est, Retrace) || kLinear;
-  static constexpr bool kUsesAux = __is_same(Est, Vtrace) || __is_same(Est, Retrace);
-  static constexpr bool kUsesPiMu = __is_same(Est, Retrace);
+  static constexpr bool kRetrace = __is_same(Est, Retrace);
+  static constexpr bool kVtrace = __is_same(Est, Vtrace);
+  // float input streams: 0 = r, 1 = v/q/b, 2 = aux, 3 = pi, 4 = mu
+  static constexpr int kStreams = kRetrace ? 5 : kVtrace ? 3
+                                  : (__is_same(Est, TdLambda) || __is_same(Est, Gae) || kLinear) ? 2 : 1;
   static constexpr bool kUsesFlags = kBackwardRl || kForwardRl;
-  // Does step t need a value carried by its scan-predecessor (t+1 backward, t-1 forward)?
-  static constexpr bool kNeedsNbValue = __is_same(Est, TdLambda) || __is_same(Est, Gae) ||
-                                        __is_same(Est, Vtrace) || __is_same(Est, Retrace);
-  static constexpr bool kNeedsNbDone = kForwardRl;
+  // value handed from a step to its scan-successor: V (TD, GAE, V-trace), EQ and c (Retrace)
+  static constexpr bool kNbValue = __is_same(Est, TdLambda) || __is_same(Est, Gae) || kVtrace || kRetrace;
+  static constexpr bool kNbDone = kForwardRl;  // the previous step's done flag
+  static constexpr bool kHasOut1 = __is_same(Est, Gae) || kVtrace;
 };
 
 template <int W> struct BlockShape { static constexpr int kThreads = (W > 4 ? 64 * W : 256); };
@@ -113,11 +119,33 @@ __device__ __forceinline__ double dpp_f64(double old, double src) {
   return __builtin_bit_cast(double, ((unsigned long long)(unsigned)hi << 32) | (unsigned long long)(unsigned)lo);
 }
 
+// 32-bit DPP move whose source-less lanes read 0 (bound_ctrl), so no `old`
+// value has to be materialised; valid only with every row enabled.
+template <int CTRL>
+__device__ __forceinline__ int dpp_zero(int src) {
+  return __builtin_amdgcn_update_dpp(0, src, CTRL, 0xf, 0xf, true);
+}
+
+// The pair of lane (i - shift) or the identity element (1, 0) where the source
+// lane is missing (or its row masked off).  Words of the identity that are 0
+// come from bound_ctrl's zero fill; only the high word of a = 1.0 needs `old`.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ AB dpp_ab(const AB& v) {
   AB r;
-  r.a = dpp_f64<CTRL, ROW_MASK>(1.0, v.a);  // identity element (1, 0) where no source
-  r.b = dpp_f64<CTRL, ROW_MASK>(0.0, v.b);
+  if constexpr (ROW_MASK == 0xf) {
+    const unsigned long long ua = __builtin_bit_cast(unsigned long long, v.a);
+    const unsigned long long ub = __builtin_bit_cast(unsigned long long, v.b);
+    const unsigned alo = (unsigned)dpp_zero<CTRL>((int)(unsigned)ua);
+    const unsigned ahi = (unsigned)__builtin_amdgcn_update_dpp((int)0x3ff00000, (int)(unsigned)(ua >> 32), CTRL,
+                                                               0xf, 0xf, false);
+    const unsigned blo = (unsigned)dpp_zero<CTRL>((int)(unsigned)ub);
+    const unsigned bhi = (unsigned)dpp_zero<CTRL>((int)(unsigned)(ub >> 32));
+    r.a = __builtin_bit_cast(double, ((unsigned long long)ahi << 32) | alo);
+    r.b = __builtin_bit_cast(double, ((unsigned long long)bhi << 32) | blo);
+  } else {
+    r.a = dpp_f64<CTRL, ROW_MASK>(1.0, v.a);
+    r.b = dpp_f64<CTRL, ROW_MASK>(0.0, v.b);
+  }
   return r;
 }
 
@@ -141,8 +169,8 @@ __device__ __forceinline__ double shift_up_f64(double v) { return dpp_f64<0x138,
 __device__ __forceinline__ float shift_up_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x138, 0xf, 0xf, false));
 }
-__device__ __forceinline__ int shift_up_i32(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, 0x138, 0xf, 0xf, false);
+__device__ __forceinline__ unsigned shift_up_u32(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xf, 0xf, false);
 }
 
 // Broadcast of lane (group start + L - 1) to the group.
@@ -158,85 +186,369 @@ __device__ __forceinline__ double group_last_f64(double v, int lane) {
   }
 }
 
-// ----------------------------------------------------------------- loads / stores
+// ----------------------------------------------------------------- streaming loads / stores
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Every [E,T] array is addressed as (wave-uniform base pointer) + (32-bit lane
+// offset in elements); all arrays share one layout, so one offset register
+// serves every stream and the loads use the scalar-base addressing mode.
+
+// base + off elements, formed as a 32-bit byte offset so the compiler can use
+// the scalar-base + 32-bit vector-offset addressing mode.
+__device__ __forceinline__ const float* at(const float* base, uint32_t off) {
+  return reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + (uint32_t)(off * 4u));
+}
+__device__ __forceinline__ float* at(float* base, uint32_t off) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(base) + (uint32_t)(off * 4u));
+}
+__device__ __forceinline__ const uint8_t* at(const uint8_t* base, uint32_t off) { return base + off; }
+
+// K consecutive floats at base[off].  VEC: one aligned vector load (the whole
+// chunk lies inside its row); otherwise each element is read at its column
+// clamped into the row (`last` = offset of the row's last element), so the
+// address is always valid.
 template <int K, bool VEC>
-__device__ __forceinline__ void load_f32(const float* __restrict__ p, int64_t idx, int nv, float (&o)[K]) {
-  if (VEC && nv == K) {
+__device__ __forceinline__ void load_chunk(const float* __restrict__ base, uint32_t off, uint32_t last,
+                                           float (&o)[K]) {
+  if constexpr (VEC) {
     if constexpr (K == 1) {
-      o[0] = p[idx];
+      o[0] = __builtin_nontemporal_load(at(base, off));
     } else if constexpr (K == 2) {
-      const float2 t = *reinterpret_cast<const float2*>(p + idx);
+      const f32x2 t = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(at(base, off)));
       o[0] = t.x; o[1] = t.y;
     } else if constexpr (K == 4) {
-      const float4 t = *reinterpret_cast<const float4*>(p + idx);
+      const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(at(base, off)));
       o[0] = t.x; o[1] = t.y; o[2] = t.z; o[3] = t.w;
     } else {
       static_assert(K == 8, "chunk");
-      const float4 t0 = *reinterpret_cast<const float4*>(p + idx);
-      const float4 t1 = *reinterpret_cast<const float4*>(p + idx + 4);
+      const f32x4 t0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(at(base, off)));
+      const f32x4 t1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(at(base, off + 4)));
       o[0] = t0.x; o[1] = t0.y; o[2] = t0.z; o[3] = t0.w;
       o[4] = t1.x; o[5] = t1.y; o[6] = t1.z; o[7] = t1.w;
     }
   } else {
 #pragma unroll
-    for (int m = 0; m < K; ++m) o[m] = (m < nv) ? p[idx + m] : 0.0f;
+    for (int m = 0; m < K; ++m) {
+      const uint32_t c = off + m < last ? off + m : last;
+      o[m] = __builtin_nontemporal_load(at(base, c));
+    }
   }
 }
 
-// Bit m of the result is set iff byte m of the chunk is nonzero (flags).
+// K flag bytes at base[off], loaded raw (decoded only when the item is
+// computed, so the loads stay in flight): VEC with K >= 4 reads K/4 dwords,
+// otherwise each byte is read at its clamped column.
+template <int K> struct FlagRaw {
+  unsigned t[K], r[K];
+};
+
 template <int K, bool VEC>
-__device__ __forceinline__ unsigned load_flags(const uint8_t* __restrict__ p, int64_t idx, int nv) {
-  unsigned bits = 0;
-  if (VEC && nv == K) {
-    if constexpr (K == 1) {
-      bits = p[idx] != 0;
-    } else if constexpr (K == 2) {
-      const unsigned w = *reinterpret_cast<const uint16_t*>(p + idx);
-      bits = ((w & 0xffu) != 0) | (((w >> 8) != 0) << 1);
-    } else if constexpr (K == 4) {
-      const unsigned w = *reinterpret_cast<const uint32_t*>(p + idx);
+__device__ __forceinline__ void load_flag_raw(const uint8_t* __restrict__ base, uint32_t off, uint32_t last,
+                                              unsigned (&o)[K]) {
+  if constexpr (VEC && K >= 4) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) bits |= (((w >> (8 * m)) & 0xffu) != 0) << m;
-    } else {
-      const uint2 w = *reinterpret_cast<const uint2*>(p + idx);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) bits |= (((w.x >> (8 * m)) & 0xffu) != 0) << m;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) bits |= (((w.y >> (8 * m)) & 0xffu) != 0) << (m + 4);
-    }
+    for (int i = 0; i < K / 4; ++i)
+      o[i] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(at(base, off + 4 * i)));
   } else {
 #pragma unroll
-    for (int m = 0; m < K; ++m)
-      if (m < nv) bits |= (p[idx + m] != 0) << m;
+    for (int m = 0; m < K; ++m) {
+      const uint32_t c = off + m < last ? off + m : last;
+      o[m] = __builtin_nontemporal_load(at(base, c));
+    }
+  }
+}
+
+// Packed flag words (4 bytes each) to a bit mask: bit 4i+b is set iff byte b
+// of word i is nonzero.
+template <int NW>
+__device__ __forceinline__ unsigned flag_bits_words(const unsigned* w) {
+  unsigned bits = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    // bit 7 of each byte of nz is set iff that byte is nonzero
+    const unsigned nz = (((w[i] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[i]) & 0x80808080u;
+    const unsigned b4 = ((nz >> 7) & 1u) | ((nz >> 14) & 2u) | ((nz >> 21) & 4u) | ((nz >> 28) & 8u);
+    bits |= b4 << (4 * i);
+  }
+  return bits;
+}
+
+// Bit m of the result is set iff flag byte m is nonzero.
+template <int K, bool VEC>
+__device__ __forceinline__ unsigned flag_bits(const unsigned (&o)[K]) {
+  unsigned bits = 0;
+  if constexpr (VEC && K >= 4) {
+    bits = flag_bits_words<K / 4>(o);
+  } else {
+#pragma unroll
+    for (int m = 0; m < K; ++m) bits |= (unsigned)(o[m] != 0) << m;
   }
   return bits;
 }
 
 template <int K, bool VEC>
-__device__ __forceinline__ void store_f32(float* __restrict__ p, int64_t idx, int nv, const float (&o)[K]) {
-  if (VEC && nv == K) {
+__device__ __forceinline__ void store_chunk(float* __restrict__ base, uint32_t off, int nv, const float (&o)[K]) {
+  if constexpr (VEC) {
     if constexpr (K == 1) {
-      p[idx] = o[0];
+      __builtin_nontemporal_store(o[0], at(base, off));
     } else if constexpr (K == 2) {
-      *reinterpret_cast<float2*>(p + idx) = make_float2(o[0], o[1]);
+      __builtin_nontemporal_store((f32x2){o[0], o[1]}, reinterpret_cast<f32x2*>(at(base, off)));
     } else if constexpr (K == 4) {
-      *reinterpret_cast<float4*>(p + idx) = make_float4(o[0], o[1], o[2], o[3]);
+      __builtin_nontemporal_store((f32x4){o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(at(base, off)));
     } else {
-      *reinterpret_cast<float4*>(p + idx) = make_float4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<float4*>(p + idx + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      __builtin_nontemporal_store((f32x4){o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(at(base, off)));
+      __builtin_nontemporal_store((f32x4){o[4], o[5], o[6], o[7]}, reinterpret_cast<f32x4*>(at(base, off + 4)));
     }
   } else {
 #pragma unroll
     for (int m = 0; m < K; ++m)
-      if (m < nv) p[idx + m] = o[m];
+      if (m < nv) __builtin_nontemporal_store(o[m], at(base, off + m));
   }
 }
+
+// A value every lane of the wave holds, moved to a scalar register.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// ----------------------------------------------------------------- one row tile, one lane
+// The estimator-specific part of the scan, shared by both kernels: from one
+// lane's K raw steps to its K pairs (a_t, b_t), and from the scanned values
+// x_t back to the outputs.
+
+// Inputs of one lane's chunk of one row tile.
+template <class Est, int K> struct LaneIn {
+  float s[Traits<Est>::kStreams][K];  // raw inputs, memory order
+  float tb[K];                        // truncation bootstraps (valid where truncated)
+  float rowv;                         // bootstrap / init / carry of the row
+};
+
+// Scalars of a call.
+struct ScanScalars {
+  double gamma, lam, gl;  // gl = gamma * lambda
+  float rho_bar, c_bar;
+  bool has_row, has_tboot;
+};
+
+// Inputs of the scan predecessor of the team-first lane's innermost step
+// (it lives in another wave, team slot or tile).
+struct PredIn {
+  float v;        // V_{t+1} (TD, GAE, V-trace) or EQ_{t+1} (Retrace)
+  double c;       // c_{t+1} (Retrace)
+  unsigned done;  // done_{t-1} (forward estimators)
+};
+
+// Per-lane result of building the pairs.
+template <int K> struct LanePairs {
+  AB e[K];           // pairs in scan order (j = 0 nearest the carry)
+  double rho[K];     // V-trace: rho_t
+  double succv[K];   // V-trace: the cut's successor value
+  unsigned cut;      // K-bit mask of steps after which the episode chain stops
+  float nb_v;        // value handed in for the innermost step (V-trace epilogue)
+};
+
+// Build the K pairs of one lane.  cs: column of the lane's lowest-addressed
+// step; nv: steps inside the row (VEC: always K); tbits / rbits: terminated /
+// truncated bit masks (bit m = memory index m).
+template <class Est, int K, bool VEC>
+__device__ __forceinline__ LanePairs<K> build_pairs(const LaneIn<Est, K>& d, const ScanScalars& sc, unsigned tbits,
+                                                    unsigned rbits, uint32_t cs, int64_t T, int nv,
+                                                    bool team_first_lane, const PredIn& pred) {
+  using Tr = Traits<Est>;
+  constexpr bool REV = Est::kReverse;
+  constexpr int MLAST = REV ? 0 : K - 1;  // memory index of the lane's outermost step
+  LanePairs<K> out;
+  const double gamma = sc.gamma, lam = sc.lam, gl = sc.gl;
+
+  // ---- step kinds as K-bit lane masks
+  const unsigned te = tbits;                    // terminated
+  const unsigned trm = rbits & ~te;             // truncated (terminated wins)
+  unsigned endm = 0;                            // plain window end, t = T - 1
+  {
+    const int64_t e_m = T - 1 - (int64_t)cs;
+    if (e_m >= 0 && e_m < K) endm = (1u << e_m) & ~te & ~trm;
+  }
+  const unsigned cut = te | trm | endm;
+  const unsigned trb = sc.has_tboot ? trm : 0u;  // truncations with a supplied bootstrap
+  const float brow = sc.has_row ? d.rowv : 0.0f;
+  out.cut = cut;
+
+  // ---- scan-predecessor values for the lane's innermost step
+  double cown[K];
+  if constexpr (Tr::kRetrace) {
+#pragma unroll
+    for (int m = 0; m < K; ++m) {
+      const double ratio = (double)d.s[3][m] / (double)d.s[4][m];
+      cown[m] = lam * (ratio < 1.0 ? ratio : 1.0);
+    }
+  }
+  float nb_v = 0.0f;
+  double nb_c = 0.0;
+  unsigned nb_done = 0;
+  if constexpr (Tr::kNbValue) {
+    nb_v = shift_up_f32(Tr::kRetrace ? d.s[2][MLAST] : d.s[1][MLAST]);
+    if constexpr (Tr::kRetrace) nb_c = shift_up_f64(cown[MLAST]);
+  }
+  if constexpr (Tr::kNbDone) nb_done = shift_up_u32(((tbits | rbits) >> MLAST) & 1u);
+  if (team_first_lane) {
+    nb_v = pred.v;
+    nb_c = pred.c;
+    nb_done = pred.done;
+  }
+  out.nb_v = nb_v;
+
+  // ---- pairs, scan order j = 0..K-1
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int m = REV ? (K - 1 - j) : j;
+    AB c;
+    out.rho[j] = 0.0;
+    out.succv[j] = 0.0;
+    if constexpr (Tr::kBackwardRl) {
+      const bool is_cut = (cut >> m) & 1u;
+      // successor value at a cut (0 terminated / trunc bootstrap / row bootstrap)
+      const float bvf = ((trb >> m) & 1u) ? d.tb[m] : (((endm >> m) & 1u) ? brow : 0.0f);
+      float vnx = 0.0f;  // raw next-step input (V or EQ) in the same episode
+      double cn = 0.0;
+      if constexpr (Tr::kNbValue) {
+        if (j == 0) {
+          vnx = nb_v;
+          if constexpr (Tr::kRetrace) cn = nb_c;
+        } else {
+          const int mp = REV ? m + 1 : m - 1;
+          vnx = Tr::kRetrace ? d.s[2][mp] : d.s[1][mp];
+          if constexpr (Tr::kRetrace) cn = cown[mp];
+        }
+      }
+      const double nu = (double)(is_cut ? bvf : vnx);  // successor value
+      const double r = (double)d.s[0][m];
+      if constexpr (__is_same(Est, DiscountedReturn)) {
+        c.a = is_cut ? 0.0 : gamma;
+        c.b = __builtin_fma(gamma, (double)bvf, r);  // bvf is 0 off cuts
+      } else if constexpr (__is_same(Est, TdLambda)) {
+        c.a = is_cut ? 0.0 : gl;
+        c.b = __builtin_fma(is_cut ? gamma : (gamma - gl), nu, r);  // r + g((1-l) V' or boot)
+      } else if constexpr (__is_same(Est, Gae)) {
+        c.a = is_cut ? 0.0 : gl;
+        c.b = __builtin_fma(gamma, nu, r) - (double)d.s[1][m];
+      } else if constexpr (Tr::kVtrace) {
+        const float ratio = expf(d.s[2][m]);
+        const double rh = (double)fminf(ratio, sc.rho_bar);
+        const double ct = (double)fminf(ratio, sc.c_bar);
+        c.a = is_cut ? 0.0 : gl * ct;
+        c.b = rh * (__builtin_fma(gamma, nu, r) - (double)d.s[1][m]);
+        out.rho[j] = rh;
+        out.succv[j] = (double)bvf;
+      } else if constexpr (Tr::kRetrace) {
+        c.a = is_cut ? 0.0 : gamma * cn;
+        c.b = __builtin_fma(gamma, nu, r) - (double)d.s[1][m];
+      }
+    } else if constexpr (Tr::kForwardRl) {
+      // keep the running value unless the previous step ended an episode
+      const unsigned prev_done = (j == 0) ? nb_done : (((tbits | rbits) >> (m - 1)) & 1u);
+      const bool keep = !prev_done || (cs + m == 0);
+      if constexpr (__is_same(Est, EligibilityTrace)) c.a = keep ? gl : 0.0;
+      else c.a = keep ? 1.0 : 0.0;
+      c.b = (double)d.s[0][m];
+    } else {
+      c.a = (double)d.s[0][m];
+      c.b = (double)d.s[1][m];
+    }
+    if constexpr (!VEC) {
+      if (m >= nv) c = AB{1.0, 0.0};  // past the row end: identity
+    }
+    out.e[j] = c;
+  }
+  return out;
+}
+
+// Serial fold of the lane's K pairs (outermost applied last).
+template <int K>
+__device__ __forceinline__ AB fold_lane(const AB (&e)[K]) {
+  AB agg = e[0];
+#pragma unroll
+  for (int j = 1; j < K; ++j) agg = compose(e[j], agg);
+  return agg;
+}
+
+// Re-walk the lane's K steps from the value entering it.
+template <int K>
+__device__ __forceinline__ void rewalk(const AB (&e)[K], double x_in, double (&xs)[K]) {
+  double x = x_in;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    x = __builtin_fma(e[j].a, x, e[j].b);
+    xs[j] = x;
+  }
+}
+
+// Outputs of the lane's K steps (memory order), rounded once to fp32.
+template <class Est, int K>
+__device__ __forceinline__ void epilogue(const LaneIn<Est, K>& d, const LanePairs<K>& lp, const ScanScalars& sc,
+                                         double x_in, const double (&xs)[K], float (&o0)[K], float (&o1)[K]) {
+  using Tr = Traits<Est>;
+  constexpr bool REV = Est::kReverse;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int m = REV ? (K - 1 - j) : j;
+    double y = xs[j];
+    double y1 = 0.0;
+    if constexpr (__is_same(Est, Gae)) {
+      y1 = y + (double)d.s[1][m];
+    } else if constexpr (Tr::kVtrace) {
+      // pg_t = rho_t (r_t + gamma vs_{t+1} - V_t); vs_{t+1} = V_{t+1} + x_{t+1} inside
+      // the episode, the cut's successor value otherwise
+      const double xprev = (j == 0) ? x_in : xs[j - 1];
+      const int mp = REV ? m + 1 : m - 1;
+      const float vnx = (j == 0) ? lp.nb_v : d.s[1][(mp < 0 || mp >= K) ? 0 : mp];
+      const double succ = ((lp.cut >> m) & 1u) ? lp.succv[j] : ((double)vnx + xprev);
+      y1 = lp.rho[j] * (__builtin_fma(sc.gamma, succ, (double)d.s[0][m]) - (double)d.s[1][m]);
+      y = (double)d.s[1][m] + y;
+    } else if constexpr (Tr::kRetrace) {
+      y = (double)d.s[1][m] + y;
+    }
+    o0[m] = (float)y;
+    o1[m] = (float)y1;
+  }
+}
+
+// ----------------------------------------------------------------- per-item registers
+// An item is one tile of R rows.  Its lane-level position within the tile is
+// the same for all R rows.
+struct TilePos {
+  uint32_t cs;  // column of this lane's lowest-addressed step
+  uint32_t tn;  // column of the team-first lane's scan predecessor, clamped into the row
+  int nv;       // steps of this lane's chunk that lie inside the row (0..K)
+  bool nb_ok;   // the scan predecessor of the team-first lane exists
+  bool first;   // first tile of its rows in scan order
+};
+
+// The item's rows: a wave-uniform base row plus, per row, the element offset
+// of the row start relative to that base.
+template <int R> struct ItemRows {
+  int64_t wb;        // base row (uniform across the wave)
+  uint32_t roff[R];  // (row - wb) * T, rows clamped to E - 1
+  uint32_t rsel[R];  // row - wb
+  bool ok[R];        // the row exists
+};
+
+template <class Est, int K> struct RowData : LaneIn<Est, K> {
+  float nb[3];       // raw inputs of the team-first lane's scan predecessor
+  unsigned nbf[2];   // its raw terminated / truncated bytes (forward estimators)
+};
 
 // ----------------------------------------------------------------- the kernel
 // Template parameters: estimator tag, team width L (lanes per row when W = 1),
 // chunk K (steps per lane per tile), W (waves per row; W > 1 requires L = 64),
-// VEC (rows are aligned for K-wide vector accesses and T % K == 0).
-template <class Est, int L, int K, int W, bool VEC>
+// R (rows a team scans side by side per item: more bytes in flight per wave),
+// VEC (rows aligned for K-wide vector accesses and T % SPAN == 0, so every
+// tile is whole; otherwise every element is loaded at a clamped column), OPT
+// (bit 0: a flag array is present; bit 1: the second output is written).
+// The host guarantees T < 2^26, so every in-wave element offset fits 32 bits.
+template <class Est, int L, int K, int W, int R, bool VEC, int OPT>
 __global__ void __launch_bounds__(BlockShape<W>::kThreads)
 scan_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
@@ -245,270 +557,291 @@ scan_kernel(const KernelArgs p) {
   constexpr int TEAM_LANES = (W > 1) ? 64 * W : L;
   constexpr int TEAMS = BLOCK / TEAM_LANES;
   constexpr int SPAN = TEAM_LANES * K;
+  constexpr int NS = Tr::kStreams;
+  constexpr bool USE_FLAGS = (OPT & 1) && Tr::kUsesFlags;
+  constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
+  constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
   static_assert(W == 1 || L == 64, "multi-wave teams use full waves");
   static_assert(BLOCK % TEAM_LANES == 0, "block shape");
 
-  __shared__ double s_tot[(W > 1) ? 2 : 1][TEAMS][(W > 1) ? W : 1][2];
+  __shared__ double s_tot[(W > 1) ? 2 : 1][TEAMS][R][(W > 1) ? W : 1][2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int team = tid / TEAM_LANES;
-  const int w = (W > 1) ? ((tid >> 6) % W) : 0;  // wave index inside the team (0 = nearest carry)
-  const int g = (W > 1) ? lane : (lane & (L - 1));  // lane index inside the wave's part of the team
-  const bool team_first_lane = (g == 0);            // scan-predecessor lives outside this wave
+  const int w = (W > 1) ? ((tid >> 6) % W) : 0;     // wave inside the team (0 = nearest the carry)
+  const int g = (W > 1) ? lane : (lane & (L - 1));  // lane inside this wave's part of the team
+  const int team_in_wave = (W > 1) ? 0 : lane / L;  // teams sharing this wave, in lane order
+  const bool team_first_lane = (g == 0);            // scan predecessor lives outside this wave
+  const int pos0 = (w * 64 + g) * K;                // scan position of this lane's innermost step
 
   const int64_t T = p.T;
   const int64_t E = p.E;
+  const uint32_t T32 = (uint32_t)T;
   const int64_t ntiles = (T + SPAN - 1) / SPAN;
-  const int pos0 = (w * 64 + g) * K;  // scan position (within a tile) of this lane's innermost step
+  const int64_t groups = (E + R - 1) / R;  // row groups of R consecutive rows
+  const int64_t teams_total = (int64_t)gridDim.x * TEAMS;
+  const int64_t my_team = (int64_t)blockIdx.x * TEAMS + team;
+  // Block-uniform item count: the block's first team has the most row groups.
+  const int64_t first_team = (int64_t)blockIdx.x * TEAMS;
+  const int64_t groups_first = first_team < groups ? (groups - first_team + teams_total - 1) / teams_total : 0;
+  const int64_t n_items = groups_first * ntiles;
 
   const double gamma = p.gamma;
   const double lam = p.lam;
   const double gl = gamma * lam;
+  const unsigned tmask = p.has_term ? ~0u : 0u;
+  const unsigned rmask = p.has_trunc ? ~0u : 0u;
 
-  for (int64_t row_base = (int64_t)blockIdx.x * TEAMS; row_base < E; row_base += (int64_t)gridDim.x * TEAMS) {
-    const int64_t row = row_base + team;
-    const bool row_ok = row < E;
-    const int64_t off = row_ok ? row * T : 0;
-
-    // Running value entering the next tile from the carry side.
-    double C = 0.0;
-    float boot_row = 0.0f;
-    if constexpr (Tr::kBackwardRl) {
-      if (row_ok && p.row) boot_row = p.row[row];
-    } else {
-      if (row_ok && p.row) C = (double)p.row[row];
+  // ---------------------------------------------------------------- item cursors
+  // An item is (j, ts): the j-th row group of this team, ts-th tile in scan order.
+  struct Cursor {
+    int64_t k, j, ts;
+  };
+  auto advance = [&](Cursor c) __attribute__((always_inline)) {
+    c.k += 1;
+    c.ts += 1;
+    if (c.ts == ntiles) {
+      c.ts = 0;
+      c.j += 1;
     }
-
-    for (int64_t it = 0; it < ntiles; ++it) {
-      const int64_t tile = REV ? (ntiles - 1 - it) : it;
-      const int64_t tile_start = tile * SPAN;
-      // Memory index (within the row) of this lane's lowest-addressed step.
-      const int64_t cs = REV ? (tile_start + SPAN - pos0 - K) : (tile_start + pos0);
-      int nv = 0;
-      if (row_ok) {
-        const int64_t rem = T - cs;
-        nv = rem <= 0 ? 0 : (rem >= K ? K : (int)rem);
-      }
-      const int64_t base = off + cs;
-
-      // ---- (a1) raw inputs, memory order m = 0..K-1
-      float rr[K], vv[K], xa[K], pp[K], mm[K];
-      load_f32<K, VEC>(p.r, base, nv, rr);
-      if constexpr (Tr::kUsesV) load_f32<K, VEC>(p.v, base, nv, vv);
-      if constexpr (Tr::kUsesAux) load_f32<K, VEC>(p.aux, base, nv, xa);
-      if constexpr (Tr::kUsesPiMu) {
-        load_f32<K, VEC>(p.pi, base, nv, pp);
-        load_f32<K, VEC>(p.mu, base, nv, mm);
-      }
-      unsigned tbits = 0, rbits = 0;
-      if constexpr (Tr::kUsesFlags) {
-        if (p.term) tbits = load_flags<K, VEC>(p.term, base, nv);
-        if (p.trunc) rbits = load_flags<K, VEC>(p.trunc, base, nv);
-      }
-
-      // Per-step quantity handed to the scan-successor: V (TD/GAE/V-trace),
-      // EQ and the trace c (Retrace), done flag (forward estimators).
-      double cown[K];
-      if constexpr (__is_same(Est, Retrace)) {
+    return c;
+  };
+  auto tile_pos = [&](const Cursor& c) __attribute__((always_inline)) {
+    TilePos q;
+    const uint32_t tile = (uint32_t)(REV ? (ntiles - 1 - c.ts) : c.ts);
+    const uint32_t tile_start = tile * (uint32_t)SPAN;
+    q.cs = REV ? (tile_start + SPAN - pos0 - K) : (tile_start + pos0);
+    const int rem = (int)((int64_t)T - (int64_t)q.cs);
+    q.nv = rem <= 0 ? 0 : (rem >= K ? K : rem);
+    const int64_t cs0 = REV ? (int64_t)tile_start + SPAN - w * 64 * K - K : (int64_t)tile_start + w * 64 * K;
+    const int64_t tn = REV ? (cs0 + K) : (cs0 - 1);
+    q.nb_ok = tn >= 0 && tn < T;
+    q.tn = (uint32_t)(tn < 0 ? 0 : (tn >= T ? T - 1 : tn));
+    q.first = (c.ts == 0);
+    return q;
+  };
+  auto item_rows = [&](const Cursor& c) __attribute__((always_inline)) {
+    ItemRows<R> ir;
+    const int64_t grp = my_team + c.j * teams_total;
+    const int64_t wave_grp = grp - team_in_wave;  // this wave's first team
+    int64_t wb = wave_grp * R;
+    wb = wb < E ? wb : E - 1;
+    ir.wb = uniform64(wb);
 #pragma unroll
-        for (int m = 0; m < K; ++m) {
-          const double ratio = (double)pp[m] / (double)mm[m];
-          cown[m] = lam * (ratio < 1.0 ? ratio : 1.0);
-        }
-      }
-      // Scan-last step of this lane (outermost): memory m = 0 backward, K-1 forward.
-      constexpr int MLAST = REV ? 0 : K - 1;
-      float nb_v = 0.0f;   // V_{t+1} / EQ_{t+1} for this lane's innermost step
-      double nb_c = 0.0;   // c_{t+1} (Retrace)
-      int nb_done = 0;     // done_{t-1} (forward)
-      if constexpr (Tr::kNeedsNbValue) {
-        const float src = __is_same(Est, Retrace) ? xa[MLAST] : vv[MLAST];
-        nb_v = shift_up_f32(src);
-        if constexpr (__is_same(Est, Retrace)) nb_c = shift_up_f64(cown[MLAST]);
-      }
-      if constexpr (Tr::kNeedsNbDone) {
-        nb_done = shift_up_i32((int)(((tbits | rbits) >> MLAST) & 1u));
-      }
-      if (team_first_lane) {
-        // Predecessor in scan order is in another wave, team slot or tile: reload it.
-        const int64_t tn = REV ? (cs + K) : (cs - 1);  // its memory index within the row
-        // needed only if this lane's innermost step exists: m = K-1 backward, m = 0 forward
-        const bool inner_ok = REV ? (nv == K) : (nv > 0);
-        const bool ok = row_ok && inner_ok && tn >= 0 && tn < T;
-        if constexpr (Tr::kNeedsNbValue) {
-          nb_v = 0.0f;
-          nb_c = 0.0;
-          if (ok) {
-            if constexpr (__is_same(Est, Retrace)) {
-              nb_v = p.aux[off + tn];
-              const double ratio = (double)p.pi[off + tn] / (double)p.mu[off + tn];
-              nb_c = lam * (ratio < 1.0 ? ratio : 1.0);
-            } else {
-              nb_v = p.v[off + tn];
-            }
-          }
-        }
-        if constexpr (Tr::kNeedsNbDone) {
-          nb_done = 0;
-          if (ok) nb_done = (p.term && p.term[off + tn]) || (p.trunc && p.trunc[off + tn]);
-        }
-      }
+    for (int rr = 0; rr < R; ++rr) {
+      const int64_t row = grp * R + rr;
+      ir.ok[rr] = (c.k < n_items) && row < E;
+      const int64_t rc = row < E ? row : E - 1;
+      ir.rsel[rr] = (uint32_t)(rc - ir.wb);
+      ir.roff[rr] = ir.rsel[rr] * T32;
+    }
+    return ir;
+  };
 
-      // ---- (a2) coefficients, scan order j = 0..K-1 (j = 0 nearest the carry)
-      AB e[K];
-      double aux0[K];  // per-step extras for the epilogue (V-trace: rho)
-      double bootv[K];
-      bool contk[K];
-      double vnext[K];
+  // ---------------------------------------------------------------- pipeline stages
+  auto issue_flags = [&](const Cursor& c, FlagRaw<K> (&f)[R]) __attribute__((always_inline)) {
+    if constexpr (USE_FLAGS) {
+      const TilePos q = tile_pos(c);
+      const ItemRows<R> ir = item_rows(c);
+      const uint8_t* tb = p.term + ir.wb * T;
+      const uint8_t* rb = p.trunc + ir.wb * T;
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const int m = REV ? (K - 1 - j) : j;
-        const int64_t t = cs + m;
-        const bool valid = m < nv;
-        AB c{1.0, 0.0};
-        contk[j] = false;
-        bootv[j] = 0.0;
-        vnext[j] = 0.0;
-        aux0[j] = 0.0;
-        if constexpr (Tr::kBackwardRl) {
-          const bool te = (tbits >> m) & 1u;
-          const bool tr = !te && ((rbits >> m) & 1u);
-          const bool end = !te && !tr && (t == T - 1);
-          const bool cont = !(te || tr || end);
-          double bv = 0.0;
-          if (valid && tr && p.tboot) bv = (double)p.tboot[off + t];
-          if (end) bv = (double)boot_row;
-          // value of the successor step's input (scan predecessor): same lane or neighbour
-          double nx = 0.0;
-          double cn = 0.0;
-          if constexpr (Tr::kNeedsNbValue) {
-            if (j == 0) {
-              nx = (double)nb_v;
-              if constexpr (__is_same(Est, Retrace)) cn = nb_c;
-            } else {
-              const int mp = REV ? m + 1 : m - 1;
-              nx = __is_same(Est, Retrace) ? (double)xa[mp] : (double)vv[mp];
-              if constexpr (__is_same(Est, Retrace)) cn = cown[mp];
-            }
-          }
-          const double nu = cont ? nx : bv;  // successor value
-          const double r = (double)rr[m];
-          if constexpr (__is_same(Est, DiscountedReturn)) {
-            c.a = cont ? gamma : 0.0;
-            c.b = cont ? r : __builtin_fma(gamma, bv, r);
-          } else if constexpr (__is_same(Est, TdLambda)) {
-            c.a = cont ? gl : 0.0;
-            // r + gamma * ((1 - lambda) V_{t+1})  or  r + gamma * boot
-            c.b = __builtin_fma(cont ? (gamma - gl) : gamma, nu, r);
-          } else if constexpr (__is_same(Est, Gae)) {
-            c.a = cont ? gl : 0.0;
-            c.b = __builtin_fma(gamma, nu, r) - (double)vv[m];
-          } else if constexpr (__is_same(Est, Vtrace)) {
-            const double ratio = (double)expf(xa[m]);
-            const double rho = ratio < p.rho_bar ? ratio : p.rho_bar;
-            const double ct = lam * (ratio < p.c_bar ? ratio : p.c_bar);
-            c.a = cont ? gamma * ct : 0.0;
-            c.b = rho * (__builtin_fma(gamma, nu, r) - (double)vv[m]);
-            aux0[j] = rho;
-          } else if constexpr (__is_same(Est, Retrace)) {
-            c.a = cont ? gamma * cn : 0.0;
-            c.b = __builtin_fma(gamma, nu, r) - (double)vv[m];
-          }
-          contk[j] = cont;
-          bootv[j] = bv;
-          vnext[j] = nx;
-        } else if constexpr (Tr::kForwardRl) {
-          // keep the running value unless the previous step ended an episode
-          int prev_done;
-          if (j == 0) {
-            prev_done = nb_done;
-          } else {
-            const int mp = m - 1;
-            prev_done = (int)(((tbits | rbits) >> mp) & 1u);
-          }
-          const double keep = (t == 0 || !prev_done) ? 1.0 : 0.0;
-          c.a = __is_same(Est, EligibilityTrace) ? gl * keep : keep;
-          c.b = (double)rr[m];
+      for (int rr = 0; rr < R; ++rr) {
+        const uint32_t last = ir.roff[rr] + T32 - 1;
+        load_flag_raw<K, VEC>(tb, ir.roff[rr] + q.cs, last, f[rr].t);
+        load_flag_raw<K, VEC>(rb, ir.roff[rr] + q.cs, last, f[rr].r);
+      }
+    }
+  };
+
+  auto decode = [&](const FlagRaw<K> (&f)[R], unsigned (&tbits)[R], unsigned (&rbits)[R])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      tbits[rr] = 0;
+      rbits[rr] = 0;
+      if constexpr (USE_FLAGS) {
+        tbits[rr] = flag_bits<K, VEC>(f[rr].t) & tmask;
+        rbits[rr] = flag_bits<K, VEC>(f[rr].r) & rmask;
+      }
+    }
+  };
+
+  auto issue_data = [&](const Cursor& c, const unsigned (&tbits)[R], const unsigned (&rbits)[R],
+                        RowData<Est, K> (&dd)[R]) __attribute__((always_inline)) {
+    const TilePos q = tile_pos(c);
+    const ItemRows<R> ir = item_rows(c);
+    const int64_t eb = ir.wb * T;  // element index of the base row
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      RowData<Est, K>& d = dd[rr];
+      const uint32_t off = ir.roff[rr] + q.cs;
+      const uint32_t last = ir.roff[rr] + T32 - 1;
+      load_chunk<K, VEC>(p.r + eb, off, last, d.s[0]);
+      if constexpr (NS >= 2) load_chunk<K, VEC>(p.v + eb, off, last, d.s[1]);
+      if constexpr (NS >= 3) load_chunk<K, VEC>(p.aux + eb, off, last, d.s[2]);
+      if constexpr (NS >= 5) {
+        load_chunk<K, VEC>(p.pi + eb, off, last, d.s[3]);
+        load_chunk<K, VEC>(p.mu + eb, off, last, d.s[4]);
+      }
+      // the team-first lane's scan predecessor: one address per team part (one request)
+      const uint32_t noff = ir.roff[rr] + q.tn;
+      if constexpr (Tr::kRetrace) {
+        d.nb[0] = __builtin_nontemporal_load(at(p.aux + eb, noff));
+        d.nb[1] = __builtin_nontemporal_load(at(p.pi + eb, noff));
+        d.nb[2] = __builtin_nontemporal_load(at(p.mu + eb, noff));
+      } else if constexpr (Tr::kNbValue) {
+        d.nb[0] = __builtin_nontemporal_load(at(p.v + eb, noff));
+      } else if constexpr (Tr::kNbDone && USE_FLAGS) {
+        d.nbf[0] = __builtin_nontemporal_load(at(p.term + eb, noff));
+        d.nbf[1] = __builtin_nontemporal_load(at(p.trunc + eb, noff));
+      }
+      d.rowv = *at(p.row + ir.wb, ir.rsel[rr]);
+      // Truncation bootstraps of this lane's chunk; lanes without a truncated
+      // step read the array's first chunk instead (one line shared by all waves).
+      if constexpr (GATHER_TB) {
+        const unsigned need = rbits[rr] & ~tbits[rr];
+        const float* tbase = p.tboot + eb;
+        if constexpr (VEC) {
+          const float* src = need ? at(tbase, off) : p.tboot;
+          load_chunk<K, true>(src, 0, 0, d.tb);
         } else {
-          c.a = (double)rr[m];
-          c.b = (double)vv[m];
-        }
-        if (!valid) c = AB{1.0, 0.0};
-        e[j] = c;
-      }
-
-      // ---- (a3) serial fold of this lane's K steps
-      AB agg = e[0];
 #pragma unroll
-      for (int j = 1; j < K; ++j) agg = compose(e[j], agg);
-
-      // ---- (a4) wave scan over lanes
-      const AB incl = lane_scan<(W > 1 ? 64 : L)>(agg);
-
-      // ---- (a5) block carry across the waves of a team (LDS)
-      double Cw = C;        // value entering this wave's first step
-      double C_next = 0.0;  // value leaving the tile
-      if constexpr (W > 1) {
-        const int buf = (int)(it & 1);
-        if (lane == 63) {
-          s_tot[buf][team][w][0] = incl.a;
-          s_tot[buf][team][w][1] = incl.b;
-        }
-        __syncthreads();
-        double x = C;
-#pragma unroll
-        for (int u = 0; u < W; ++u) {
-          if (u == w) Cw = x;
-          x = __builtin_fma(s_tot[buf][team][u][0], x, s_tot[buf][team][u][1]);
-        }
-        C_next = x;
-      }
-
-      // ---- (a6) value entering each lane, then re-walk
-      const double y_last = __builtin_fma(incl.a, Cw, incl.b);  // value after this lane's steps
-      const double from_below = shift_up_f64(y_last);
-      const double x_in = team_first_lane ? Cw : from_below;
-      if constexpr (W == 1) C_next = group_last_f64<L>(y_last, lane);
-
-      double xs[K];
-      {
-        double x = x_in;
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-          x = __builtin_fma(e[j].a, x, e[j].b);
-          xs[j] = x;
+          for (int m = 0; m < K; ++m) {
+            const uint32_t col = off + m < last ? off + m : last;
+            d.tb[m] = __builtin_nontemporal_load(((need >> m) & 1u) ? at(tbase, col) : p.tboot);
+          }
         }
       }
-
-      // ---- (a7) epilogue and one store per output
-      float o0[K], o1[K];
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const int m = REV ? (K - 1 - j) : j;
-        double y = xs[j];
-        double y1 = 0.0;
-        if constexpr (__is_same(Est, Gae)) {
-          y1 = y + (double)vv[m];
-        } else if constexpr (__is_same(Est, Vtrace)) {
-          const double xprev = (j == 0) ? x_in : xs[j - 1];
-          const double succ = contk[j] ? (vnext[j] + xprev) : bootv[j];
-          y1 = aux0[j] * (__builtin_fma(gamma, succ, (double)rr[m]) - (double)vv[m]);
-          y = (double)vv[m] + y;
-        } else if constexpr (__is_same(Est, Retrace)) {
-          y = (double)vv[m] + y;
-        }
-        o0[m] = (float)y;
-        o1[m] = (float)y1;
-      }
-      if (nv > 0) {
-        store_f32<K, VEC>(p.out0, base, nv, o0);
-        if constexpr (__is_same(Est, Gae) || __is_same(Est, Vtrace)) {
-          if (p.out1) store_f32<K, VEC>(p.out1, base, nv, o1);
-        }
-      }
-      C = C_next;
     }
+  };
+
+  const ScanScalars sc{gamma, lam, gl, (float)p.rho_bar, (float)p.c_bar, p.has_row != 0, p.has_tboot != 0};
+
+  // Scan one row of an item and form its outputs; C is the running value of the row.
+  auto scan_row = [&](int64_t k, int rr, const TilePos& q, bool row_ok, const RowData<Est, K>& d,
+                      unsigned tbits, unsigned rbits, double& C, float (&o0)[K], float (&o1)[K])
+      __attribute__((always_inline)) {
+    if (q.first) {
+      if constexpr (Tr::kBackwardRl) C = 0.0;
+      else C = (row_ok && p.has_row) ? (double)d.rowv : 0.0;
+    }
+    const int nv = row_ok ? q.nv : 0;
+
+    // the team-first lane's scan predecessor, reloaded from memory
+    PredIn pred{0.0f, 0.0, 0u};
+    if constexpr (Tr::kRetrace) {
+      pred.v = d.nb[0];
+      const double ratio = (double)d.nb[1] / (double)d.nb[2];
+      pred.c = q.nb_ok ? lam * (ratio < 1.0 ? ratio : 1.0) : 0.0;
+    } else if constexpr (Tr::kNbValue) {
+      pred.v = d.nb[0];
+    } else if constexpr (Tr::kNbDone && USE_FLAGS) {
+      const unsigned dn = ((unsigned)(d.nbf[0] != 0) & tmask) | ((unsigned)(d.nbf[1] != 0) & rmask);
+      pred.done = (q.nb_ok && dn) ? 1u : 0u;
+    }
+    const LanePairs<K> lp = build_pairs<Est, K, VEC>(d, sc, tbits, rbits, q.cs, T, nv, team_first_lane, pred);
+
+    // ---- (a3) serial fold, (a4) wave scan over lanes
+    const AB incl = lane_scan<(W > 1 ? 64 : L)>(fold_lane<K>(lp.e));
+
+    // ---- (a5) block carry across the waves of a team (LDS)
+    double Cw = C;        // value entering this wave's innermost step
+    double C_next = 0.0;  // value leaving the tile
+    if constexpr (W > 1) {
+      const int buf = (int)(k & 1);
+      if (lane == 63) {
+        s_tot[buf][team][rr][w][0] = incl.a;
+        s_tot[buf][team][rr][w][1] = incl.b;
+      }
+      __syncthreads();
+      double x = C;
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        if (u == w) Cw = x;
+        x = __builtin_fma(s_tot[buf][team][rr][u][0], x, s_tot[buf][team][rr][u][1]);
+      }
+      C_next = x;
+    }
+
+    // ---- (a6) value entering each lane, then re-walk; (a7) epilogue
+    const double y_last = __builtin_fma(incl.a, Cw, incl.b);  // value after this lane's steps
+    const double from_below = shift_up_f64(y_last);
+    const double x_in = team_first_lane ? Cw : from_below;
+    if constexpr (W == 1) C_next = group_last_f64<L>(y_last, lane);
+    double xs[K];
+    rewalk<K>(lp.e, x_in, xs);
+    epilogue<Est, K>(d, lp, sc, x_in, xs, o0, o1);
+    C = C_next;
+  };
+
+  // Scan all rows of item k, then store them (stores last: a pending store
+  // makes the next wait on a load drain the memory counter).
+  auto compute = [&](int64_t k, const Cursor& c, const RowData<Est, K> (&dd)[R], const unsigned (&tbits)[R],
+                     const unsigned (&rbits)[R], double (&C)[R]) __attribute__((always_inline)) {
+    const TilePos q = tile_pos(c);
+    const ItemRows<R> ir = item_rows(c);
+    float o0[R][K], o1[R][K];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) scan_row(k, rr, q, ir.ok[rr], dd[rr], tbits[rr], rbits[rr], C[rr], o0[rr], o1[rr]);
+    const int64_t eb = ir.wb * T;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int nv = ir.ok[rr] ? q.nv : 0;
+      if (nv > 0) {
+        const uint32_t off = ir.roff[rr] + q.cs;
+        store_chunk<K, VEC>(p.out0 + eb, off, nv, o0[rr]);
+        if constexpr (OUT1) store_chunk<K, VEC>(p.out1 + eb, off, nv, o1[rr]);
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- the pipeline
+  // Two register sets (X: even items, Y: odd items) swap roles each step, so no
+  // in-flight load is ever copied.  Step k: decode the flags of item k+1, issue
+  // the flags of item k+2 and the inputs + bootstrap gather of item k+1, then
+  // scan and store item k.
+  FlagRaw<K> FX[R], FY[R];
+  RowData<Est, K> DX[R], DY[R];
+  Cursor c0{0, 0, 0};
+  Cursor c1 = advance(c0);
+  Cursor c2 = advance(c1);
+  unsigned bt_cur[R], br_cur[R], bt_nxt[R], br_nxt[R];
+  issue_flags(c0, FX);
+  issue_flags(c1, FY);
+  decode(FX, bt_cur, br_cur);
+  issue_data(c0, bt_cur, br_cur, DX);
+  double C[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) C[rr] = 0.0;
+  for (int64_t k = 0; k < n_items; k += 2) {
+    // item k (set X)
+    decode(FY, bt_nxt, br_nxt);
+    issue_flags(c2, FX);
+    issue_data(c1, bt_nxt, br_nxt, DY);
+    compute(k, c0, DX, bt_cur, br_cur, C);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      bt_cur[rr] = bt_nxt[rr];
+      br_cur[rr] = br_nxt[rr];
+    }
+    c0 = c1;
+    c1 = c2;
+    c2 = advance(c2);
+    // item k+1 (set Y)
+    decode(FX, bt_nxt, br_nxt);
+    issue_flags(c2, FY);
+    issue_data(c1, bt_nxt, br_nxt, DX);
+    compute(k + 1, c0, DY, bt_cur, br_cur, C);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      bt_cur[rr] = bt_nxt[rr];
+      br_cur[rr] = br_nxt[rr];
+    }
+    c0 = c1;
+    c1 = c2;
+    c2 = advance(c2);
   }
 }
 

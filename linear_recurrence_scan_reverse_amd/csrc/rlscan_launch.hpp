@@ -1,8 +1,10 @@
-// rlscan_launch.hpp -- host-side launch of the scan kernel: picks the team
-// shape for a row length T and launches one kernel on the caller's stream.
+// rlscan_launch.hpp -- host-side launch of the scan kernel: resolves optional
+// inputs, picks the team shape for a row length T, sizes a persistent grid
+// and launches one kernel on the caller's stream.
 #pragma once
 
 #include "rlscan_kernel.hpp"
+#include "rlscan_stream.hpp"
 
 namespace rlscan {
 
@@ -24,12 +26,27 @@ inline LaunchShape pick_shape(int64_t T) {
   return {64, 4, 4};
 }
 
-// K-wide vector accesses need every row start aligned: T % K == 0 and every
-// array base aligned to its K-element chunk.
-inline bool vector_ok(const KernelArgs& a, int K) {
-  if (a.T % K != 0) return false;
+// Resident blocks per CU the persistent grid aims for.
+inline int blocks_per_cu(const LaunchShape&) { return 4; }
+
+// Rows a team scans side by side per item.  A lane must keep enough bytes in
+// flight to cover HBM latency (Little's law at ~5.5 TB/s over 256 CUs asks
+// for ~64 KiB in flight per CU), so estimators that move few bytes per step
+// take more rows per item.
+template <class Est, int K>
+constexpr int rows_per_item() {
+  using Tr = Traits<Est>;
+  constexpr int per_step = 4 * Tr::kStreams + (Tr::kUsesFlags ? 2 : 0) + 4 * (Tr::kHasOut1 ? 2 : 1);
+  constexpr int bytes = per_step * K;
+  return bytes < 0 ? 2 : 1;  // one row per item on this path
+}
+
+// The vector path needs whole tiles (T % span == 0) and every dense array base
+// aligned to its K-element chunk.
+inline bool vector_ok(const KernelArgs& a, int K, int span) {
+  if (a.T % span != 0) return false;
   const uintptr_t fa = (uintptr_t)(4 * K), ba = (uintptr_t)K;
-  const float* fl[] = {a.r, a.v, a.aux, a.pi, a.mu, a.out0, a.out1};
+  const float* fl[] = {a.r, a.v, a.aux, a.pi, a.mu, a.tboot, a.out0, a.out1};
   for (const float* q : fl)
     if (q && ((uintptr_t)q % fa) != 0) return false;
   const uint8_t* bl[] = {a.term, a.trunc};
@@ -38,35 +55,125 @@ inline bool vector_ok(const KernelArgs& a, int K) {
   return true;
 }
 
-template <class Est, int L, int K, int W, bool VEC>
-inline hipError_t launch_one(const KernelArgs& a, hipStream_t s) {
+// Replace absent optional inputs by valid stand-in addresses so the kernel's
+// loads never branch; the has_* switches tell the kernel to ignore them.
+inline KernelArgs resolve_optional(KernelArgs a) {
+  a.has_term = a.term != nullptr;
+  a.has_trunc = a.trunc != nullptr;
+  if (!a.term) a.term = a.trunc;
+  if (!a.trunc) a.trunc = a.term;
+  a.has_row = a.row != nullptr;
+  if (!a.row) a.row = a.r;  // [E,T] with T >= 1 holds at least E floats
+  a.has_tboot = a.tboot != nullptr;
+  if (!a.tboot) a.tboot = a.r;
+  return a;
+}
+
+inline int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+template <class Est, int L, int K, int W, bool VEC, int OPT>
+inline hipError_t launch_one(const KernelArgs& a, hipStream_t s, const LaunchShape& sh) {
   constexpr int BLOCK = BlockShape<W>::kThreads;
   constexpr int TEAMS = BLOCK / ((W > 1) ? 64 * W : L);
-  int64_t blocks = (a.E + TEAMS - 1) / TEAMS;
-  const int64_t kMaxBlocks = (int64_t)1 << 30;  // larger E: grid-stride loop in the kernel
-  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+  constexpr int R = rows_per_item<Est, K>();
+  const int64_t groups = (a.E + R - 1) / R;
+  int64_t blocks = (groups + TEAMS - 1) / TEAMS;
+  const int64_t resident = (int64_t)cu_count() * blocks_per_cu(sh);
+  if (blocks > resident) blocks = resident;
   KernelArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_kernel<Est, L, K, W, VEC>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_kernel<Est, L, K, W, R, VEC, OPT>),
                          dim3((unsigned)blocks), dim3(BLOCK), params, 0, s);
 }
 
+template <class Est, int L, int K, int W, int OPT>
+inline hipError_t launch_vec(const KernelArgs& a, hipStream_t s, const LaunchShape& sh) {
+  constexpr int SPAN = ((W > 1) ? 64 * W : L) * K;
+  return vector_ok(a, K, SPAN) ? launch_one<Est, L, K, W, true, OPT>(a, s, sh)
+                         : launch_one<Est, L, K, W, false, OPT>(a, s, sh);
+}
+
+// OPT bit 0: a flag array is present; bit 1: the second output is written.
 template <class Est, int L, int K, int W>
-inline hipError_t launch_shape(const KernelArgs& a, hipStream_t s) {
-  return vector_ok(a, K) ? launch_one<Est, L, K, W, true>(a, s) : launch_one<Est, L, K, W, false>(a, s);
+inline hipError_t launch_shape(const KernelArgs& a, hipStream_t s, const LaunchShape& sh) {
+  using Tr = Traits<Est>;
+  const bool flags = a.has_term || a.has_trunc;
+  if constexpr (Tr::kHasOut1) {
+    const bool out1 = a.out1 != nullptr;
+    if (flags) return out1 ? launch_vec<Est, L, K, W, 3>(a, s, sh) : launch_vec<Est, L, K, W, 1>(a, s, sh);
+    return out1 ? launch_vec<Est, L, K, W, 2>(a, s, sh) : launch_vec<Est, L, K, W, 0>(a, s, sh);
+  } else if constexpr (Tr::kUsesFlags) {
+    return flags ? launch_vec<Est, L, K, W, 1>(a, s, sh) : launch_vec<Est, L, K, W, 0>(a, s, sh);
+  } else {
+    return launch_vec<Est, L, K, W, 0>(a, s, sh);
+  }
+}
+
+// ----------------------------------------------------------------- streaming path
+template <class Est, int L, int K, int OPT>
+inline hipError_t launch_stream_one(const KernelArgs& a, hipStream_t s) {
+  using Cfg = StreamCfg<Est, K, (OPT & 1) != 0>;
+  constexpr int G = 64 / L;
+  const int64_t nrg = (a.E + G - 1) / G;
+  const int64_t cap = (int64_t)cu_count() * 2;  // two blocks per CU (LDS)
+  const int64_t per_wave = (nrg + Cfg::NC * cap - 1) / (Cfg::NC * cap);
+  int64_t blocks = (nrg + Cfg::NC * per_wave - 1) / (Cfg::NC * per_wave);
+  if (blocks < 1) blocks = 1;
+  KernelArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_kernel<Est, L, K, OPT>), dim3((unsigned)blocks),
+                         dim3(Cfg::kThreads), params, 0, s);
+}
+
+template <class Est, int L, int K>
+inline hipError_t launch_stream(const KernelArgs& a, hipStream_t s) {
+  using Tr = Traits<Est>;
+  const bool flags = a.has_term || a.has_trunc;
+  if constexpr (Tr::kHasOut1) {
+    const bool out1 = a.out1 != nullptr;
+    if (flags) return out1 ? launch_stream_one<Est, L, K, 3>(a, s) : launch_stream_one<Est, L, K, 1>(a, s);
+    return out1 ? launch_stream_one<Est, L, K, 2>(a, s) : launch_stream_one<Est, L, K, 0>(a, s);
+  } else if constexpr (Tr::kUsesFlags) {
+    return flags ? launch_stream_one<Est, L, K, 1>(a, s) : launch_stream_one<Est, L, K, 0>(a, s);
+  } else {
+    return launch_stream_one<Est, L, K, 0>(a, s);
+  }
+}
+
+// The streaming kernel takes rows made of whole 16-byte-aligned tiles.
+inline int stream_team(const KernelArgs& a) {
+  if (a.T >= ((int64_t)1 << 26)) return 0;
+  int L = 0;
+  if (a.T == 64) L = 16;
+  else if (a.T == 128) L = 32;
+  else if (a.T % 256 == 0) L = 64;
+  if (L == 0 || !vector_ok(a, 4, L * 4)) return 0;
+  return L;
 }
 
 template <class Est>
-hipError_t launch(const KernelArgs& a, hipStream_t s) {
+hipError_t launch(const KernelArgs& in, hipStream_t s) {
+  const KernelArgs a = resolve_optional(in);
+  switch (stream_team(a)) {
+    case 16: return launch_stream<Est, 16, 4>(a, s);
+    case 32: return launch_stream<Est, 32, 4>(a, s);
+    case 64: return launch_stream<Est, 64, 4>(a, s);
+    default: break;
+  }
   const LaunchShape sh = pick_shape(a.T);
   switch (sh.W * 1000 + sh.L * 10 + sh.K) {
-    case 1000 + 160 + 1: return launch_shape<Est, 16, 1, 1>(a, s);
-    case 1000 + 160 + 2: return launch_shape<Est, 16, 2, 1>(a, s);
-    case 1000 + 160 + 4: return launch_shape<Est, 16, 4, 1>(a, s);
-    case 1000 + 320 + 4: return launch_shape<Est, 32, 4, 1>(a, s);
-    case 1000 + 640 + 4: return launch_shape<Est, 64, 4, 1>(a, s);
-    case 2000 + 640 + 4: return launch_shape<Est, 64, 4, 2>(a, s);
-    case 4000 + 640 + 4: return launch_shape<Est, 64, 4, 4>(a, s);
+    case 1000 + 160 + 1: return launch_shape<Est, 16, 1, 1>(a, s, sh);
+    case 1000 + 160 + 2: return launch_shape<Est, 16, 2, 1>(a, s, sh);
+    case 1000 + 160 + 4: return launch_shape<Est, 16, 4, 1>(a, s, sh);
+    case 1000 + 320 + 4: return launch_shape<Est, 32, 4, 1>(a, s, sh);
+    case 1000 + 640 + 4: return launch_shape<Est, 64, 4, 1>(a, s, sh);
+    case 2000 + 640 + 4: return launch_shape<Est, 64, 4, 2>(a, s, sh);
+    case 4000 + 640 + 4: return launch_shape<Est, 64, 4, 4>(a, s, sh);
     default: return hipErrorInvalidConfiguration;
   }
 }

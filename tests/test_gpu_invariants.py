@@ -62,7 +62,8 @@ def test_episode_isolation_bitwise(T, j):
     for k in ("r", "v", "log_rhos", "q", "exp_q", "trunc_bootstrap"):
         later[k][e, j + 1:] += 3.5
     later["pi"][e, j + 1:] *= 0.5
-    later["bootstrap_value"][e] += 2.0
+    # (bootstrap_value is left alone: the forward estimators take it as init, which
+    # belongs to the earlier episode)
     after = {n: _np(run_gpu(n, to_dev(later))) for n in NAMES}
     for n in NAMES:
         for k in base[n]:
@@ -94,12 +95,12 @@ def test_forward_windows_chain_through_init():
     full = rl.episodic_prefix_sum(xd, td)
     first = rl.episodic_prefix_sum(xd[:, :T1].contiguous(), td[:, :T1].contiguous())
     init = torch.where(td[:, T1 - 1] != 0, torch.zeros_like(first[:, -1]), first[:, -1]).contiguous()
-    second = rl.episodic_prefix_sum(xd[:, T1:].contiguous(), td[:, T1:].contiguous(), init)
+    second = rl.episodic_prefix_sum(xd[:, T1:].contiguous(), td[:, T1:].contiguous(), init=init)
     assert torch.equal(torch.cat([first, second], 1), full)
     tr_full = rl.eligibility_traces(xd, td, gamma=0.9, lam=0.8)
     tr1 = rl.eligibility_traces(xd[:, :T1].contiguous(), td[:, :T1].contiguous(), gamma=0.9, lam=0.8)
     init = torch.where(td[:, T1 - 1] != 0, torch.zeros_like(tr1[:, -1]), tr1[:, -1]).contiguous()
-    tr2 = rl.eligibility_traces(xd[:, T1:].contiguous(), td[:, T1:].contiguous(), init, gamma=0.9, lam=0.8)
+    tr2 = rl.eligibility_traces(xd[:, T1:].contiguous(), td[:, T1:].contiguous(), init=init, gamma=0.9, lam=0.8)
     # the chained result rounds the carry to fp32 once at the window edge
     assert parity_err(torch.cat([tr1, tr2], 1).cpu().numpy(), tr_full.cpu().numpy()) <= TOL
 
