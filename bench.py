@@ -187,10 +187,11 @@ def copy_ceiling(torch, device, nbytes=1 << 30, reps=20):
     return 2 * nbytes * reps / secs / 1e9
 
 
-def read_traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+def read_traffic(est, workload):
+    """HBM bytes per launch of one estimator's kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a calibration copy), or None
     when the summary is missing or was taken on other kernel sources."""
-    path = os.path.join(PROFILES, "traffic_%s.txt" % kernel_key)
+    path = os.path.join(PROFILES, "hbm_traffic_rlscan_%s.txt" % workload)
     if not os.path.exists(path):
         return None, "no counter summary"
     vals = {}
@@ -202,7 +203,7 @@ def read_traffic(kernel_key):
     if vals.get("kernel_source_sha256") != kernel_source_hash():
         return None, "kernel sources changed since the counters were taken"
     try:
-        return float(vals["hbm_bytes_per_launch"]), path
+        return float(vals["%s.hbm_bytes_per_launch" % est]), os.path.relpath(path, ROOT)
     except (KeyError, ValueError):
         return None, "malformed counter summary"
 
@@ -340,7 +341,7 @@ def main():
                                                               100 * per[n]["frac_of_peak"]))
 
     dom = max(per, key=lambda k: per[k]["us_per_launch"])
-    traffic, traffic_src = read_traffic("%s_%s" % (dom, w.name))
+    traffic, traffic_src = read_traffic(dom, w.name)
     roofline = {
         "bound": "hbm",
         "kernel": dom,

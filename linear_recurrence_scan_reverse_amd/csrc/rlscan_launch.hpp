@@ -115,33 +115,52 @@ inline hipError_t launch_shape(const KernelArgs& a, hipStream_t s, const LaunchS
 }
 
 // ----------------------------------------------------------------- streaming path
-template <class Est, int L, int K, int OPT>
+// Data lead (ticks) and blocks per CU of the streaming kernel (a sweep over
+// leads 2..4 and 2..6 blocks per CU at 16384 x 256 favoured 2 and 2).
+template <class Est>
+constexpr int stream_lead() { return 2; }
+constexpr int kStreamBlocksPerCu = 2;
+
+// Whether an estimator takes the streaming kernel when its rows allow it.
+// Measured at 16384 x 256: discounted returns and Retrace with flags present
+// run faster on the pipelined persistent kernel (the per-wave bootstrap
+// gather there overlaps better with their compute than the tick-synchronous
+// gather wave does); the rest run faster streaming.
+template <class Est>
+inline bool prefer_stream(const KernelArgs& a) {
+  constexpr bool pipelined_with_flags = __is_same(Est, DiscountedReturn) || __is_same(Est, Retrace);
+  return !(pipelined_with_flags && (a.has_term || a.has_trunc));
+}
+
+template <class Est, int L, int OPT>
 inline hipError_t launch_stream_one(const KernelArgs& a, hipStream_t s) {
-  using Cfg = StreamCfg<Est, K, (OPT & 1) != 0>;
+  constexpr int P = stream_lead<Est>();
+  constexpr int BPC = kStreamBlocksPerCu;
+  using Cfg = StreamCfg<Est, (OPT & 1) != 0, P, BPC>;
   constexpr int G = 64 / L;
   const int64_t nrg = (a.E + G - 1) / G;
-  const int64_t cap = (int64_t)cu_count() * 2;  // two blocks per CU (LDS)
+  const int64_t cap = (int64_t)cu_count() * BPC;
   const int64_t per_wave = (nrg + Cfg::NC * cap - 1) / (Cfg::NC * cap);
   int64_t blocks = (nrg + Cfg::NC * per_wave - 1) / (Cfg::NC * per_wave);
   if (blocks < 1) blocks = 1;
   KernelArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_kernel<Est, L, K, OPT>), dim3((unsigned)blocks),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_kernel<Est, L, OPT, P, BPC>), dim3((unsigned)blocks),
                          dim3(Cfg::kThreads), params, 0, s);
 }
 
-template <class Est, int L, int K>
+template <class Est, int L>
 inline hipError_t launch_stream(const KernelArgs& a, hipStream_t s) {
   using Tr = Traits<Est>;
   const bool flags = a.has_term || a.has_trunc;
   if constexpr (Tr::kHasOut1) {
     const bool out1 = a.out1 != nullptr;
-    if (flags) return out1 ? launch_stream_one<Est, L, K, 3>(a, s) : launch_stream_one<Est, L, K, 1>(a, s);
-    return out1 ? launch_stream_one<Est, L, K, 2>(a, s) : launch_stream_one<Est, L, K, 0>(a, s);
+    if (flags) return out1 ? launch_stream_one<Est, L, 3>(a, s) : launch_stream_one<Est, L, 1>(a, s);
+    return out1 ? launch_stream_one<Est, L, 2>(a, s) : launch_stream_one<Est, L, 0>(a, s);
   } else if constexpr (Tr::kUsesFlags) {
-    return flags ? launch_stream_one<Est, L, K, 1>(a, s) : launch_stream_one<Est, L, K, 0>(a, s);
+    return flags ? launch_stream_one<Est, L, 1>(a, s) : launch_stream_one<Est, L, 0>(a, s);
   } else {
-    return launch_stream_one<Est, L, K, 0>(a, s);
+    return launch_stream_one<Est, L, 0>(a, s);
   }
 }
 
@@ -153,16 +172,18 @@ inline int stream_team(const KernelArgs& a) {
   else if (a.T == 128) L = 32;
   else if (a.T % 256 == 0) L = 64;
   if (L == 0 || !vector_ok(a, 4, L * 4)) return 0;
+  // flag bytes are fetched 16 at a time
+  if ((uintptr_t)a.term % 16 != 0 || (uintptr_t)a.trunc % 16 != 0) return 0;
   return L;
 }
 
 template <class Est>
 hipError_t launch(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
-  switch (stream_team(a)) {
-    case 16: return launch_stream<Est, 16, 4>(a, s);
-    case 32: return launch_stream<Est, 32, 4>(a, s);
-    case 64: return launch_stream<Est, 64, 4>(a, s);
+  switch (prefer_stream<Est>(a) ? stream_team(a) : 0) {
+    case 16: return launch_stream<Est, 16>(a, s);
+    case 32: return launch_stream<Est, 32>(a, s);
+    case 64: return launch_stream<Est, 64>(a, s);
     default: break;
   }
   const LaunchShape sh = pick_shape(a.T);

@@ -1,6 +1,6 @@
 // rlscan_stream.hpp -- the streaming kernel: a loader wave feeds compute waves
-// through an LDS ring (gfx950 global->LDS DMA), for rows made of whole,
-// aligned tiles.
+// through LDS rings (gfx950 global->LDS DMA), for rows made of whole,
+// aligned tiles of 4 L steps.
 //
 // Why: the scan is HBM-bound, and keeping enough bytes in flight (~64 KiB per
 // CU at ~5.5 TB/s) decides the speed.  A wave that both loads and stores
@@ -8,22 +8,28 @@
 // so waiting for any load also drains pending stores and every later load),
 // and data in flight held in VGPRs costs occupancy.  So each wave gets one
 // kind of memory traffic:
-//   * the loader (wave 0) only issues global->LDS DMA (global_load_lds): the
-//     flag bytes of an item one tick before its input streams and row
-//     values; its waits are exact counts and the data occupies no VGPRs;
+//   * the loader (wave 0) only issues global->LDS DMA: flag bytes, input
+//     streams and row values.  Its waits are exact counts of its own DMA
+//     instructions (they complete in issue order), and the data occupies no
+//     VGPRs;
 //   * the gather wave (wave 1, estimators with truncation bootstraps) reads
-//     the landed flags from LDS, copies them next to the item's data and
-//     DMAs the bootstrap of every truncated step (lanes without one fetch a
-//     single shared, cache-resident line), so that gather never stalls a
-//     compute wave;
+//     landed flags from LDS and DMAs the bootstrap of every truncated step
+//     (lanes without one fetch a single shared, cache-resident line);
 //   * the compute waves read LDS, scan and store; they never wait on memory.
-// Time advances in ticks separated by s_barrier.  At tick t compute wave c
-// scans item t of its own item sequence from data slot t % S, while the
-// loader fills items t + P (data) and t + P + 1 (flags) and the gather wave
-// serves item t + 2.
 //
-// An item is 64*K consecutive elements of every [E,T] array: G = 64 / L whole
-// rows when a row is a single tile (T == L * K), or one tile of one row.  A
+// Time advances in ticks separated by s_barrier; at tick t every compute wave
+// scans item t of its own item sequence.  Under load the memory system is a
+// queue about P ticks deep (whatever is issued lands about P ticks later), so
+// every stage gets a lead of P ticks:
+//   data of item t+P               issued by the loader at tick t,
+//   bootstrap gather of item t+P   issued by the gather wave at tick t, from the
+//   flags of item t+2P             issued by the loader at tick t.
+// Before tick 0 the loader issues the flags of items 0..2P-1 and the data of
+// items 0..P-1 in one burst, and the gather wave serves items 0..P-1 in P
+// warm-up ticks as their flags land.
+//
+// An item is 256 consecutive elements of every [E,T] array: G = 64 / L whole
+// rows when a row is a single tile (T == 4 L), or one tile of one row.  A
 // compute wave walks the tiles of a row in scan order and carries the running
 // value and the boundary inputs (V_{t+1} / EQ_{t+1}, c_{t+1}, done_{t-1})
 // across tiles in registers.
@@ -45,6 +51,32 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0) only.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
 
+// vmcnt <= n for a wave-uniform run-time n (s_waitcnt takes only an
+// immediate, so this is a jump table); n is clamped to [0, 63].
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n <= 0 ? 0 : (n >= 63 ? 63 : n)) {
+#define RLSCAN_WAIT_CASE(i) \
+  case i:                   \
+    wait_vmcnt<i>();        \
+    break;
+#define RLSCAN_WAIT_CASE8(i)                                                                     \
+  RLSCAN_WAIT_CASE(i) RLSCAN_WAIT_CASE(i + 1) RLSCAN_WAIT_CASE(i + 2) RLSCAN_WAIT_CASE(i + 3) \
+  RLSCAN_WAIT_CASE(i + 4) RLSCAN_WAIT_CASE(i + 5) RLSCAN_WAIT_CASE(i + 6) RLSCAN_WAIT_CASE(i + 7)
+    RLSCAN_WAIT_CASE8(0)
+    RLSCAN_WAIT_CASE8(8)
+    RLSCAN_WAIT_CASE8(16)
+    RLSCAN_WAIT_CASE8(24)
+    RLSCAN_WAIT_CASE8(32)
+    RLSCAN_WAIT_CASE8(40)
+    RLSCAN_WAIT_CASE8(48)
+    RLSCAN_WAIT_CASE8(56)
+#undef RLSCAN_WAIT_CASE8
+#undef RLSCAN_WAIT_CASE
+    default:
+      break;
+  }
+}
+
 // Block barrier without the memory fences of __syncthreads (which would drain
 // the loader's in-flight DMA); the empty asm keeps the compiler from moving
 // memory accesses across it.
@@ -54,89 +86,96 @@ __device__ __forceinline__ void tick_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <class Est, int K, bool FLAGS>
+constexpr int kStreamItem = 256;  // elements per item (64 lanes x 4 steps)
+
+template <class Est, bool FLAGS, int P_, int BPC>
 struct StreamCfg {
   using Tr = Traits<Est>;
   static constexpr int NS = Tr::kStreams;
   static constexpr bool USE_FLAGS = FLAGS && Tr::kUsesFlags;
-  static constexpr bool GATHER = USE_FLAGS && Tr::kBackwardRl;  // a gather wave, early flags
-  static constexpr int N = 64 * K;          // elements per item
-  static constexpr int P = NS >= 5 ? 2 : 3;  // items the data DMA runs ahead
-  static constexpr int S = P + 1;           // data ring slots
-  static constexpr int SF = 4;              // early-flag ring slots: flags of item j land from tick j-4 to j-2
-  // bytes of one data slot (streams, bootstraps, flags, row values) and of the flag ring
-  static constexpr int kSlotBytes = 4 * NS * N + (GATHER ? 4 * N : 0) + (USE_FLAGS ? 2 * N : 0) + 16;
-  static constexpr int kFlagBytes = GATHER ? 2 * N : 0;
-  static constexpr int kPerWave = S * kSlotBytes + SF * kFlagBytes;
-  // compute waves per block: fill half of the 160 KiB LDS (two blocks per CU)
-  static constexpr int kLdsBudget = 80 * 1024;
-  // DMA instructions per item and compute wave: data (+ flags when not early), early flags, gather
-  static constexpr int kOpsData = NS * (K / 4) + 1 + ((USE_FLAGS && !GATHER) ? 2 * (K / 4) : 0);
-  static constexpr int kOpsFlags = GATHER ? 2 * (K / 4) : 0;
-  static constexpr int kOpsGather = GATHER ? K / 4 : 0;
-  // Loader schedule (see the kernel): DMA ops per compute wave that stay in
-  // flight at each of its waits.  With early flags: before the start-up
-  // barrier (flags 0..3 and data 0 issued, flags 0-1 complete), before the
-  // first tick (data 0 complete), and every tick (data t+1 and flags t+3
-  // complete while flags t+4 and data t+P were issued last).
-  static constexpr int kWaitPre1 = 2 * kOpsFlags + kOpsData;
-  static constexpr int kWaitPre0 = (P - 1) * kOpsData;
-  static constexpr int kWaitTick = GATHER ? (P == 3 ? 2 * kOpsData + kOpsFlags : kOpsFlags + kOpsData)
-                                          : (P - 1) * kOpsData;
-  static constexpr int kWaitMax = kWaitPre1 > kWaitPre0 ? (kWaitPre1 > kWaitTick ? kWaitPre1 : kWaitTick)
-                                                        : (kWaitPre0 > kWaitTick ? kWaitPre0 : kWaitTick);
-  static constexpr int NC_LDS = kLdsBudget / kPerWave;
-  static constexpr int NC_VM = 63 / kWaitMax;
-  static constexpr int NC_RAW = NC_LDS < NC_VM ? NC_LDS : NC_VM;
-  static constexpr int NC = NC_RAW > 7 ? 7 : (NC_RAW < 1 ? 1 : NC_RAW);
-  static constexpr int kHelpers = GATHER ? 2 : 1;  // loader (+ gather wave)
+  static constexpr bool GATHER = USE_FLAGS && Tr::kBackwardRl;  // a gather wave
+  static constexpr int N = kStreamItem;
+  static constexpr int P = P_;                       // data lead (ticks)
+  static constexpr int LG = GATHER ? P : 0;          // gather lead
+  static constexpr int LF = LG + P;                  // flag lead
+  static constexpr int S = P + 1;                    // data ring slots
+  static constexpr int SF = USE_FLAGS ? LF + 1 : 1;  // flag ring slots
+  static constexpr int kHelpers = GATHER ? 2 : 1;    // loader (+ gather wave)
+  static constexpr int kLdsBudget = 160 * 1024 / BPC;
+  // LDS bytes for nc compute waves (16 bytes of slack per slot for padding)
+  static constexpr int lds_bytes(int nc) {
+    const int slot = 4 * NS * nc * N + (GATHER ? 4 * nc * N : 0) + 16 * nc + 16;
+    const int fslot = USE_FLAGS ? 2 * nc * N : 16;
+    return S * slot + SF * fslot;
+  }
+  // DMA instructions per tick of the loader: flags (16 B per lane, four items
+  // per instruction and array), data (one per stream and item) and row values
+  static constexpr int fops(int nc) { return USE_FLAGS ? 2 * ((nc + 3) / 4) : 0; }
+  static constexpr int dops(int nc) { return NS * nc + 1; }
+  // most DMA instructions the loader ever has in flight: after the start-up
+  // burst, and right after a steady-state issue
+  static constexpr int max_inflight(int nc) {
+    const int a = LF * fops(nc) + P * dops(nc);
+    const int b = P * (fops(nc) + dops(nc));
+    return a > b ? a : b;
+  }
+  static constexpr int pick_nc() {
+    int best = 1;
+    for (int nc = 1; nc + kHelpers <= 16; ++nc)
+      if (lds_bytes(nc) <= kLdsBudget && max_inflight(nc) <= 63 && (!GATHER || P * nc <= 63)) best = nc;
+    return best;
+  }
+  static constexpr int NC = pick_nc();
+  static constexpr int F = fops(NC);
+  static constexpr int D = dops(NC);
   static constexpr int kThreads = 64 * (NC + kHelpers);
+  static_assert(max_inflight(NC) <= 63, "loader DMA in flight must fit the 6-bit counter");
 };
 
-template <class Est, int K, bool FLAGS>
-struct Slot {
-  using C = StreamCfg<Est, K, FLAGS>;
-  float s[C::NS][C::N];
-  float tb[C::GATHER ? C::N : 1];
-  unsigned fl[C::USE_FLAGS ? 2 : 1][C::USE_FLAGS ? C::N / 4 : 1];  // raw flag bytes, 4 per word
-  float rowv[4];
+// One tick's data for all compute waves of a block.
+template <class Cfg>
+struct alignas(16) TickSlot {
+  float s[Cfg::NS][Cfg::NC][Cfg::N];
+  float tb[Cfg::GATHER ? Cfg::NC : 1][Cfg::GATHER ? Cfg::N : 1];
+  float rowv[Cfg::NC * 4];
 };
-
-template <class Est, int K, bool FLAGS>
-struct FlagSlot {
-  using C = StreamCfg<Est, K, FLAGS>;
-  unsigned fl[2][C::GATHER ? C::N / 4 : 1];
+// One tick's flag bytes (terminated, truncated) for all compute waves.
+template <class Cfg>
+struct alignas(16) FlagTick {
+  uint8_t fl[Cfg::USE_FLAGS ? 2 : 1][Cfg::USE_FLAGS ? Cfg::NC : 1][Cfg::USE_FLAGS ? Cfg::N : 4];
 };
 
 // Template parameters: estimator tag, team width L (16, 32 or 64 lanes per
-// row), chunk K (4 or 8 steps per lane), OPT (bit 0: flags present; bit 1:
-// second output).  Requires T % (L * K) == 0, L < 64 only when T == L * K,
-// every dense array aligned to 16 bytes, and T < 2^26.
-template <class Est, int L, int K, int OPT>
-__global__ void __launch_bounds__((StreamCfg<Est, K, (OPT & 1) != 0>::kThreads))
+// row), OPT (bit 0: flags present; bit 1: second output), data lead P, blocks
+// per CU the LDS is split for.  Requires T % (4 L) == 0, L < 64 only when
+// T == 4 L, every dense array aligned to 16 bytes, and T < 2^26.
+template <class Est, int L, int OPT, int P, int BPC>
+__global__ void __launch_bounds__((StreamCfg<Est, (OPT & 1) != 0, P, BPC>::kThreads))
 stream_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
-  using Cfg = StreamCfg<Est, K, (OPT & 1) != 0>;
-  using SlotT = Slot<Est, K, (OPT & 1) != 0>;
-  using FlagT = FlagSlot<Est, K, (OPT & 1) != 0>;
+  using Cfg = StreamCfg<Est, (OPT & 1) != 0, P, BPC>;
+  using SlotT = TickSlot<Cfg>;
+  using FlagT = FlagTick<Cfg>;
+  constexpr int K = 4;
   constexpr bool REV = Est::kReverse;
   constexpr int NS = Cfg::NS;
   constexpr int NC = Cfg::NC;
   constexpr int S = Cfg::S;
   constexpr int SF = Cfg::SF;
-  constexpr int P = Cfg::P;
+  constexpr int LG = Cfg::LG;
+  constexpr int LF = Cfg::LF;
   constexpr int G = 64 / L;    // rows per item when a row is one tile
   constexpr int SPAN = L * K;  // tile length
   constexpr bool USE_FLAGS = Cfg::USE_FLAGS;
   constexpr bool GATHER = Cfg::GATHER;
   constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
   constexpr int FIRST_COMPUTE = Cfg::kHelpers;
-  static_assert(K % 4 == 0 && K <= 8, "chunk of 4 or 8 steps");
-  static_assert(P == 2 || P == 3, "lead of two or three items");
-  static_assert(S * NC * sizeof(SlotT) + SF * NC * sizeof(FlagT) <= 96 * 1024, "LDS ring");
+  static_assert(P >= 1 && P <= 4, "lead of one to four items");
+  static_assert(NC * G <= 64, "one row-value DMA per tick");
+  static_assert(S * sizeof(SlotT) + SF * sizeof(FlagT) <= (size_t)Cfg::kLdsBudget, "LDS rings");
 
-  __shared__ SlotT ring[S][NC];
-  __shared__ FlagT fring[SF][NC];
+  __shared__ SlotT ring[S];
+  __shared__ FlagT fring[SF];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -148,7 +187,7 @@ stream_kernel(const KernelArgs p) {
   const int64_t ncw = (int64_t)gridDim.x * NC;
   const int64_t cw0 = (int64_t)blockIdx.x * NC;  // first compute wave of this block
   // block-uniform tick count: the block's first compute wave has the most row groups
-  const int64_t ticks = (cw0 < nrg ? (nrg - cw0 + ncw - 1) / ncw : 0) * ntiles;
+  const int ticks = (int)((cw0 < nrg ? (nrg - cw0 + ncw - 1) / ncw : 0) * ntiles);
 
   // An item position (the same for every compute wave of the block): the j-th
   // row group of the wave, ts-th tile in scan order, with the ring slots it
@@ -167,21 +206,18 @@ stream_kernel(const KernelArgs p) {
     q.fslot = q.fslot + 1 == SF ? 0 : q.fslot + 1;
     return q;
   };
-  auto item_rg = [&](int c, const Cursor& q) { return cw0 + c + q.j * ncw; };
   auto item_tile = [&](const Cursor& q) { return REV ? ntiles - 1 - q.ts : q.ts; };
   const int64_t last_rg = nrg - 1;
-  // element index of an item's first element, rows past E clamped
-  auto item_base = [&](int c, const Cursor& cur, int64_t& base) {
-    int64_t rg = item_rg(c, cur);
+  // element index of the first element of compute wave c's item, rows past E clamped
+  auto item_base = [&](int64_t c, const Cursor& cur, int64_t& base) {
+    int64_t rg = cw0 + c + cur.j * ncw;
     rg = rg < last_rg ? rg : last_rg;
     base = (G > 1) ? rg * G * T : rg * T + item_tile(cur) * SPAN;
     return rg;
   };
-  // element offset of this lane's q-th 4-element group inside the item (G > 1
-  // only when T == SPAN, so rows split at the constant SPAN); rows past E read
-  // row E - 1
-  auto lane_off = [&](int64_t rg, int q) -> uint32_t {
-    const uint32_t f = (uint32_t)(q * 256 + lane * 4);
+  // offset of element f of an item (G > 1 only when T == SPAN, so rows split
+  // at the constant SPAN); rows past E read row E - 1
+  auto elem_off = [&](int64_t rg, uint32_t f) -> uint32_t {
     if constexpr (G > 1) {
       const int64_t row = rg * G + f / SPAN;
       if (row >= E) return (uint32_t)((E - 1 - rg * G) * SPAN + f % SPAN);
@@ -191,142 +227,146 @@ stream_kernel(const KernelArgs p) {
 
   if (wave == 0) {
     // ================================================================ loader
-    // Tick t issues the flags of item t+4 (early-flag estimators) and the data
-    // of item t+P; before the barrier that ends tick t, the data of item t+1
-    // and the flags of item t+3 are complete.
+    constexpr int F = Cfg::F, D = Cfg::D;
     const float* srcs[5] = {p.r, p.v, p.aux, p.pi, p.mu};
+    // flags of one tick: instruction q, lane l -> item 4q + l/16, bytes 16 (l%16) ..
     auto issue_flags = [&](const Cursor& cur) __attribute__((always_inline)) {
-      if constexpr (GATHER) {
+      if constexpr (USE_FLAGS) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          int64_t base;
-          const int64_t rg = item_base(c, cur, base);
-          FlagT& fs = fring[cur.fslot][c];
-#pragma unroll
-          for (int q = 0; q < K / 4; ++q) {
-            const uint32_t off = lane_off(rg, q);
-            __builtin_amdgcn_global_load_lds((gbl_void_ptr)(p.term + base + off), (lds_void_ptr)&fs.fl[0][q * 64], 4,
-                                             0, 0);
-            __builtin_amdgcn_global_load_lds((gbl_void_ptr)(p.trunc + base + off), (lds_void_ptr)&fs.fl[1][q * 64], 4,
-                                             0, 0);
+        for (int q = 0; q < (NC + 3) / 4; ++q) {
+          const int c = 4 * q + (lane >> 4);
+          if (c < NC) {
+            int64_t base;
+            const int64_t rg = item_base(c, cur, base);
+            const uint32_t off = elem_off(rg, (uint32_t)(lane & 15) * 16);
+            __builtin_amdgcn_global_load_lds((gbl_void_ptr)(p.term + base + off),
+                                             (lds_void_ptr)&fring[cur.fslot].fl[0][4 * q][0], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void_ptr)(p.trunc + base + off),
+                                             (lds_void_ptr)&fring[cur.fslot].fl[1][4 * q][0], 16, 0, 0);
           }
         }
       }
     };
     auto issue_data = [&](const Cursor& cur) __attribute__((always_inline)) {
+      SlotT& sl = ring[cur.slot];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         int64_t base;
         const int64_t rg = item_base(c, cur, base);
-        SlotT& sl = ring[cur.slot][c];
+        const uint32_t off = elem_off(rg, (uint32_t)lane * 4);
 #pragma unroll
-        for (int q = 0; q < K / 4; ++q) {
-          const uint32_t off = lane_off(rg, q);
-#pragma unroll
-          for (int st = 0; st < NS; ++st)
-            __builtin_amdgcn_global_load_lds((gbl_void_ptr)at(srcs[st] + base, off), (lds_void_ptr)&sl.s[st][q * 256],
-                                             16, 0, 0);
-          if constexpr (USE_FLAGS && !GATHER) {
-            __builtin_amdgcn_global_load_lds((gbl_void_ptr)(p.term + base + off), (lds_void_ptr)&sl.fl[0][q * 64], 4,
-                                             0, 0);
-            __builtin_amdgcn_global_load_lds((gbl_void_ptr)(p.trunc + base + off), (lds_void_ptr)&sl.fl[1][q * 64], 4,
-                                             0, 0);
-          }
-        }
-        // row values: lane i (< G) lands in rowv[i]; the DMA writes one word per active
-        // lane, so the other lanes stay off
-        if (lane < G) {
-          int64_t row = rg * G + lane;
-          row = row < E ? row : E - 1;
-          __builtin_amdgcn_global_load_lds((gbl_void_ptr)(p.row + row), (lds_void_ptr)&sl.rowv[0], 4, 0, 0);
-        }
+        for (int st = 0; st < NS; ++st)
+          __builtin_amdgcn_global_load_lds((gbl_void_ptr)at(srcs[st] + base, off), (lds_void_ptr)&sl.s[st][c][0], 16,
+                                           0, 0);
+      }
+      // row values: lane c*G + g -> row g of compute wave c's item
+      if (lane < NC * G) {
+        int64_t base;
+        const int64_t rg = item_base(lane / G, cur, base);
+        int64_t row = rg * G + lane % G;
+        row = row < E ? row : E - 1;
+        __builtin_amdgcn_global_load_lds((gbl_void_ptr)(p.row + row), (lds_void_ptr)&sl.rowv[0], 4, 0, 0);
       }
     };
-    Cursor cd{0, 0, 0, 0};
-    if constexpr (GATHER) {
-      Cursor cf = cd;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {  // flags of items 0..3
-        issue_flags(cf);
-        cf = advance(cf);
-      }
-      issue_data(cd);  // data of item 0
+    // start-up burst: flags of items 0..LF-1, then data of items 0..P-1
+    const int LFv = ticks < LF ? ticks : LF;
+    const int Pv = ticks < P ? ticks : P;
+    Cursor cf{0, 0, 0, 0}, cd{0, 0, 0, 0};
+    for (int k = 0; k < LFv; ++k) {
+      issue_flags(cf);
+      cf = advance(cf);
+    }
+    for (int k = 0; k < Pv; ++k) {
+      issue_data(cd);
       cd = advance(cd);
-      wait_vmcnt<NC * Cfg::kWaitPre1>();  // flags of items 0, 1 complete
-      tick_barrier();                     // start-up barrier: the gather wave serves items 0, 1
+    }
+    int cum = LFv * F + Pv * D;  // DMA instructions issued so far
+    // warm-up ticks: before the barrier that ends warm-up tick w (w = -LG-1 .. -1)
+    // the flags of item w+LG+1 have landed, and at w = -1 also the data of item 0
 #pragma unroll
-      for (int i = 1; i < P; ++i) {
-        issue_data(cd);
-        cd = advance(cd);
-      }
-      wait_vmcnt<NC * Cfg::kWaitPre0>();  // data of item 0 (and flags of item 2) complete
+    for (int w = -LG - 1; w <= -1; ++w) {
+      const int k = w + LG + 1;
+      int n = cum;
+      if (USE_FLAGS && k < LFv) n = cum - (k + 1) * F;
+      if (w == -1) n = (Pv - 1) * D < n ? (Pv - 1) * D : n;
+      wait_vmcnt_dyn(n);
       tick_barrier();
-      for (int64_t t = 0; t < ticks; ++t) {
+    }
+    // steady ticks: issue flags of item t+LF and data of item t+P; before the
+    // barrier that ends tick t the data of item t+1 has landed, and with it
+    // (issued no later) the flags of item t+1+LG
+    int hist[P];  // hist[i]: DMA instructions issued up to the end of tick t-i
+#pragma unroll
+    for (int i = 0; i < P; ++i) hist[i] = 0;
+    for (int t = 0; t < ticks; ++t) {
+      if (t + LF < ticks) {
         issue_flags(cf);
         cf = advance(cf);
+        cum += F;
+      }
+      if (t + P < ticks) {
         issue_data(cd);
         cd = advance(cd);
-        wait_vmcnt<NC * Cfg::kWaitTick>();
-        tick_barrier();
+        cum += D;
       }
-    } else {
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        issue_data(cd);
-        cd = advance(cd);
+      for (int i = P - 1; i > 0; --i) hist[i] = hist[i - 1];
+      hist[0] = cum;
+      if (t + 1 < ticks) {
+        const int req = (t + 1 < P) ? LFv * F + (t + 2) * D : hist[P - 1];
+        wait_vmcnt_dyn(cum - req);
       }
-      wait_vmcnt<NC * Cfg::kWaitPre0>();  // data of item 0 complete
       tick_barrier();
-      for (int64_t t = 0; t < ticks; ++t) {
-        issue_data(cd);
-        cd = advance(cd);
-        wait_vmcnt<NC * Cfg::kWaitTick>();
-        tick_barrier();
-      }
     }
     wait_vmcnt<0>();  // no DMA into this block's LDS may outlive the block
   } else if (GATHER && wave == 1) {
     // ================================================================ gather wave
-    // Tick t serves item t+2 (its flags landed before the barrier that opened
-    // tick t); before the barrier that ends tick t, item t+1 is complete.
+    // Serves item k at tick k-LG (warm-up ticks for k < LG): reads its landed
+    // flags and DMAs the bootstrap chunk of every lane that has a truncated,
+    // not terminated step.  Before the barrier that ends tick t, the gather
+    // of item t+1 has landed.
+    constexpr int GO = NC;  // DMA instructions per served item-tick
     auto serve = [&](const Cursor& cur) __attribute__((always_inline)) {
+      SlotT& sl = ring[cur.slot];
+      const FlagT& fs = fring[cur.fslot];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         int64_t base;
         const int64_t rg = item_base(c, cur, base);
-        SlotT& sl = ring[cur.slot][c];
-        const FlagT& fs = fring[cur.fslot][c];
-#pragma unroll
-        for (int q = 0; q < K / 4; ++q) {
-          const unsigned w_t = fs.fl[0][q * 64 + lane];
-          const unsigned w_r = fs.fl[1][q * 64 + lane];
-          sl.fl[0][q * 64 + lane] = w_t;
-          sl.fl[1][q * 64 + lane] = w_r;
-          // some step truncated and not terminated (nonzero byte of w_r over a zero byte of w_t)
-          const unsigned m_t = w_t & (p.has_term ? ~0u : 0u);
-          const unsigned m_r = w_r & (p.has_trunc ? ~0u : 0u);
-          const unsigned nz_t = (((m_t & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_t) & 0x80808080u;
-          const unsigned nz_r = (((m_r & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_r) & 0x80808080u;
-          const bool need = (nz_r & ~nz_t) != 0u && p.has_tboot;
-          const float* src = need ? at(p.tboot + base, lane_off(rg, q)) : p.tboot;
-          __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)&sl.tb[q * 256], 16, 0, 0);
-        }
+        const unsigned w_t = reinterpret_cast<const unsigned*>(&fs.fl[0][c][0])[lane];
+        const unsigned w_r = reinterpret_cast<const unsigned*>(&fs.fl[1][c][0])[lane];
+        // some step truncated and not terminated (nonzero byte of w_r over a zero byte of w_t)
+        const unsigned m_t = w_t & (p.has_term ? ~0u : 0u);
+        const unsigned m_r = w_r & (p.has_trunc ? ~0u : 0u);
+        const unsigned nz_t = (((m_t & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_t) & 0x80808080u;
+        const unsigned nz_r = (((m_r & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_r) & 0x80808080u;
+        const bool need = (nz_r & ~nz_t) != 0u && p.has_tboot;
+        const float* src = need ? at(p.tboot + base, elem_off(rg, (uint32_t)lane * 4)) : p.tboot;
+        __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)&sl.tb[c][0], 16, 0, 0);
       }
     };
+    // gathers allowed in flight at the end of tick w: those of items w+2 .. min(w+LG, ticks-1)
+    auto after = [&](int w) {
+      const int hi = (w + LG < ticks - 1) ? w + LG : ticks - 1;
+      const int n = hi - (w + 1);
+      return n > 0 ? n * GO : 0;
+    };
     Cursor cg{0, 0, 0, 0};
-    tick_barrier();  // start-up barrier: flags of items 0, 1 have landed
-    serve(cg);
-    cg = advance(cg);
-    serve(cg);
-    cg = advance(cg);
-    wait_vmcnt<NC * Cfg::kOpsGather>();  // item 0 complete
-    wait_lgkm0();
-    tick_barrier();
-    for (int64_t t = 0; t < ticks; ++t) {
-      serve(cg);
-      cg = advance(cg);
-      wait_vmcnt<NC * Cfg::kOpsGather>();
-      wait_lgkm0();
+#pragma unroll
+    for (int w = -LG - 1; w <= -1; ++w) {
+      if (w >= -LG && w + LG < ticks) {
+        serve(cg);
+        cg = advance(cg);
+      }
+      if (w == -1) wait_vmcnt_dyn(after(w));
+      tick_barrier();
+    }
+    for (int t = 0; t < ticks; ++t) {
+      if (t + LG < ticks) {
+        serve(cg);
+        cg = advance(cg);
+      }
+      if (t + 1 < ticks) wait_vmcnt_dyn(after(t));
       tick_barrier();
     }
     wait_vmcnt<0>();
@@ -347,12 +387,12 @@ stream_kernel(const KernelArgs p) {
     double C = 0.0;
     PredIn carry{0.0f, 0.0, 0u};  // boundary inputs handed from the previous tile of the row
 
-    tick_barrier();
-    if constexpr (GATHER) tick_barrier();  // the gather wave's start-up tick
+#pragma unroll
+    for (int w = -LG - 1; w <= -1; ++w) tick_barrier();
     Cursor cur{0, 0, 0, 0};
-    for (int64_t t = 0; t < ticks; ++t, cur = advance(cur)) {
-      const SlotT& sl = ring[cur.slot][c];
-      const int64_t rg = item_rg(c, cur);
+    for (int t = 0; t < ticks; ++t, cur = advance(cur)) {
+      const SlotT& sl = ring[cur.slot];
+      const int64_t rg = cw0 + c + cur.j * ncw;
       const int64_t tile = item_tile(cur);
       const bool first_tile = cur.ts == 0;
       const int64_t row = rg * G + team;
@@ -362,33 +402,24 @@ stream_kernel(const KernelArgs p) {
       LaneIn<Est, K> d;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-#pragma unroll
-        for (int q = 0; q < K / 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(&sl.s[st][lds_idx + 4 * q]);
-          d.s[st][4 * q + 0] = v.x; d.s[st][4 * q + 1] = v.y; d.s[st][4 * q + 2] = v.z; d.s[st][4 * q + 3] = v.w;
-        }
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sl.s[st][c][lds_idx]);
+        d.s[st][0] = v.x; d.s[st][1] = v.y; d.s[st][2] = v.z; d.s[st][3] = v.w;
       }
       if constexpr (GATHER) {
-#pragma unroll
-        for (int q = 0; q < K / 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(&sl.tb[lds_idx + 4 * q]);
-          d.tb[4 * q + 0] = v.x; d.tb[4 * q + 1] = v.y; d.tb[4 * q + 2] = v.z; d.tb[4 * q + 3] = v.w;
-        }
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sl.tb[c][lds_idx]);
+        d.tb[0] = v.x; d.tb[1] = v.y; d.tb[2] = v.z; d.tb[3] = v.w;
       } else {
 #pragma unroll
         for (int m = 0; m < K; ++m) d.tb[m] = 0.0f;
       }
-      d.rowv = sl.rowv[team];
+      d.rowv = sl.rowv[c * G + team];
       unsigned tbits = 0, rbits = 0;
       if constexpr (USE_FLAGS) {
-        unsigned tw[K / 4], rw[K / 4];
-#pragma unroll
-        for (int q = 0; q < K / 4; ++q) {
-          tw[q] = sl.fl[0][lds_idx / 4 + q];
-          rw[q] = sl.fl[1][lds_idx / 4 + q];
-        }
-        tbits = flag_bits_words<K / 4>(tw) & tmask;
-        rbits = flag_bits_words<K / 4>(rw) & rmask;
+        const FlagT& fs = fring[cur.fslot];
+        const unsigned tw[1] = {*reinterpret_cast<const unsigned*>(&fs.fl[0][c][lds_idx])};
+        const unsigned rw[1] = {*reinterpret_cast<const unsigned*>(&fs.fl[1][c][lds_idx])};
+        tbits = flag_bits_words<1>(tw) & tmask;
+        rbits = flag_bits_words<1>(rw) & rmask;
       }
 
       if (first_tile) {
