@@ -45,7 +45,8 @@
  *             never synchronises.  Outputs are valid once the stream has
  *             reached that point.
  * Errors      Validation happens before any HIP call and returns:
- *               RLSCAN_ERR_SHAPE  E < 0, T < 0, or E*T overflows int64;
+ *               RLSCAN_ERR_SHAPE  E < 0, T < 0, T >= RLSCAN_MAX_T (2^30), or
+ *                                 E*T overflows int64;
  *               RLSCAN_ERR_PARAM  a parameter is non-finite or out of range;
  *               RLSCAN_ERR_NULL   a required pointer is NULL while E*T > 0;
  *               RLSCAN_ERR_ALIGN  a float pointer is not 4-byte aligned;
@@ -64,6 +65,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Longest row (time steps) any entry point accepts: rows are addressed with
+ * 32-bit byte offsets. */
+#define RLSCAN_MAX_T ((int64_t)1 << 30)
 
 typedef enum rlscan_status {
   RLSCAN_OK = 0,

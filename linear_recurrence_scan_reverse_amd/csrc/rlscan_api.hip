@@ -16,9 +16,10 @@ using rlscan::KernelArgs;
 bool finite(float x) { return std::isfinite(x); }
 bool in_unit(float x) { return finite(x) && x >= 0.0f && x <= 1.0f; }
 
-// E, T >= 0 and E*T*8 bytes representable (int64).
+// E, T >= 0, T below 2^30 (the kernels address a row with 32-bit byte
+// offsets) and E*T*8 bytes representable (int64).
 rlscan_status check_shape(int64_t E, int64_t T) {
-  if (E < 0 || T < 0) return RLSCAN_ERR_SHAPE;
+  if (E < 0 || T < 0 || T >= RLSCAN_MAX_T) return RLSCAN_ERR_SHAPE;
   if (T > 0 && E > (INT64_MAX / 8) / T) return RLSCAN_ERR_SHAPE;
   return RLSCAN_OK;
 }
@@ -96,7 +97,7 @@ const char* rlscan_status_string(rlscan_status s) {
   switch (s) {
     case RLSCAN_OK: return "ok";
     case RLSCAN_ERR_NULL: return "a required pointer is NULL";
-    case RLSCAN_ERR_SHAPE: return "invalid shape: E or T negative, or E*T too large";
+    case RLSCAN_ERR_SHAPE: return "invalid shape: E or T negative, T >= 2^30, or E*T too large";
     case RLSCAN_ERR_PARAM: return "invalid parameter: non-finite, or outside its range";
     case RLSCAN_ERR_HIP: return "HIP kernel launch failed";
     case RLSCAN_ERR_ALIGN: return "a float pointer is not 4-byte aligned";

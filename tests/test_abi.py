@@ -71,6 +71,9 @@ def test_shape_errors(lib):
     assert lib.rlscan_gae(A, B, None, None, None, None, C, None, 4, -1, 0.99, 0.95, S) == ERR_SHAPE
     assert lib.rlscan_gae(A, B, None, None, None, None, C, None, 2 ** 40, 2 ** 40, 0.99, 0.95, S) == ERR_SHAPE
     assert lib.rlscan_linear_scan(A, B, None, C, -3, 1, 1, S) == ERR_SHAPE
+    # rows longer than 2^30 - 1 steps are rejected before any launch
+    assert lib.rlscan_episodic_prefix_sum(A, None, None, None, C, 1, 2 ** 30, S) == ERR_SHAPE
+    assert lib.rlscan_linear_scan(A, B, None, C, 1, 2 ** 30, 0, S) == ERR_SHAPE
 
 
 @pytest.mark.parametrize("g,l", [(1.5, 0.9), (-0.1, 0.9), (0.9, 1.01), (math.nan, 0.5), (0.5, math.inf)])
