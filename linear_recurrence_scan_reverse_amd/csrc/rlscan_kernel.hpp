@@ -547,7 +547,7 @@ template <class Est, int K> struct RowData : LaneIn<Est, K> {
 // VEC (rows aligned for K-wide vector accesses and T % SPAN == 0, so every
 // tile is whole; otherwise every element is loaded at a clamped column), OPT
 // (bit 0: a flag array is present; bit 1: the second output is written).
-// The host guarantees T < 2^26, so every in-wave element offset fits 32 bits.
+// The C ABI guarantees T < 2^30, so every in-row byte offset fits 32 bits.
 template <class Est, int L, int K, int W, int R, bool VEC, int OPT>
 __global__ void __launch_bounds__(BlockShape<W>::kThreads)
 scan_kernel(const KernelArgs p) {

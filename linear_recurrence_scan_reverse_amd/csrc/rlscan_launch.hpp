@@ -166,7 +166,6 @@ inline hipError_t launch_stream(const KernelArgs& a, hipStream_t s) {
 
 // The streaming kernel takes rows made of whole 16-byte-aligned tiles.
 inline int stream_team(const KernelArgs& a) {
-  if (a.T >= ((int64_t)1 << 26)) return 0;
   int L = 0;
   if (a.T == 64) L = 16;
   else if (a.T == 128) L = 32;

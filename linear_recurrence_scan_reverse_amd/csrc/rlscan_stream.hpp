@@ -148,7 +148,8 @@ struct alignas(16) FlagTick {
 // Template parameters: estimator tag, team width L (16, 32 or 64 lanes per
 // row), OPT (bit 0: flags present; bit 1: second output), data lead P, blocks
 // per CU the LDS is split for.  Requires T % (4 L) == 0, L < 64 only when
-// T == 4 L, every dense array aligned to 16 bytes, and T < 2^26.
+// T == 4 L, every dense array and flag array aligned to 16 bytes, and
+// T < 2^30 (checked by the C ABI).
 template <class Est, int L, int OPT, int P, int BPC>
 __global__ void __launch_bounds__((StreamCfg<Est, (OPT & 1) != 0, P, BPC>::kThreads))
 stream_kernel(const KernelArgs p) {
