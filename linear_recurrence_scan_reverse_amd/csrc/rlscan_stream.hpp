@@ -88,6 +88,17 @@ __device__ __forceinline__ void tick_barrier() {
 
 constexpr int kStreamItem = 256;  // elements per item (64 lanes x 4 steps)
 
+// Most compute waves per block for an estimator.  Measured at 16384 x 256
+// (two blocks per CU, lead 2): a power of two that splits the rows evenly over
+// the blocks beats filling the LDS for the light estimators, while V-trace and
+// Retrace are fastest with as many waves as the LDS holds.
+template <class Est>
+constexpr int stream_nc_cap() {
+  if constexpr (__is_same(Est, Vtrace) || __is_same(Est, Retrace)) return 16;
+  if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae)) return 4;
+  return 8;
+}
+
 template <class Est, bool FLAGS, int P_, int BPC>
 struct StreamCfg {
   using Tr = Traits<Est>;
@@ -121,7 +132,7 @@ struct StreamCfg {
   }
   static constexpr int pick_nc() {
     int best = 1;
-    for (int nc = 1; nc + kHelpers <= 16; ++nc)
+    for (int nc = 1; nc + kHelpers <= 16 && nc <= stream_nc_cap<Est>(); ++nc)
       if (lds_bytes(nc) <= kLdsBudget && max_inflight(nc) <= 63 && (!GATHER || P * nc <= 63)) best = nc;
     return best;
   }
