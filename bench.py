@@ -189,6 +189,29 @@ def copy_ceiling(torch, device, nbytes=1 << 30, reps=20):
     return 2 * nbytes * reps / secs / 1e9
 
 
+def copy_same_bytes(torch, device, nbytes, reps=50):
+    """Practical ceiling at one launch's size: device copies that move the same
+    bytes (half read, half written), rotating over > 1 GiB of buffers so the
+    256 MB MALL cannot serve them.  Returns GB/s."""
+    half = max(4, (nbytes // 2) // 4 * 4)
+    nsets = int(min(64, max(2, -(-(1 << 30) // (2 * half)) + 1)))
+    src = [torch.empty(half, dtype=torch.uint8, device=device).fill_(1) for _ in range(nsets)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=device) for _ in range(nsets)]
+    for i in range(nsets):
+        dst[i].copy_(src[i])
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(reps):
+        dst[i % nsets].copy_(src[i % nsets])
+    e.record()
+    e.synchronize()
+    secs = s.elapsed_time(e) / 1e3
+    del src, dst
+    return 2 * half * reps / secs / 1e9
+
+
 def read_traffic(est, workload):
     """HBM bytes per launch of one estimator's kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a calibration copy), or None
@@ -339,8 +362,11 @@ def main():
             "GBps": b / (us * 1e-6) / 1e9,
             "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
         }
-        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak" % (n, us, per[n]["GBps"],
-                                                              100 * per[n]["frac_of_peak"]))
+    for n in names:
+        per[n]["copy_same_bytes_GBps"] = round(copy_same_bytes(torch, device, per[n]["alg_bytes"]), 1)
+        per[n]["frac_of_copy"] = round(per[n]["GBps"] / per[n]["copy_same_bytes_GBps"], 4)
+        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  %5.1f%% of a same-size copy" % (
+            n, per[n]["us_per_launch"], per[n]["GBps"], 100 * per[n]["frac_of_peak"], 100 * per[n]["frac_of_copy"]))
 
     dom = max(per, key=lambda k: per[k]["us_per_launch"])
     traffic, traffic_src = read_traffic(dom, w.name)

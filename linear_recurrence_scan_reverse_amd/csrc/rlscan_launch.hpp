@@ -26,8 +26,11 @@ inline LaunchShape pick_shape(int64_t T) {
   return {64, 4, 4};
 }
 
-// Resident blocks per CU the persistent grid aims for.
-inline int blocks_per_cu(const LaunchShape&) { return 4; }
+// Resident blocks per CU the persistent grid aims for (discounted returns, the
+// lightest kernel, measured faster with more waves in flight: 11.4 vs 11.9 us
+// at 16384 x 256).
+template <class Est>
+inline int blocks_per_cu(const LaunchShape&) { return __is_same(Est, DiscountedReturn) ? 8 : 4; }
 
 // Rows a team scans side by side per item.  A lane must keep enough bytes in
 // flight to cover HBM latency (Little's law at ~5.5 TB/s over 256 CUs asks
@@ -83,7 +86,7 @@ inline hipError_t launch_one(const KernelArgs& a, hipStream_t s, const LaunchSha
   constexpr int R = rows_per_item<Est, K>();
   const int64_t groups = (a.E + R - 1) / R;
   int64_t blocks = (groups + TEAMS - 1) / TEAMS;
-  const int64_t resident = (int64_t)cu_count() * blocks_per_cu(sh);
+  const int64_t resident = (int64_t)cu_count() * blocks_per_cu<Est>(sh);
   if (blocks > resident) blocks = resident;
   KernelArgs arg = a;
   void* params[] = {&arg};
