@@ -84,6 +84,7 @@ def alg_bytes(name, d, E, T, with_flags=True):
         "retrace": 5 * f + flags + sparse + row + f,
         "eligibility_traces": f + flags + row + f,
         "episodic_prefix_sum": f + flags + row + f,
+        "returns_and_td_lambda": 2 * f + flags + sparse + row + 2 * f,
     }
     return table[name]
 
@@ -123,6 +124,11 @@ class Runner:
         elif name == "td_lambda":
             rc = L.rlscan_td_lambda(p["r"], p["v"], p["terminated"], p["truncated"], p["bootstrap_value"],
                                     p["trunc_bootstrap"], p["out_" + name], E, T, w.gamma, w.lam, st)
+        elif name == "returns_and_td_lambda":
+            rc = L.rlscan_returns_and_td_lambda(p["r"], p["v"], p["terminated"], p["truncated"],
+                                                p["bootstrap_value"], p["trunc_bootstrap"],
+                                                p["out_discounted_returns"], p["out_td_lambda"], E, T,
+                                                w.gamma, w.lam, st)
         elif name == "gae":
             rc = L.rlscan_gae(p["r"], p["v"], p["terminated"], p["truncated"], p["bootstrap_value"],
                               p["trunc_bootstrap"], p["out_" + name], None, E, T, w.gamma, w.lam, st)
@@ -368,6 +374,23 @@ def main():
         log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  %5.1f%% of a same-size copy" % (
             n, per[n]["us_per_launch"], per[n]["GBps"], 100 * per[n]["frac_of_peak"], 100 * per[n]["frac_of_copy"]))
 
+    # ---- the one-pass returns + TD(lambda) entry (not part of the step)
+    fused = None
+    if "discounted_returns" in names and "td_lambda" in names:
+        n = "returns_and_td_lambda"
+        reps = max(args.steps, 20)
+        for _ in range(3):
+            runner.call(n, runner.next_set())
+        s = time_region(runner, lambda: runner.call(n, runner.next_set()), reps)
+        us = s / reps * 1e6
+        b = alg_bytes(n, d, w.E, w.T)
+        sep = per["discounted_returns"]["us_per_launch"] + per["td_lambda"]["us_per_launch"]
+        fused = {n: {"us_per_launch": round(us, 3), "alg_bytes": b, "GBps": b / (us * 1e-6) / 1e9,
+                     "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                     "separate_calls_us": round(sep, 3), "speedup_vs_separate": round(sep / us, 3)}}
+        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  (separate calls: %.2f us)" % (
+            "returns+td_lambda", us, fused[n]["GBps"], 100 * fused[n]["frac_of_peak"], sep))
+
     dom = max(per, key=lambda k: per[k]["us_per_launch"])
     traffic, traffic_src = read_traffic(dom, w.name)
     roofline = {
@@ -415,6 +438,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_estimator": per,
+        "one_pass_entries": fused,
         "copy_ceiling_GBps": round(ceiling, 1),
         "kernel_source_sha256": kernel_source_hash(),
         "context": "rl-triton pages: 1.6-5.70x full-call speedup vs a vectorized torch.compile scan "

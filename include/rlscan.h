@@ -112,6 +112,24 @@ rlscan_status rlscan_td_lambda(const float *rewards, const float *values,
                                float *returns, int64_t E, int64_t T, float gamma, float lambda,
                                hipStream_t stream);
 
+/* Discounted return and TD(lambda) return of the same rollout in one pass
+ * (the two entries above, sharing every input read).  The pages pair these
+ * two value targets in their benchmark configurations and name fused kernels
+ * that read raw inputs once (gist.science summary of rl-triton,
+ * "Methodologie" section 2); reading rewards, flags and bootstraps once for
+ * both outputs is that principle applied across two estimators.
+ * In:  as rlscan_td_lambda.
+ * Out: returns [E,T] (required) = rlscan_discounted_returns;
+ *      td_returns [E,T] (required) = rlscan_td_lambda with the same gamma.
+ * Rows of whole 256-step tiles (T = 64, 128 or a multiple of 256, arrays
+ * 16-byte aligned) take one kernel; other shapes run the two single-output
+ * kernels in turn on `stream`.  gamma, lambda in [0,1]. */
+rlscan_status rlscan_returns_and_td_lambda(const float *rewards, const float *values,
+                                          const uint8_t *terminated, const uint8_t *truncated,
+                                          const float *bootstrap_value, const float *trunc_bootstrap,
+                                          float *returns, float *td_returns, int64_t E, int64_t T,
+                                          float gamma, float lambda, hipStream_t stream);
+
 /* Generalized Advantage Estimation (Schulman et al. 2016):
  *   delta_t = r_t + gamma * nu_t - V_t, nu_t = V_{t+1} while continuing, else
  *             the cut's successor value;

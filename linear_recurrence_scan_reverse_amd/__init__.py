@@ -18,7 +18,7 @@ import threading
 
 __all__ = [
     "RlscanError", "lib", "library_path", "version",
-    "discounted_returns", "td_lambda", "gae", "vtrace", "retrace",
+    "discounted_returns", "td_lambda", "returns_and_td_lambda", "gae", "vtrace", "retrace",
     "eligibility_traces", "episodic_prefix_sum", "linear_scan",
 ]
 
@@ -36,6 +36,7 @@ _int = ctypes.c_int
 _SIGNATURES = {
     "rlscan_discounted_returns": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
     "rlscan_td_lambda": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _vp],
+    "rlscan_returns_and_td_lambda": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _vp],
     "rlscan_gae": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _vp],
     "rlscan_vtrace": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _f32, _f32, _vp],
     "rlscan_retrace": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _vp],
@@ -201,6 +202,28 @@ def td_lambda(rewards, values, terminated=None, truncated=None, bootstrap_value=
     _call("rlscan_td_lambda", _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(out),
           E, T, float(gamma), float(lam), _stream(dev, stream))
     return out
+
+
+def returns_and_td_lambda(rewards, values, terminated=None, truncated=None, bootstrap_value=None,
+                          trunc_bootstrap=None, *, gamma=0.99, lam=0.95, returns=None, td_returns=None,
+                          stream=None):
+    """Discounted returns and TD(lambda) returns of one rollout in one pass.
+
+    Returns (returns, td_returns), equal to ``discounted_returns`` and
+    ``td_lambda`` with the same arguments."""
+    shape, dev = _prep(rewards, "rewards")
+    E, T = shape
+    r = _check_f32(rewards, "rewards", shape, dev)
+    v = _check_f32(values, "values", shape, dev)
+    te = _check_flags(terminated, "terminated", shape, dev)
+    tr = _check_flags(truncated, "truncated", shape, dev)
+    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
+    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
+    returns = _out(returns, "returns", shape, dev)
+    td_returns = _out(td_returns, "td_returns", shape, dev)
+    _call("rlscan_returns_and_td_lambda", _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb),
+          _ptr(returns), _ptr(td_returns), E, T, float(gamma), float(lam), _stream(dev, stream))
+    return returns, td_returns
 
 
 def gae(rewards, values, terminated=None, truncated=None, bootstrap_value=None,

@@ -165,6 +165,39 @@ rlscan_status rlscan_td_lambda(const float* rewards, const float* values, const 
   return launched(rlscan::launch<rlscan::TdLambda>(a, stream));
 }
 
+rlscan_status rlscan_returns_and_td_lambda(const float* rewards, const float* values,
+                                          const uint8_t* terminated, const uint8_t* truncated,
+                                          const float* bootstrap_value, const float* trunc_bootstrap,
+                                          float* returns, float* td_returns, int64_t E, int64_t T, float gamma,
+                                          float lambda, hipStream_t stream) {
+  rlscan_status st = check_shape(E, T);
+  if (st != RLSCAN_OK) return st;
+  if (!in_unit(gamma) || !in_unit(lambda)) return RLSCAN_ERR_PARAM;
+  if (E * T == 0) return RLSCAN_OK;
+  if (!rewards || !values || !returns || !td_returns) return RLSCAN_ERR_NULL;
+  if (misaligned(rewards) || misaligned(values)) return RLSCAN_ERR_ALIGN;
+  Io io;
+  io.add_in(rewards, 4 * E * T);
+  io.add_in(values, 4 * E * T);
+  if ((st = common_backward(io, terminated, truncated, bootstrap_value, trunc_bootstrap, E, T)) != RLSCAN_OK)
+    return st;
+  io.add_out(returns);
+  io.add_out(td_returns);
+  if ((st = check_io(io, E, T)) != RLSCAN_OK) return st;
+  KernelArgs a = blank(E, T);
+  a.r = rewards;
+  a.v = values;
+  a.term = terminated;
+  a.trunc = truncated;
+  a.row = bootstrap_value;
+  a.tboot = trunc_bootstrap;
+  a.out0 = returns;
+  a.out1 = td_returns;
+  a.gamma = gamma;
+  a.lam = lambda;
+  return launched(rlscan::launch_returns_td_lambda(a, stream));
+}
+
 rlscan_status rlscan_gae(const float* rewards, const float* values, const uint8_t* terminated,
                          const uint8_t* truncated, const float* bootstrap_value,
                          const float* trunc_bootstrap, float* advantages, float* returns, int64_t E,

@@ -71,23 +71,26 @@ struct EligibilityTrace { static constexpr bool kReverse = false; };
 struct EpisodicPrefixSum { static constexpr bool kReverse = false; };
 struct LinearScanReverse { static constexpr bool kReverse = true; };
 struct LinearScanForward { static constexpr bool kReverse = false; };
+// Discounted return and TD(lambda) return of the same rollout in one pass.
+struct ReturnsTdLambda { static constexpr bool kReverse = true; };
 
 template <class Est> struct Traits {
+  static constexpr bool kDual = __is_same(Est, ReturnsTdLambda);  // two recurrences per pass
   static constexpr bool kBackwardRl =
       __is_same(Est, DiscountedReturn) || __is_same(Est, TdLambda) || __is_same(Est, Gae) ||
-      __is_same(Est, Vtrace) || __is_same(Est, Retrace);
+      __is_same(Est, Vtrace) || __is_same(Est, Retrace) || kDual;
   static constexpr bool kForwardRl = __is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum);
   static constexpr bool kLinear = __is_same(Est, LinearScanReverse) || __is_same(Est, LinearScanForward);
   static constexpr bool kRetrace = __is_same(Est, Retrace);
   static constexpr bool kVtrace = __is_same(Est, Vtrace);
   // float input streams: 0 = r, 1 = v/q/b, 2 = aux, 3 = pi, 4 = mu
   static constexpr int kStreams = kRetrace ? 5 : kVtrace ? 3
-                                  : (__is_same(Est, TdLambda) || __is_same(Est, Gae) || kLinear) ? 2 : 1;
+                                  : (__is_same(Est, TdLambda) || __is_same(Est, Gae) || kLinear || kDual) ? 2 : 1;
   static constexpr bool kUsesFlags = kBackwardRl || kForwardRl;
   // value handed from a step to its scan-successor: V (TD, GAE, V-trace), EQ and c (Retrace)
-  static constexpr bool kNbValue = __is_same(Est, TdLambda) || __is_same(Est, Gae) || kVtrace || kRetrace;
+  static constexpr bool kNbValue = __is_same(Est, TdLambda) || __is_same(Est, Gae) || kVtrace || kRetrace || kDual;
   static constexpr bool kNbDone = kForwardRl;  // the previous step's done flag
-  static constexpr bool kHasOut1 = __is_same(Est, Gae) || kVtrace;
+  static constexpr bool kHasOut1 = __is_same(Est, Gae) || kVtrace || kDual;
 };
 
 template <int W> struct BlockShape { static constexpr int kThreads = (W > 4 ? 64 * W : 256); };

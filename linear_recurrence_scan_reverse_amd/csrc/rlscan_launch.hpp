@@ -201,6 +201,10 @@ hipError_t launch(const KernelArgs& in, hipStream_t s) {
   }
 }
 
+// Discounted returns (out0) and TD(lambda) returns (out1) of one rollout: one
+// streaming pass where the rows allow it, else the two single-output kernels.
+hipError_t launch_returns_td_lambda(const KernelArgs& in, hipStream_t s);
+
 // One translation unit per estimator instantiates launch<Est>.
 extern template hipError_t launch<DiscountedReturn>(const KernelArgs&, hipStream_t);
 extern template hipError_t launch<TdLambda>(const KernelArgs&, hipStream_t);

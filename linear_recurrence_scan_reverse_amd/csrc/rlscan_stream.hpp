@@ -95,7 +95,7 @@ constexpr int kStreamItem = 256;  // elements per item (64 lanes x 4 steps)
 template <class Est>
 constexpr int stream_nc_cap() {
   if constexpr (__is_same(Est, Vtrace) || __is_same(Est, Retrace)) return 16;
-  if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae)) return 4;
+  if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae) || __is_same(Est, ReturnsTdLambda)) return 4;
   return 8;
 }
 
@@ -155,6 +155,44 @@ template <class Cfg>
 struct alignas(16) FlagTick {
   uint8_t fl[Cfg::USE_FLAGS ? 2 : 1][Cfg::USE_FLAGS ? Cfg::NC : 1][Cfg::USE_FLAGS ? Cfg::N : 4];
 };
+
+// One lane's part of one tile of one row: pairs, wave scan, re-walk and
+// outputs.  C is the row's running value (in: beyond this tile; out: beyond
+// the next one), `carry` the boundary inputs handed between tiles of the row.
+template <class E2, int L, int K>
+__device__ __forceinline__ void stream_tile(const LaneIn<E2, K>& d, const ScanScalars& sc, unsigned tbits,
+                                            unsigned rbits, uint32_t cs, int64_t T, bool team_first_lane, int lane,
+                                            double& C, PredIn& carry, float (&o0)[K], float (&o1)[K]) {
+  using Tr = Traits<E2>;
+  constexpr int MLAST = E2::kReverse ? 0 : K - 1;
+  const LanePairs<K> lp = build_pairs<E2, K, true>(d, sc, tbits, rbits, cs, T, K, team_first_lane, carry);
+  const AB incl = lane_scan<L>(fold_lane<K>(lp.e));
+  const double y_last = __builtin_fma(incl.a, C, incl.b);
+  const double from_below = shift_up_f64(y_last);
+  const double x_in = team_first_lane ? C : from_below;
+  const double C_next = group_last_f64<L>(y_last, lane);
+  double xs[K];
+  rewalk<K>(lp.e, x_in, xs);
+  epilogue<E2, K>(d, lp, sc, x_in, xs, o0, o1);
+
+  // boundary inputs for the next tile of this row (held by the scan-last lane, 63)
+  if constexpr (L == 64) {
+    if constexpr (Tr::kRetrace) {
+      const double ratio = (double)d.s[3][MLAST] / (double)d.s[4][MLAST];
+      const double cl = sc.lam * (ratio < 1.0 ? ratio : 1.0);
+      carry.v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d.s[2][MLAST]), 63));
+      const unsigned long long u = __builtin_bit_cast(unsigned long long, cl);
+      const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, 63);
+      const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), 63);
+      carry.c = __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+    } else if constexpr (Tr::kNbValue) {
+      carry.v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d.s[1][MLAST]), 63));
+    } else if constexpr (Tr::kNbDone) {
+      carry.done = (unsigned)__builtin_amdgcn_readlane((int)(((tbits | rbits) >> MLAST) & 1u), 63);
+    }
+  }
+  C = C_next;
+}
 
 // Template parameters: estimator tag, team width L (16, 32 or 64 lanes per
 // row), OPT (bit 0: flags present; bit 1: second output), data lead P, blocks
@@ -394,10 +432,10 @@ stream_kernel(const KernelArgs p) {
     const ScanScalars sc{gamma, lam, gl, (float)p.rho_bar, (float)p.c_bar, p.has_row != 0, p.has_tboot != 0};
     const unsigned tmask = p.has_term ? ~0u : 0u;
     const unsigned rmask = p.has_trunc ? ~0u : 0u;
-    constexpr int MLAST = REV ? 0 : K - 1;
-
     double C = 0.0;
     PredIn carry{0.0f, 0.0, 0u};  // boundary inputs handed from the previous tile of the row
+    double C2 = 0.0;               // the second recurrence of a two-output pass
+    PredIn carry2{0.0f, 0.0, 0u};
 
 #pragma unroll
     for (int w = -LG - 1; w <= -1; ++w) tick_barrier();
@@ -438,35 +476,28 @@ stream_kernel(const KernelArgs p) {
         if constexpr (Tr::kBackwardRl) C = 0.0;
         else C = (row_ok && p.has_row) ? (double)d.rowv : 0.0;
         carry = PredIn{0.0f, 0.0, 0u};
+        C2 = 0.0;
+        carry2 = PredIn{0.0f, 0.0, 0u};
       }
-      const LanePairs<K> lp = build_pairs<Est, K, true>(d, sc, tbits, rbits, cs, T, K, team_first_lane, carry);
-      const AB incl = lane_scan<L>(fold_lane<K>(lp.e));
-      const double y_last = __builtin_fma(incl.a, C, incl.b);
-      const double from_below = shift_up_f64(y_last);
-      const double x_in = team_first_lane ? C : from_below;
-      const double C_next = group_last_f64<L>(y_last, lane);
-      double xs[K];
-      rewalk<K>(lp.e, x_in, xs);
       float o0[K], o1[K];
-      epilogue<Est, K>(d, lp, sc, x_in, xs, o0, o1);
-
-      // boundary inputs for the next tile of this row (held by the scan-last lane, 63)
-      if constexpr (L == 64) {
-        if constexpr (Tr::kRetrace) {
-          const double ratio = (double)d.s[3][MLAST] / (double)d.s[4][MLAST];
-          const double cl = lam * (ratio < 1.0 ? ratio : 1.0);
-          carry.v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d.s[2][MLAST]), 63));
-          const unsigned long long u = __builtin_bit_cast(unsigned long long, cl);
-          const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, 63);
-          const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), 63);
-          carry.c = __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
-        } else if constexpr (Tr::kNbValue) {
-          carry.v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d.s[1][MLAST]), 63));
-        } else if constexpr (Tr::kNbDone) {
-          carry.done = (unsigned)__builtin_amdgcn_readlane((int)(((tbits | rbits) >> MLAST) & 1u), 63);
+      if constexpr (Tr::kDual) {
+        // discounted return (rewards only) and TD(lambda) return (rewards, values)
+        LaneIn<DiscountedReturn, K> da;
+        LaneIn<TdLambda, K> db;
+#pragma unroll
+        for (int m = 0; m < K; ++m) {
+          da.s[0][m] = d.s[0][m];
+          db.s[0][m] = d.s[0][m];
+          db.s[1][m] = d.s[1][m];
+          da.tb[m] = db.tb[m] = d.tb[m];
         }
+        da.rowv = db.rowv = d.rowv;
+        float unused[K];
+        stream_tile<DiscountedReturn, L, K>(da, sc, tbits, rbits, cs, T, team_first_lane, lane, C, carry, o0, unused);
+        stream_tile<TdLambda, L, K>(db, sc, tbits, rbits, cs, T, team_first_lane, lane, C2, carry2, o1, unused);
+      } else {
+        stream_tile<Est, L, K>(d, sc, tbits, rbits, cs, T, team_first_lane, lane, C, carry, o0, o1);
       }
-      C = C_next;
 
       if (row_ok) {
         const int64_t eb = rg * G * T;  // element index of the item's first row

@@ -11,7 +11,7 @@ import numpy as np
 import oracle
 
 NAMES = ("discounted_returns", "td_lambda", "gae", "vtrace", "retrace",
-         "eligibility_traces", "episodic_prefix_sum")
+         "eligibility_traces", "episodic_prefix_sum", "returns_and_td_lambda")
 
 DEFAULT_PARAMS = dict(gamma=0.99, lam=0.95, vtrace_lam=1.0, rho_bar=1.0, c_bar=1.0)
 
@@ -47,6 +47,9 @@ def run_oracle(name, d, P=None, **variant):
         return {"out": oracle.discounted_returns(d["r"], te, tr, bv, tb, gamma=g)}
     if name == "td_lambda":
         return {"out": oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=g, lam=l)}
+    if name == "returns_and_td_lambda":
+        return {"out": oracle.discounted_returns(d["r"], te, tr, bv, tb, gamma=g),
+                "out1": oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=g, lam=l)}
     if name == "gae":
         adv, ret = oracle.gae(d["r"], d["v"], te, tr, bv, tb, gamma=g, lam=l, with_returns=True)
         return {"out": adv, "out1": ret}
@@ -81,6 +84,9 @@ def run_gpu(name, dd, P=None, **variant):
         return {"out": rl.discounted_returns(dd["r"], te, tr, bv, tb, gamma=g)}
     if name == "td_lambda":
         return {"out": rl.td_lambda(dd["r"], dd["v"], te, tr, bv, tb, gamma=g, lam=l)}
+    if name == "returns_and_td_lambda":
+        ret, tdr = rl.returns_and_td_lambda(dd["r"], dd["v"], te, tr, bv, tb, gamma=g, lam=l)
+        return {"out": ret, "out1": tdr}
     if name == "gae":
         adv, ret = rl.gae(dd["r"], dd["v"], te, tr, bv, tb, gamma=g, lam=l, with_returns=True)
         return {"out": adv, "out1": ret}

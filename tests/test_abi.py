@@ -38,7 +38,8 @@ def lib():
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
-    for n in ["rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_gae", "rlscan_vtrace",
+    for n in ["rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_returns_and_td_lambda",
+              "rlscan_gae", "rlscan_vtrace",
               "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum",
               "rlscan_linear_scan", "rlscan_status_string", "rlscan_version"]:
         assert n in names
@@ -135,6 +136,20 @@ def test_overlapping_outputs_are_rejected(lib):
     # output overlaps the per-row bootstrap
     assert lib.rlscan_td_lambda(A, B, None, None, F, None, F, E, T, 0.9, 0.9, S) == ERR_ALIAS
     assert lib.rlscan_linear_scan(A, B, None, B, E, T, 1, S) == ERR_ALIAS
+
+
+def test_returns_and_td_lambda_validation(lib):
+    E, T = 8, 16
+    n = 4 * E * T
+    f = lib.rlscan_returns_and_td_lambda
+    assert f(A, B, None, None, None, None, C, D, -1, T, 0.99, 0.9, S) == ERR_SHAPE
+    assert f(A, B, None, None, None, None, C, D, E, T, 0.99, 1.5, S) == ERR_PARAM
+    assert f(A, B, None, None, None, None, C, None, E, T, 0.99, 0.9, S) == ERR_NULL   # td_returns required
+    assert f(A, None, None, None, None, None, C, D, E, T, 0.99, 0.9, S) == ERR_NULL   # values required
+    assert f(A, B, None, None, None, None, C, C + n - 4, E, T, 0.99, 0.9, S) == ERR_ALIAS  # outputs overlap
+    assert f(A, B, None, None, None, None, C, B, E, T, 0.99, 0.9, S) == ERR_ALIAS  # output over an input
+    assert f(A, B + 2, None, None, None, None, C, D, E, T, 0.99, 0.9, S) == ERR_ALIGN
+    assert f(None, None, None, None, None, None, None, None, 0, T, 0.99, 0.9, S) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -159,3 +159,33 @@ def test_large_rows_few_envs():
     d = synth.draw(2, 20000, seed=17, p_term=0.001, p_trunc=0.001)
     for name in NAMES:
         _assert_ok(name, compare(name, d), "T=20000")
+
+
+@pytest.mark.parametrize("wname", ["dr_td_4096x64", "all7_16384x256"])
+def test_returns_and_td_lambda_full_size(wname):
+    """The one-pass returns + TD(lambda) entry at full workload sizes."""
+    w = synth.WORKLOADS[wname]
+    d = synth.workload_inputs(w)
+    res = compare("returns_and_td_lambda", d, _params_for(w),
+                  term="terminated" in d, trunc="truncated" in d,
+                  boot="bootstrap_value" in d, tboot="trunc_bootstrap" in d)
+    _say("  returns_and_td_lambda", wname, {k: "%.2e" % v[0] for k, v in res.items()})
+    _assert_ok("returns_and_td_lambda", res, wname)
+
+
+@pytest.mark.parametrize("T", [64, 128, 256, 512, 100, 1000])
+def test_returns_and_td_lambda_equals_single_entries(T):
+    """Both outputs equal the single-output entries; bitwise for TD(lambda), which
+    runs the same per-lane arithmetic in both kernels."""
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    from tests.estimators import to_dev, parity_err
+    d = synth.draw(300, T, seed=31 + T, p_term=0.01, p_trunc=0.01)
+    dd = to_dev(d)
+    args = (dd["terminated"], dd["truncated"], dd["bootstrap_value"], dd["trunc_bootstrap"])
+    ret, tdr = rl.returns_and_td_lambda(dd["r"], dd["v"], *args, gamma=0.97, lam=0.9)
+    ret1 = rl.discounted_returns(dd["r"], *args, gamma=0.97)
+    tdr1 = rl.td_lambda(dd["r"], dd["v"], *args, gamma=0.97, lam=0.9)
+    torch.cuda.synchronize()
+    assert torch.equal(tdr, tdr1)
+    assert parity_err(ret.cpu().numpy(), ret1.cpu().numpy()) <= 1e-6
