@@ -70,7 +70,7 @@ def alg_bytes(name, d, E, T, with_flags=True):
     only where a step is truncated and not terminated."""
     n = E * T
     f = 4 * n
-    flags = (2 * n) if with_flags else 0
+    flags = n * (int("terminated" in d) + int("truncated" in d)) if with_flags else 0
     sparse = 0
     if with_flags and "truncated" in d:
         tb_steps = int(np.count_nonzero(d["truncated"] & (d["terminated"] == 0)))
@@ -110,7 +110,9 @@ class Runner:
             for o in ORDER:
                 s["out_" + o] = torch.empty((w.E, w.T), dtype=torch.float32, device=device)
             s["out_vtrace_pg"] = torch.empty((w.E, w.T), dtype=torch.float32, device=device)
-            self.sets.append({k: v.data_ptr() for k, v in s.items()})
+            ptrs = {k: None for k in ("terminated", "truncated", "bootstrap_value", "trunc_bootstrap")}
+            ptrs.update({k: v.data_ptr() for k, v in s.items()})
+            self.sets.append(ptrs)
             self.sets[-1]["_keep"] = s
         self.set_bytes = sum(v.numel() * v.element_size() for v in self.sets[0]["_keep"].values())
         self.counter = 0
@@ -299,6 +301,56 @@ def cpu_baseline(w, d, budget_s=10.0):
 
 
 # ----------------------------------------------------------------- main
+GRID_E = (256, 1024, 4096, 16384, 65536)
+GRID_T = (64, 128, 256, 512, 1024, 2048, 4096)
+
+
+def drop_truncation(d):
+    """The same inputs without per-step truncation (flags and bootstraps absent)."""
+    return {k: v for k, v in d.items() if k not in ("truncated", "trunc_bootstrap")}
+
+
+def time_estimators(runner, names, d, w, reps):
+    per = {}
+    for n in names:
+        for _ in range(3):
+            runner.call(n, runner.next_set())
+        s = time_region(runner, lambda: runner.call(n, runner.next_set()), reps)
+        us = s / reps * 1e6
+        b = alg_bytes(n, d, w.E, w.T)
+        per[n] = {"us_per_launch": round(us, 3), "env_steps_per_s": w.E * w.T / (us * 1e-6), "alg_bytes": b,
+                  "GBps": b / (us * 1e-6) / 1e9, "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+    return per
+
+
+def run_grid(torch, device, args):
+    """Every estimator over the E x T grid with the all-seven distributions; one
+    JSON line per grid point (buffer sets above 1 GiB are skipped)."""
+    import dataclasses
+    base = synth.WORKLOADS["all7_16384x256"]
+    names = list(base.estimators)
+    for T in GRID_T:
+        for E in GRID_E:
+            set_bytes = E * T * (4 * 8 + 2 + 4 * 8) + 4 * E
+            if set_bytes > (1 << 30):
+                log("grid %6d x %4d: buffer set %.2f GiB > 1 GiB, skipped" % (E, T, set_bytes / 2**30))
+                continue
+            w = dataclasses.replace(base, name="all7_%dx%d" % (E, T), E=E, T=T)
+            d = synth.workload_inputs(w)
+            if args.no_trunc:
+                d = drop_truncation(d)
+            nsets = int(min(64, max(2, -(-(1 << 30) // set_bytes) + 1)))
+            runner = Runner(w, d, nsets, device)
+            per = time_estimators(runner, names, d, w, max(args.steps, 20))
+            log("grid %6d x %4d: " % (E, T) + "  ".join("%s %.2f us %.1f%%" % (
+                n[:6], per[n]["us_per_launch"], 100 * per[n]["frac_of_peak"]) for n in names))
+            print(json.dumps({"grid": True, "workload": w.name, "E": E, "T": T,
+                              "truncation": not args.no_trunc, "buffer_sets": nsets,
+                              "per_estimator": per}), flush=True)
+            del runner
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +361,8 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0 = enough for > 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-only", action="store_true", help="only run the copy calibration kernel")
+    ap.add_argument("--grid", action="store_true", help="every estimator over the E x T grid, one line each")
+    ap.add_argument("--no-trunc", action="store_true", help="inputs without per-step truncation")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -328,6 +382,10 @@ def main():
         log("copy ceiling %.1f GB/s" % gbps)
         return
 
+    if args.grid:
+        run_grid(torch, device, args)
+        return
+
     w = synth.WORKLOADS[args.workload]
     names = [n for n in ORDER if n in w.estimators]
     if args.only:
@@ -336,6 +394,8 @@ def main():
         names = [args.only]
     log("workload %s: E=%d T=%d estimators=%s" % (w.name, w.E, w.T, ",".join(names)))
     d = synth.workload_inputs(w)
+    if args.no_trunc:
+        d = drop_truncation(d)
     set_bytes_est = sum(v.nbytes for v in d.values()) + 8 * 4 * w.E * w.T
     nsets = args.sets or int(min(64, max(2, -(-(1 << 30) // set_bytes_est) + 1)))
     runner = Runner(w, d, nsets, device)
@@ -353,21 +413,7 @@ def main():
     log("step: %.3f ms  (%.3g env-steps/s through %d estimators)" % (ms_per_step, value, len(names)))
 
     # ---- per-estimator back-to-back launches (same rotation), HIP events on the launch stream
-    per = {}
-    for n in names:
-        reps = max(args.steps, 20)
-        for _ in range(3):
-            runner.call(n, runner.next_set())
-        s = time_region(runner, lambda: runner.call(n, runner.next_set()), reps)
-        us = s / reps * 1e6
-        b = alg_bytes(n, d, w.E, w.T)
-        per[n] = {
-            "us_per_launch": round(us, 3),
-            "env_steps_per_s": w.E * w.T / (us * 1e-6),
-            "alg_bytes": b,
-            "GBps": b / (us * 1e-6) / 1e9,
-            "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-        }
+    per = time_estimators(runner, names, d, w, max(args.steps, 20))
     for n in names:
         per[n]["copy_same_bytes_GBps"] = round(copy_same_bytes(torch, device, per[n]["alg_bytes"]), 1)
         per[n]["frac_of_copy"] = round(per[n]["GBps"] / per[n]["copy_same_bytes_GBps"], 4)
@@ -434,6 +480,7 @@ def main():
             "p_term": w.p_term, "p_trunc": w.p_trunc, "gamma": w.gamma, "lambda": w.lam,
             "vtrace_lambda": w.vtrace_lam, "rho_bar": w.rho_bar, "c_bar": w.c_bar,
             "buffer_sets": nsets, "gae_returns_written": False, "vtrace_pg_written": True,
+            "truncation": not args.no_trunc,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
