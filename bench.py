@@ -313,7 +313,7 @@ def drop_truncation(d):
 def time_estimators(runner, names, d, w, reps):
     per = {}
     for n in names:
-        for _ in range(3):
+        for _ in range(max(3, len(runner.sets))):  # every buffer set once before timing
             runner.call(n, runner.next_set())
         s = time_region(runner, lambda: runner.call(n, runner.next_set()), reps)
         us = s / reps * 1e6
@@ -329,8 +329,10 @@ def run_grid(torch, device, args):
     import dataclasses
     base = synth.WORKLOADS["all7_16384x256"]
     names = list(base.estimators)
-    for T in GRID_T:
-        for E in GRID_E:
+    grid_e = [int(x) for x in args.grid_e.split(",")] if args.grid_e else GRID_E
+    grid_t = [int(x) for x in args.grid_t.split(",")] if args.grid_t else GRID_T
+    for T in grid_t:
+        for E in grid_e:
             set_bytes = E * T * (4 * 8 + 2 + 4 * 8) + 4 * E
             if set_bytes > (1 << 30):
                 log("grid %6d x %4d: buffer set %.2f GiB > 1 GiB, skipped" % (E, T, set_bytes / 2**30))
@@ -363,6 +365,8 @@ def main():
     ap.add_argument("--copy-only", action="store_true", help="only run the copy calibration kernel")
     ap.add_argument("--grid", action="store_true", help="every estimator over the E x T grid, one line each")
     ap.add_argument("--no-trunc", action="store_true", help="inputs without per-step truncation")
+    ap.add_argument("--grid-e", default=None, help="comma-separated E values for --grid")
+    ap.add_argument("--grid-t", default=None, help="comma-separated T values for --grid")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -5,7 +5,8 @@ namespace rlscan {
 
 hipError_t launch_returns_td_lambda(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
-  switch (stream_team(a)) {
+  const int team = stream_team(a);
+  switch ((team != 0 && prefer_stream<ReturnsTdLambda>(a, team)) ? team : 0) {
     case 16: return launch_stream<ReturnsTdLambda, 16>(a, s);
     case 32: return launch_stream<ReturnsTdLambda, 32>(a, s);
     case 64: return launch_stream<ReturnsTdLambda, 64>(a, s);

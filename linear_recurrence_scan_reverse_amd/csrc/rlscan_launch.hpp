@@ -124,17 +124,6 @@ template <class Est>
 constexpr int stream_lead() { return 2; }
 constexpr int kStreamBlocksPerCu = 2;
 
-// Whether an estimator takes the streaming kernel when its rows allow it.
-// Measured at 16384 x 256: discounted returns and Retrace with flags present
-// run faster on the pipelined persistent kernel (the per-wave bootstrap
-// gather there overlaps better with their compute than the tick-synchronous
-// gather wave does); the rest run faster streaming.
-template <class Est>
-inline bool prefer_stream(const KernelArgs& a) {
-  constexpr bool pipelined_with_flags = __is_same(Est, DiscountedReturn) || __is_same(Est, Retrace);
-  return !(pipelined_with_flags && (a.has_term || a.has_trunc));
-}
-
 template <class Est, int L, int OPT>
 inline hipError_t launch_stream_one(const KernelArgs& a, hipStream_t s) {
   constexpr int P = stream_lead<Est>();
@@ -179,10 +168,37 @@ inline int stream_team(const KernelArgs& a) {
   return L;
 }
 
+// Whether the streaming kernel should take a call its rows allow (team width
+// L).  Measured over E in {256 .. 16384} x T in {64 .. 4096}:
+//  * a streaming compute wave walks the tiles of its rows one per tick, so
+//    rows of 8 or more tiles, with fewer than two rows per compute wave the
+//    grid can hold, run faster on the pipelined kernel, whose 4-wave teams
+//    split a long row (up to 2.3x at 256 x 4096);
+//  * V-trace with rows of more than one tile, and discounted returns and
+//    Retrace with flags present, run faster pipelined at every size measured
+//    from 4096 rows up (the per-wave bootstrap gather and, for Retrace, the
+//    heavier per-step arithmetic overlap better there than in ticks).
+template <class Est>
+inline bool prefer_stream(const KernelArgs& a, int L) {
+  const bool flags = a.has_term || a.has_trunc;
+  if ((__is_same(Est, DiscountedReturn) || __is_same(Est, Retrace)) && flags) return false;
+  if (__is_same(Est, Vtrace) && a.T > 256) return false;
+  const int64_t ntiles = a.T / (4 * L);
+  if (ntiles >= 8) {
+    constexpr int P = stream_lead<Est>();
+    constexpr int BPC = kStreamBlocksPerCu;
+    const int nc = flags ? StreamCfg<Est, true, P, BPC>::NC : StreamCfg<Est, false, P, BPC>::NC;
+    const int64_t nrg = (a.E + (64 / L) - 1) / (64 / L);
+    if (nrg < 2 * (int64_t)cu_count() * BPC * nc) return false;
+  }
+  return true;
+}
+
 template <class Est>
 hipError_t launch(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
-  switch (prefer_stream<Est>(a) ? stream_team(a) : 0) {
+  const int team = stream_team(a);
+  switch ((team != 0 && prefer_stream<Est>(a, team)) ? team : 0) {
     case 16: return launch_stream<Est, 16>(a, s);
     case 32: return launch_stream<Est, 32>(a, s);
     case 64: return launch_stream<Est, 64>(a, s);
