@@ -40,10 +40,15 @@
  * Optional    A NULL terminated/truncated array means "no such flags" and is
  *             not read.  A NULL bootstrap_value, trunc_bootstrap, init or carry
  *             means zeros.  Outputs documented as optional may be NULL.
- * Streams     Each call validates its arguments on the host, then enqueues ONE
- *             kernel on `stream` (NULL = the default stream) and returns; it
+ * Streams     Each call validates its arguments on the host, then enqueues its
+ *             kernels on `stream` (NULL = the default stream) and returns; it
  *             never synchronises.  Outputs are valid once the stream has
- *             reached that point.
+ *             reached that point.  Most calls are one kernel.  Rows of 16384
+ *             steps or more, 64 rows or fewer, are split into segments scanned
+ *             in parallel by three kernels in turn; until the last of them, the
+ *             first output array holds per-segment intermediate values (so it
+ *             must not be read or shared before the stream reaches the end of
+ *             the call, which the rule above already implies).
  * Errors      Validation happens before any HIP call and returns:
  *               RLSCAN_ERR_SHAPE  E < 0, T < 0, T >= RLSCAN_MAX_T (2^30), or
  *                                 E*T overflows int64;
