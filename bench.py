@@ -85,6 +85,7 @@ def alg_bytes(name, d, E, T, with_flags=True):
         "eligibility_traces": f + flags + row + f,
         "episodic_prefix_sum": f + flags + row + f,
         "returns_and_td_lambda": 2 * f + flags + sparse + row + 2 * f,
+        "linear_scan_segmented": 2 * f + (n if "terminated" in d else 0) + f,
     }
     return table[name]
 
@@ -131,6 +132,10 @@ class Runner:
                                                 p["bootstrap_value"], p["trunc_bootstrap"],
                                                 p["out_discounted_returns"], p["out_td_lambda"], E, T,
                                                 w.gamma, w.lam, st)
+        elif name == "linear_scan_segmented":
+            # the generic episode-cut recurrence: a = pi (in (0.05, 1)), b = r, cuts at terminations
+            rc = L.rlscan_linear_scan_segmented(p["pi"], p["r"], p["terminated"], None,
+                                                p["out_episodic_prefix_sum"], E, T, 1, st)
         elif name == "gae":
             rc = L.rlscan_gae(p["r"], p["v"], p["terminated"], p["truncated"], p["bootstrap_value"],
                               p["trunc_bootstrap"], p["out_" + name], None, E, T, w.gamma, w.lam, st)
@@ -424,22 +429,21 @@ def main():
         log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  %5.1f%% of a same-size copy" % (
             n, per[n]["us_per_launch"], per[n]["GBps"], 100 * per[n]["frac_of_peak"], 100 * per[n]["frac_of_copy"]))
 
-    # ---- the one-pass returns + TD(lambda) entry (not part of the step)
+    # ---- the other entry points (not part of the step): the one-pass returns + TD(lambda)
+    # entry and the generic episode-cut recurrence
     fused = None
     if "discounted_returns" in names and "td_lambda" in names:
+        fused = time_estimators(runner, ["returns_and_td_lambda", "linear_scan_segmented"], d, w,
+                                max(args.steps, 20))
         n = "returns_and_td_lambda"
-        reps = max(args.steps, 20)
-        for _ in range(3):
-            runner.call(n, runner.next_set())
-        s = time_region(runner, lambda: runner.call(n, runner.next_set()), reps)
-        us = s / reps * 1e6
-        b = alg_bytes(n, d, w.E, w.T)
         sep = per["discounted_returns"]["us_per_launch"] + per["td_lambda"]["us_per_launch"]
-        fused = {n: {"us_per_launch": round(us, 3), "alg_bytes": b, "GBps": b / (us * 1e-6) / 1e9,
-                     "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                     "separate_calls_us": round(sep, 3), "speedup_vs_separate": round(sep / us, 3)}}
+        fused[n]["separate_calls_us"] = round(sep, 3)
+        fused[n]["speedup_vs_separate"] = round(sep / fused[n]["us_per_launch"], 3)
         log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  (separate calls: %.2f us)" % (
-            "returns+td_lambda", us, fused[n]["GBps"], 100 * fused[n]["frac_of_peak"], sep))
+            "returns+td_lambda", fused[n]["us_per_launch"], fused[n]["GBps"], 100 * fused[n]["frac_of_peak"], sep))
+        n = "linear_scan_segmented"
+        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak" % (
+            "generic, with cuts", fused[n]["us_per_launch"], fused[n]["GBps"], 100 * fused[n]["frac_of_peak"]))
 
     dom = max(per, key=lambda k: per[k]["us_per_launch"])
     traffic, traffic_src = read_traffic(dom, w.name)

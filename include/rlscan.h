@@ -206,6 +206,21 @@ rlscan_status rlscan_episodic_prefix_sum(const float *x, const uint8_t *terminat
 rlscan_status rlscan_linear_scan(const float *a, const float *b, const float *carry, float *x,
                                  int64_t E, int64_t T, int reverse, hipStream_t stream);
 
+/* The generic recurrence cut into episodes by a flag array: the same
+ * recurrence as rlscan_linear_scan, except that a flagged step breaks the
+ * chain, as terminated/truncated flags do for the estimators (gist.science
+ * summary, "Methodologie" sections 1 and 3):
+ *   reverse != 0:  x_t = b_t + (done[t]   ? 0 : a_t x_{t+1}),  x_T    = carry[e]
+ *   reverse == 0:  x_t = b_t + (done[t-1] ? 0 : a_t x_{t-1}),  x_{-1} = carry[e]
+ * (forward: the step after a flagged one starts a new episode; the carry
+ * enters step 0 through a_0 as in rlscan_linear_scan).  done[e,t] is uint8,
+ * nonzero = cut; NULL means no cuts (then this equals rlscan_linear_scan).
+ * In:  a, b [E,T] (required); done [E,T] (optional); carry [E] (optional).
+ * Out: x [E,T] (required). */
+rlscan_status rlscan_linear_scan_segmented(const float *a, const float *b, const uint8_t *done,
+                                           const float *carry, float *x, int64_t E, int64_t T, int reverse,
+                                           hipStream_t stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

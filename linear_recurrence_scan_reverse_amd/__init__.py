@@ -19,7 +19,7 @@ import threading
 __all__ = [
     "RlscanError", "lib", "library_path", "version",
     "discounted_returns", "td_lambda", "returns_and_td_lambda", "gae", "vtrace", "retrace",
-    "eligibility_traces", "episodic_prefix_sum", "linear_scan",
+    "eligibility_traces", "episodic_prefix_sum", "linear_scan", "linear_scan_segmented",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,6 +43,7 @@ _SIGNATURES = {
     "rlscan_eligibility_traces": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _vp],
     "rlscan_episodic_prefix_sum": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "rlscan_linear_scan": [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp],
+    "rlscan_linear_scan_segmented": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _vp],
 }
 
 
@@ -326,4 +327,20 @@ def linear_scan(a, b, carry=None, *, reverse=True, out=None, stream=None):
     out = _out(out, "out", shape, dev)
     _call("rlscan_linear_scan", _ptr(aa), _ptr(bb), _ptr(c0), _ptr(out), E, T, 1 if reverse else 0,
           _stream(dev, stream))
+    return out
+
+
+def linear_scan_segmented(a, b, done=None, carry=None, *, reverse=True, out=None, stream=None):
+    """The generic recurrence cut into episodes: a step flagged in ``done`` breaks
+    the chain (backward: nothing enters it from t+1; forward: the next step
+    starts afresh)."""
+    shape, dev = _prep(a, "a")
+    E, T = shape
+    aa = _check_f32(a, "a", shape, dev)
+    bb = _check_f32(b, "b", shape, dev)
+    dn = _check_flags(done, "done", shape, dev)
+    c0 = _check_f32(carry, "carry", (E,), dev)
+    out = _out(out, "out", shape, dev)
+    _call("rlscan_linear_scan_segmented", _ptr(aa), _ptr(bb), _ptr(dn), _ptr(c0), _ptr(out), E, T,
+          1 if reverse else 0, _stream(dev, stream))
     return out

@@ -381,4 +381,29 @@ rlscan_status rlscan_linear_scan(const float* a_coef, const float* b_coef, const
                  : launched(rlscan::launch<rlscan::LinearScanForward>(a, stream));
 }
 
+rlscan_status rlscan_linear_scan_segmented(const float* a_coef, const float* b_coef, const uint8_t* done,
+                                           const float* carry, float* x, int64_t E, int64_t T, int reverse,
+                                           hipStream_t stream) {
+  rlscan_status st = check_shape(E, T);
+  if (st != RLSCAN_OK) return st;
+  if (E * T == 0) return RLSCAN_OK;
+  if (!a_coef || !b_coef || !x) return RLSCAN_ERR_NULL;
+  if (misaligned(a_coef) || misaligned(b_coef) || misaligned(carry)) return RLSCAN_ERR_ALIGN;
+  Io io;
+  io.add_in(a_coef, 4 * E * T);
+  io.add_in(b_coef, 4 * E * T);
+  io.add_in(done, E * T);
+  io.add_in(carry, 4 * E);
+  io.add_out(x);
+  if ((st = check_io(io, E, T)) != RLSCAN_OK) return st;
+  KernelArgs a = blank(E, T);
+  a.r = a_coef;
+  a.v = b_coef;
+  a.term = done;
+  a.row = carry;
+  a.out0 = x;
+  return reverse ? launched(rlscan::launch<rlscan::LinearScanReverse>(a, stream))
+                 : launched(rlscan::launch<rlscan::LinearScanForward>(a, stream));
+}
+
 }  // extern "C"

@@ -86,10 +86,10 @@ template <class Est> struct Traits {
   // float input streams: 0 = r, 1 = v/q/b, 2 = aux, 3 = pi, 4 = mu
   static constexpr int kStreams = kRetrace ? 5 : kVtrace ? 3
                                   : (__is_same(Est, TdLambda) || __is_same(Est, Gae) || kLinear || kDual) ? 2 : 1;
-  static constexpr bool kUsesFlags = kBackwardRl || kForwardRl;
+  static constexpr bool kUsesFlags = kBackwardRl || kForwardRl || kLinear;  // (linear: episode cuts)
   // value handed from a step to its scan-successor: V (TD, GAE, V-trace), EQ and c (Retrace)
   static constexpr bool kNbValue = __is_same(Est, TdLambda) || __is_same(Est, Gae) || kVtrace || kRetrace || kDual;
-  static constexpr bool kNbDone = kForwardRl;  // the previous step's done flag
+  static constexpr bool kNbDone = kForwardRl || __is_same(Est, LinearScanForward);  // previous step's done flag
   static constexpr bool kHasOut1 = __is_same(Est, Gae) || kVtrace || kDual;
 };
 
@@ -457,7 +457,16 @@ __device__ __forceinline__ LanePairs<K> build_pairs(const LaneIn<Est, K>& d, con
       else c.a = keep ? 1.0 : 0.0;
       c.b = (double)d.s[0][m];
     } else {
-      c.a = (double)d.s[0][m];
+      // generic recurrence; a flagged step cuts the chain: backward, nothing
+      // enters step t from t+1; forward, nothing enters step t from t-1
+      bool keep = true;
+      if constexpr (REV) {
+        keep = !(((tbits | rbits) >> m) & 1u);
+      } else {
+        const unsigned prev_done = (j == 0) ? nb_done : (((tbits | rbits) >> (m - 1)) & 1u);
+        keep = !prev_done || (cs + m == 0);
+      }
+      c.a = keep ? (double)d.s[0][m] : 0.0;
       c.b = (double)d.s[1][m];
     }
     if constexpr (!VEC) {

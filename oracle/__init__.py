@@ -58,6 +58,7 @@ def _bind(lib):
         "oracle_eligibility_traces": [_f32p, _u8p, _u8p, _f32p, _f64p, _i64, _i64, _f32, _f32],
         "oracle_episodic_prefix_sum": [_f32p, _u8p, _u8p, _f32p, _f64p, _i64, _i64],
         "oracle_linear_scan": [_f32p, _f32p, _f32p, _f64p, _i64, _i64, ctypes.c_int],
+        "oracle_linear_scan_segmented": [_f32p, _f32p, _u8p, _f32p, _f64p, _i64, _i64, ctypes.c_int],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -226,6 +227,16 @@ def linear_scan(a, b, carry=None, reverse=True):
     keep = [_f32_in(a, shape), _f32_in(b, shape), _row_in(carry, E)]
     out, po = _out(shape)
     _load().oracle_linear_scan(*(k[1] for k in keep), po, E, T, 1 if reverse else 0)
+    return out
+
+
+def linear_scan_segmented(a, b, done=None, carry=None, reverse=True):
+    """The generic recurrence with episode cuts at flagged steps."""
+    shape = _shape(a)
+    E, T = shape
+    keep = [_f32_in(a, shape), _f32_in(b, shape), _u8_in(done, shape), _row_in(carry, E)]
+    out, po = _out(shape)
+    _load().oracle_linear_scan_segmented(*(k[1] for k in keep), po, E, T, 1 if reverse else 0)
     return out
 
 

@@ -295,3 +295,25 @@ void oracle_linear_scan(const float *a, const float *b, const float *carry,
     }
   }
 }
+
+/* The generic recurrence cut into episodes by a flag array: a flagged step
+ * breaks the chain, as the estimators' terminated / truncated flags do
+ * (gist.science summary, "Methodologie" sections 1 and 3).
+ *   reverse: x_t = b_t + (done[t] ? 0 : a_t x_{t+1}),              x_T    = carry
+ *   forward: x_t = b_t + (t > 0 && done[t-1] ? 0 : a_t x_{t-1}),   x_{-1} = carry
+ * done == NULL means no cuts. */
+void oracle_linear_scan_segmented(const float *a, const float *b, const uint8_t *done,
+                                  const float *carry, double *x, int64_t E, int64_t T,
+                                  int reverse) {
+  for (int64_t e = 0; e < E; ++e) {
+    double state = carry ? (double)carry[e] : 0.0;
+    for (int64_t k = 0; k < T; ++k) {
+      const int64_t t = reverse ? (T - 1 - k) : k;
+      const int64_t i = e * T + t;
+      int cut = 0;
+      if (done) cut = reverse ? (done[i] != 0) : (t > 0 && done[i - 1] != 0);
+      state = (cut ? 0.0 : (double)a[i] * state) + (double)b[i];
+      x[i] = state;
+    }
+  }
+}

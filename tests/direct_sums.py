@@ -232,3 +232,32 @@ def linear_scan(a, b, carry=None, reverse=True):
                 acc += math.prod(aa[0:t + 1]) * c0
             out[e, t] = acc
     return out
+
+
+def linear_scan_segmented(a, b, done=None, carry=None, reverse=True):
+    """Episode-cut generic recurrence as a direct sum: backward, x_t sums b_j
+    weighted by prod a_t..a_{j-1} for j from t through the first flagged step
+    at or after t (the carry enters only if no step from t on is flagged);
+    forward, x_t sums b_j weighted by prod a_{j+1}..a_t for j from the first
+    step of t's episode (the step after the last flagged one before t) through
+    t, plus the carry through a_0..a_t when that episode starts at 0."""
+    E, T = np.asarray(a).shape
+    out = np.zeros((E, T))
+    for e in range(E):
+        aa, bb = _row(a, e), _row(b, e)
+        dd = [bool(x) for x in _row(done, e)] if done is not None else [False] * T
+        c0 = _rowval(carry, e) or 0.0
+        for t in range(T):
+            if reverse:
+                end = next((j for j in range(t, T) if dd[j]), None)
+                last = T - 1 if end is None else end
+                acc = sum(math.prod(aa[t:j]) * bb[j] for j in range(t, last + 1))
+                if end is None:
+                    acc += math.prod(aa[t:T]) * c0
+            else:
+                s0 = _episode_start(dd, t)
+                acc = sum(math.prod(aa[j + 1:t + 1]) * bb[j] for j in range(s0, t + 1))
+                if s0 == 0:
+                    acc += math.prod(aa[0:t + 1]) * c0
+            out[e, t] = acc
+    return out

@@ -41,7 +41,8 @@ def test_header_declares_the_expected_entry_points():
     for n in ["rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_returns_and_td_lambda",
               "rlscan_gae", "rlscan_vtrace",
               "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum",
-              "rlscan_linear_scan", "rlscan_status_string", "rlscan_version"]:
+              "rlscan_linear_scan", "rlscan_linear_scan_segmented", "rlscan_status_string",
+              "rlscan_version"]:
         assert n in names
 
 
@@ -150,6 +151,17 @@ def test_returns_and_td_lambda_validation(lib):
     assert f(A, B, None, None, None, None, C, B, E, T, 0.99, 0.9, S) == ERR_ALIAS  # output over an input
     assert f(A, B + 2, None, None, None, None, C, D, E, T, 0.99, 0.9, S) == ERR_ALIGN
     assert f(None, None, None, None, None, None, None, None, 0, T, 0.99, 0.9, S) == OK
+
+
+def test_linear_scan_segmented_validation(lib):
+    E, T = 8, 16
+    f = lib.rlscan_linear_scan_segmented
+    assert f(A, B, D, None, C, -1, T, 1, S) == ERR_SHAPE
+    assert f(A, None, D, None, C, E, T, 1, S) == ERR_NULL
+    assert f(A, B, D, None, None, E, T, 0, S) == ERR_NULL
+    assert f(A + 1, B, D, None, C, E, T, 1, S) == ERR_ALIGN
+    assert f(A, B, D, None, D + E * T - 4, E, T, 1, S) == ERR_ALIAS  # output over the flags
+    assert f(None, None, None, None, None, E, 0, 1, S) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -50,8 +50,12 @@ MUTATIONS = [
      "if (step_done(term, trunc, i)) prev = 0.0;\n      const double cur = decay"),
     ("prefix_ignores_init", "double prev = init ? (double)init[e] : 0.0;\n    for (int64_t t = 0; t < T; ++t) {\n      const int64_t i = e * T + t;\n      if (t > 0 && step_done(term, trunc, i - 1)) prev = 0.0;\n      const double cur = prev +",
      "double prev = 0.0;\n    for (int64_t t = 0; t < T; ++t) {\n      const int64_t i = e * T + t;\n      if (t > 0 && step_done(term, trunc, i - 1)) prev = 0.0;\n      const double cur = prev +"),
-    ("scan_direction_flipped", "const int64_t t = reverse ? (T - 1 - k) : k;",
-     "const int64_t t = reverse ? k : (T - 1 - k);"),
+    ("scan_direction_flipped", "const int64_t t = reverse ? (T - 1 - k) : k;\n      const int64_t i = e * T + t;\n      state = (double)a[i]",
+     "const int64_t t = reverse ? k : (T - 1 - k);\n      const int64_t i = e * T + t;\n      state = (double)a[i]"),
+    ("segmented_forward_cut_same_step", "cut = reverse ? (done[i] != 0) : (t > 0 && done[i - 1] != 0);",
+     "cut = reverse ? (done[i] != 0) : (done[i] != 0);"),
+    ("segmented_cut_keeps_chain", "state = (cut ? 0.0 : (double)a[i] * state) + (double)b[i];",
+     "state = (double)a[i] * state + (double)b[i] + 0.0 * cut;"),
 ]
 
 
@@ -84,6 +88,13 @@ def _pins_pass() -> bool:
     b = rng.standard_normal((5, 9)).astype(np.float32)
     for rev in (True, False):
         checks.append((oracle.linear_scan(a, b, None, reverse=rev), ds.linear_scan(a, b, None, reverse=rev)))
+    cuts = term | trunc
+    a4 = rng.uniform(-1, 1, cuts.shape).astype(np.float32)
+    b4 = rng.standard_normal(cuts.shape).astype(np.float32)
+    c4 = rng.standard_normal(cuts.shape[0]).astype(np.float32)
+    for rev in (True, False):
+        checks.append((oracle.linear_scan_segmented(a4, b4, cuts, c4, reverse=rev),
+                       ds.linear_scan_segmented(a4, b4, cuts, c4, reverse=rev)))
     return all(_err(g, r) < 1e-12 for g, r in checks)
 
 

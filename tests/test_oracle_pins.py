@@ -121,6 +121,48 @@ def test_generic_scan_against_direct_sums():
                        ds.linear_scan(a, b, carry, reverse=rev)) < TOL
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 5])
+def test_segmented_generic_scan_against_direct_sums(T):
+    """Every cut pattern of length T, both directions, with and without a carry."""
+    rng = np.random.default_rng(50 + T)
+    pats = np.array(list(itertools.product([0, 1], repeat=T)), dtype=np.uint8)
+    E = len(pats)
+    a = rng.uniform(-1.2, 1.2, size=(E, T)).astype(np.float32)
+    b = rng.standard_normal((E, T)).astype(np.float32)
+    c = rng.standard_normal(E).astype(np.float32)
+    for rev in (True, False):
+        for carry in (None, c):
+            assert err(oracle.linear_scan_segmented(a, b, pats, carry, reverse=rev),
+                       ds.linear_scan_segmented(a, b, pats, carry, reverse=rev)) < TOL
+
+
+def test_segmented_generic_scan_reductions():
+    """No cuts -> the plain recurrence; a = 1 forward -> episodic prefix sums;
+    a = gamma backward -> discounted returns without bootstraps; a = gamma*lambda
+    forward -> eligibility traces (each with the matching flags)."""
+    rng = np.random.default_rng(51)
+    E, T = 6, 40
+    a = rng.uniform(-1.0, 1.0, size=(E, T)).astype(np.float32)
+    x = rng.standard_normal((E, T)).astype(np.float32)
+    c = rng.standard_normal(E).astype(np.float32)
+    term = (rng.random((E, T)) < 0.15).astype(np.uint8)
+    zeros = np.zeros((E, T), dtype=np.uint8)
+    for rev in (True, False):
+        ref = oracle.linear_scan(a, x, c, reverse=rev)
+        assert np.array_equal(oracle.linear_scan_segmented(a, x, None, c, reverse=rev), ref)
+        assert np.array_equal(oracle.linear_scan_segmented(a, x, zeros, c, reverse=rev), ref)
+    ones = np.ones((E, T), dtype=np.float32)
+    assert err(oracle.linear_scan_segmented(ones, x, term, c, reverse=False),
+               oracle.episodic_prefix_sum(x, term, None, c)) < TOL
+    g = np.float32(0.97)
+    assert err(oracle.linear_scan_segmented(np.full((E, T), g, np.float32), x, term, None, reverse=True),
+               oracle.discounted_returns(x, term, None, None, None, gamma=float(g))) < TOL
+    gl = np.float32(np.float32(0.9) * np.float32(0.8))
+    got = oracle.linear_scan_segmented(np.full((E, T), gl, np.float32), x, term, c, reverse=False)
+    # traces multiply the carry by gamma*lambda at t = 0, as a_0 does here
+    assert err(got, oracle.eligibility_traces(x, term, None, c, gamma=0.9, lam=0.8)) < 1e-6
+
+
 # ------------------------------------------------------------------ closed forms
 def test_discounted_constant_reward_closed_form():
     """Constant reward c, no flags, zero bootstrap: G_t = c (1 - g^(T-t)) / (1 - g)."""
