@@ -328,6 +328,50 @@ def time_estimators(runner, names, d, w, reps):
     return per
 
 
+def time_traces_vec(torch, device, args, E, T, D, p_term, p_trunc):
+    """Per-launch time of the vector traces entry on rotating [E, T, D] buffers."""
+    import linear_recurrence_scan_reverse_amd as rl
+    f = synth.draw_features(E, T, D, seed=0, p_term=p_term, p_trunc=p_trunc)
+    set_bytes = 8 * E * T * D + 2 * E * T + 4 * E * D
+    nsets = int(min(16, max(2, -(-(1 << 30) // set_bytes) + 1)))
+    base = {k: torch.from_numpy(v).to(device) for k, v in f.items()}
+    sets = []
+    for i in range(nsets):
+        s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
+        s["out"] = torch.empty_like(s["x"])
+        sets.append(s)
+    lib = rl.lib()
+    stream = torch.cuda.current_stream(device)
+    st = stream.cuda_stream
+    k = [0]
+
+    def call():
+        s = sets[k[0] % nsets]
+        k[0] += 1
+        rc = lib.rlscan_eligibility_traces_vec(s["x"].data_ptr(), s["terminated"].data_ptr(),
+                                               s["truncated"].data_ptr(), s["init"].data_ptr(),
+                                               s["out"].data_ptr(), E, T, D, 0.99, 0.95, st)
+        if rc != 0:
+            raise RuntimeError("rlscan_eligibility_traces_vec returned status %d" % rc)
+
+    for _ in range(nsets + 2):
+        call()
+    reps = max(args.steps, 20)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        call()
+    end.record(stream)
+    end.synchronize()
+    us = start.elapsed_time(end) / reps * 1e3
+    b = 8 * E * T * D + 2 * E * T + 4 * E * D
+    del sets, base
+    return {"shape": "E=%d T=%d D=%d" % (E, T, D), "us_per_launch": round(us, 3), "alg_bytes": b,
+            "GBps": b / (us * 1e-6) / 1e9, "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+
+
 def run_grid(torch, device, args):
     """Every estimator over the E x T grid with the all-seven distributions; one
     JSON line per grid point (buffer sets above 1 GiB are skipped)."""
@@ -444,6 +488,14 @@ def main():
         n = "linear_scan_segmented"
         log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak" % (
             "generic, with cuts", fused[n]["us_per_launch"], fused[n]["GBps"], 100 * fused[n]["frac_of_peak"]))
+
+    # ---- vector-valued traces over [E, T, D] features (not part of the step)
+    if "eligibility_traces" in names:
+        vt = time_traces_vec(torch, device, args, E=1024, T=w.T, D=64, p_term=w.p_term, p_trunc=w.p_trunc)
+        fused = dict(fused or {})
+        fused["eligibility_traces_vec"] = vt
+        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  (%s)" % (
+            "traces, D=64", vt["us_per_launch"], vt["GBps"], 100 * vt["frac_of_peak"], vt["shape"]))
 
     dom = max(per, key=lambda k: per[k]["us_per_launch"])
     traffic, traffic_src = read_traffic(dom, w.name)

@@ -189,6 +189,25 @@ rlscan_status rlscan_eligibility_traces(const float *x, const uint8_t *terminate
                                         int64_t E, int64_t T, float gamma, float lambda,
                                         hipStream_t stream);
 
+/* Eligibility traces of a feature vector per step ([E,T,D] features, e.g. the
+ * gradient of the value estimate), forward in time: every column d follows
+ * rlscan_eligibility_traces with the row's flags,
+ *   e_t[d] = gamma*lambda * (t == 0 ? init[d] : (done_{t-1} ? 0 : e_{t-1}[d])) + x_t[d],
+ * done = terminated or truncated (gist.science summary, "Methodologie"
+ * section 1 names eligibility traces as the forward-time recurrence; the pages
+ * print no vector form, and this entry reads one as the same recurrence run
+ * column by column with the row's shared decay and cuts).
+ * Layout: x and traces [E,T,D] row-major (element (e,t,d) at (e*T + t)*D + d);
+ * terminated, truncated [E,T] (optional); init [E,D] (optional, NULL -> 0).
+ * Out: traces [E,T,D] (required).  gamma, lambda in [0,1].  Each column is
+ * folded serially by one lane; full speed needs E*D in the thousands.
+ * Errors as above, with D < 0, T*D >= RLSCAN_MAX_T or E*T*D overflowing
+ * reported as RLSCAN_ERR_SHAPE. */
+rlscan_status rlscan_eligibility_traces_vec(const float *x, const uint8_t *terminated,
+                                            const uint8_t *truncated, const float *init, float *traces,
+                                            int64_t E, int64_t T, int64_t D, float gamma, float lambda,
+                                            hipStream_t stream);
+
 /* Episodic inclusive prefix sum, forward in time:
  *   S_t = S_{t-1} + x_t, S_{-1} = init[e] (NULL -> 0), restarting from 0 after
  *   any step that terminated or was truncated.

@@ -19,7 +19,8 @@ import threading
 __all__ = [
     "RlscanError", "lib", "library_path", "version",
     "discounted_returns", "td_lambda", "returns_and_td_lambda", "gae", "vtrace", "retrace",
-    "eligibility_traces", "episodic_prefix_sum", "linear_scan", "linear_scan_segmented",
+    "eligibility_traces", "eligibility_traces_vec", "episodic_prefix_sum", "linear_scan",
+    "linear_scan_segmented",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +45,7 @@ _SIGNATURES = {
     "rlscan_episodic_prefix_sum": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "rlscan_linear_scan": [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp],
     "rlscan_linear_scan_segmented": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _vp],
+    "rlscan_eligibility_traces_vec": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _f32, _vp],
 }
 
 
@@ -343,4 +345,25 @@ def linear_scan_segmented(a, b, done=None, carry=None, *, reverse=True, out=None
     out = _out(out, "out", shape, dev)
     _call("rlscan_linear_scan_segmented", _ptr(aa), _ptr(bb), _ptr(dn), _ptr(c0), _ptr(out), E, T,
           1 if reverse else 0, _stream(dev, stream))
+    return out
+
+
+def eligibility_traces_vec(x, terminated=None, truncated=None, init=None, *, gamma=0.99, lam=0.95,
+                           out=None, stream=None):
+    """Eligibility traces of feature vectors: x [E, T, D], flags [E, T], init [E, D];
+    every column follows the scalar trace with the row's flags."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a [E, T, D] tensor")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a GPU device, got %s" % x.device)
+    E, T, D = x.shape
+    dev = x.device
+    xx = _check_f32(x, "x", (E, T, D), dev)
+    te = _check_flags(terminated, "terminated", (E, T), dev)
+    tr = _check_flags(truncated, "truncated", (E, T), dev)
+    it = _check_f32(init, "init", (E, D), dev)
+    out = _out(out, "out", (E, T, D), dev)
+    _call("rlscan_eligibility_traces_vec", _ptr(xx), _ptr(te), _ptr(tr), _ptr(it), _ptr(out), E, T, D,
+          float(gamma), float(lam), _stream(dev, stream))
     return out

@@ -406,4 +406,26 @@ rlscan_status rlscan_linear_scan_segmented(const float* a_coef, const float* b_c
                  : launched(rlscan::launch<rlscan::LinearScanForward>(a, stream));
 }
 
+rlscan_status rlscan_eligibility_traces_vec(const float* x, const uint8_t* terminated, const uint8_t* truncated,
+                                            const float* init, float* traces, int64_t E, int64_t T, int64_t D,
+                                            float gamma, float lambda, hipStream_t stream) {
+  if (D < 0 || (D > 0 && T >= RLSCAN_MAX_T / D)) return RLSCAN_ERR_SHAPE;  // T*D < 2^30
+  rlscan_status st = check_shape(E, T);
+  if (st != RLSCAN_OK) return st;
+  if ((st = check_shape(E, T * D)) != RLSCAN_OK) return st;
+  if (!in_unit(gamma) || !in_unit(lambda)) return RLSCAN_ERR_PARAM;
+  if (E * T * D == 0) return RLSCAN_OK;
+  if (!x || !traces) return RLSCAN_ERR_NULL;
+  if (misaligned(x) || misaligned(init)) return RLSCAN_ERR_ALIGN;
+  Io io;
+  io.add_in(x, 4 * E * T * D);
+  io.add_in(terminated, E * T);
+  io.add_in(truncated, E * T);
+  io.add_in(init, 4 * E * D);
+  io.add_out(traces);
+  if ((st = check_io(io, E, T * D)) != RLSCAN_OK) return st;
+  return launched(rlscan::launch_traces_vec(x, terminated, truncated, init, traces, E, T, D, gamma, lambda,
+                                            stream));
+}
+
 }  // extern "C"

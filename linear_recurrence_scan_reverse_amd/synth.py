@@ -137,3 +137,16 @@ def flag_patterns(T: int):
     term = ((digits & 1) != 0).astype(np.uint8)
     trunc = ((digits & 2) != 0).astype(np.uint8)
     return term, trunc
+
+
+def draw_features(E: int, T: int, D: int, *, seed: int = 0, p_term: float = 0.0,
+                  p_trunc: float = 0.0) -> dict:
+    """Per-step feature vectors for the vector traces: x float32 [E, T, D] ~ N(0,1),
+    init float32 [E, D] ~ N(0,1), terminated / truncated uint8 [E, T] ~ Bernoulli."""
+    rng = np.random.default_rng(seed)
+    return {
+        "x": rng.standard_normal((int(E), int(T), int(D)), dtype=np.float32),
+        "init": rng.standard_normal((int(E), int(D)), dtype=np.float32),
+        "terminated": (rng.random((int(E), int(T))) < p_term).astype(np.uint8),
+        "truncated": (rng.random((int(E), int(T))) < p_trunc).astype(np.uint8),
+    }

@@ -59,6 +59,7 @@ def _bind(lib):
         "oracle_episodic_prefix_sum": [_f32p, _u8p, _u8p, _f32p, _f64p, _i64, _i64],
         "oracle_linear_scan": [_f32p, _f32p, _f32p, _f64p, _i64, _i64, ctypes.c_int],
         "oracle_linear_scan_segmented": [_f32p, _f32p, _u8p, _f32p, _f64p, _i64, _i64, ctypes.c_int],
+        "oracle_eligibility_traces_vec": [_f32p, _u8p, _u8p, _f32p, _f64p, _i64, _i64, _i64, _f32, _f32],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -237,6 +238,22 @@ def linear_scan_segmented(a, b, done=None, carry=None, reverse=True):
     keep = [_f32_in(a, shape), _f32_in(b, shape), _u8_in(done, shape), _row_in(carry, E)]
     out, po = _out(shape)
     _load().oracle_linear_scan_segmented(*(k[1] for k in keep), po, E, T, 1 if reverse else 0)
+    return out
+
+
+def eligibility_traces_vec(x, terminated=None, truncated=None, init=None, gamma=0.99, lam=0.95):
+    """Eligibility traces of feature vectors: x [E, T, D], flags [E, T], init [E, D]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 3:
+        raise ValueError("x must be [E, T, D]")
+    E, T, D = x.shape
+    te = _u8_in(terminated, (E, T))
+    tr = _u8_in(truncated, (E, T))
+    it = (None, None) if init is None else _f32_in(init, (E, D))
+    out = np.empty((E, T, D), dtype=np.float64)
+    _load().oracle_eligibility_traces_vec(x.ctypes.data_as(_f32p), te[1], tr[1], it[1],
+                                          out.ctypes.data_as(_f64p), E, T, D,
+                                          float(np.float32(gamma)), float(np.float32(lam)))
     return out
 
 

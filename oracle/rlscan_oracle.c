@@ -317,3 +317,25 @@ void oracle_linear_scan_segmented(const float *a, const float *b, const uint8_t 
     }
   }
 }
+
+/* Eligibility traces of a feature vector per step: x, out [E,T,D] row-major
+ * ((e,t,d) at (e*T + t)*D + d), flags [E,T], init [E,D].  Each column d
+ * follows the scalar trace recurrence with the row's flags:
+ *   e_t[d] = decay * (t == 0 ? init[d] : (done_{t-1} ? 0 : e_{t-1}[d])) + x_t[d]. */
+void oracle_eligibility_traces_vec(const float *x, const uint8_t *term, const uint8_t *trunc,
+                                   const float *init, double *out, int64_t E, int64_t T, int64_t D,
+                                   float gamma_f, float lambda_f) {
+  const double decay = (double)gamma_f * (double)lambda_f;
+  for (int64_t e = 0; e < E; ++e) {
+    for (int64_t d = 0; d < D; ++d) {
+      double prev = init ? (double)init[e * D + d] : 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        if (t > 0 && step_done(term, trunc, e * T + t - 1)) prev = 0.0;
+        const int64_t i = (e * T + t) * D + d;
+        const double cur = decay * prev + (double)x[i];
+        out[i] = cur;
+        prev = cur;
+      }
+    }
+  }
+}

@@ -41,7 +41,8 @@ def test_header_declares_the_expected_entry_points():
     for n in ["rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_returns_and_td_lambda",
               "rlscan_gae", "rlscan_vtrace",
               "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum",
-              "rlscan_linear_scan", "rlscan_linear_scan_segmented", "rlscan_status_string",
+              "rlscan_linear_scan", "rlscan_linear_scan_segmented", "rlscan_eligibility_traces_vec",
+              "rlscan_status_string",
               "rlscan_version"]:
         assert n in names
 
@@ -162,6 +163,19 @@ def test_linear_scan_segmented_validation(lib):
     assert f(A + 1, B, D, None, C, E, T, 1, S) == ERR_ALIGN
     assert f(A, B, D, None, D + E * T - 4, E, T, 1, S) == ERR_ALIAS  # output over the flags
     assert f(None, None, None, None, None, E, 0, 1, S) == OK
+
+
+def test_eligibility_traces_vec_validation(lib):
+    E, T, Dm = 4, 8, 16
+    f = lib.rlscan_eligibility_traces_vec
+    assert f(A, None, None, None, C, E, T, -1, 0.9, 0.9, S) == ERR_SHAPE
+    assert f(A, None, None, None, C, E, 2 ** 40, 2 ** 40, 0.9, 0.9, S) == ERR_SHAPE
+    assert f(A, None, None, None, C, E, T, Dm, 0.9, 1.5, S) == ERR_PARAM
+    assert f(None, None, None, None, C, E, T, Dm, 0.9, 0.9, S) == ERR_NULL
+    assert f(A, None, None, F + 2, C, E, T, Dm, 0.9, 0.9, S) == ERR_ALIGN
+    assert f(A, None, None, None, A + 4 * E * T * Dm - 4, E, T, Dm, 0.9, 0.9, S) == ERR_ALIAS
+    assert f(A, D, None, None, D + 8, E, T, Dm, 0.9, 0.9, S) == ERR_ALIAS  # output over the flags
+    assert f(None, None, None, None, None, E, T, 0, 0.9, 0.9, S) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -54,6 +54,10 @@ MUTATIONS = [
      "const int64_t t = reverse ? k : (T - 1 - k);\n      const int64_t i = e * T + t;\n      state = (double)a[i]"),
     ("segmented_forward_cut_same_step", "cut = reverse ? (done[i] != 0) : (t > 0 && done[i - 1] != 0);",
      "cut = reverse ? (done[i] != 0) : (done[i] != 0);"),
+    ("vector_traces_transposed_layout", "const int64_t i = (e * T + t) * D + d;",
+     "const int64_t i = (e * D + d) * T + t;"),
+    ("vector_traces_cut_on_current_step", "if (t > 0 && step_done(term, trunc, e * T + t - 1)) prev = 0.0;\n        const int64_t i",
+     "if (step_done(term, trunc, e * T + t)) prev = 0.0;\n        const int64_t i"),
     ("segmented_cut_keeps_chain", "state = (cut ? 0.0 : (double)a[i] * state) + (double)b[i];",
      "state = (double)a[i] * state + (double)b[i] + 0.0 * cut;"),
 ]
@@ -95,6 +99,12 @@ def _pins_pass() -> bool:
     for rev in (True, False):
         checks.append((oracle.linear_scan_segmented(a4, b4, cuts, c4, reverse=rev),
                        ds.linear_scan_segmented(a4, b4, cuts, c4, reverse=rev)))
+    xv = rng.standard_normal((term.shape[0], 4, 3)).astype(np.float32)
+    iv = rng.standard_normal((term.shape[0], 3)).astype(np.float32)
+    gv = oracle.eligibility_traces_vec(xv, term, trunc, iv, gamma=0.9, lam=0.7)
+    for d in range(3):
+        checks.append((gv[:, :, d], ds.eligibility_traces(np.ascontiguousarray(xv[:, :, d]), term, trunc,
+                                                           np.ascontiguousarray(iv[:, d]), gamma=0.9, lam=0.7)))
     return all(_err(g, r) < 1e-12 for g, r in checks)
 
 

@@ -163,6 +163,39 @@ def test_segmented_generic_scan_reductions():
     assert err(got, oracle.eligibility_traces(x, term, None, c, gamma=0.9, lam=0.8)) < 1e-6
 
 
+def test_vector_traces_against_direct_sums():
+    """Every flag pattern of length 4 on a 3-feature vector: each column is the
+    scalar trace's direct sum with the row's flags."""
+    rng = np.random.default_rng(52)
+    term, trunc = synth.flag_patterns(4)
+    E, T, D = term.shape[0], 4, 3
+    x = rng.standard_normal((E, T, D)).astype(np.float32)
+    init = rng.standard_normal((E, D)).astype(np.float32)
+    got = oracle.eligibility_traces_vec(x, term, trunc, init, gamma=0.9, lam=0.7)
+    for d in range(D):
+        ref = ds.eligibility_traces(np.ascontiguousarray(x[:, :, d]), term, trunc,
+                                    np.ascontiguousarray(init[:, d]), gamma=0.9, lam=0.7)
+        assert err(got[:, :, d], ref) < TOL
+
+
+def test_vector_traces_columns_equal_scalar_traces():
+    """One column at a time, the vector form equals the scalar estimator exactly
+    (same recursion, same order of operations), with and without init."""
+    rng = np.random.default_rng(53)
+    E, T, D = 5, 37, 6
+    x = rng.standard_normal((E, T, D)).astype(np.float32)
+    init = rng.standard_normal((E, D)).astype(np.float32)
+    term = (rng.random((E, T)) < 0.1).astype(np.uint8)
+    trunc = (rng.random((E, T)) < 0.1).astype(np.uint8)
+    for it in (None, init):
+        got = oracle.eligibility_traces_vec(x, term, trunc, it, gamma=0.99, lam=0.95)
+        for d in range(D):
+            ref = oracle.eligibility_traces(np.ascontiguousarray(x[:, :, d]), term, trunc,
+                                            None if it is None else np.ascontiguousarray(it[:, d]),
+                                            gamma=0.99, lam=0.95)
+            assert np.array_equal(got[:, :, d], ref)
+
+
 # ------------------------------------------------------------------ closed forms
 def test_discounted_constant_reward_closed_form():
     """Constant reward c, no flags, zero bootstrap: G_t = c (1 - g^(T-t)) / (1 - g)."""
