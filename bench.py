@@ -18,6 +18,9 @@ Printed (one JSON line on stdout):
                  traffic rocprofv3 counted for it (when the committed counter
                  summary matches the current kernel sources)
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
+  formats_and_layouts  the seven estimators with bfloat16 / float16 value
+                 storage and in the time-major [T, E] layout (the _ex
+                 entries), same workload, not part of the step
   copy_ceiling   device-to-device copy bandwidth measured in the same run
 Context only (not comparable): the rl-triton pages report 1.6-5.70x full-call
 speedups over a vectorized torch.compile scan on NVIDIA GPUs (H100 80GB HBM3
@@ -64,18 +67,18 @@ def kernel_source_hash() -> str:
 
 
 # ----------------------------------------------------------------- algorithmic bytes
-def alg_bytes(name, d, E, T, with_flags=True):
+def alg_bytes(name, d, E, T, with_flags=True, vb=4):
     """Bytes the method itself must move for one call: every dense input read once,
     every output written once, [E] arrays once per row, the truncation bootstrap
-    only where a step is truncated and not terminated."""
+    only where a step is truncated and not terminated (vb bytes per value)."""
     n = E * T
-    f = 4 * n
+    f = vb * n
     flags = n * (int("terminated" in d) + int("truncated" in d)) if with_flags else 0
     sparse = 0
     if with_flags and "truncated" in d:
         tb_steps = int(np.count_nonzero(d["truncated"] & (d["terminated"] == 0)))
-        sparse = 4 * tb_steps
-    row = 4 * E
+        sparse = vb * tb_steps
+    row = vb * E
     table = {
         "discounted_returns": f + flags + sparse + row + f,
         "td_lambda": 2 * f + flags + sparse + row + f,
@@ -91,26 +94,49 @@ def alg_bytes(name, d, E, T, with_flags=True):
 
 
 # ----------------------------------------------------------------- GPU side
+# storage formats of the _ex entries (rlscan_format) and their value dtypes
+FORMATS = {"f32": (0, "float32"), "bf16": (1, "bfloat16"), "f16": (2, "float16")}
+VALUE_KEYS = ("r", "v", "log_rhos", "q", "exp_q", "pi", "mu", "bootstrap_value", "trunc_bootstrap")
+ROW_KEYS = ("bootstrap_value",)
+
+
+class _Ex:
+    """The library with every estimator entry bound to one storage format and layout."""
+
+    def __init__(self, lib, fmt, layout):
+        self._lib, self._fmt, self._layout = lib, fmt, layout
+
+    def __getattr__(self, name):
+        fn = getattr(self._lib, name + "_ex")
+        return lambda *a: fn(self._fmt, self._layout, *a)
+
+
 class Runner:
     """Pre-resolved C-ABI calls over rotating device buffer sets."""
 
-    def __init__(self, w, d, nsets, device):
+    def __init__(self, w, d, nsets, device, storage="f32", time_major=False):
         import torch
         import linear_recurrence_scan_reverse_amd as rl
 
         self.torch = torch
-        self.lib = rl.lib()
+        fmt, dname = FORMATS[storage]
+        vdt = getattr(torch, dname)
+        self.vb = torch.empty(0, dtype=vdt).element_size()
+        self.lib = rl.lib() if (fmt == 0 and not time_major) else _Ex(rl.lib(), fmt, 1 if time_major else 0)
         self.E, self.T = w.E, w.T
         self.w = w
         self.stream = torch.cuda.current_stream(device)
         self.sptr = self.stream.cuda_stream
         base = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in d.items()}
+        base = {k: (v.to(vdt) if k in VALUE_KEYS else v) for k, v in base.items()}
+        if time_major:  # [T, E] per-step arrays (E and T keep their meaning)
+            base = {k: (v if k in ROW_KEYS else v.t().contiguous()) for k, v in base.items()}
         self.sets = []
         for i in range(nsets):
             s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
             for o in ORDER:
-                s["out_" + o] = torch.empty((w.E, w.T), dtype=torch.float32, device=device)
-            s["out_vtrace_pg"] = torch.empty((w.E, w.T), dtype=torch.float32, device=device)
+                s["out_" + o] = torch.empty((w.E, w.T), dtype=vdt, device=device)
+            s["out_vtrace_pg"] = torch.empty((w.E, w.T), dtype=vdt, device=device)
             ptrs = {k: None for k in ("terminated", "truncated", "bootstrap_value", "trunc_bootstrap")}
             ptrs.update({k: v.data_ptr() for k, v in s.items()})
             self.sets.append(ptrs)
@@ -322,7 +348,7 @@ def time_estimators(runner, names, d, w, reps):
             runner.call(n, runner.next_set())
         s = time_region(runner, lambda: runner.call(n, runner.next_set()), reps)
         us = s / reps * 1e6
-        b = alg_bytes(n, d, w.E, w.T)
+        b = alg_bytes(n, d, w.E, w.T, vb=runner.vb)
         per[n] = {"us_per_launch": round(us, 3), "env_steps_per_s": w.E * w.T / (us * 1e-6), "alg_bytes": b,
                   "GBps": b / (us * 1e-6) / 1e9, "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
     return per
@@ -416,6 +442,7 @@ def main():
     ap.add_argument("--no-trunc", action="store_true", help="inputs without per-step truncation")
     ap.add_argument("--grid-e", default=None, help="comma-separated E values for --grid")
     ap.add_argument("--grid-t", default=None, help="comma-separated T values for --grid")
+    ap.add_argument("--no-16", action="store_true", help="skip the 16-bit storage and time-major timings")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -497,6 +524,28 @@ def main():
         log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  (%s)" % (
             "traces, D=64", vt["us_per_launch"], vt["GBps"], 100 * vt["frac_of_peak"], vt["shape"]))
 
+    # ---- the seven estimators with 16-bit storage and in the time-major layout
+    # (not part of the step)
+    variants = None
+    if not args.only and not args.no_16:
+        variants = {}
+        del runner
+        torch.cuda.empty_cache()
+        for key, st, tm in (("bf16", "bf16", False), ("f16", "f16", False), ("time_major_f32", "f32", True),
+                            ("time_major_bf16", "bf16", True)):
+            vb = 2 if st != "f32" else 4
+            nsets_v = int(min(64, max(2, -(-(1 << 30) // (set_bytes_est * vb // 4)) + 1)))
+            rv = Runner(w, d, nsets_v, device, storage=st, time_major=tm)
+            pv = time_estimators(rv, names, d, w, max(args.steps, 20))
+            for n in names:
+                pv[n]["f32_us_per_launch"] = per[n]["us_per_launch"]
+                pv[n]["speedup_vs_f32"] = round(per[n]["us_per_launch"] / pv[n]["us_per_launch"], 3)
+            variants[key] = pv
+            log("  %-15s " % key + "  ".join("%s %.2f us %.1f%%" % (
+                n[:6], pv[n]["us_per_launch"], 100 * pv[n]["frac_of_peak"]) for n in names))
+            del rv
+            torch.cuda.empty_cache()
+
     dom = max(per, key=lambda k: per[k]["us_per_launch"])
     traffic, traffic_src = read_traffic(dom, w.name)
     roofline = {
@@ -546,6 +595,7 @@ def main():
         "cpu_baseline": cpu,
         "per_estimator": per,
         "one_pass_entries": fused,
+        "formats_and_layouts": variants,
         "copy_ceiling_GBps": round(ceiling, 1),
         "kernel_source_sha256": kernel_source_hash(),
         "context": "rl-triton pages: 1.6-5.70x full-call speedup vs a vectorized torch.compile scan "

@@ -24,9 +24,10 @@
  *             pointers must be 4-byte aligned.  The caller owns and allocates
  *             every buffer; the library allocates nothing, keeps no state
  *             between calls and is safe to call from several host threads.
- * Types       Values are IEEE float32; flags are uint8 with nonzero = true.
- *             The scan runs in float64 on-chip and each output is rounded
- *             once to float32 (round to nearest).
+ * Types       Values are IEEE float32 (the _ex entries also take bfloat16
+ *             or float16 storage and a time-major layout, see below); flags
+ *             are uint8 with nonzero = true.  The scan runs in float64 on-chip and each output is
+ *             rounded once to float32 (round to nearest).
  * Flags       terminated[e,t] / truncated[e,t] describe transition t (the same
  *             index as reward t).  Terminated: the successor state's value is
  *             0.  Truncated: the successor's value is trunc_bootstrap[e,t].  If
@@ -54,7 +55,9 @@
  *                                 E*T overflows int64;
  *               RLSCAN_ERR_PARAM  a parameter is non-finite or out of range;
  *               RLSCAN_ERR_NULL   a required pointer is NULL while E*T > 0;
- *               RLSCAN_ERR_ALIGN  a float pointer is not 4-byte aligned;
+ *               RLSCAN_ERR_ALIGN  a value pointer is not aligned to its element
+ *                                 size (4 bytes for float32, 2 for the 16-bit
+ *                                 storage formats);
  *               RLSCAN_ERR_ALIAS  an output range overlaps an input range or
  *                                 another output range;
  *             E*T == 0 (after shape/parameter checks) is a no-op returning
@@ -199,8 +202,9 @@ rlscan_status rlscan_eligibility_traces(const float *x, const uint8_t *terminate
  * column by column with the row's shared decay and cuts).
  * Layout: x and traces [E,T,D] row-major (element (e,t,d) at (e*T + t)*D + d);
  * terminated, truncated [E,T] (optional); init [E,D] (optional, NULL -> 0).
- * Out: traces [E,T,D] (required).  gamma, lambda in [0,1].  Each column is
- * folded serially by one lane; full speed needs E*D in the thousands.
+ * Out: traces [E,T,D] (required).  gamma, lambda in [0,1].  One block of four
+ * waves covers 64 columns of a row; full speed needs E*ceil(D/64) blocks in
+ * the thousands.
  * Errors as above, with D < 0, T*D >= RLSCAN_MAX_T or E*T*D overflowing
  * reported as RLSCAN_ERR_SHAPE. */
 rlscan_status rlscan_eligibility_traces_vec(const float *x, const uint8_t *terminated,
@@ -239,6 +243,81 @@ rlscan_status rlscan_linear_scan(const float *a, const float *b, const float *ca
 rlscan_status rlscan_linear_scan_segmented(const float *a, const float *b, const uint8_t *done,
                                            const float *carry, float *x, int64_t E, int64_t T, int reverse,
                                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Storage format and layout.  The seven estimators again, each with two more
+ * leading arguments; every other argument means what it means for the
+ * float32 entry of the same name.
+ *
+ * fmt     The type of every value array (inputs, bootstraps, init and
+ *         outputs): float32, bfloat16 or float16.  16-bit storage halves the
+ *         HBM bytes per step; the pages fix no precision, so this is an
+ *         extension for rollouts already kept in 16 bits (the gist.science
+ *         summary's plain-language part names specialised data formats as
+ *         work still to do).  Inputs are widened exactly on load, the scan runs in float64
+ *         as above, and each output is rounded to float32 and then to the
+ *         format (round to nearest even both times; float16 overflow gives
+ *         +-inf).  Flags stay uint8.  Value pointers must be aligned to the
+ *         element size (2 bytes for the 16-bit formats).
+ * layout  RLSCAN_LAYOUT_ENV_MAJOR: [E,T] arrays as above, (e,t) at e*T + t.
+ *         RLSCAN_LAYOUT_TIME_MAJOR: [T,E] arrays, (e,t) at t*E + e, the order
+ *         of rollout buffers that append one step for all environments (the
+ *         rl-triton skill page, skillsdirectory.com, "Implementation
+ *         Workflow" step 2, lists contiguous and strided layouts).  This
+ *         applies to rewards, values and every other [E,T] input or output,
+ *         flags and trunc_bootstrap included; [E] arrays are unchanged.  E and
+ *         T keep their meaning (environments, steps).  Time-major calls are
+ *         one kernel whose blocks each cover 64 environments; full speed
+ *         needs E in the thousands.
+ * An unknown fmt or layout is RLSCAN_ERR_PARAM.  (RLSCAN_FORMAT_F32,
+ * RLSCAN_LAYOUT_ENV_MAJOR) is exactly the float32 entry.
+ * ------------------------------------------------------------------------ */
+typedef enum rlscan_format {
+  RLSCAN_FORMAT_F32 = 0,  /* IEEE binary32 */
+  RLSCAN_FORMAT_BF16 = 1, /* bfloat16: 8-bit exponent, 7-bit mantissa */
+  RLSCAN_FORMAT_F16 = 2   /* IEEE binary16 */
+} rlscan_format;
+
+typedef enum rlscan_layout {
+  RLSCAN_LAYOUT_ENV_MAJOR = 0, /* [E,T] row-major: (e,t) at e*T + t */
+  RLSCAN_LAYOUT_TIME_MAJOR = 1 /* [T,E] row-major: (e,t) at t*E + e */
+} rlscan_layout;
+
+rlscan_status rlscan_discounted_returns_ex(rlscan_format fmt, rlscan_layout layout, const void *rewards,
+                                           const uint8_t *terminated, const uint8_t *truncated,
+                                           const void *bootstrap_value, const void *trunc_bootstrap, void *returns,
+                                           int64_t E, int64_t T, float gamma, hipStream_t stream);
+
+rlscan_status rlscan_td_lambda_ex(rlscan_format fmt, rlscan_layout layout, const void *rewards, const void *values,
+                                  const uint8_t *terminated, const uint8_t *truncated, const void *bootstrap_value,
+                                  const void *trunc_bootstrap, void *returns, int64_t E, int64_t T, float gamma,
+                                  float lambda, hipStream_t stream);
+
+rlscan_status rlscan_gae_ex(rlscan_format fmt, rlscan_layout layout, const void *rewards, const void *values,
+                            const uint8_t *terminated, const uint8_t *truncated, const void *bootstrap_value,
+                            const void *trunc_bootstrap, void *advantages, void *returns, int64_t E, int64_t T,
+                            float gamma, float lambda, hipStream_t stream);
+
+rlscan_status rlscan_vtrace_ex(rlscan_format fmt, rlscan_layout layout, const void *rewards, const void *values,
+                               const void *log_rhos, const uint8_t *terminated, const uint8_t *truncated,
+                               const void *bootstrap_value, const void *trunc_bootstrap, void *vs, void *pg_advantages,
+                               int64_t E, int64_t T, float gamma, float lambda, float rho_bar, float c_bar,
+                               hipStream_t stream);
+
+rlscan_status rlscan_retrace_ex(rlscan_format fmt, rlscan_layout layout, const void *rewards, const void *q_values,
+                                const void *expected_q, const void *pi_prob, const void *mu_prob,
+                                const uint8_t *terminated, const uint8_t *truncated, const void *bootstrap_value,
+                                const void *trunc_bootstrap, void *q_ret, int64_t E, int64_t T, float gamma,
+                                float lambda, hipStream_t stream);
+
+rlscan_status rlscan_eligibility_traces_ex(rlscan_format fmt, rlscan_layout layout, const void *x,
+                                           const uint8_t *terminated, const uint8_t *truncated, const void *init,
+                                           void *traces, int64_t E, int64_t T, float gamma, float lambda,
+                                           hipStream_t stream);
+
+rlscan_status rlscan_episodic_prefix_sum_ex(rlscan_format fmt, rlscan_layout layout, const void *x,
+                                            const uint8_t *terminated, const uint8_t *truncated, const void *init,
+                                            void *sums, int64_t E, int64_t T, hipStream_t stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

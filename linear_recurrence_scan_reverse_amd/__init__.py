@@ -9,6 +9,13 @@ no fallback: if the library is not built or cannot be loaded, every call raises.
 Estimators (rl-triton, arxivlens.com paper view, Abstract): discounted returns,
 TD(lambda) returns, GAE, V-trace, Retrace(lambda), eligibility traces and
 episodic prefix sums, plus the generic recurrence ``linear_scan``.
+
+Storage dtype and layout: the seven estimators take float32, bfloat16 or
+float16 value tensors (all of one dtype, taken from the first value argument)
+and return outputs of that dtype.  With ``time_major=True`` every per-step
+tensor is [T, E] instead of [E, T] (per-env tensors stay [E]).  16-bit or
+time-major calls go to the ``rlscan_*_ex`` entries.  The scan itself always
+runs in float64 on the GPU.
 """
 from __future__ import annotations
 
@@ -47,6 +54,16 @@ _SIGNATURES = {
     "rlscan_linear_scan_segmented": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _vp],
     "rlscan_eligibility_traces_vec": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _f32, _vp],
 }
+# The _ex entries take the storage format and the layout first, then the float32
+# entry's arguments.
+_EX = ("rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_gae", "rlscan_vtrace", "rlscan_retrace",
+       "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum")
+for _n in _EX:
+    _SIGNATURES[_n + "_ex"] = [_int, _int] + _SIGNATURES[_n]
+del _n
+
+# rlscan_format codes by storage dtype name
+_FORMATS = {"float32": 0, "bfloat16": 1, "float16": 2}
 
 
 class RlscanError(RuntimeError):
@@ -107,14 +124,16 @@ def _rows(x, name):
     return x
 
 
-def _check_f32(x, name, shape, device):
+def _check_val(x, name, shape, device, dtype=None):
+    """A value tensor: ``dtype`` (float32 when None), shape, device, contiguous."""
     torch = _torch()
     if x is None:
         return None
+    dtype = torch.float32 if dtype is None else dtype
     if not isinstance(x, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if x.dtype != torch.float32:
-        raise TypeError("%s must be float32, got %s" % (name, x.dtype))
+    if x.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, str(dtype).replace("torch.", ""), x.dtype))
     if tuple(x.shape) != tuple(shape):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(x.shape)))
     if x.device != device:
@@ -122,6 +141,34 @@ def _check_f32(x, name, shape, device):
     if not x.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return x
+
+
+_check_f32 = _check_val
+
+
+def _storage(x, name):
+    """The storage dtype of a primary value tensor (float32, bfloat16 or float16)."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    key = str(x.dtype).replace("torch.", "")
+    if key not in _FORMATS:
+        raise TypeError("%s must be float32, bfloat16 or float16, got %s" % (name, x.dtype))
+    return x.dtype
+
+
+def _entry(fname, dtype, time_major, *args):
+    """Call the float32 row-major entry, or its _ex variant (16-bit storage or time-major)."""
+    key = str(dtype).replace("torch.", "")
+    if key == "float32" and not time_major:
+        _call(fname, *args)
+    else:
+        _call(fname + "_ex", _FORMATS[key], 1 if time_major else 0, *args)
+
+
+def _dims(shape, time_major):
+    """(E, T) from the shape of a per-step tensor."""
+    return (shape[1], shape[0]) if time_major else (shape[0], shape[1])
 
 
 def _check_flags(x, name, shape, device):
@@ -153,11 +200,12 @@ def _stream(device, stream):
     return s.cuda_stream
 
 
-def _out(x, name, shape, device):
+def _out(x, name, shape, device, dtype=None):
     torch = _torch()
+    dtype = torch.float32 if dtype is None else dtype
     if x is None:
-        return torch.empty(shape, dtype=torch.float32, device=device)
-    return _check_f32(x, name, shape, device)
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _check_val(x, name, shape, device, dtype)
 
 
 def _call(fname, *args):
@@ -175,35 +223,37 @@ def _prep(primary, name):
 
 # ----------------------------------------------------------------- estimators
 def discounted_returns(rewards, terminated=None, truncated=None, bootstrap_value=None,
-                       trunc_bootstrap=None, *, gamma=0.99, out=None, stream=None):
+                       trunc_bootstrap=None, *, time_major=False, gamma=0.99, out=None, stream=None):
     """Discounted returns G_t = r_t + gamma * G_{t+1}, cut and bootstrapped at episode ends."""
     shape, dev = _prep(rewards, "rewards")
-    E, T = shape
-    r = _check_f32(rewards, "rewards", shape, dev)
+    E, T = _dims(shape, time_major)
+    dt = _storage(rewards, "rewards")
+    r = _check_val(rewards, "rewards", shape, dev, dt)
     te = _check_flags(terminated, "terminated", shape, dev)
     tr = _check_flags(truncated, "truncated", shape, dev)
-    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
-    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
-    out = _out(out, "out", shape, dev)
-    _call("rlscan_discounted_returns", _ptr(r), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(out),
-          E, T, float(gamma), _stream(dev, stream))
+    bv = _check_val(bootstrap_value, "bootstrap_value", (E,), dev, dt)
+    tb = _check_val(trunc_bootstrap, "trunc_bootstrap", shape, dev, dt)
+    out = _out(out, "out", shape, dev, dt)
+    _entry("rlscan_discounted_returns", dt, time_major, _ptr(r), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(out),
+           E, T, float(gamma), _stream(dev, stream))
     return out
 
 
 def td_lambda(rewards, values, terminated=None, truncated=None, bootstrap_value=None,
-              trunc_bootstrap=None, *, gamma=0.99, lam=0.95, out=None, stream=None):
+              trunc_bootstrap=None, *, time_major=False, gamma=0.99, lam=0.95, out=None, stream=None):
     """TD(lambda) returns (recursive lambda-return)."""
     shape, dev = _prep(rewards, "rewards")
-    E, T = shape
-    r = _check_f32(rewards, "rewards", shape, dev)
-    v = _check_f32(values, "values", shape, dev)
+    E, T = _dims(shape, time_major)
+    dt = _storage(rewards, "rewards")
+    r = _check_val(rewards, "rewards", shape, dev, dt)
+    v = _check_val(values, "values", shape, dev, dt)
     te = _check_flags(terminated, "terminated", shape, dev)
     tr = _check_flags(truncated, "truncated", shape, dev)
-    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
-    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
-    out = _out(out, "out", shape, dev)
-    _call("rlscan_td_lambda", _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(out),
-          E, T, float(gamma), float(lam), _stream(dev, stream))
+    bv = _check_val(bootstrap_value, "bootstrap_value", (E,), dev, dt)
+    tb = _check_val(trunc_bootstrap, "trunc_bootstrap", shape, dev, dt)
+    out = _out(out, "out", shape, dev, dt)
+    _entry("rlscan_td_lambda", dt, time_major, _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(out),
+           E, T, float(gamma), float(lam), _stream(dev, stream))
     return out
 
 
@@ -230,92 +280,97 @@ def returns_and_td_lambda(rewards, values, terminated=None, truncated=None, boot
 
 
 def gae(rewards, values, terminated=None, truncated=None, bootstrap_value=None,
-        trunc_bootstrap=None, *, gamma=0.99, lam=0.95, with_returns=False, advantages=None,
+        trunc_bootstrap=None, *, time_major=False, gamma=0.99, lam=0.95, with_returns=False, advantages=None,
         returns=None, stream=None):
     """Generalized advantage estimates; with_returns=True also returns A + V."""
     shape, dev = _prep(rewards, "rewards")
-    E, T = shape
-    r = _check_f32(rewards, "rewards", shape, dev)
-    v = _check_f32(values, "values", shape, dev)
+    E, T = _dims(shape, time_major)
+    dt = _storage(rewards, "rewards")
+    r = _check_val(rewards, "rewards", shape, dev, dt)
+    v = _check_val(values, "values", shape, dev, dt)
     te = _check_flags(terminated, "terminated", shape, dev)
     tr = _check_flags(truncated, "truncated", shape, dev)
-    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
-    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
-    adv = _out(advantages, "advantages", shape, dev)
-    ret = _out(returns, "returns", shape, dev) if (with_returns or returns is not None) else None
-    _call("rlscan_gae", _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(adv), _ptr(ret),
-          E, T, float(gamma), float(lam), _stream(dev, stream))
+    bv = _check_val(bootstrap_value, "bootstrap_value", (E,), dev, dt)
+    tb = _check_val(trunc_bootstrap, "trunc_bootstrap", shape, dev, dt)
+    adv = _out(advantages, "advantages", shape, dev, dt)
+    ret = _out(returns, "returns", shape, dev, dt) if (with_returns or returns is not None) else None
+    _entry("rlscan_gae", dt, time_major, _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb), _ptr(adv), _ptr(ret),
+           E, T, float(gamma), float(lam), _stream(dev, stream))
     return (adv, ret) if ret is not None else adv
 
 
 def vtrace(rewards, values, log_rhos, terminated=None, truncated=None, bootstrap_value=None,
-           trunc_bootstrap=None, *, gamma=0.99, lam=1.0, rho_bar=1.0, c_bar=1.0, with_pg=True,
+           trunc_bootstrap=None, *, time_major=False, gamma=0.99, lam=1.0, rho_bar=1.0, c_bar=1.0, with_pg=True,
            vs=None, pg_advantages=None, stream=None):
     """V-trace targets vs (and policy-gradient advantages when with_pg)."""
     shape, dev = _prep(rewards, "rewards")
-    E, T = shape
-    r = _check_f32(rewards, "rewards", shape, dev)
-    v = _check_f32(values, "values", shape, dev)
-    lr = _check_f32(log_rhos, "log_rhos", shape, dev)
+    E, T = _dims(shape, time_major)
+    dt = _storage(rewards, "rewards")
+    r = _check_val(rewards, "rewards", shape, dev, dt)
+    v = _check_val(values, "values", shape, dev, dt)
+    lr = _check_val(log_rhos, "log_rhos", shape, dev, dt)
     te = _check_flags(terminated, "terminated", shape, dev)
     tr = _check_flags(truncated, "truncated", shape, dev)
-    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
-    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
-    vs = _out(vs, "vs", shape, dev)
-    pg = _out(pg_advantages, "pg_advantages", shape, dev) if (with_pg or pg_advantages is not None) else None
-    _call("rlscan_vtrace", _ptr(r), _ptr(v), _ptr(lr), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb),
-          _ptr(vs), _ptr(pg), E, T, float(gamma), float(lam), float(rho_bar), float(c_bar),
-          _stream(dev, stream))
+    bv = _check_val(bootstrap_value, "bootstrap_value", (E,), dev, dt)
+    tb = _check_val(trunc_bootstrap, "trunc_bootstrap", shape, dev, dt)
+    vs = _out(vs, "vs", shape, dev, dt)
+    pg = _out(pg_advantages, "pg_advantages", shape, dev, dt) if (with_pg or pg_advantages is not None) else None
+    _entry("rlscan_vtrace", dt, time_major, _ptr(r), _ptr(v), _ptr(lr), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb),
+           _ptr(vs), _ptr(pg), E, T, float(gamma), float(lam), float(rho_bar), float(c_bar),
+           _stream(dev, stream))
     return (vs, pg) if pg is not None else vs
 
 
 def retrace(rewards, q_values, expected_q, pi_prob, mu_prob, terminated=None, truncated=None,
-            bootstrap_value=None, trunc_bootstrap=None, *, gamma=0.99, lam=0.95, out=None,
+            bootstrap_value=None, trunc_bootstrap=None, *, time_major=False, gamma=0.99, lam=0.95, out=None,
             stream=None):
     """Retrace(lambda) targets Q^ret."""
     shape, dev = _prep(rewards, "rewards")
-    E, T = shape
-    r = _check_f32(rewards, "rewards", shape, dev)
-    q = _check_f32(q_values, "q_values", shape, dev)
-    eq = _check_f32(expected_q, "expected_q", shape, dev)
-    pi = _check_f32(pi_prob, "pi_prob", shape, dev)
-    mu = _check_f32(mu_prob, "mu_prob", shape, dev)
+    E, T = _dims(shape, time_major)
+    dt = _storage(rewards, "rewards")
+    r = _check_val(rewards, "rewards", shape, dev, dt)
+    q = _check_val(q_values, "q_values", shape, dev, dt)
+    eq = _check_val(expected_q, "expected_q", shape, dev, dt)
+    pi = _check_val(pi_prob, "pi_prob", shape, dev, dt)
+    mu = _check_val(mu_prob, "mu_prob", shape, dev, dt)
     te = _check_flags(terminated, "terminated", shape, dev)
     tr = _check_flags(truncated, "truncated", shape, dev)
-    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
-    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
-    out = _out(out, "out", shape, dev)
-    _call("rlscan_retrace", _ptr(r), _ptr(q), _ptr(eq), _ptr(pi), _ptr(mu), _ptr(te), _ptr(tr),
-          _ptr(bv), _ptr(tb), _ptr(out), E, T, float(gamma), float(lam), _stream(dev, stream))
+    bv = _check_val(bootstrap_value, "bootstrap_value", (E,), dev, dt)
+    tb = _check_val(trunc_bootstrap, "trunc_bootstrap", shape, dev, dt)
+    out = _out(out, "out", shape, dev, dt)
+    _entry("rlscan_retrace", dt, time_major, _ptr(r), _ptr(q), _ptr(eq), _ptr(pi), _ptr(mu), _ptr(te), _ptr(tr),
+           _ptr(bv), _ptr(tb), _ptr(out), E, T, float(gamma), float(lam), _stream(dev, stream))
     return out
 
 
-def eligibility_traces(x, terminated=None, truncated=None, init=None, *, gamma=0.99, lam=0.95,
+def eligibility_traces(x, terminated=None, truncated=None, init=None, *, time_major=False, gamma=0.99, lam=0.95,
                        out=None, stream=None):
     """Accumulating eligibility traces of x, forward in time, reset after each episode end."""
     shape, dev = _prep(x, "x")
-    E, T = shape
-    xx = _check_f32(x, "x", shape, dev)
+    E, T = _dims(shape, time_major)
+    dt = _storage(x, "x")
+    xx = _check_val(x, "x", shape, dev, dt)
     te = _check_flags(terminated, "terminated", shape, dev)
     tr = _check_flags(truncated, "truncated", shape, dev)
-    i0 = _check_f32(init, "init", (E,), dev)
-    out = _out(out, "out", shape, dev)
-    _call("rlscan_eligibility_traces", _ptr(xx), _ptr(te), _ptr(tr), _ptr(i0), _ptr(out), E, T,
-          float(gamma), float(lam), _stream(dev, stream))
+    i0 = _check_val(init, "init", (E,), dev, dt)
+    out = _out(out, "out", shape, dev, dt)
+    _entry("rlscan_eligibility_traces", dt, time_major, _ptr(xx), _ptr(te), _ptr(tr), _ptr(i0), _ptr(out), E, T,
+           float(gamma), float(lam), _stream(dev, stream))
     return out
 
 
-def episodic_prefix_sum(x, terminated=None, truncated=None, init=None, *, out=None, stream=None):
+def episodic_prefix_sum(x, terminated=None, truncated=None, init=None, *, time_major=False, out=None, stream=None):
     """Inclusive prefix sums of x within each episode, forward in time."""
     shape, dev = _prep(x, "x")
-    E, T = shape
-    xx = _check_f32(x, "x", shape, dev)
+    E, T = _dims(shape, time_major)
+    dt = _storage(x, "x")
+    xx = _check_val(x, "x", shape, dev, dt)
     te = _check_flags(terminated, "terminated", shape, dev)
     tr = _check_flags(truncated, "truncated", shape, dev)
-    i0 = _check_f32(init, "init", (E,), dev)
-    out = _out(out, "out", shape, dev)
-    _call("rlscan_episodic_prefix_sum", _ptr(xx), _ptr(te), _ptr(tr), _ptr(i0), _ptr(out), E, T,
-          _stream(dev, stream))
+    i0 = _check_val(init, "init", (E,), dev, dt)
+    out = _out(out, "out", shape, dev, dt)
+    _entry("rlscan_episodic_prefix_sum", dt, time_major, _ptr(xx), _ptr(te), _ptr(tr), _ptr(i0), _ptr(out), E, T,
+           _stream(dev, stream))
     return out
 
 

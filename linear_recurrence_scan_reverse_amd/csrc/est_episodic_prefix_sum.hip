@@ -4,4 +4,9 @@
 
 namespace rlscan {
 template hipError_t launch<EpisodicPrefixSum>(const KernelArgs&, hipStream_t);
+template hipError_t launch_typed<EpisodicPrefixSum, Bf16S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_typed<EpisodicPrefixSum, F16S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_tm<EpisodicPrefixSum, F32S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_tm<EpisodicPrefixSum, Bf16S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_tm<EpisodicPrefixSum, F16S>(const KernelArgs&, hipStream_t);
 }  // namespace rlscan

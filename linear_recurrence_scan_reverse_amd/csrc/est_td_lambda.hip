@@ -4,4 +4,9 @@
 
 namespace rlscan {
 template hipError_t launch<TdLambda>(const KernelArgs&, hipStream_t);
+template hipError_t launch_typed<TdLambda, Bf16S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_typed<TdLambda, F16S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_tm<TdLambda, F32S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_tm<TdLambda, Bf16S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_tm<TdLambda, F16S>(const KernelArgs&, hipStream_t);
 }  // namespace rlscan

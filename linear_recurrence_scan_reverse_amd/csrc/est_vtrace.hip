@@ -4,4 +4,9 @@
 
 namespace rlscan {
 template hipError_t launch<Vtrace>(const KernelArgs&, hipStream_t);
+template hipError_t launch_typed<Vtrace, Bf16S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_typed<Vtrace, F16S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_tm<Vtrace, F32S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_tm<Vtrace, Bf16S>(const KernelArgs&, hipStream_t);
+template hipError_t launch_tm<Vtrace, F16S>(const KernelArgs&, hipStream_t);
 }  // namespace rlscan

@@ -310,6 +310,100 @@ __device__ __forceinline__ void store_chunk(float* __restrict__ base, uint32_t o
   }
 }
 
+// ----------------------------------------------------------------- storage formats
+// Values live in HBM as fp32 (the default) or as 16-bit bf16 / fp16; they are
+// widened on load and the fp64 results rounded once to fp32, then (16-bit
+// formats) to the storage format, round to nearest even.  Kernel arguments keep
+// `const float*` fields; for 16-bit formats they address 16-bit elements.
+struct F32S {
+  using T = float;
+};
+struct Bf16S {
+  using T = uint16_t;
+};
+struct F16S {
+  using T = uint16_t;
+};
+
+template <class S>
+__device__ __forceinline__ float s_to_f32(typename S::T v) {
+  if constexpr (__is_same(S, F32S)) return v;
+  else if constexpr (__is_same(S, Bf16S)) return __builtin_bit_cast(float, (uint32_t)v << 16);
+  else return (float)__builtin_bit_cast(_Float16, v);
+}
+template <class S>
+__device__ __forceinline__ typename S::T f32_to_s(float v) {
+  // round to nearest even (v_cvt_pk_bf16_f32 / v_cvt_f16_f32).  The empty asm
+  // keeps v a float32: without it the compiler folds the earlier fp64 -> fp32
+  // rounding and this one into a single fp64 -> fp16 rounding (a long
+  // software sequence, and not the documented two roundings).
+  if constexpr (__is_same(S, F32S)) {
+    return v;
+  } else {
+    __asm__("" : "+v"(v));
+    if constexpr (__is_same(S, Bf16S)) return __builtin_bit_cast(uint16_t, (__bf16)v);
+    else return __builtin_bit_cast(uint16_t, (_Float16)v);
+  }
+}
+
+// One element: base[bidx + off], widened.
+template <class S>
+__device__ __forceinline__ float load1(const float* base, int64_t bidx, uint32_t off) {
+  if constexpr (__is_same(S, F32S)) return __builtin_nontemporal_load(at(base + bidx, off));
+  else return s_to_f32<S>(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base) + bidx + off));
+}
+
+// K consecutive elements at base[bidx + off] (same contract as load_chunk).
+template <class S, int K, bool VEC>
+__device__ __forceinline__ void load_s(const float* base, int64_t bidx, uint32_t off, uint32_t last,
+                                       float (&o)[K]) {
+  if constexpr (__is_same(S, F32S)) {
+    load_chunk<K, VEC>(base + bidx, off, last, o);
+  } else {
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(base) + bidx;
+    if constexpr (VEC && K == 4) {
+      // integer loads: a float-vector load of these bits was narrowed to one
+      // dword by the compiler
+      const unsigned long long q = __builtin_nontemporal_load(reinterpret_cast<const unsigned long long*>(b + off));
+      const uint32_t w0 = (uint32_t)q, w1 = (uint32_t)(q >> 32);
+      o[0] = s_to_f32<S>((uint16_t)w0); o[1] = s_to_f32<S>((uint16_t)(w0 >> 16));
+      o[2] = s_to_f32<S>((uint16_t)w1); o[3] = s_to_f32<S>((uint16_t)(w1 >> 16));
+    } else if constexpr (VEC && K == 2) {
+      const uint32_t w0 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(b + off));
+      o[0] = s_to_f32<S>((uint16_t)w0); o[1] = s_to_f32<S>((uint16_t)(w0 >> 16));
+    } else {
+#pragma unroll
+      for (int m = 0; m < K; ++m) {
+        const uint32_t c = off + m < last ? off + m : last;
+        o[m] = s_to_f32<S>(__builtin_nontemporal_load(b + c));
+      }
+    }
+  }
+}
+
+// K consecutive outputs at base[bidx + off] (same contract as store_chunk).
+template <class S, int K, bool VEC>
+__device__ __forceinline__ void store_s(float* base, int64_t bidx, uint32_t off, int nv, const float (&o)[K]) {
+  if constexpr (__is_same(S, F32S)) {
+    store_chunk<K, VEC>(base + bidx, off, nv, o);
+  } else {
+    uint16_t* b = reinterpret_cast<uint16_t*>(base) + bidx;
+    if constexpr (VEC && K == 4) {
+      const uint32_t w0 = (uint32_t)f32_to_s<S>(o[0]) | ((uint32_t)f32_to_s<S>(o[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_s<S>(o[2]) | ((uint32_t)f32_to_s<S>(o[3]) << 16);
+      __builtin_nontemporal_store((unsigned long long)w0 | ((unsigned long long)w1 << 32),
+                                  reinterpret_cast<unsigned long long*>(b + off));
+    } else if constexpr (VEC && K == 2) {
+      const uint32_t w0 = (uint32_t)f32_to_s<S>(o[0]) | ((uint32_t)f32_to_s<S>(o[1]) << 16);
+      __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t*>(b + off));
+    } else {
+#pragma unroll
+      for (int m = 0; m < K; ++m)
+        if (m < nv) __builtin_nontemporal_store(f32_to_s<S>(o[m]), b + off + m);
+    }
+  }
+}
+
 // A value every lane of the wave holds, moved to a scalar register.
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
@@ -560,7 +654,7 @@ template <class Est, int K> struct RowData : LaneIn<Est, K> {
 // tile is whole; otherwise every element is loaded at a clamped column), OPT
 // (bit 0: a flag array is present; bit 1: the second output is written).
 // The C ABI guarantees T < 2^30, so every in-row byte offset fits 32 bits.
-template <class Est, int L, int K, int W, int R, bool VEC, int OPT>
+template <class Est, int L, int K, int W, int R, bool VEC, int OPT, class S = F32S>
 __global__ void __launch_bounds__(BlockShape<W>::kThreads)
 scan_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
@@ -690,39 +784,38 @@ scan_kernel(const KernelArgs p) {
       RowData<Est, K>& d = dd[rr];
       const uint32_t off = ir.roff[rr] + q.cs;
       const uint32_t last = ir.roff[rr] + T32 - 1;
-      load_chunk<K, VEC>(p.r + eb, off, last, d.s[0]);
-      if constexpr (NS >= 2) load_chunk<K, VEC>(p.v + eb, off, last, d.s[1]);
-      if constexpr (NS >= 3) load_chunk<K, VEC>(p.aux + eb, off, last, d.s[2]);
+      load_s<S, K, VEC>(p.r, eb, off, last, d.s[0]);
+      if constexpr (NS >= 2) load_s<S, K, VEC>(p.v, eb, off, last, d.s[1]);
+      if constexpr (NS >= 3) load_s<S, K, VEC>(p.aux, eb, off, last, d.s[2]);
       if constexpr (NS >= 5) {
-        load_chunk<K, VEC>(p.pi + eb, off, last, d.s[3]);
-        load_chunk<K, VEC>(p.mu + eb, off, last, d.s[4]);
+        load_s<S, K, VEC>(p.pi, eb, off, last, d.s[3]);
+        load_s<S, K, VEC>(p.mu, eb, off, last, d.s[4]);
       }
       // the team-first lane's scan predecessor: one address per team part (one request)
       const uint32_t noff = ir.roff[rr] + q.tn;
       if constexpr (Tr::kRetrace) {
-        d.nb[0] = __builtin_nontemporal_load(at(p.aux + eb, noff));
-        d.nb[1] = __builtin_nontemporal_load(at(p.pi + eb, noff));
-        d.nb[2] = __builtin_nontemporal_load(at(p.mu + eb, noff));
+        d.nb[0] = load1<S>(p.aux, eb, noff);
+        d.nb[1] = load1<S>(p.pi, eb, noff);
+        d.nb[2] = load1<S>(p.mu, eb, noff);
       } else if constexpr (Tr::kNbValue) {
-        d.nb[0] = __builtin_nontemporal_load(at(p.v + eb, noff));
+        d.nb[0] = load1<S>(p.v, eb, noff);
       } else if constexpr (Tr::kNbDone && USE_FLAGS) {
         d.nbf[0] = __builtin_nontemporal_load(at(p.term + eb, noff));
         d.nbf[1] = __builtin_nontemporal_load(at(p.trunc + eb, noff));
       }
-      d.rowv = *at(p.row + ir.wb, ir.rsel[rr]);
+      d.rowv = load1<S>(p.row, ir.wb, ir.rsel[rr]);
       // Truncation bootstraps of this lane's chunk; lanes without a truncated
       // step read the array's first chunk instead (one line shared by all waves).
       if constexpr (GATHER_TB) {
         const unsigned need = rbits[rr] & ~tbits[rr];
-        const float* tbase = p.tboot + eb;
         if constexpr (VEC) {
-          const float* src = need ? at(tbase, off) : p.tboot;
-          load_chunk<K, true>(src, 0, 0, d.tb);
+          load_s<S, K, true>(p.tboot, need ? eb : 0, need ? off : 0u, 0u, d.tb);
         } else {
 #pragma unroll
           for (int m = 0; m < K; ++m) {
             const uint32_t col = off + m < last ? off + m : last;
-            d.tb[m] = __builtin_nontemporal_load(((need >> m) & 1u) ? at(tbase, col) : p.tboot);
+            const bool sel = (need >> m) & 1u;
+            d.tb[m] = load1<S>(p.tboot, sel ? eb : 0, sel ? col : 0u);
           }
         }
       }
@@ -803,8 +896,8 @@ scan_kernel(const KernelArgs p) {
       const int nv = ir.ok[rr] ? q.nv : 0;
       if (nv > 0) {
         const uint32_t off = ir.roff[rr] + q.cs;
-        store_chunk<K, VEC>(p.out0 + eb, off, nv, o0[rr]);
-        if constexpr (OUT1) store_chunk<K, VEC>(p.out1 + eb, off, nv, o1[rr]);
+        store_s<S, K, VEC>(p.out0, eb, off, nv, o0[rr]);
+        if constexpr (OUT1) store_s<S, K, VEC>(p.out1, eb, off, nv, o1[rr]);
       }
     }
   };

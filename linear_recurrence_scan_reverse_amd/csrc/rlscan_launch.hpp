@@ -6,6 +6,7 @@
 #include "rlscan_kernel.hpp"
 #include "rlscan_segment.hpp"
 #include "rlscan_stream.hpp"
+#include "rlscan_timemajor.hpp"
 
 namespace rlscan {
 
@@ -33,23 +34,16 @@ inline LaunchShape pick_shape(int64_t T) {
 template <class Est>
 inline int blocks_per_cu(const LaunchShape&) { return __is_same(Est, DiscountedReturn) ? 8 : 4; }
 
-// Rows a team scans side by side per item.  A lane must keep enough bytes in
-// flight to cover HBM latency (Little's law at ~5.5 TB/s over 256 CUs asks
-// for ~64 KiB in flight per CU), so estimators that move few bytes per step
-// take more rows per item.
+// Rows a team scans per work item: one on this path (the kernel keeps the
+// count as a template parameter, R).
 template <class Est, int K>
-constexpr int rows_per_item() {
-  using Tr = Traits<Est>;
-  constexpr int per_step = 4 * Tr::kStreams + (Tr::kUsesFlags ? 2 : 0) + 4 * (Tr::kHasOut1 ? 2 : 1);
-  constexpr int bytes = per_step * K;
-  return bytes < 0 ? 2 : 1;  // one row per item on this path
-}
+constexpr int rows_per_item() { return 1; }
 
 // The vector path needs whole tiles (T % span == 0) and every dense array base
 // aligned to its K-element chunk.
-inline bool vector_ok(const KernelArgs& a, int K, int span) {
+inline bool vector_ok(const KernelArgs& a, int K, int span, int esize = 4) {
   if (a.T % span != 0) return false;
-  const uintptr_t fa = (uintptr_t)(4 * K), ba = (uintptr_t)K;
+  const uintptr_t fa = (uintptr_t)(esize * K), ba = (uintptr_t)K;
   const float* fl[] = {a.r, a.v, a.aux, a.pi, a.mu, a.tboot, a.out0, a.out1};
   for (const float* q : fl)
     if (q && ((uintptr_t)q % fa) != 0) return false;
@@ -80,7 +74,7 @@ inline int cu_count() {
   return n;
 }
 
-template <class Est, int L, int K, int W, bool VEC, int OPT>
+template <class Est, int L, int K, int W, bool VEC, int OPT, class S = F32S>
 inline hipError_t launch_one(const KernelArgs& a, hipStream_t s, const LaunchShape& sh) {
   constexpr int BLOCK = BlockShape<W>::kThreads;
   constexpr int TEAMS = BLOCK / ((W > 1) ? 64 * W : L);
@@ -91,30 +85,30 @@ inline hipError_t launch_one(const KernelArgs& a, hipStream_t s, const LaunchSha
   if (blocks > resident) blocks = resident;
   KernelArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_kernel<Est, L, K, W, R, VEC, OPT>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_kernel<Est, L, K, W, R, VEC, OPT, S>),
                          dim3((unsigned)blocks), dim3(BLOCK), params, 0, s);
 }
 
-template <class Est, int L, int K, int W, int OPT>
+template <class Est, int L, int K, int W, int OPT, class S = F32S>
 inline hipError_t launch_vec(const KernelArgs& a, hipStream_t s, const LaunchShape& sh) {
   constexpr int SPAN = ((W > 1) ? 64 * W : L) * K;
-  return vector_ok(a, K, SPAN) ? launch_one<Est, L, K, W, true, OPT>(a, s, sh)
-                         : launch_one<Est, L, K, W, false, OPT>(a, s, sh);
+  return vector_ok(a, K, SPAN, (int)sizeof(typename S::T)) ? launch_one<Est, L, K, W, true, OPT, S>(a, s, sh)
+                                                           : launch_one<Est, L, K, W, false, OPT, S>(a, s, sh);
 }
 
 // OPT bit 0: a flag array is present; bit 1: the second output is written.
-template <class Est, int L, int K, int W>
+template <class Est, int L, int K, int W, class S = F32S>
 inline hipError_t launch_shape(const KernelArgs& a, hipStream_t s, const LaunchShape& sh) {
   using Tr = Traits<Est>;
   const bool flags = a.has_term || a.has_trunc;
   if constexpr (Tr::kHasOut1) {
     const bool out1 = a.out1 != nullptr;
-    if (flags) return out1 ? launch_vec<Est, L, K, W, 3>(a, s, sh) : launch_vec<Est, L, K, W, 1>(a, s, sh);
-    return out1 ? launch_vec<Est, L, K, W, 2>(a, s, sh) : launch_vec<Est, L, K, W, 0>(a, s, sh);
+    if (flags) return out1 ? launch_vec<Est, L, K, W, 3, S>(a, s, sh) : launch_vec<Est, L, K, W, 1, S>(a, s, sh);
+    return out1 ? launch_vec<Est, L, K, W, 2, S>(a, s, sh) : launch_vec<Est, L, K, W, 0, S>(a, s, sh);
   } else if constexpr (Tr::kUsesFlags) {
-    return flags ? launch_vec<Est, L, K, W, 1>(a, s, sh) : launch_vec<Est, L, K, W, 0>(a, s, sh);
+    return flags ? launch_vec<Est, L, K, W, 1, S>(a, s, sh) : launch_vec<Est, L, K, W, 0, S>(a, s, sh);
   } else {
-    return launch_vec<Est, L, K, W, 0>(a, s, sh);
+    return launch_vec<Est, L, K, W, 0, S>(a, s, sh);
   }
 }
 
@@ -214,39 +208,40 @@ inline int64_t segment_length(const KernelArgs& a) {
   return len < a.T ? len : 0;
 }
 
-template <class Est, int OPT>
+template <class Est, int OPT, class S = F32S>
 inline hipError_t launch_segmented_opt(const KernelArgs& a, hipStream_t s, int64_t len) {
   int64_t seg_len = len;
   int64_t nseg = (a.T + len - 1) / len;
   KernelArgs arg = a;
   void* params[] = {&arg, &seg_len, &nseg};
-  const bool vec = vector_ok(a, 4, kSegTile);
+  const bool vec = vector_ok(a, 4, kSegTile, (int)sizeof(typename S::T));
   const dim3 block(256);
   const dim3 grid_seg((unsigned)((a.E * nseg + 3) / 4));
   const dim3 grid_row((unsigned)((a.E + 3) / 4));
-  const void* agg = vec ? reinterpret_cast<const void*>(&seg_kernel<Est, true, true, OPT>)
-                        : reinterpret_cast<const void*>(&seg_kernel<Est, true, false, OPT>);
-  const void* apply = vec ? reinterpret_cast<const void*>(&seg_kernel<Est, false, true, OPT>)
-                          : reinterpret_cast<const void*>(&seg_kernel<Est, false, false, OPT>);
+  const void* agg = vec ? reinterpret_cast<const void*>(&seg_kernel<Est, true, true, OPT, S>)
+                        : reinterpret_cast<const void*>(&seg_kernel<Est, true, false, OPT, S>);
+  const void* apply = vec ? reinterpret_cast<const void*>(&seg_kernel<Est, false, true, OPT, S>)
+                          : reinterpret_cast<const void*>(&seg_kernel<Est, false, false, OPT, S>);
   hipError_t e = hipLaunchKernel(agg, grid_seg, block, params, 0, s);
   if (e != hipSuccess) return e;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&seg_carry_kernel<Est>), grid_row, block, params, 0, s);
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&seg_carry_kernel<Est, S>), grid_row, block, params, 0, s);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(apply, grid_seg, block, params, 0, s);
 }
 
-template <class Est>
+template <class Est, class S = F32S>
 inline hipError_t launch_segmented(const KernelArgs& a, hipStream_t s, int64_t len) {
   using Tr = Traits<Est>;
   const bool flags = a.has_term || a.has_trunc;
   if constexpr (Tr::kHasOut1) {
     const bool out1 = a.out1 != nullptr;
-    if (flags) return out1 ? launch_segmented_opt<Est, 3>(a, s, len) : launch_segmented_opt<Est, 1>(a, s, len);
-    return out1 ? launch_segmented_opt<Est, 2>(a, s, len) : launch_segmented_opt<Est, 0>(a, s, len);
+    if (flags)
+      return out1 ? launch_segmented_opt<Est, 3, S>(a, s, len) : launch_segmented_opt<Est, 1, S>(a, s, len);
+    return out1 ? launch_segmented_opt<Est, 2, S>(a, s, len) : launch_segmented_opt<Est, 0, S>(a, s, len);
   } else if constexpr (Tr::kUsesFlags) {
-    return flags ? launch_segmented_opt<Est, 1>(a, s, len) : launch_segmented_opt<Est, 0>(a, s, len);
+    return flags ? launch_segmented_opt<Est, 1, S>(a, s, len) : launch_segmented_opt<Est, 0, S>(a, s, len);
   } else {
-    return launch_segmented_opt<Est, 0>(a, s, len);
+    return launch_segmented_opt<Est, 0, S>(a, s, len);
   }
 }
 
@@ -274,6 +269,60 @@ hipError_t launch(const KernelArgs& in, hipStream_t s) {
   }
 }
 
+// Values stored as 16-bit bf16 / fp16 (S = Bf16S, F16S): the pipelined kernel,
+// or the segmented path for long rows (the streaming kernel moves fp32 only).
+template <class Est, class S>
+hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
+  const KernelArgs a = resolve_optional(in);
+  if (const int64_t len = segment_length(a)) return launch_segmented<Est, S>(a, s, len);
+  const LaunchShape sh = pick_shape(a.T);
+  switch (sh.W * 1000 + sh.L * 10 + sh.K) {
+    case 1000 + 160 + 1: return launch_shape<Est, 16, 1, 1, S>(a, s, sh);
+    case 1000 + 160 + 2: return launch_shape<Est, 16, 2, 1, S>(a, s, sh);
+    case 1000 + 160 + 4: return launch_shape<Est, 16, 4, 1, S>(a, s, sh);
+    case 1000 + 320 + 4: return launch_shape<Est, 32, 4, 1, S>(a, s, sh);
+    case 1000 + 640 + 4: return launch_shape<Est, 64, 4, 1, S>(a, s, sh);
+    case 2000 + 640 + 4: return launch_shape<Est, 64, 4, 2, S>(a, s, sh);
+    case 4000 + 640 + 4: return launch_shape<Est, 64, 4, 4, S>(a, s, sh);
+    default: return hipErrorInvalidConfiguration;
+  }
+}
+
+// ----------------------------------------------------------------- time-major path
+// [T, E] arrays: one block of W waves per 64 environments, K steps per wave
+// chunk.  Blocks of 16 waves keep 16 waves per CU at 16384 environments;
+// the estimators with one input stream take 16-step chunks, the others 8
+// (fewer live registers per lane).
+template <class Est>
+constexpr int tm_waves() { return 16; }
+template <class Est>
+constexpr int tm_chunk() { return Traits<Est>::kStreams >= 2 ? 8 : 16; }
+
+template <class Est, int OPT, class S>
+inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
+  constexpr int W = tm_waves<Est>(), K = tm_chunk<Est>();
+  const int64_t blocks = (a.E + 63) / 64;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  KernelArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&tm_kernel<Est, W, K, OPT, S>), dim3((unsigned)blocks),
+                         dim3(64 * W), params, 0, s);
+}
+
+template <class Est, class S = F32S>
+hipError_t launch_tm(const KernelArgs& in, hipStream_t s) {
+  using Tr = Traits<Est>;
+  const KernelArgs a = resolve_optional(in);
+  const bool flags = a.has_term || a.has_trunc;
+  if constexpr (Tr::kHasOut1) {
+    const bool out1 = a.out1 != nullptr;
+    if (flags) return out1 ? launch_tm_opt<Est, 3, S>(a, s) : launch_tm_opt<Est, 1, S>(a, s);
+    return out1 ? launch_tm_opt<Est, 2, S>(a, s) : launch_tm_opt<Est, 0, S>(a, s);
+  } else {
+    return flags ? launch_tm_opt<Est, 1, S>(a, s) : launch_tm_opt<Est, 0, S>(a, s);
+  }
+}
+
 // Discounted returns (out0) and TD(lambda) returns (out1) of one rollout: one
 // streaming pass where the rows allow it, else the two single-output kernels.
 hipError_t launch_returns_td_lambda(const KernelArgs& in, hipStream_t s);
@@ -293,5 +342,19 @@ extern template hipError_t launch<EligibilityTrace>(const KernelArgs&, hipStream
 extern template hipError_t launch<EpisodicPrefixSum>(const KernelArgs&, hipStream_t);
 extern template hipError_t launch<LinearScanReverse>(const KernelArgs&, hipStream_t);
 extern template hipError_t launch<LinearScanForward>(const KernelArgs&, hipStream_t);
+#define RLSCAN_TYPED_EXTERN(EST)                                                       \
+  extern template hipError_t launch_typed<EST, Bf16S>(const KernelArgs&, hipStream_t); \
+  extern template hipError_t launch_typed<EST, F16S>(const KernelArgs&, hipStream_t);  \
+  extern template hipError_t launch_tm<EST, F32S>(const KernelArgs&, hipStream_t);     \
+  extern template hipError_t launch_tm<EST, Bf16S>(const KernelArgs&, hipStream_t);    \
+  extern template hipError_t launch_tm<EST, F16S>(const KernelArgs&, hipStream_t);
+RLSCAN_TYPED_EXTERN(DiscountedReturn)
+RLSCAN_TYPED_EXTERN(TdLambda)
+RLSCAN_TYPED_EXTERN(Gae)
+RLSCAN_TYPED_EXTERN(Vtrace)
+RLSCAN_TYPED_EXTERN(Retrace)
+RLSCAN_TYPED_EXTERN(EligibilityTrace)
+RLSCAN_TYPED_EXTERN(EpisodicPrefixSum)
+#undef RLSCAN_TYPED_EXTERN
 
 }  // namespace rlscan

@@ -16,8 +16,8 @@
 //   3. apply: one wave per (row, segment) rescans the segment from that value
 //      and writes the outputs.
 // Inputs are read twice, outputs written once.  Between the passes, the
-// segment's (A, B) and then its entering value live in the first four floats
-// of the segment's own range of the first output, which pass 3 overwrites;
+// segment's (A, B) and then its entering value live in the first 16 bytes of
+// the segment's own range of the first output, which pass 3 overwrites;
 // nothing else is allocated.
 #pragma once
 
@@ -27,22 +27,41 @@ namespace rlscan {
 
 constexpr int kSegTile = 256;  // steps per tile (64 lanes x 4)
 
-// A double kept in two consecutive floats of an output range (bit copies).
-__device__ __forceinline__ void put_f64(float* p, double v) {
+// A double kept in the first 8 bytes at element `idx` of an output array in
+// storage format S (bit copies, element-aligned stores).
+template <class S>
+__device__ __forceinline__ void put_f64(float* base, int64_t idx, double v) {
   const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
-  p[0] = __builtin_bit_cast(float, (unsigned)u);
-  p[1] = __builtin_bit_cast(float, (unsigned)(u >> 32));
+  if constexpr (__is_same(S, F32S)) {
+    base[idx] = __builtin_bit_cast(float, (unsigned)u);
+    base[idx + 1] = __builtin_bit_cast(float, (unsigned)(u >> 32));
+  } else {
+    uint16_t* b = reinterpret_cast<uint16_t*>(base) + idx;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (uint16_t)(u >> (16 * i));
+  }
 }
-__device__ __forceinline__ double get_f64(const float* p) {
-  const unsigned lo = __builtin_bit_cast(unsigned, p[0]);
-  const unsigned hi = __builtin_bit_cast(unsigned, p[1]);
-  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+template <class S>
+__device__ __forceinline__ double get_f64(const float* base, int64_t idx) {
+  unsigned long long u = 0;
+  if constexpr (__is_same(S, F32S)) {
+    u = (unsigned long long)__builtin_bit_cast(unsigned, base[idx]) |
+        ((unsigned long long)__builtin_bit_cast(unsigned, base[idx + 1]) << 32);
+  } else {
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(base) + idx;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u |= (unsigned long long)b[i] << (16 * i);
+  }
+  return __builtin_bit_cast(double, u);
 }
+// elements of format S that hold one double
+template <class S>
+constexpr int f64_elems() { return __is_same(S, F32S) ? 2 : 4; }
 
 // Passes 1 (AGG) and 3 (apply).  One wave per (row, segment); segments are
 // seg_len steps (a multiple of 256) and the last one of a row may be shorter.
 // VEC: T % 256 == 0 and every array 16-byte aligned.
-template <class Est, bool AGG, bool VEC, int OPT>
+template <class Est, bool AGG, bool VEC, int OPT, class S = F32S>
 __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t seg_len, int64_t nseg) {
   using Tr = Traits<Est>;
   constexpr int K = 4;
@@ -70,12 +89,12 @@ __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t se
                        p.has_tboot != 0};
   const unsigned tmask = p.has_term ? ~0u : 0u;
   const unsigned rmask = p.has_trunc ? ~0u : 0u;
-  const float rowv = p.has_row ? p.row[row] : 0.0f;
-  float* slot = p.out0 + rb + t_begin;  // the segment's first four output floats
+  const float rowv = p.has_row ? load1<S>(p.row, row, 0u) : 0.0f;
+  const int64_t slot = rb + t_begin;  // element index of the segment's first output
 
   double C = 0.0;          // apply: value entering the current tile
   double A = 1.0, B = 0.0;  // aggregate: map of the tiles done so far
-  if constexpr (!AGG) C = get_f64(slot);
+  if constexpr (!AGG) C = get_f64<S>(p.out0, slot);
 
   for (int64_t i = 0; i < ntl; ++i) {
     const int64_t tile_start = REV ? t_begin + (ntl - 1 - i) * kSegTile : t_begin + i * kSegTile;
@@ -85,12 +104,12 @@ __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t se
     const int nv = rem <= 0 ? 0 : (rem >= K ? K : (int)rem);
 
     LaneIn<Est, K> d;
-    load_chunk<K, VEC>(p.r + rb, cs, last, d.s[0]);
-    if constexpr (NS >= 2) load_chunk<K, VEC>(p.v + rb, cs, last, d.s[1]);
-    if constexpr (NS >= 3) load_chunk<K, VEC>(p.aux + rb, cs, last, d.s[2]);
+    load_s<S, K, VEC>(p.r, rb, cs, last, d.s[0]);
+    if constexpr (NS >= 2) load_s<S, K, VEC>(p.v, rb, cs, last, d.s[1]);
+    if constexpr (NS >= 3) load_s<S, K, VEC>(p.aux, rb, cs, last, d.s[2]);
     if constexpr (NS >= 5) {
-      load_chunk<K, VEC>(p.pi + rb, cs, last, d.s[3]);
-      load_chunk<K, VEC>(p.mu + rb, cs, last, d.s[4]);
+      load_s<S, K, VEC>(p.pi, rb, cs, last, d.s[3]);
+      load_s<S, K, VEC>(p.mu, rb, cs, last, d.s[4]);
     }
     unsigned tbits = 0, rbits = 0;
     if constexpr (USE_FLAGS) {
@@ -108,7 +127,7 @@ __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t se
       for (int m = 0; m < K; ++m) {
         if ((need >> m) & 1u) {
           const uint32_t c = cs + m < last ? cs + m : last;
-          d.tb[m] = *at(p.tboot + rb, c);
+          d.tb[m] = load1<S>(p.tboot, rb, c);
         }
       }
     }
@@ -121,11 +140,11 @@ __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t se
     if (tn >= 0 && tn < T) {
       const uint32_t n = (uint32_t)tn;
       if constexpr (Tr::kRetrace) {
-        pred.v = *at(p.aux + rb, n);
-        const double ratio = (double)*at(p.pi + rb, n) / (double)*at(p.mu + rb, n);
+        pred.v = load1<S>(p.aux, rb, n);
+        const double ratio = (double)load1<S>(p.pi, rb, n) / (double)load1<S>(p.mu, rb, n);
         pred.c = lam * (ratio < 1.0 ? ratio : 1.0);
       } else if constexpr (Tr::kNbValue) {
-        pred.v = *at(p.v + rb, n);
+        pred.v = load1<S>(p.v, rb, n);
       } else if constexpr (Tr::kNbDone && USE_FLAGS) {
         const unsigned dn = ((unsigned)(*at(p.term + rb, n) != 0) & tmask) |
                             ((unsigned)(*at(p.trunc + rb, n) != 0) & rmask);
@@ -149,15 +168,15 @@ __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t se
       rewalk<K>(lp.e, x_in, xs);
       float o0[K], o1[K];
       epilogue<Est, K>(d, lp, sc, x_in, xs, o0, o1);
-      store_chunk<K, VEC>(p.out0 + rb, cs, nv, o0);
-      if constexpr (OUT1) store_chunk<K, VEC>(p.out1 + rb, cs, nv, o1);
+      store_s<S, K, VEC>(p.out0, rb, cs, nv, o0);
+      if constexpr (OUT1) store_s<S, K, VEC>(p.out1, rb, cs, nv, o1);
       C = C_next;
     }
   }
   if constexpr (AGG) {
     if (first_lane) {
-      put_f64(slot, A);
-      put_f64(slot + 2, B);
+      put_f64<S>(p.out0, slot, A);
+      put_f64<S>(p.out0, slot + f64_elems<S>(), B);
     }
   }
 }
@@ -166,7 +185,7 @@ __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t se
 // and replaces each segment's (A, B) by the value entering it.  The value
 // entering the row is 0 for the backward estimators (their bootstraps sit in
 // the pairs) and the row's init / carry otherwise.
-template <class Est>
+template <class Est, class S = F32S>
 __global__ void __launch_bounds__(256) seg_carry_kernel(const KernelArgs p, int64_t seg_len, int64_t nseg) {
   using Tr = Traits<Est>;
   constexpr bool REV = Est::kReverse;
@@ -174,23 +193,23 @@ __global__ void __launch_bounds__(256) seg_carry_kernel(const KernelArgs p, int6
   const int64_t row = uniform64((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6));
   if (row >= p.E) return;  // (wave-uniform)
   double c = 0.0;
-  if constexpr (!Tr::kBackwardRl) c = p.has_row ? (double)p.row[row] : 0.0;
-  float* base = p.out0 + row * p.T;
+  if constexpr (!Tr::kBackwardRl) c = p.has_row ? (double)load1<S>(p.row, row, 0u) : 0.0;
+  const int64_t base = row * p.T;
   for (int64_t k0 = 0; k0 < nseg; k0 += 64) {
     const int64_t k = k0 + lane;  // position in scan order
     const bool ok = k < nseg;
     const int64_t s = REV ? nseg - 1 - k : k;
-    float* slot = base + (ok ? s : 0) * seg_len;
+    const int64_t slot = base + (ok ? s : 0) * seg_len;
     AB f{1.0, 0.0};
     if (ok) {
-      f.a = get_f64(slot);
-      f.b = get_f64(slot + 2);
+      f.a = get_f64<S>(p.out0, slot);
+      f.b = get_f64<S>(p.out0, slot + f64_elems<S>());
     }
     const AB incl = lane_scan<64>(f);
     const double y = __builtin_fma(incl.a, c, incl.b);  // value leaving segment k
     const double from_below = shift_up_f64(y);
     const double cin = lane == 0 ? c : from_below;
-    if (ok) put_f64(slot, cin);
+    if (ok) put_f64<S>(p.out0, slot, cin);
     c = group_last_f64<64>(y, lane);
   }
 }

@@ -1,0 +1,157 @@
+// rlscan_timemajor.hpp -- the estimators over time-major [T, E] arrays.
+//
+// Element (t, e) sits at t*E + e: one time step of every environment is
+// contiguous, the order of rollout buffers that append one step for all
+// environments at a time.  The recurrence and its pairs are those of the
+// row-major kernels (gist.science summary of rl-triton, "Methodologie"
+// sections 1 and 3); only the mapping to the machine changes.  The rl-triton
+// skill page (skillsdirectory.com, "Implementation Workflow", step 2) lists
+// the choice between contiguous and strided memory layouts among a kernel's
+// settings; this is the strided one.
+//
+// Lanes map to environments: lane l of a block owns column e0 + l, so every
+// load and store of one step is one coalesced run of 64 consecutive values.
+// Time is cut into super-tiles of W x K steps; wave w owns the w-th chunk of
+// K steps in scan order.  Each lane builds its K pairs with the per-lane code
+// of the row-major kernels (a lane is its own team, and the scan predecessor
+// of its chunk is loaded from memory), folds them into one affine map, and
+// the W maps of a column meet in LDS: wave w composes the maps of the waves
+// before it with the value entering the super-tile, rewalks its chunk from
+// there and stores.  The composed map of all W chunks carries the column into
+// the next super-tile.  Every input is read once (plus one predecessor step
+// per chunk, which the neighbouring wave reads too) and every output written
+// once; arithmetic is fp64 as everywhere else.
+#pragma once
+
+#include "rlscan_kernel.hpp"
+
+namespace rlscan {
+
+// One element of format S at index idx, narrowed from fp32 (non-temporal).
+template <class S>
+__device__ __forceinline__ void store1(float* base, int64_t idx, float v) {
+  if constexpr (__is_same(S, F32S)) __builtin_nontemporal_store(v, base + idx);
+  else __builtin_nontemporal_store(f32_to_s<S>(v), reinterpret_cast<uint16_t*>(base) + idx);
+}
+
+// W waves per block, K steps per wave chunk.  OPT as for scan_kernel.
+template <class Est, int W, int K, int OPT, class S = F32S>
+__global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p) {
+  using Tr = Traits<Est>;
+  constexpr bool REV = Est::kReverse;
+  constexpr int NS = Tr::kStreams;
+  constexpr bool USE_FLAGS = (OPT & 1) && Tr::kUsesFlags;
+  constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
+  constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
+  constexpr int64_t SPAN = (int64_t)W * K;
+  static_assert(!Tr::kDual, "one recurrence per pass");
+
+  __shared__ double s_a[W][64];
+  __shared__ double s_b[W][64];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;  // chunk position in scan order inside a super-tile
+  const int64_t E = p.E, T = p.T;
+  const int64_t e = (int64_t)blockIdx.x * 64 + lane;
+  const bool col_ok = e < E;
+  const int64_t ec = col_ok ? e : E - 1;  // clamped column: every load stays inside the arrays
+
+  const double gamma = p.gamma, lam = p.lam;
+  const ScanScalars sc{gamma, lam, gamma * lam, (float)p.rho_bar, (float)p.c_bar, p.has_row != 0,
+                       p.has_tboot != 0};
+  const unsigned tmask = p.has_term ? ~0u : 0u;
+  const unsigned rmask = p.has_trunc ? ~0u : 0u;
+  const float rowv = p.has_row ? load1<S>(p.row, ec, 0u) : 0.0f;
+
+  // value entering the current super-tile: 0 for the backward estimators (their
+  // bootstraps sit in the pairs), the column's init / carry otherwise
+  double C = 0.0;
+  if constexpr (!Tr::kBackwardRl) C = p.has_row ? (double)rowv : 0.0;
+
+  const int64_t nst = (T + SPAN - 1) / SPAN;
+  for (int64_t s = 0; s < nst; ++s) {
+    const int64_t tile = REV ? nst - 1 - s : s;
+    const int64_t cs64 = REV ? tile * SPAN + SPAN - (int64_t)(w + 1) * K : tile * SPAN + (int64_t)w * K;
+    const int64_t rem = T - cs64;
+    const int nv = rem <= 0 ? 0 : (rem >= K ? K : (int)rem);
+    const uint32_t cs = (uint32_t)cs64;  // T < 2^30
+
+    LaneIn<Est, K> d;
+    unsigned tbits = 0, rbits = 0;
+#pragma unroll
+    for (int m = 0; m < K; ++m) {
+      const int64_t t = cs64 + m < T ? cs64 + m : T - 1;
+      const int64_t idx = t * E + ec;
+      d.s[0][m] = load1<S>(p.r, idx, 0u);
+      if constexpr (NS >= 2) d.s[1][m] = load1<S>(p.v, idx, 0u);
+      if constexpr (NS >= 3) d.s[2][m] = load1<S>(p.aux, idx, 0u);
+      if constexpr (NS >= 5) {
+        d.s[3][m] = load1<S>(p.pi, idx, 0u);
+        d.s[4][m] = load1<S>(p.mu, idx, 0u);
+      }
+      if constexpr (USE_FLAGS) {
+        tbits |= (unsigned)(__builtin_nontemporal_load(p.term + idx) != 0) << m;
+        rbits |= (unsigned)(__builtin_nontemporal_load(p.trunc + idx) != 0) << m;
+      }
+    }
+    const unsigned vmask = nv >= 32 ? ~0u : ((1u << nv) - 1u);
+    tbits &= tmask & vmask;
+    rbits &= rmask & vmask;
+#pragma unroll
+    for (int m = 0; m < K; ++m) d.tb[m] = 0.0f;
+    if constexpr (GATHER_TB) {
+      const unsigned need = rbits & ~tbits;
+#pragma unroll
+      for (int m = 0; m < K; ++m)
+        if ((need >> m) & 1u) d.tb[m] = load1<S>(p.tboot, (cs64 + m) * E + ec, 0u);
+    }
+    d.rowv = rowv;
+
+    // inputs of the scan predecessor of the chunk's innermost step
+    const int64_t tn = REV ? cs64 + K : cs64 - 1;
+    PredIn pred{0.0f, 0.0, 0u};
+    if (tn >= 0 && tn < T) {
+      const int64_t n = tn * E + ec;
+      if constexpr (Tr::kRetrace) {
+        pred.v = load1<S>(p.aux, n, 0u);
+        const double ratio = (double)load1<S>(p.pi, n, 0u) / (double)load1<S>(p.mu, n, 0u);
+        pred.c = lam * (ratio < 1.0 ? ratio : 1.0);
+      } else if constexpr (Tr::kNbValue) {
+        pred.v = load1<S>(p.v, n, 0u);
+      } else if constexpr (Tr::kNbDone && USE_FLAGS) {
+        const unsigned dn = ((unsigned)(*(p.term + n) != 0) & tmask) | ((unsigned)(*(p.trunc + n) != 0) & rmask);
+        pred.done = dn ? 1u : 0u;
+      }
+    }
+
+    const LanePairs<K> lp = build_pairs<Est, K, false>(d, sc, tbits, rbits, cs, T, nv, true, pred);
+    const AB agg = fold_lane<K>(lp.e);
+    s_a[w][lane] = agg.a;
+    s_b[w][lane] = agg.b;
+    __syncthreads();
+
+    double x_in = C;  // value entering this wave's chunk
+    for (int u = 0; u < w; ++u) x_in = __builtin_fma(s_a[u][lane], x_in, s_b[u][lane]);
+    double c_out = x_in;  // value leaving the super-tile (the same in every wave)
+    for (int u = w; u < W; ++u) c_out = __builtin_fma(s_a[u][lane], c_out, s_b[u][lane]);
+
+    double xs[K];
+    rewalk<K>(lp.e, x_in, xs);
+    float o0[K], o1[K];
+    epilogue<Est, K>(d, lp, sc, x_in, xs, o0, o1);
+    if (col_ok) {
+#pragma unroll
+      for (int m = 0; m < K; ++m) {
+        if (m < nv) {
+          const int64_t idx = (cs64 + m) * E + e;
+          store1<S>(p.out0, idx, o0[m]);
+          if constexpr (OUT1) store1<S>(p.out1, idx, o1[m]);
+        }
+      }
+    }
+    C = c_out;
+    __syncthreads();  // the LDS maps are rewritten by the next super-tile
+  }
+}
+
+}  // namespace rlscan

@@ -73,9 +73,12 @@ def to_dev(d, device="cuda"):
             for k, v in d.items()}
 
 
-def run_gpu(name, dd, P=None, **variant):
-    """dd: dict of device tensors (to_dev).  Returns a dict of device tensors."""
+def run_gpu(name, dd, P=None, time_major=False, **variant):
+    """dd: dict of device tensors (to_dev).  Returns a dict of device tensors.
+    time_major: the per-step tensors in dd are [T, E] (outputs come back [T, E])."""
     import linear_recurrence_scan_reverse_amd as rl
+    if time_major:
+        rl = _TimeMajor(rl)
     P = {**DEFAULT_PARAMS, **(P or {})}
     o = select(dd, **variant)
     te, tr, bv, tb = o["terminated"], o["truncated"], o["bootstrap_value"], o["trunc_bootstrap"]
@@ -102,6 +105,99 @@ def run_gpu(name, dd, P=None, **variant):
     if name == "episodic_prefix_sum":
         return {"out": rl.episodic_prefix_sum(dd["r"], te, tr, bv)}
     raise KeyError(name)
+
+
+class _TimeMajor:
+    """The binding with time_major=True on every estimator call."""
+
+    def __init__(self, rl):
+        self._rl = rl
+
+    def __getattr__(self, name):
+        import functools
+        return functools.partial(getattr(self._rl, name), time_major=True)
+
+
+# ----------------------------------------------------------------- storage formats and layouts
+# value arrays (stored in the call's format) and per-step arrays (transposed
+# for the time-major layout) of synth.draw
+VALUE_KEYS = ("r", "v", "log_rhos", "q", "exp_q", "pi", "mu", "bootstrap_value", "trunc_bootstrap")
+ROW_KEYS = ("bootstrap_value",)
+UNIT_ROUNDOFF = {"float32": 2.0 ** -24, "bfloat16": 2.0 ** -8, "float16": 2.0 ** -11}
+
+
+def storage_inputs(d, fmt="float32", time_major=False, misalign=False):
+    """(host, device): numpy inputs with values rounded to the format (what the
+    kernel reads, widened), and device tensors in the format and layout."""
+    import torch
+    dt = getattr(torch, fmt)
+    host, dev = {}, {}
+    for k, v in d.items():
+        if v is None:
+            host[k] = dev[k] = None
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        if k in VALUE_KEYS:
+            t = t.to(dt)
+            host[k] = t.float().numpy()
+        else:
+            host[k] = v
+        if time_major and k not in ROW_KEYS:
+            t = t.t().contiguous()
+        if misalign:
+            # the same values at a base one element past the allocation's start
+            buf = torch.empty(t.numel() + 1, dtype=t.dtype)
+            buf[1:] = t.reshape(-1)
+            t = buf.cuda()[1:].view(t.shape)
+        else:
+            t = t.cuda()
+        dev[k] = t
+    return host, dev
+
+
+def check_storage(name, d, fmt="float32", time_major=False, misalign=False, P=None, **variant):
+    """GPU (format, layout) against the oracle on the values the kernel reads.
+
+    Gate: max |g - r| / max(1, |r|) <= u + 1e-5, with u the format's unit
+    roundoff (the last rounding of each output) and 1e-5 the fp32 gate; for the
+    16-bit formats, outputs also match the oracle rounded like the kernel rounds
+    (fp64 -> fp32 -> format, nearest even) bit for bit, except at most 0.1% (or 2) that
+    differ by one unit in the last place (or, near 0, by no more than the fp32
+    gate).  Returns the worst error."""
+    import torch
+    dt = getattr(torch, fmt)
+    host, dev = storage_inputs(d, fmt, time_major, misalign)
+    got = run_gpu(name, dev, P, time_major=time_major, **variant)
+    torch.cuda.synchronize()
+    ref = run_oracle(name, host, P, **variant)
+    tol = (UNIT_ROUNDOFF[fmt] if fmt != "float32" else 0.0) + TOL
+    worst = 0.0
+    for k, r in ref.items():
+        g = got[k]
+        assert g.dtype == dt, (name, k, g.dtype)
+        if time_major:
+            g = g.t().contiguous()
+        gf = g.float().cpu().numpy()
+        err = parity_err(gf, r)
+        worst = max(worst, err)
+        assert err <= tol, "%s %s tm=%s %s: err %.3g > %.3g" % (name, fmt, time_major, k, err, tol)
+        if fmt == "float32" or r.size == 0:
+            continue
+        exp16 = torch.from_numpy(np.asarray(r, dtype=np.float64).astype(np.float32)).to(dt)
+        gb = g.cpu().view(torch.int16).numpy().astype(np.int32)
+        eb = exp16.view(torch.int16).numpy().astype(np.int32)
+        diff = gb != eb
+        nd = int(diff.sum())
+        assert nd <= max(2, 1e-3 * diff.size), "%s %s %s: %d of %d outputs differ from the rounded oracle" % (
+            name, fmt, k, nd, diff.size)
+        if diff.any():
+            # adjacent encodings (one unit in the last place), or a result so
+            # close to 0 that the kernel's fp32-level error (the 1e-5 gate, e.g.
+            # V-trace's fp32 exp) spans several of the format's units there
+            adjacent = np.abs(gb[diff] - eb[diff]) == 1
+            small = np.abs(gf[diff] - r[diff]) <= TOL * np.maximum(1.0, np.abs(r[diff]))
+            assert np.all(adjacent | small), (name, fmt, k)
+    return worst
 
 
 def compare(name, d, P=None, device="cuda", **variant):

@@ -42,7 +42,9 @@ def test_header_declares_the_expected_entry_points():
               "rlscan_gae", "rlscan_vtrace",
               "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum",
               "rlscan_linear_scan", "rlscan_linear_scan_segmented", "rlscan_eligibility_traces_vec",
-              "rlscan_status_string",
+              "rlscan_discounted_returns_ex", "rlscan_td_lambda_ex", "rlscan_gae_ex",
+              "rlscan_vtrace_ex", "rlscan_retrace_ex", "rlscan_eligibility_traces_ex",
+              "rlscan_episodic_prefix_sum_ex", "rlscan_status_string",
               "rlscan_version"]:
         assert n in names
 
@@ -176,6 +178,59 @@ def test_eligibility_traces_vec_validation(lib):
     assert f(A, None, None, None, A + 4 * E * T * Dm - 4, E, T, Dm, 0.9, 0.9, S) == ERR_ALIAS
     assert f(A, D, None, None, D + 8, E, T, Dm, 0.9, 0.9, S) == ERR_ALIAS  # output over the flags
     assert f(None, None, None, None, None, E, T, 0, 0.9, 0.9, S) == OK
+
+
+F32, BF16, F16 = 0, 1, 2
+ENV_MAJOR, TIME_MAJOR = 0, 1
+
+
+@pytest.mark.parametrize("lay", [ENV_MAJOR, TIME_MAJOR])
+def test_ex_entries_validation(lib, lay):
+    E, T = 8, 16
+
+    def gae(fmt, *a):
+        return lib.rlscan_gae_ex(fmt, lay, *a)
+
+    # unknown storage format or layout
+    assert gae(7, A, B, None, None, None, None, C, None, E, T, 0.99, 0.95, S) == ERR_PARAM
+    assert gae(-1, A, B, None, None, None, None, C, None, E, T, 0.99, 0.95, S) == ERR_PARAM
+    assert lib.rlscan_gae_ex(F32, 2, A, B, None, None, None, None, C, None, E, T, 0.99, 0.95, S) == ERR_PARAM
+    assert lib.rlscan_gae_ex(BF16, -1, A, B, None, None, None, None, C, None, E, T, 0.99, 0.95, S) == ERR_PARAM
+    for fmt in (BF16, F16):
+        # 16-bit storage needs 2-byte alignment only
+        assert gae(fmt, A + 1, B, None, None, None, None, C, None, E, T, 0.99, 0.95, S) == ERR_ALIGN
+        assert gae(fmt, A, B, None, None, None, None, C + 3, None, E, T, 0.99, 0.95, S) == ERR_ALIGN
+        assert gae(fmt, A, B, None, None, F + 1, None, C, None, E, T, 0.99, 0.95, S) == ERR_ALIGN
+        # overlap is measured in 2-byte elements: the last element of rewards
+        # overlaps, the first byte past it does not (then validation passes and
+        # a NULL output is the next error)
+        assert gae(fmt, A, B, None, None, None, None, A + 2 * E * T - 2, None, E, T, 0.99, 0.95, S) == ERR_ALIAS
+        assert gae(fmt, A, B, None, None, None, None, C, C + 2 * E * T - 2, E, T, 0.99, 0.95, S) == ERR_ALIAS
+        assert gae(fmt, A, B, None, None, None, None, None, None, E, T, 0.99, 0.95, S) == ERR_NULL
+        assert gae(fmt, A, B, None, None, None, None, C, None, -1, T, 0.99, 0.95, S) == ERR_SHAPE
+        assert gae(fmt, A, B, None, None, None, None, C, None, E, T, 0.99, 1.5, S) == ERR_PARAM
+        assert gae(fmt, None, None, None, None, None, None, None, None, 0, T, 0.99, 0.95, S) == OK
+        assert lib.rlscan_discounted_returns_ex(fmt, lay, None, None, None, None, None, C, E, T, 0.9, S) == ERR_NULL
+        assert lib.rlscan_td_lambda_ex(fmt, lay, A, None, None, None, None, None, C, E, T, 0.9, 0.9, S) == ERR_NULL
+        assert lib.rlscan_vtrace_ex(fmt, lay, A, B, D, None, None, None, None, C, None, E, T, 0.9, 1.0, 0.0, 1.0,
+                                    S) == ERR_PARAM
+        assert lib.rlscan_retrace_ex(fmt, lay, A, B, C, D, None, None, None, None, None, F, E, T, 0.9, 0.9,
+                                     S) == ERR_NULL
+        assert lib.rlscan_eligibility_traces_ex(fmt, lay, A, None, None, F + 1, C, E, T, 0.9, 0.9, S) == ERR_ALIGN
+        assert lib.rlscan_episodic_prefix_sum_ex(fmt, lay, A, None, None, None, A + 2, E, T, S) == ERR_ALIAS
+    # the float32 format through the _ex entry keeps the 4-byte rules
+    assert gae(F32, A + 2, B, None, None, None, None, C, None, E, T, 0.99, 0.95, S) == ERR_ALIGN
+    assert gae(F32, A, B, None, None, None, None, A + 4 * E * T - 4, None, E, T, 0.99, 0.95, S) == ERR_ALIAS
+
+
+def test_binding_rejects_mixed_storage_dtypes():
+    torch = pytest.importorskip("torch")
+    r = torch.zeros(2, 3, dtype=torch.bfloat16)
+    v = torch.zeros(2, 3, dtype=torch.float32)
+    with pytest.raises(TypeError, match="values must be bfloat16"):
+        rl._check_val(v, "values", (2, 3), v.device, rl._storage(r, "rewards"))
+    with pytest.raises(TypeError, match="float32, bfloat16 or float16"):
+        rl._storage(torch.zeros(2, 3, dtype=torch.float64), "rewards")
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

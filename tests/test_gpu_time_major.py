@@ -1,0 +1,102 @@
+"""Time-major [T, E] layout of the seven estimators against the oracle.
+
+The oracle runs on the [E, T] arrays; the kernel gets the same arrays
+transposed to [T, E] (flags and trunc_bootstrap included, bootstrap_value /
+init stay [E]) and its [T, E] outputs are transposed back before comparing.
+Every storage format runs: float32 within the 1e-5 gate, the 16-bit formats
+to the rule of ``estimators.check_storage``.  Shapes: one step, one env,
+environment counts around the 64-lane block (63, 64, 65, 130), ragged and
+whole super-tiles, several super-tiles per column, optional inputs absent,
+dense flags, and bases one element off alignment.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+from linear_recurrence_scan_reverse_amd import synth
+from tests.estimators import TOL, check_storage, parity_err
+
+pytestmark = pytest.mark.gpu
+
+SEVEN = ("discounted_returns", "td_lambda", "gae", "vtrace", "retrace", "eligibility_traces",
+         "episodic_prefix_sum")
+FORMATS = ("float32", "bfloat16", "float16")
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("E,T", [(1, 1), (1, 300), (5, 1), (63, 17), (64, 128), (65, 129), (130, 256),
+                                 (1000, 300), (200, 1000)])
+def test_time_major_all_estimators(fmt, E, T):
+    _say("time-major %s E=%d T=%d" % (fmt, E, T))
+    d = synth.draw(E, T, seed=80 + E, p_term=0.01, p_trunc=0.01)
+    for name in SEVEN:
+        check_storage(name, d, fmt, time_major=True)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("variant", [dict(term=False, trunc=False), dict(boot=False, tboot=False),
+                                     dict(trunc=False), dict(tboot=False)])
+def test_time_major_optional_inputs(fmt, variant):
+    d = synth.draw(96, 200, seed=81, p_term=0.02, p_trunc=0.02)
+    for name in SEVEN:
+        check_storage(name, d, fmt, time_major=True, **variant)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_time_major_dense_flags_and_misaligned(fmt):
+    d = synth.draw(70, 150, seed=82, p_term=0.2, p_trunc=0.2)
+    for name in SEVEN:
+        check_storage(name, d, fmt, time_major=True)
+        check_storage(name, d, fmt, time_major=True, misalign=True)
+
+
+def test_time_major_matches_row_major_fp32():
+    # both layouts compute the same function: float32 outputs agree within the gate
+    import torch
+    from tests.estimators import run_gpu, storage_inputs
+    d = synth.draw(512, 256, seed=83, p_term=0.01, p_trunc=0.01)
+    _, rm = storage_inputs(d)
+    _, tm = storage_inputs(d, time_major=True)
+    for name in SEVEN:
+        a = run_gpu(name, rm)
+        b = run_gpu(name, tm, time_major=True)
+        torch.cuda.synchronize()
+        for k in a:
+            err = parity_err(b[k].t().cpu().numpy(), a[k].cpu().numpy().astype(np.float64))
+            assert err <= TOL, (name, k, err)
+
+
+def test_time_major_bitwise_deterministic():
+    import torch
+    from tests.estimators import run_gpu, storage_inputs
+    d = synth.draw(300, 333, seed=84, p_term=0.01, p_trunc=0.01)
+    _, tm = storage_inputs(d, time_major=True)
+    for name in SEVEN:
+        a = {k: v.cpu().numpy() for k, v in run_gpu(name, tm, time_major=True).items()}
+        b = {k: v.cpu().numpy() for k, v in run_gpu(name, tm, time_major=True).items()}
+        torch.cuda.synchronize()
+        for k in a:
+            assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), (name, k)
+
+
+def test_time_major_exact_integer_sums():
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    import oracle
+    rng = np.random.default_rng(85)
+    E, T = 200, 500
+    x = rng.integers(-20, 21, size=(E, T)).astype(np.float32)
+    term = (rng.random((E, T)) < 0.01).astype(np.uint8)
+    init = rng.integers(-5, 6, size=E).astype(np.float32)
+    ref = oracle.episodic_prefix_sum(x, term, None, init)
+    got = rl.episodic_prefix_sum(torch.from_numpy(x.T.copy()).cuda(), torch.from_numpy(term.T.copy()).cuda(),
+                                 None, torch.from_numpy(init).cuda(), time_major=True)
+    assert tuple(got.shape) == (T, E)
+    assert np.array_equal(got.cpu().numpy().T.astype(np.float64), ref)
