@@ -290,13 +290,15 @@ hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
 
 // ----------------------------------------------------------------- time-major path
 // [T, E] arrays: one block of W waves per 64 environments, K steps per wave
-// chunk.  Blocks of 16 waves keep 16 waves per CU at 16384 environments;
-// the estimators with one input stream take 16-step chunks, the others 8
-// (fewer live registers per lane).
+// chunk.  Blocks of 16 waves keep 16 waves per CU at 16384 environments.
+// A block overlaps no loads with its compute, so fewer, longer super-tiles
+// win: 16-step chunks (a 256-step row in one super-tile), except V-trace and
+// Retrace, whose registers allow 8 (at 16384 x 256: TD(lambda) 17.5 -> 14.5
+// us from 8 to 16 steps; 8 waves per block were slower everywhere).
 template <class Est>
 constexpr int tm_waves() { return 16; }
 template <class Est>
-constexpr int tm_chunk() { return Traits<Est>::kStreams >= 2 ? 8 : 16; }
+constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 
 template <class Est, int OPT, class S>
 inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {

@@ -27,11 +27,11 @@
 
 namespace rlscan {
 
-// One element of format S at index idx, narrowed from fp32 (non-temporal).
+// One element of format S at base[bidx + off], narrowed from fp32 (non-temporal).
 template <class S>
-__device__ __forceinline__ void store1(float* base, int64_t idx, float v) {
-  if constexpr (__is_same(S, F32S)) __builtin_nontemporal_store(v, base + idx);
-  else __builtin_nontemporal_store(f32_to_s<S>(v), reinterpret_cast<uint16_t*>(base) + idx);
+__device__ __forceinline__ void store1(float* base, int64_t bidx, uint32_t off, float v) {
+  if constexpr (__is_same(S, F32S)) __builtin_nontemporal_store(v, at(base + bidx, off));
+  else __builtin_nontemporal_store(f32_to_s<S>(v), reinterpret_cast<uint16_t*>(base) + bidx + off);
 }
 
 // W waves per block, K steps per wave chunk.  OPT as for scan_kernel.
@@ -50,18 +50,22 @@ __global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p) {
   __shared__ double s_b[W][64];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;  // chunk position in scan order inside a super-tile
+  // chunk position in scan order inside a super-tile (wave-uniform)
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t E = p.E, T = p.T;
-  const int64_t e = (int64_t)blockIdx.x * 64 + lane;
-  const bool col_ok = e < E;
-  const int64_t ec = col_ok ? e : E - 1;  // clamped column: every load stays inside the arrays
+  // Addresses: a wave-uniform element index (step row + the block's first
+  // column) plus a 32-bit lane offset, the lane's column clamped into the row
+  // so every load stays inside the arrays.
+  const int64_t e0 = (int64_t)blockIdx.x * 64;
+  const bool col_ok = e0 + lane < E;
+  const uint32_t lo = (uint32_t)(col_ok ? lane : E - 1 - e0);
 
   const double gamma = p.gamma, lam = p.lam;
   const ScanScalars sc{gamma, lam, gamma * lam, (float)p.rho_bar, (float)p.c_bar, p.has_row != 0,
                        p.has_tboot != 0};
   const unsigned tmask = p.has_term ? ~0u : 0u;
   const unsigned rmask = p.has_trunc ? ~0u : 0u;
-  const float rowv = p.has_row ? load1<S>(p.row, ec, 0u) : 0.0f;
+  const float rowv = p.has_row ? load1<S>(p.row, e0, lo) : 0.0f;
 
   // value entering the current super-tile: 0 for the backward estimators (their
   // bootstraps sit in the pairs), the column's init / carry otherwise
@@ -81,17 +85,17 @@ __global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p) {
 #pragma unroll
     for (int m = 0; m < K; ++m) {
       const int64_t t = cs64 + m < T ? cs64 + m : T - 1;
-      const int64_t idx = t * E + ec;
-      d.s[0][m] = load1<S>(p.r, idx, 0u);
-      if constexpr (NS >= 2) d.s[1][m] = load1<S>(p.v, idx, 0u);
-      if constexpr (NS >= 3) d.s[2][m] = load1<S>(p.aux, idx, 0u);
+      const int64_t row = t * E + e0;
+      d.s[0][m] = load1<S>(p.r, row, lo);
+      if constexpr (NS >= 2) d.s[1][m] = load1<S>(p.v, row, lo);
+      if constexpr (NS >= 3) d.s[2][m] = load1<S>(p.aux, row, lo);
       if constexpr (NS >= 5) {
-        d.s[3][m] = load1<S>(p.pi, idx, 0u);
-        d.s[4][m] = load1<S>(p.mu, idx, 0u);
+        d.s[3][m] = load1<S>(p.pi, row, lo);
+        d.s[4][m] = load1<S>(p.mu, row, lo);
       }
       if constexpr (USE_FLAGS) {
-        tbits |= (unsigned)(__builtin_nontemporal_load(p.term + idx) != 0) << m;
-        rbits |= (unsigned)(__builtin_nontemporal_load(p.trunc + idx) != 0) << m;
+        tbits |= (unsigned)(__builtin_nontemporal_load(at(p.term + row, lo)) != 0) << m;
+        rbits |= (unsigned)(__builtin_nontemporal_load(at(p.trunc + row, lo)) != 0) << m;
       }
     }
     const unsigned vmask = nv >= 32 ? ~0u : ((1u << nv) - 1u);
@@ -103,7 +107,7 @@ __global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p) {
       const unsigned need = rbits & ~tbits;
 #pragma unroll
       for (int m = 0; m < K; ++m)
-        if ((need >> m) & 1u) d.tb[m] = load1<S>(p.tboot, (cs64 + m) * E + ec, 0u);
+        if ((need >> m) & 1u) d.tb[m] = load1<S>(p.tboot, (cs64 + m) * E + e0, lo);
     }
     d.rowv = rowv;
 
@@ -111,15 +115,15 @@ __global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p) {
     const int64_t tn = REV ? cs64 + K : cs64 - 1;
     PredIn pred{0.0f, 0.0, 0u};
     if (tn >= 0 && tn < T) {
-      const int64_t n = tn * E + ec;
+      const int64_t n = tn * E + e0;
       if constexpr (Tr::kRetrace) {
-        pred.v = load1<S>(p.aux, n, 0u);
-        const double ratio = (double)load1<S>(p.pi, n, 0u) / (double)load1<S>(p.mu, n, 0u);
+        pred.v = load1<S>(p.aux, n, lo);
+        const double ratio = (double)load1<S>(p.pi, n, lo) / (double)load1<S>(p.mu, n, lo);
         pred.c = lam * (ratio < 1.0 ? ratio : 1.0);
       } else if constexpr (Tr::kNbValue) {
-        pred.v = load1<S>(p.v, n, 0u);
+        pred.v = load1<S>(p.v, n, lo);
       } else if constexpr (Tr::kNbDone && USE_FLAGS) {
-        const unsigned dn = ((unsigned)(*(p.term + n) != 0) & tmask) | ((unsigned)(*(p.trunc + n) != 0) & rmask);
+        const unsigned dn = ((unsigned)(*at(p.term + n, lo) != 0) & tmask) | ((unsigned)(*at(p.trunc + n, lo) != 0) & rmask);
         pred.done = dn ? 1u : 0u;
       }
     }
@@ -143,9 +147,9 @@ __global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p) {
 #pragma unroll
       for (int m = 0; m < K; ++m) {
         if (m < nv) {
-          const int64_t idx = (cs64 + m) * E + e;
-          store1<S>(p.out0, idx, o0[m]);
-          if constexpr (OUT1) store1<S>(p.out1, idx, o1[m]);
+          const int64_t row = (cs64 + m) * E + e0;
+          store1<S>(p.out0, row, lo, o0[m]);
+          if constexpr (OUT1) store1<S>(p.out1, row, lo, o1[m]);
         }
       }
     }
