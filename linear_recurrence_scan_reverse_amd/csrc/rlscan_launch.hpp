@@ -169,14 +169,18 @@ inline int stream_team(const KernelArgs& a) {
 //    rows of 8 or more tiles, with fewer than two rows per compute wave the
 //    grid can hold, run faster on the pipelined kernel, whose 4-wave teams
 //    split a long row (up to 2.3x at 256 x 4096);
-//  * V-trace with rows of more than one tile, and discounted returns and
-//    Retrace with flags present, run faster pipelined at every size measured
-//    from 4096 rows up (the per-wave bootstrap gather and, for Retrace, the
-//    heavier per-step arithmetic overlap better there than in ticks).
+//  * V-trace with rows of more than one tile, and Retrace with flags
+//    present, run faster pipelined at every size measured from 4096 rows up
+//    (the per-wave bootstrap gather and the heavier per-step arithmetic
+//    overlap better there than in ticks);
+//  * discounted returns with flags stream faster up to 16384 rows (16384 x
+//    256: 11.5 vs 12.4 us; 4096 x 1024: 11.9 vs 13.5 us) but not at 65536 rows
+//    (65536 x 64: 12.6 vs 11.1 us).
 template <class Est>
 inline bool prefer_stream(const KernelArgs& a, int L) {
   const bool flags = a.has_term || a.has_trunc;
-  if ((__is_same(Est, DiscountedReturn) || __is_same(Est, Retrace)) && flags) return false;
+  if (__is_same(Est, Retrace) && flags) return false;
+  if (__is_same(Est, DiscountedReturn) && flags && a.E > 32768) return false;
   if (__is_same(Est, Vtrace) && a.T > 256) return false;
   const int64_t ntiles = a.T / (4 * L);
   if (ntiles >= 8) {

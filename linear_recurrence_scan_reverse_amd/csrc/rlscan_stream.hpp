@@ -14,7 +14,7 @@
 //     VGPRs;
 //   * the gather wave (wave 1, estimators with truncation bootstraps) reads
 //     landed flags from LDS and DMAs the bootstrap of every truncated step
-//     (lanes without one fetch a single shared, cache-resident line);
+//     (lanes without one re-read their rewards, still in L2);
 //   * the compute waves read LDS, scan and store; they never wait on memory.
 //
 // Time advances in ticks separated by s_barrier; at tick t every compute wave
@@ -91,11 +91,15 @@ constexpr int kStreamItem = 256;  // elements per item (64 lanes x 4 steps)
 // Most compute waves per block for an estimator.  Measured at 16384 x 256
 // (two blocks per CU, lead 2): a power of two that splits the rows evenly over
 // the blocks beats filling the LDS for the light estimators, while V-trace and
-// Retrace are fastest with as many waves as the LDS holds.
+// Retrace are fastest with as many waves as the LDS holds.  The estimators
+// with a gather wave run best with 4 (discounted returns: 14.5 us with 8
+// compute waves, 11.5 us with 4).
 template <class Est>
 constexpr int stream_nc_cap() {
   if constexpr (__is_same(Est, Vtrace) || __is_same(Est, Retrace)) return 16;
-  if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae) || __is_same(Est, ReturnsTdLambda)) return 4;
+  if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae) || __is_same(Est, ReturnsTdLambda) ||
+                __is_same(Est, DiscountedReturn))
+    return 4;
   return 8;
 }
 
@@ -391,7 +395,11 @@ stream_kernel(const KernelArgs p) {
         const unsigned nz_t = (((m_t & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_t) & 0x80808080u;
         const unsigned nz_r = (((m_r & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_r) & 0x80808080u;
         const bool need = (nz_r & ~nz_t) != 0u && p.has_tboot;
-        const float* src = need ? at(p.tboot + base, elem_off(rg, (uint32_t)lane * 4)) : p.tboot;
+        // lanes without a bootstrap to fetch re-read their chunk of rewards,
+        // which the loader fetched P ticks ago (an L2 hit spread over the
+        // channels like the data itself; one shared address for every lane of
+        // the GPU made a single L2 channel the bottleneck)
+        const float* src = at((need ? p.tboot : p.r) + base, elem_off(rg, (uint32_t)lane * 4));
         __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)&sl.tb[c][0], 16, 0, 0);
       }
     };
