@@ -192,6 +192,7 @@ __device__ __forceinline__ double group_last_f64(double v, int lane) {
 // ----------------------------------------------------------------- streaming loads / stores
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Every [E,T] array is addressed as (wave-uniform base pointer) + (32-bit lane
 // offset in elements); all arrays share one layout, so one offset register
@@ -361,9 +362,17 @@ __device__ __forceinline__ void load_s(const float* base, int64_t bidx, uint32_t
     load_chunk<K, VEC>(base + bidx, off, last, o);
   } else {
     const uint16_t* b = reinterpret_cast<const uint16_t*>(base) + bidx;
-    if constexpr (VEC && K == 4) {
+    if constexpr (VEC && K == 8) {
       // integer loads: a float-vector load of these bits was narrowed to one
       // dword by the compiler
+      const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + off));
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] = s_to_f32<S>((uint16_t)w[i]);
+        o[2 * i + 1] = s_to_f32<S>((uint16_t)(w[i] >> 16));
+      }
+    } else if constexpr (VEC && K == 4) {
       const unsigned long long q = __builtin_nontemporal_load(reinterpret_cast<const unsigned long long*>(b + off));
       const uint32_t w0 = (uint32_t)q, w1 = (uint32_t)(q >> 32);
       o[0] = s_to_f32<S>((uint16_t)w0); o[1] = s_to_f32<S>((uint16_t)(w0 >> 16));
@@ -388,7 +397,14 @@ __device__ __forceinline__ void store_s(float* base, int64_t bidx, uint32_t off,
     store_chunk<K, VEC>(base + bidx, off, nv, o);
   } else {
     uint16_t* b = reinterpret_cast<uint16_t*>(base) + bidx;
-    if constexpr (VEC && K == 4) {
+    if constexpr (VEC && K == 8) {
+      u32x4 q;
+      q.x = (uint32_t)f32_to_s<S>(o[0]) | ((uint32_t)f32_to_s<S>(o[1]) << 16);
+      q.y = (uint32_t)f32_to_s<S>(o[2]) | ((uint32_t)f32_to_s<S>(o[3]) << 16);
+      q.z = (uint32_t)f32_to_s<S>(o[4]) | ((uint32_t)f32_to_s<S>(o[5]) << 16);
+      q.w = (uint32_t)f32_to_s<S>(o[6]) | ((uint32_t)f32_to_s<S>(o[7]) << 16);
+      __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(b + off));
+    } else if constexpr (VEC && K == 4) {
       const uint32_t w0 = (uint32_t)f32_to_s<S>(o[0]) | ((uint32_t)f32_to_s<S>(o[1]) << 16);
       const uint32_t w1 = (uint32_t)f32_to_s<S>(o[2]) | ((uint32_t)f32_to_s<S>(o[3]) << 16);
       __builtin_nontemporal_store((unsigned long long)w0 | ((unsigned long long)w1 << 32),

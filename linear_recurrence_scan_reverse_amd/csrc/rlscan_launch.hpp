@@ -28,6 +28,22 @@ inline LaunchShape pick_shape(int64_t T) {
   return {64, 4, 4};
 }
 
+// Team shape for 16-bit storage: rows of 65 to 512 steps take 8 steps per
+// lane (one 16-byte access per lane and stream, as 4 float32 steps are), so
+// half as many lanes per row.  Measured at 16384 x 256 (bfloat16): TD(lambda)
+// and GAE 13.0 -> 11.7 us, traces and prefix sums 10.1 -> 9.5 us; V-trace
+// unchanged; Retrace 17.4 -> 18.1 us and discounted returns 11.0 -> 15.3 us
+// (its 8 blocks per CU no longer fit), so those three keep 4 steps per lane.
+template <class Est>
+inline LaunchShape pick_shape_16(int64_t T) {
+  if (__is_same(Est, DiscountedReturn) || __is_same(Est, Vtrace) || __is_same(Est, Retrace)) return pick_shape(T);
+  if (T <= 64) return pick_shape(T);
+  if (T <= 128) return {16, 8, 1};
+  if (T <= 256) return {32, 8, 1};
+  if (T <= 512) return {64, 8, 1};
+  return pick_shape(T);
+}
+
 // Resident blocks per CU the persistent grid aims for (discounted returns, the
 // lightest kernel, measured faster with more waves in flight: 11.4 vs 11.9 us
 // at 16384 x 256).
@@ -279,8 +295,11 @@ template <class Est, class S>
 hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const int64_t len = segment_length(a)) return launch_segmented<Est, S>(a, s, len);
-  const LaunchShape sh = pick_shape(a.T);
+  const LaunchShape sh = pick_shape_16<Est>(a.T);
   switch (sh.W * 1000 + sh.L * 10 + sh.K) {
+    case 1000 + 160 + 8: return launch_shape<Est, 16, 8, 1, S>(a, s, sh);
+    case 1000 + 320 + 8: return launch_shape<Est, 32, 8, 1, S>(a, s, sh);
+    case 1000 + 640 + 8: return launch_shape<Est, 64, 8, 1, S>(a, s, sh);
     case 1000 + 160 + 1: return launch_shape<Est, 16, 1, 1, S>(a, s, sh);
     case 1000 + 160 + 2: return launch_shape<Est, 16, 2, 1, S>(a, s, sh);
     case 1000 + 160 + 4: return launch_shape<Est, 16, 4, 1, S>(a, s, sh);

@@ -209,3 +209,49 @@ def test_segmented_generic_scan_long_rows_and_exact_sums():
                                        reverse=rev).cpu().numpy()
         assert np.array_equal(got.astype(np.float64),
                               oracle.linear_scan_segmented(ones, bi, done, None, reverse=rev))
+
+
+def test_graph_capture_of_formats_layouts_and_long_rows():
+    # a captured HIP graph holding a time-major bfloat16 call, a row-major
+    # float16 call and a segmented long-row call (three kernels), replayed
+    # several times with the program's own work between replays: every replay
+    # matches the eager result bit for bit
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    from tests.estimators import storage_inputs
+    d1 = synth.draw(300, 200, seed=28, p_term=0.01, p_trunc=0.01)
+    _, tm = storage_inputs(d1, "bfloat16", time_major=True)
+    _, hf = storage_inputs(d1, "float16")
+    d2 = synth.draw(2, 40000, seed=29, p_term=0.001, p_trunc=0.001)
+    lr = to_dev(d2)
+
+    def calls(outs):
+        rl.gae(tm["r"], tm["v"], tm["terminated"], tm["truncated"], tm["bootstrap_value"], tm["trunc_bootstrap"],
+               time_major=True, advantages=outs[0], returns=outs[1])
+        rl.retrace(hf["r"], hf["q"], hf["exp_q"], hf["pi"], hf["mu"], hf["terminated"], hf["truncated"],
+                   hf["bootstrap_value"], hf["trunc_bootstrap"], out=outs[2])
+        rl.discounted_returns(lr["r"], lr["terminated"], lr["truncated"], lr["bootstrap_value"],
+                              lr["trunc_bootstrap"], out=outs[3])
+
+    def fresh():
+        return [torch.empty_like(tm["r"]), torch.empty_like(tm["r"]), torch.empty_like(hf["r"]),
+                torch.empty_like(lr["r"])]
+
+    eager = fresh()
+    calls(eager)
+    torch.cuda.synchronize()
+    eager = [x.cpu() for x in eager]
+    outs = fresh()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(outs)
+    for rep in range(3):
+        for x in outs:
+            x.fill_(float("nan"))
+        calls(fresh())  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a.cpu().view(torch.int16) if a.element_size() == 2 else a.cpu(),
+                               b.view(torch.int16) if b.element_size() == 2 else b), rep
