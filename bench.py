@@ -328,7 +328,22 @@ def cpu_baseline(w, d, budget_s=10.0):
                   "estimators, fp64 C oracle (gcc -O2), %d threads over row blocks, %.1f s"
                   % (rows, w.T, w.E, threads, secs),
         "single_thread_env_steps_per_s": single,
+        "host": host_info(),
     }
+
+
+def host_info():
+    """CPU count, affinity-limited count and model of the host the oracle ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "model": model}
 
 
 # ----------------------------------------------------------------- main
@@ -428,6 +443,28 @@ def run_grid(torch, device, args):
             torch.cuda.empty_cache()
 
 
+def run_configs(torch, device, args):
+    """The smaller named workloads (parity cases of the tests), each estimator's
+    per-launch time on rotating buffers: one JSON line per workload.  The
+    smallest are cache-resident, so their HBM fraction is not meaningful; their
+    figure is latency and env-steps/s."""
+    for name, w in synth.WORKLOADS.items():
+        if name == "all7_16384x256":
+            continue
+        d = synth.workload_inputs(w)
+        set_bytes = sum(v.nbytes for v in d.values()) + 8 * 4 * w.E * w.T
+        nsets = int(min(64, max(2, -(-(1 << 30) // set_bytes) + 1)))
+        runner = Runner(w, d, nsets, device)
+        names = [n for n in ORDER if n in w.estimators]
+        per = time_estimators(runner, names, d, w, max(args.steps, 100))
+        log("config %-18s " % name + "  ".join("%s %.2f us (%.3g env-steps/s)" % (
+            n, per[n]["us_per_launch"], per[n]["env_steps_per_s"]) for n in names))
+        print(json.dumps({"config": True, "workload": name, "E": w.E, "T": w.T, "buffer_sets": nsets,
+                          "per_estimator": per}), flush=True)
+        del runner
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -443,6 +480,7 @@ def main():
     ap.add_argument("--grid-e", default=None, help="comma-separated E values for --grid")
     ap.add_argument("--grid-t", default=None, help="comma-separated T values for --grid")
     ap.add_argument("--no-16", action="store_true", help="skip the 16-bit storage and time-major timings")
+    ap.add_argument("--configs", action="store_true", help="the smaller named workloads, one line each")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -464,6 +502,10 @@ def main():
 
     if args.grid:
         run_grid(torch, device, args)
+        return
+
+    if args.configs:
+        run_configs(torch, device, args)
         return
 
     w = synth.WORKLOADS[args.workload]
