@@ -135,11 +135,11 @@ template <class Est>
 constexpr int stream_lead() { return 2; }
 constexpr int kStreamBlocksPerCu = 2;
 
-template <class Est, int L, int OPT>
+template <class Est, int L, int OPT, class Fmt = F32S>
 inline hipError_t launch_stream_one(const KernelArgs& a, hipStream_t s) {
   constexpr int P = stream_lead<Est>();
   constexpr int BPC = kStreamBlocksPerCu;
-  using Cfg = StreamCfg<Est, (OPT & 1) != 0, P, BPC>;
+  using Cfg = StreamCfg<Est, (OPT & 1) != 0, P, BPC, Fmt>;
   constexpr int G = 64 / L;
   const int64_t nrg = (a.E + G - 1) / G;
   const int64_t cap = (int64_t)cu_count() * BPC;
@@ -148,34 +148,40 @@ inline hipError_t launch_stream_one(const KernelArgs& a, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   KernelArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_kernel<Est, L, OPT, P, BPC>), dim3((unsigned)blocks),
-                         dim3(Cfg::kThreads), params, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_kernel<Est, L, OPT, P, BPC, Fmt>),
+                         dim3((unsigned)blocks), dim3(Cfg::kThreads), params, 0, s);
 }
 
-template <class Est, int L>
+template <class Est, int L, class Fmt = F32S>
 inline hipError_t launch_stream(const KernelArgs& a, hipStream_t s) {
   using Tr = Traits<Est>;
   const bool flags = a.has_term || a.has_trunc;
   if constexpr (Tr::kHasOut1) {
     const bool out1 = a.out1 != nullptr;
-    if (flags) return out1 ? launch_stream_one<Est, L, 3>(a, s) : launch_stream_one<Est, L, 1>(a, s);
-    return out1 ? launch_stream_one<Est, L, 2>(a, s) : launch_stream_one<Est, L, 0>(a, s);
+    if (flags) return out1 ? launch_stream_one<Est, L, 3, Fmt>(a, s) : launch_stream_one<Est, L, 1, Fmt>(a, s);
+    return out1 ? launch_stream_one<Est, L, 2, Fmt>(a, s) : launch_stream_one<Est, L, 0, Fmt>(a, s);
   } else if constexpr (Tr::kUsesFlags) {
-    return flags ? launch_stream_one<Est, L, 1>(a, s) : launch_stream_one<Est, L, 0>(a, s);
+    return flags ? launch_stream_one<Est, L, 1, Fmt>(a, s) : launch_stream_one<Est, L, 0, Fmt>(a, s);
   } else {
-    return launch_stream_one<Est, L, 0>(a, s);
+    return launch_stream_one<Est, L, 0, Fmt>(a, s);
   }
 }
 
-// The streaming kernel takes rows made of whole 16-byte-aligned tiles.
+// The streaming kernel takes rows made of whole tiles with every dense array
+// 16-byte aligned (a lane moves 16 bytes per DMA); for 16-bit formats the
+// row-value array must be 4-byte aligned and E even (row values travel as the
+// aligned word holding them).
+template <class Fmt = F32S>
 inline int stream_team(const KernelArgs& a) {
+  constexpr int ES = (int)sizeof(typename Fmt::T);
   int L = 0;
   if (a.T == 64) L = 16;
   else if (a.T == 128) L = 32;
   else if (a.T % 256 == 0) L = 64;
-  if (L == 0 || !vector_ok(a, 4, L * 4)) return 0;
+  if (L == 0 || !vector_ok(a, 16 / ES, L * 4, ES)) return 0;
   // flag bytes are fetched 16 at a time
   if ((uintptr_t)a.term % 16 != 0 || (uintptr_t)a.trunc % 16 != 0) return 0;
+  if (ES == 2 && ((uintptr_t)a.row % 4 != 0 || a.E % 2 != 0)) return 0;
   return L;
 }
 
@@ -269,7 +275,7 @@ template <class Est>
 hipError_t launch(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const int64_t len = segment_length(a)) return launch_segmented<Est>(a, s, len);
-  const int team = stream_team(a);
+  const int team = stream_team<F32S>(a);
   switch ((team != 0 && prefer_stream<Est>(a, team)) ? team : 0) {
     case 16: return launch_stream<Est, 16>(a, s);
     case 32: return launch_stream<Est, 32>(a, s);
@@ -289,12 +295,27 @@ hipError_t launch(const KernelArgs& in, hipStream_t s) {
   }
 }
 
-// Values stored as 16-bit bf16 / fp16 (S = Bf16S, F16S): the pipelined kernel,
-// or the segmented path for long rows (the streaming kernel moves fp32 only).
+// Values stored as 16-bit bf16 / fp16 (S = Bf16S, F16S): the segmented path
+// for long rows; the streaming kernel for traces and prefix sums where the
+// rows allow it and the float32 routing rule prefers it; else the pipelined
+// kernel.  At 16384 x 256 (bfloat16) the streaming kernel ran traces and
+// prefix sums in 8.7-9.3 us against 9.6-9.9 pipelined, but the five backward
+// estimators 0.5-1.9 us slower than pipelined: at this size a streaming block
+// walks only four items after a fill of up to four ticks, so halving the
+// bytes does not shorten it.
 template <class Est, class S>
 hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const int64_t len = segment_length(a)) return launch_segmented<Est, S>(a, s, len);
+  if constexpr (Traits<Est>::kForwardRl) {
+    const int team = stream_team<S>(a);
+    switch ((team != 0 && prefer_stream<Est>(a, team)) ? team : 0) {
+      case 16: return launch_stream<Est, 16, S>(a, s);
+      case 32: return launch_stream<Est, 32, S>(a, s);
+      case 64: return launch_stream<Est, 64, S>(a, s);
+      default: break;
+    }
+  }
   const LaunchShape sh = pick_shape_16<Est>(a.T);
   switch (sh.W * 1000 + sh.L * 10 + sh.K) {
     case 1000 + 160 + 8: return launch_shape<Est, 16, 8, 1, S>(a, s, sh);

@@ -103,9 +103,12 @@ constexpr int stream_nc_cap() {
   return 8;
 }
 
-template <class Est, bool FLAGS, int P_, int BPC>
+template <class Est, bool FLAGS, int P_, int BPC, class Fmt = F32S>
 struct StreamCfg {
   using Tr = Traits<Est>;
+  using ET = typename Fmt::T;                 // stored element type
+  static constexpr int ES = (int)sizeof(ET);  // bytes per stored value
+  static constexpr int IPD = 4 / ES;          // items per 16-byte-per-lane DMA (16-bit: two)
   static constexpr int NS = Tr::kStreams;
   static constexpr bool USE_FLAGS = FLAGS && Tr::kUsesFlags;
   static constexpr bool GATHER = USE_FLAGS && Tr::kBackwardRl;  // a gather wave
@@ -119,14 +122,16 @@ struct StreamCfg {
   static constexpr int kLdsBudget = 160 * 1024 / BPC;
   // LDS bytes for nc compute waves (16 bytes of slack per slot for padding)
   static constexpr int lds_bytes(int nc) {
-    const int slot = 4 * NS * nc * N + (GATHER ? 4 * nc * N : 0) + 16 * nc + 16;
+    const int slot = ES * NS * nc * N + (GATHER ? ES * nc * N : 0) + 16 * nc + 16;
     const int fslot = USE_FLAGS ? 2 * nc * N : 16;
     return S * slot + SF * fslot;
   }
   // DMA instructions per tick of the loader: flags (16 B per lane, four items
-  // per instruction and array), data (one per stream and item) and row values
+  // per instruction and array), data (one per stream and IPD items) and row
+  // values; and of the gather wave (one per IPD items)
   static constexpr int fops(int nc) { return USE_FLAGS ? 2 * ((nc + 3) / 4) : 0; }
-  static constexpr int dops(int nc) { return NS * nc + 1; }
+  static constexpr int dops(int nc) { return NS * ((nc + IPD - 1) / IPD) + 1; }
+  static constexpr int gops(int nc) { return (nc + IPD - 1) / IPD; }
   // most DMA instructions the loader ever has in flight: after the start-up
   // burst, and right after a steady-state issue
   static constexpr int max_inflight(int nc) {
@@ -137,7 +142,7 @@ struct StreamCfg {
   static constexpr int pick_nc() {
     int best = 1;
     for (int nc = 1; nc + kHelpers <= 16 && nc <= stream_nc_cap<Est>(); ++nc)
-      if (lds_bytes(nc) <= kLdsBudget && max_inflight(nc) <= 63 && (!GATHER || P * nc <= 63)) best = nc;
+      if (lds_bytes(nc) <= kLdsBudget && max_inflight(nc) <= 63 && (!GATHER || P * gops(nc) <= 63)) best = nc;
     return best;
   }
   static constexpr int NC = pick_nc();
@@ -147,13 +152,34 @@ struct StreamCfg {
   static_assert(max_inflight(NC) <= 63, "loader DMA in flight must fit the 6-bit counter");
 };
 
-// One tick's data for all compute waves of a block.
+// One tick's data for all compute waves of a block (values in the stored
+// format; a row value is the 4-byte word holding it).
 template <class Cfg>
 struct alignas(16) TickSlot {
-  float s[Cfg::NS][Cfg::NC][Cfg::N];
-  float tb[Cfg::GATHER ? Cfg::NC : 1][Cfg::GATHER ? Cfg::N : 1];
-  float rowv[Cfg::NC * 4];
+  typename Cfg::ET s[Cfg::NS][Cfg::NC][Cfg::N];
+  typename Cfg::ET tb[Cfg::GATHER ? Cfg::NC : 1][Cfg::GATHER ? Cfg::N : 1];
+  uint32_t rowv[Cfg::NC * 4];
 };
+
+// K = 4 stored values at an LDS element address, widened.
+template <class Fmt>
+__device__ __forceinline__ void lds_read4(const typename Fmt::T* q, float (&o)[4]) {
+  if constexpr (__is_same(Fmt, F32S)) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(q);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  } else {
+    const unsigned long long v = *reinterpret_cast<const unsigned long long*>(q);
+    const uint32_t w0 = (uint32_t)v, w1 = (uint32_t)(v >> 32);
+    o[0] = s_to_f32<Fmt>((uint16_t)w0); o[1] = s_to_f32<Fmt>((uint16_t)(w0 >> 16));
+    o[2] = s_to_f32<Fmt>((uint16_t)w1); o[3] = s_to_f32<Fmt>((uint16_t)(w1 >> 16));
+  }
+}
+
+// Address of element bidx + off of a value array of ES-byte elements.
+template <int ES>
+__device__ __forceinline__ const void* elem_addr(const float* base, int64_t bidx, uint32_t off) {
+  return reinterpret_cast<const char*>(base) + ES * bidx + (uint32_t)(off * (uint32_t)ES);
+}
 // One tick's flag bytes (terminated, truncated) for all compute waves.
 template <class Cfg>
 struct alignas(16) FlagTick {
@@ -200,14 +226,16 @@ __device__ __forceinline__ void stream_tile(const LaneIn<E2, K>& d, const ScanSc
 
 // Template parameters: estimator tag, team width L (16, 32 or 64 lanes per
 // row), OPT (bit 0: flags present; bit 1: second output), data lead P, blocks
-// per CU the LDS is split for.  Requires T % (4 L) == 0, L < 64 only when
-// T == 4 L, every dense array and flag array aligned to 16 bytes, and
-// T < 2^30 (checked by the C ABI).
-template <class Est, int L, int OPT, int P, int BPC>
-__global__ void __launch_bounds__((StreamCfg<Est, (OPT & 1) != 0, P, BPC>::kThreads))
+// per CU the LDS is split for, storage format.  Requires T % (4 L) == 0,
+// L < 64 only when T == 4 L, every dense array and flag array aligned to 16
+// bytes, and T < 2^30 (checked by the C ABI); 16-bit formats also need the
+// row-value array 4-byte aligned and E even (row values travel as the 4-byte
+// word holding them).
+template <class Est, int L, int OPT, int P, int BPC, class Fmt = F32S>
+__global__ void __launch_bounds__((StreamCfg<Est, (OPT & 1) != 0, P, BPC, Fmt>::kThreads))
 stream_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
-  using Cfg = StreamCfg<Est, (OPT & 1) != 0, P, BPC>;
+  using Cfg = StreamCfg<Est, (OPT & 1) != 0, P, BPC, Fmt>;
   using SlotT = TickSlot<Cfg>;
   using FlagT = FlagTick<Cfg>;
   constexpr int K = 4;
@@ -224,6 +252,9 @@ stream_kernel(const KernelArgs p) {
   constexpr bool GATHER = Cfg::GATHER;
   constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
   constexpr int FIRST_COMPUTE = Cfg::kHelpers;
+  constexpr int ES = Cfg::ES;    // bytes per stored value
+  constexpr int IPD = Cfg::IPD;  // items per 16-byte-per-lane DMA
+  static_assert(!Tr::kDual || ES == 4, "the two-output pass stores float32");
   static_assert(P >= 1 && P <= 4, "lead of one to four items");
   static_assert(NC * G <= 64, "one row-value DMA per tick");
   static_assert(S * sizeof(SlotT) + SF * sizeof(FlagT) <= (size_t)Cfg::kLdsBudget, "LDS rings");
@@ -301,25 +332,36 @@ stream_kernel(const KernelArgs p) {
         }
       }
     };
+    // data: one DMA per stream moves 16 bytes per lane, i.e. one float32 item
+    // (64 lanes x 4 values) or two 16-bit items (lanes 32..63 take the next
+    // compute wave's item, which follows in LDS)
     auto issue_data = [&](const Cursor& cur) __attribute__((always_inline)) {
       SlotT& sl = ring[cur.slot];
+      const int ci_off = IPD == 2 ? (lane >> 5) : 0;
+      const uint32_t li = IPD == 2 ? (uint32_t)(lane & 31) : (uint32_t)lane;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        int64_t base;
-        const int64_t rg = item_base(c, cur, base);
-        const uint32_t off = elem_off(rg, (uint32_t)lane * 4);
+      for (int c = 0; c < NC; c += IPD) {
+        const int ci = c + ci_off;
+        if (ci < NC) {  // (an odd NC leaves the upper half of the last 16-bit DMA idle)
+          int64_t base;
+          const int64_t rg = item_base(ci, cur, base);
+          const uint32_t off = elem_off(rg, li * (16 / ES));
 #pragma unroll
-        for (int st = 0; st < NS; ++st)
-          __builtin_amdgcn_global_load_lds((gbl_void_ptr)at(srcs[st] + base, off), (lds_void_ptr)&sl.s[st][c][0], 16,
-                                           0, 0);
+          for (int st = 0; st < NS; ++st)
+            __builtin_amdgcn_global_load_lds((gbl_void_ptr)elem_addr<ES>(srcs[st], base, off),
+                                             (lds_void_ptr)&sl.s[st][c][0], 16, 0, 0);
+        }
       }
-      // row values: lane c*G + g -> row g of compute wave c's item
+      // row values: lane c*G + g -> row g of compute wave c's item (16-bit: the
+      // aligned word holding it)
       if (lane < NC * G) {
         int64_t base;
         const int64_t rg = item_base(lane / G, cur, base);
         int64_t row = rg * G + lane % G;
         row = row < E ? row : E - 1;
-        __builtin_amdgcn_global_load_lds((gbl_void_ptr)(p.row + row), (lds_void_ptr)&sl.rowv[0], 4, 0, 0);
+        const void* src = ES == 4 ? (const void*)(p.row + row)
+                                  : (const void*)(reinterpret_cast<const uint32_t*>(p.row) + (row >> 1));
+        __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)&sl.rowv[0], 4, 0, 0);
       }
     };
     // start-up burst: flags of items 0..LF-1, then data of items 0..P-1
@@ -379,28 +421,40 @@ stream_kernel(const KernelArgs p) {
     // flags and DMAs the bootstrap chunk of every lane that has a truncated,
     // not terminated step.  Before the barrier that ends tick t, the gather
     // of item t+1 has landed.
-    constexpr int GO = NC;  // DMA instructions per served item-tick
+    constexpr int GO = Cfg::gops(NC);  // DMA instructions per served item-tick
     auto serve = [&](const Cursor& cur) __attribute__((always_inline)) {
       SlotT& sl = ring[cur.slot];
       const FlagT& fs = fring[cur.fslot];
+      // the same lane -> item mapping as the data DMA: a lane covers 16 / ES steps
+      const int ci_off = IPD == 2 ? (lane >> 5) : 0;
+      const uint32_t li = IPD == 2 ? (uint32_t)(lane & 31) : (uint32_t)lane;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        int64_t base;
-        const int64_t rg = item_base(c, cur, base);
-        const unsigned w_t = reinterpret_cast<const unsigned*>(&fs.fl[0][c][0])[lane];
-        const unsigned w_r = reinterpret_cast<const unsigned*>(&fs.fl[1][c][0])[lane];
-        // some step truncated and not terminated (nonzero byte of w_r over a zero byte of w_t)
-        const unsigned m_t = w_t & (p.has_term ? ~0u : 0u);
-        const unsigned m_r = w_r & (p.has_trunc ? ~0u : 0u);
-        const unsigned nz_t = (((m_t & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_t) & 0x80808080u;
-        const unsigned nz_r = (((m_r & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_r) & 0x80808080u;
-        const bool need = (nz_r & ~nz_t) != 0u && p.has_tboot;
-        // lanes without a bootstrap to fetch re-read their chunk of rewards,
-        // which the loader fetched P ticks ago (an L2 hit spread over the
-        // channels like the data itself; one shared address for every lane of
-        // the GPU made a single L2 channel the bottleneck)
-        const float* src = at((need ? p.tboot : p.r) + base, elem_off(rg, (uint32_t)lane * 4));
-        __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)&sl.tb[c][0], 16, 0, 0);
+      for (int c = 0; c < NC; c += IPD) {
+        const int ci = c + ci_off;
+        if (ci < NC) {
+          int64_t base;
+          const int64_t rg = item_base(ci, cur, base);
+          // some step truncated and not terminated (a nonzero truncated byte over
+          // a zero terminated byte), over the lane's flag words
+          unsigned nz = 0;
+#pragma unroll
+          for (int h = 0; h < 4 / ES; ++h) {
+            const unsigned w_t = reinterpret_cast<const unsigned*>(&fs.fl[0][ci][0])[li * (4 / ES) + h];
+            const unsigned w_r = reinterpret_cast<const unsigned*>(&fs.fl[1][ci][0])[li * (4 / ES) + h];
+            const unsigned m_t = w_t & (p.has_term ? ~0u : 0u);
+            const unsigned m_r = w_r & (p.has_trunc ? ~0u : 0u);
+            const unsigned nz_t = (((m_t & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_t) & 0x80808080u;
+            const unsigned nz_r = (((m_r & 0x7f7f7f7fu) + 0x7f7f7f7fu) | m_r) & 0x80808080u;
+            nz |= nz_r & ~nz_t;
+          }
+          const bool need = nz != 0u && p.has_tboot;
+          // lanes without a bootstrap to fetch re-read their chunk of rewards,
+          // which the loader fetched P ticks ago (an L2 hit spread over the
+          // channels like the data itself; one shared address for every lane of
+          // the GPU made a single L2 channel the bottleneck)
+          const void* src = elem_addr<ES>(need ? p.tboot : p.r, base, elem_off(rg, li * (16 / ES)));
+          __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)&sl.tb[c][0], 16, 0, 0);
+        }
       }
     };
     // gathers allowed in flight at the end of tick w: those of items w+2 .. min(w+LG, ticks-1)
@@ -459,18 +513,22 @@ stream_kernel(const KernelArgs p) {
 
       LaneIn<Est, K> d;
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&sl.s[st][c][lds_idx]);
-        d.s[st][0] = v.x; d.s[st][1] = v.y; d.s[st][2] = v.z; d.s[st][3] = v.w;
-      }
+      for (int st = 0; st < NS; ++st) lds_read4<Fmt>(&sl.s[st][c][lds_idx], d.s[st]);
       if constexpr (GATHER) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&sl.tb[c][lds_idx]);
-        d.tb[0] = v.x; d.tb[1] = v.y; d.tb[2] = v.z; d.tb[3] = v.w;
+        lds_read4<Fmt>(&sl.tb[c][lds_idx], d.tb);
       } else {
 #pragma unroll
         for (int m = 0; m < K; ++m) d.tb[m] = 0.0f;
       }
-      d.rowv = sl.rowv[c * G + team];
+      {
+        const uint32_t wv = sl.rowv[c * G + team];
+        if constexpr (ES == 4) {
+          d.rowv = __builtin_bit_cast(float, wv);
+        } else {
+          const int64_t rw = row_ok ? row : E - 1;  // the row the loader fetched
+          d.rowv = s_to_f32<Fmt>((uint16_t)((rw & 1) ? (wv >> 16) : wv));
+        }
+      }
       unsigned tbits = 0, rbits = 0;
       if constexpr (USE_FLAGS) {
         const FlagT& fs = fring[cur.fslot];
@@ -510,8 +568,8 @@ stream_kernel(const KernelArgs p) {
       if (row_ok) {
         const int64_t eb = rg * G * T;  // element index of the item's first row
         const uint32_t off = (uint32_t)team * T32 + cs;
-        store_chunk<K, true>(p.out0 + eb, off, K, o0);
-        if constexpr (OUT1) store_chunk<K, true>(p.out1 + eb, off, K, o1);
+        store_s<Fmt, K, true>(p.out0, eb, off, K, o0);
+        if constexpr (OUT1) store_s<Fmt, K, true>(p.out1, eb, off, K, o1);
       }
       wait_lgkm0();
       tick_barrier();

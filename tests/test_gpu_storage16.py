@@ -12,9 +12,11 @@ to the format, both to nearest even, so (``estimators.check_storage``):
   way; the rest (a float64 result within a few ulps of a rounding midpoint)
   differ by one unit in the last place.
 
-Shapes cover the vector path (whole tiles, aligned), ragged rows, short rows
-sharing a wave, multi-wave rows, long rows on the segmented path, absent
-optional inputs and arrays whose base is only 2-byte aligned.
+Shapes cover the streaming kernel (traces and prefix sums; whole tiles,
+16-byte aligned, E even), the pipelined kernel's vector path and element path
+(ragged rows, odd E, arrays whose base is only 2-byte aligned), short rows
+sharing a wave, multi-wave rows, long rows on the segmented path and absent
+optional inputs.
 """
 from __future__ import annotations
 
@@ -38,7 +40,7 @@ def _say(*a):
 
 @pytest.mark.parametrize("fmt", ["bfloat16", "float16"])
 @pytest.mark.parametrize("E,T", [(1, 1), (3, 5), (256, 128), (100, 256), (37, 1000), (64, 1024), (513, 300),
-                                 (64, 64)])
+                                 (64, 64), (33, 256), (2000, 256), (1000, 128), (998, 64)])
 def test_storage16_all_estimators(fmt, E, T):
     _say("16-bit storage %s E=%d T=%d" % (fmt, E, T))
     d = synth.draw(E, T, seed=70 + T, p_term=0.01, p_trunc=0.01)
