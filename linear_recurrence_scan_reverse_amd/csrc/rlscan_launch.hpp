@@ -3,6 +3,8 @@
 // and launches one kernel on the caller's stream.
 #pragma once
 
+#include <atomic>
+
 #include "rlscan_kernel.hpp"
 #include "rlscan_segment.hpp"
 #include "rlscan_stream.hpp"
@@ -83,10 +85,21 @@ inline KernelArgs resolve_optional(KernelArgs a) {
   return a;
 }
 
+// Compute units of the current device, queried once per device (grids are
+// sized from it on every call).
 inline int cu_count() {
-  int dev = 0, n = 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  if (cached) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
