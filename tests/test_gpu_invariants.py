@@ -255,3 +255,47 @@ def test_graph_capture_of_formats_layouts_and_long_rows():
         for a, b in zip(outs, eager):
             assert torch.equal(a.cpu().view(torch.int16) if a.element_size() == 2 else a.cpu(),
                                b.view(torch.int16) if b.element_size() == 2 else b), rep
+
+
+def test_concurrent_host_threads():
+    # the library keeps no state between calls (a per-device compute-unit count
+    # aside): four host threads, each on its own stream, calling different
+    # estimators and formats at once give the single-threaded results bit for bit
+    import threading
+
+    import torch
+    from tests.estimators import storage_inputs
+    d = synth.draw(700, 256, seed=31, p_term=0.01, p_trunc=0.01)
+    jobs = [("gae", "float32", False), ("retrace", "float32", False), ("vtrace", "bfloat16", False),
+            ("td_lambda", "float16", True)]
+    inputs = [storage_inputs(d, fmt, time_major=tm)[1] for _, fmt, tm in jobs]
+
+    def raw(outs):
+        return {k: v.cpu().view(torch.int16 if v.element_size() == 2 else torch.int32) for k, v in outs.items()}
+
+    ref = [raw(run_gpu(name, dev, time_major=tm)) for (name, _, tm), dev in zip(jobs, inputs)]
+    torch.cuda.synchronize()
+    results = [None] * len(jobs)
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = None
+                for _ in range(20):
+                    outs = run_gpu(jobs[i][0], inputs[i], time_major=jobs[i][2])
+                s.synchronize()
+                results[i] = raw(outs)
+        except Exception as ex:  # reported below
+            errors.append(repr(ex))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i, (r, g) in enumerate(zip(ref, results)):
+        for k in r:
+            assert torch.equal(r[k], g[k]), (jobs[i], k)
