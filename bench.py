@@ -5,7 +5,7 @@
 A step is one pass of all seven estimators (discounted returns, TD(lambda),
 GAE, V-trace vs + pg, Retrace, eligibility traces, episodic prefix sums) over
 one synthetic rollout batch of E = 16384 envs x T = 256 steps, each estimator
-one kernel launch through the C ABI.  Inputs are resident in HBM before the
+one call (one kernel) through the C ABI, back to back on one stream.  Inputs are resident in HBM before the
 timed region.  To keep the 256 MB Infinity Cache from serving repeat reads,
 calls rotate through buffer sets totalling > 1 GiB, so every launch reads cold
 data.

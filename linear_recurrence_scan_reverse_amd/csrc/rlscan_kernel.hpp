@@ -1,6 +1,6 @@
 // rlscan_kernel.hpp -- device side of librlscan (gfx950 / CDNA4, wave64).
 //
-// One kernel template solves every estimator as an affine scan.  The method
+// The pipelined kernel template solves every estimator as an affine scan.  The method
 // (rl-triton; gist.science summary, "Methodologie" sections 1-2): each step t
 // contributes a pair (a_t, b_t) such that x_t = a_t x_{t+1} + b_t (backward)
 // or x_t = a_t x_{t-1} + b_t (forward); pairs compose associatively,
@@ -32,8 +32,11 @@
 //     branch-free: out-of-range elements read a clamped in-row address and
 //     are masked in registers, so the compiler can count outstanding loads
 //     exactly.
-// All scan arithmetic is float64; inputs are float32 and each output is
-// rounded once.
+// All scan arithmetic is float64; inputs are float32 (or bfloat16 / float16,
+// widened exactly) and each output is rounded to float32 once (then to the
+// 16-bit format).  The per-lane code below (pairs, fold, re-walk, epilogue)
+// is shared by every kernel of the library: this pipelined kernel, the
+// streaming kernel, the segmented long-row path and the time-major kernel.
 #pragma once
 
 #include <hip/hip_runtime.h>

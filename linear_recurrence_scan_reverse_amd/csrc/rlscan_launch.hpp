@@ -1,6 +1,8 @@
-// rlscan_launch.hpp -- host-side launch of the scan kernel: resolves optional
-// inputs, picks the team shape for a row length T, sizes a persistent grid
-// and launches one kernel on the caller's stream.
+// rlscan_launch.hpp -- host-side launch of the scan kernels: resolves optional
+// inputs, routes a call to one of the kernels (streaming, pipelined,
+// segmented for long rows, time-major), picks its team shape, sizes its grid
+// and launches it on the caller's stream (one kernel; three for the
+// segmented path).
 #pragma once
 
 #include <atomic>
