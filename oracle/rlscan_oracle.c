@@ -29,7 +29,10 @@
  *                          forward in time (the forward-time mirror named in
  *                          the same gist.science section)
  *       episodic prefix    S_t = S_{t-1} + x_t, forward, reset per episode
- *       generic scan       x_t = a_t x_{t+1} + b_t  (or forward mirror)
+ *       generic scan       x_t = a_t x_{t+1} + b_t  (or forward mirror), and
+ *                          the same recurrence cut at flagged steps
+ *       vector traces      the eligibility trace of every column of an
+ *                          [E,T,D] feature array, with the row's flags
  *   - Episode boundaries follow gist.science "Methodologie" section 3
  *     (Expliciete Boundary Semantiek): a terminated step has successor value
  *     zero; a truncated step uses a supplied bootstrap value; the rollout
@@ -42,6 +45,17 @@
  *       * NULL flag arrays mean "no flags"; NULL bootstrap arrays mean 0;
  *       * forward estimators reset after any terminated-or-truncated step
  *         and take init[e] as the value before t = 0 (NULL -> 0).
+ *
+ * Pins (tests that check this file against something other than itself):
+ * independent direct sums over every flag pattern of short rows and over
+ * random rows (every function); closed forms (constant-reward returns,
+ * unit-signal traces, integer prefix sums, degenerate generic scans);
+ * reductions between estimators (GAE at lambda 0 and 1, TD(lambda) - V =
+ * GAE, TD(1) = discounted return, on-policy V-trace = TD(lambda), Retrace at
+ * lambda 0 and on-policy); hand-worked examples; per-column equality of the
+ * vector traces with the scalar traces; and planted mistakes that each of
+ * these must catch.  No function is left without a pin.  The readings above
+ * are pinned only to themselves: the pages do not fix them.
  *
  * Precision: inputs are fp32 and are upcast exactly; parameters arrive as
  * float (as in the GPU ABI) and are upcast exactly; all arithmetic is IEEE
