@@ -245,9 +245,9 @@ rlscan_status rlscan_linear_scan_segmented(const float *a, const float *b, const
                                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Storage format and layout.  The seven estimators again, each with two more
- * leading arguments; every other argument means what it means for the
- * float32 entry of the same name.
+ * Storage format and layout.  The seven estimators and the generic scan
+ * again, each with two more leading arguments; every other argument means
+ * what it means for the float32 entry of the same name.
  *
  * fmt     The type of every value array (inputs, bootstraps, init and
  *         outputs): float32, bfloat16 or float16.  16-bit storage halves the
@@ -318,6 +318,14 @@ rlscan_status rlscan_eligibility_traces_ex(rlscan_format fmt, rlscan_layout layo
 rlscan_status rlscan_episodic_prefix_sum_ex(rlscan_format fmt, rlscan_layout layout, const void *x,
                                             const uint8_t *terminated, const uint8_t *truncated, const void *init,
                                             void *sums, int64_t E, int64_t T, hipStream_t stream);
+
+/* The generic recurrence with episode cuts (rlscan_linear_scan_segmented;
+ * done = NULL gives rlscan_linear_scan) in a storage format and layout: a, b,
+ * carry and x in format fmt, a, b, done and x in the layout (carry stays
+ * [E]). */
+rlscan_status rlscan_linear_scan_segmented_ex(rlscan_format fmt, rlscan_layout layout, const void *a, const void *b,
+                                              const uint8_t *done, const void *carry, void *x, int64_t E, int64_t T,
+                                              int reverse, hipStream_t stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

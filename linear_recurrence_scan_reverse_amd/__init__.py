@@ -58,7 +58,7 @@ _SIGNATURES = {
 # entry's arguments.
 _EX = ("rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_gae", "rlscan_vtrace", "rlscan_retrace",
        "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum")
-for _n in _EX:
+for _n in _EX + ("rlscan_linear_scan_segmented",):
     _SIGNATURES[_n + "_ex"] = [_int, _int] + _SIGNATURES[_n]
 del _n
 
@@ -374,32 +374,35 @@ def episodic_prefix_sum(x, terminated=None, truncated=None, init=None, *, time_m
     return out
 
 
-def linear_scan(a, b, carry=None, *, reverse=True, out=None, stream=None):
+def linear_scan(a, b, carry=None, *, reverse=True, time_major=False, out=None, stream=None):
     """The generic recurrence x_t = a_t x_{t+1} + b_t (reverse) or x_t = a_t x_{t-1} + b_t."""
-    shape, dev = _prep(a, "a")
-    E, T = shape
-    aa = _check_f32(a, "a", shape, dev)
-    bb = _check_f32(b, "b", shape, dev)
-    c0 = _check_f32(carry, "carry", (E,), dev)
-    out = _out(out, "out", shape, dev)
-    _call("rlscan_linear_scan", _ptr(aa), _ptr(bb), _ptr(c0), _ptr(out), E, T, 1 if reverse else 0,
-          _stream(dev, stream))
-    return out
+    return linear_scan_segmented(a, b, None, carry, reverse=reverse, time_major=time_major, out=out,
+                                 stream=stream)
 
 
-def linear_scan_segmented(a, b, done=None, carry=None, *, reverse=True, out=None, stream=None):
+def linear_scan_segmented(a, b, done=None, carry=None, *, reverse=True, time_major=False, out=None,
+                          stream=None):
     """The generic recurrence cut into episodes: a step flagged in ``done`` breaks
     the chain (backward: nothing enters it from t+1; forward: the next step
-    starts afresh)."""
+    starts afresh).  float32, bfloat16 or float16 values (the dtype of ``a``);
+    ``time_major`` takes [T, E] arrays."""
     shape, dev = _prep(a, "a")
-    E, T = shape
-    aa = _check_f32(a, "a", shape, dev)
-    bb = _check_f32(b, "b", shape, dev)
+    E, T = _dims(shape, time_major)
+    dt = _storage(a, "a")
+    aa = _check_val(a, "a", shape, dev, dt)
+    bb = _check_val(b, "b", shape, dev, dt)
     dn = _check_flags(done, "done", shape, dev)
-    c0 = _check_f32(carry, "carry", (E,), dev)
-    out = _out(out, "out", shape, dev)
-    _call("rlscan_linear_scan_segmented", _ptr(aa), _ptr(bb), _ptr(dn), _ptr(c0), _ptr(out), E, T,
-          1 if reverse else 0, _stream(dev, stream))
+    c0 = _check_val(carry, "carry", (E,), dev, dt)
+    out = _out(out, "out", shape, dev, dt)
+    args = (_ptr(aa), _ptr(bb), _ptr(dn), _ptr(c0), _ptr(out), E, T, 1 if reverse else 0, _stream(dev, stream))
+    if str(dt) == "torch.float32" and not time_major:
+        if dn is None:
+            _call("rlscan_linear_scan", args[0], args[1], args[3], args[4], *args[5:])
+        else:
+            _call("rlscan_linear_scan_segmented", *args)
+    else:
+        _call("rlscan_linear_scan_segmented_ex", _FORMATS[str(dt).replace("torch.", "")],
+              1 if time_major else 0, *args)
     return out
 
 

@@ -321,6 +321,35 @@ rlscan_status impl_forward(rlscan_format f, rlscan_layout l, bool traces, const 
                          : launch_fmt<rlscan::EpisodicPrefixSum>(f, l, a, stream));
 }
 
+// The generic recurrence, optionally cut by a done array (rlscan_linear_scan
+// passes none).
+rlscan_status impl_linear_scan(rlscan_format f, rlscan_layout l, const void* a_coef, const void* b_coef,
+                               const uint8_t* done, const void* carry, void* x, int64_t E, int64_t T, int reverse,
+                               hipStream_t stream) {
+  const int es = elem_size(f);
+  rlscan_status st = check_shape(E, T);
+  if (st != RLSCAN_OK) return st;
+  if (es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
+  if (E * T == 0) return RLSCAN_OK;
+  if (!a_coef || !b_coef || !x) return RLSCAN_ERR_NULL;
+  if (misaligned(a_coef, es) || misaligned(b_coef, es) || misaligned(carry, es)) return RLSCAN_ERR_ALIGN;
+  Io io;
+  io.add_in(a_coef, es * E * T);
+  io.add_in(b_coef, es * E * T);
+  io.add_in(done, E * T);
+  io.add_in(carry, es * E);
+  io.add_out(x);
+  if ((st = check_io(io, E, T, es)) != RLSCAN_OK) return st;
+  KernelArgs a = blank(E, T);
+  a.r = fp(a_coef);
+  a.v = fp(b_coef);
+  a.term = done;
+  a.row = fp(carry);
+  a.out0 = fp(x);
+  return reverse ? launched(launch_fmt<rlscan::LinearScanReverse>(f, l, a, stream))
+                 : launched(launch_fmt<rlscan::LinearScanForward>(f, l, a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -487,49 +516,21 @@ rlscan_status rlscan_episodic_prefix_sum_ex(rlscan_format fmt, rlscan_layout lay
 
 rlscan_status rlscan_linear_scan(const float* a_coef, const float* b_coef, const float* carry, float* x,
                                  int64_t E, int64_t T, int reverse, hipStream_t stream) {
-  rlscan_status st = check_shape(E, T);
-  if (st != RLSCAN_OK) return st;
-  if (E * T == 0) return RLSCAN_OK;
-  if (!a_coef || !b_coef || !x) return RLSCAN_ERR_NULL;
-  if (misaligned(a_coef) || misaligned(b_coef) || misaligned(carry)) return RLSCAN_ERR_ALIGN;
-  Io io;
-  io.add_in(a_coef, 4 * E * T);
-  io.add_in(b_coef, 4 * E * T);
-  io.add_in(carry, 4 * E);
-  io.add_out(x);
-  if ((st = check_io(io, E, T)) != RLSCAN_OK) return st;
-  KernelArgs a = blank(E, T);
-  a.r = a_coef;
-  a.v = b_coef;
-  a.row = carry;
-  a.out0 = x;
-  return reverse ? launched(rlscan::launch<rlscan::LinearScanReverse>(a, stream))
-                 : launched(rlscan::launch<rlscan::LinearScanForward>(a, stream));
+  return impl_linear_scan(RLSCAN_FORMAT_F32, RLSCAN_LAYOUT_ENV_MAJOR, a_coef, b_coef, nullptr, carry, x, E, T,
+                          reverse, stream);
 }
 
 rlscan_status rlscan_linear_scan_segmented(const float* a_coef, const float* b_coef, const uint8_t* done,
                                            const float* carry, float* x, int64_t E, int64_t T, int reverse,
                                            hipStream_t stream) {
-  rlscan_status st = check_shape(E, T);
-  if (st != RLSCAN_OK) return st;
-  if (E * T == 0) return RLSCAN_OK;
-  if (!a_coef || !b_coef || !x) return RLSCAN_ERR_NULL;
-  if (misaligned(a_coef) || misaligned(b_coef) || misaligned(carry)) return RLSCAN_ERR_ALIGN;
-  Io io;
-  io.add_in(a_coef, 4 * E * T);
-  io.add_in(b_coef, 4 * E * T);
-  io.add_in(done, E * T);
-  io.add_in(carry, 4 * E);
-  io.add_out(x);
-  if ((st = check_io(io, E, T)) != RLSCAN_OK) return st;
-  KernelArgs a = blank(E, T);
-  a.r = a_coef;
-  a.v = b_coef;
-  a.term = done;
-  a.row = carry;
-  a.out0 = x;
-  return reverse ? launched(rlscan::launch<rlscan::LinearScanReverse>(a, stream))
-                 : launched(rlscan::launch<rlscan::LinearScanForward>(a, stream));
+  return impl_linear_scan(RLSCAN_FORMAT_F32, RLSCAN_LAYOUT_ENV_MAJOR, a_coef, b_coef, done, carry, x, E, T,
+                          reverse, stream);
+}
+
+rlscan_status rlscan_linear_scan_segmented_ex(rlscan_format fmt, rlscan_layout layout, const void* a_coef,
+                                              const void* b_coef, const uint8_t* done, const void* carry, void* x,
+                                              int64_t E, int64_t T, int reverse, hipStream_t stream) {
+  return impl_linear_scan(fmt, layout, a_coef, b_coef, done, carry, x, E, T, reverse, stream);
 }
 
 rlscan_status rlscan_eligibility_traces_vec(const float* x, const uint8_t* terminated, const uint8_t* truncated,

@@ -416,6 +416,8 @@ RLSCAN_TYPED_EXTERN(Vtrace)
 RLSCAN_TYPED_EXTERN(Retrace)
 RLSCAN_TYPED_EXTERN(EligibilityTrace)
 RLSCAN_TYPED_EXTERN(EpisodicPrefixSum)
+RLSCAN_TYPED_EXTERN(LinearScanReverse)
+RLSCAN_TYPED_EXTERN(LinearScanForward)
 #undef RLSCAN_TYPED_EXTERN
 
 }  // namespace rlscan

@@ -165,39 +165,47 @@ def check_storage(name, d, fmt="float32", time_major=False, misalign=False, P=No
     differ by one unit in the last place (or, near 0, by no more than the fp32
     gate).  Returns the worst error."""
     import torch
-    dt = getattr(torch, fmt)
     host, dev = storage_inputs(d, fmt, time_major, misalign)
     got = run_gpu(name, dev, P, time_major=time_major, **variant)
     torch.cuda.synchronize()
     ref = run_oracle(name, host, P, **variant)
-    tol = (UNIT_ROUNDOFF[fmt] if fmt != "float32" else 0.0) + TOL
     worst = 0.0
     for k, r in ref.items():
         g = got[k]
-        assert g.dtype == dt, (name, k, g.dtype)
         if time_major:
             g = g.t().contiguous()
-        gf = g.float().cpu().numpy()
-        err = parity_err(gf, r)
-        worst = max(worst, err)
-        assert err <= tol, "%s %s tm=%s %s: err %.3g > %.3g" % (name, fmt, time_major, k, err, tol)
-        if fmt == "float32" or r.size == 0:
-            continue
-        exp16 = torch.from_numpy(np.asarray(r, dtype=np.float64).astype(np.float32)).to(dt)
-        gb = g.cpu().view(torch.int16).numpy().astype(np.int32)
-        eb = exp16.view(torch.int16).numpy().astype(np.int32)
-        diff = gb != eb
-        nd = int(diff.sum())
-        assert nd <= max(2, 1e-3 * diff.size), "%s %s %s: %d of %d outputs differ from the rounded oracle" % (
-            name, fmt, k, nd, diff.size)
-        if diff.any():
-            # adjacent encodings (one unit in the last place), or a result so
-            # close to 0 that the kernel's fp32-level error (the 1e-5 gate, e.g.
-            # V-trace's fp32 exp) spans several of the format's units there
-            adjacent = np.abs(gb[diff] - eb[diff]) == 1
-            small = np.abs(gf[diff] - r[diff]) <= TOL * np.maximum(1.0, np.abs(r[diff]))
-            assert np.all(adjacent | small), (name, fmt, k)
+        worst = max(worst, check_rounded(g, r, fmt, "%s %s tm=%s %s" % (name, fmt, time_major, k)))
     return worst
+
+
+def check_rounded(g, r, fmt, label):
+    """One output tensor g (device or host, storage dtype) against the fp64
+    oracle r: the error gate, and (16-bit formats) bit agreement with r rounded
+    fp64 -> fp32 -> format.  Returns the error."""
+    import torch
+    dt = getattr(torch, fmt)
+    assert g.dtype == dt, (label, g.dtype)
+    gf = g.float().cpu().numpy()
+    tol = (UNIT_ROUNDOFF[fmt] if fmt != "float32" else 0.0) + TOL
+    err = parity_err(gf, r)
+    assert err <= tol, "%s: err %.3g > %.3g" % (label, err, tol)
+    if fmt == "float32" or r.size == 0:
+        return err
+    exp16 = torch.from_numpy(np.asarray(r, dtype=np.float64).astype(np.float32)).to(dt)
+    gb = g.cpu().view(torch.int16).numpy().astype(np.int32)
+    eb = exp16.view(torch.int16).numpy().astype(np.int32)
+    diff = gb != eb
+    nd = int(diff.sum())
+    assert nd <= max(2, 1e-3 * diff.size), "%s: %d of %d outputs differ from the rounded oracle" % (
+        label, nd, diff.size)
+    if diff.any():
+        # adjacent encodings (one unit in the last place), or a result so
+        # close to 0 that the kernel's fp32-level error (the 1e-5 gate, e.g.
+        # V-trace's fp32 exp) spans several of the format's units there
+        adjacent = np.abs(gb[diff] - eb[diff]) == 1
+        small = np.abs(gf[diff] - r[diff]) <= TOL * np.maximum(1.0, np.abs(r[diff]))
+        assert np.all(adjacent | small), label
+    return err
 
 
 def compare(name, d, P=None, device="cuda", **variant):

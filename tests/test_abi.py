@@ -44,7 +44,7 @@ def test_header_declares_the_expected_entry_points():
               "rlscan_linear_scan", "rlscan_linear_scan_segmented", "rlscan_eligibility_traces_vec",
               "rlscan_discounted_returns_ex", "rlscan_td_lambda_ex", "rlscan_gae_ex",
               "rlscan_vtrace_ex", "rlscan_retrace_ex", "rlscan_eligibility_traces_ex",
-              "rlscan_episodic_prefix_sum_ex", "rlscan_status_string",
+              "rlscan_episodic_prefix_sum_ex", "rlscan_linear_scan_segmented_ex", "rlscan_status_string",
               "rlscan_version"]:
         assert n in names
 
@@ -218,6 +218,13 @@ def test_ex_entries_validation(lib, lay):
                                      S) == ERR_NULL
         assert lib.rlscan_eligibility_traces_ex(fmt, lay, A, None, None, F + 1, C, E, T, 0.9, 0.9, S) == ERR_ALIGN
         assert lib.rlscan_episodic_prefix_sum_ex(fmt, lay, A, None, None, None, A + 2, E, T, S) == ERR_ALIAS
+    lsx = lib.rlscan_linear_scan_segmented_ex
+    assert lsx(9, lay, A, B, None, None, C, E, T, 1, S) == ERR_PARAM
+    assert lsx(BF16, 3, A, B, None, None, C, E, T, 1, S) == ERR_PARAM
+    assert lsx(BF16, lay, A + 1, B, None, None, C, E, T, 1, S) == ERR_ALIGN
+    assert lsx(F16, lay, A, None, None, None, C, E, T, 0, S) == ERR_NULL
+    assert lsx(F16, lay, A, B, D, None, D + E * T - 2, E, T, 0, S) == ERR_ALIAS  # output over the flags
+    assert lsx(BF16, lay, None, None, None, None, None, 0, T, 1, S) == OK
     # the float32 format through the _ex entry keeps the 4-byte rules
     assert gae(F32, A + 2, B, None, None, None, None, C, None, E, T, 0.99, 0.95, S) == ERR_ALIGN
     assert gae(F32, A, B, None, None, None, None, A + 4 * E * T - 4, None, E, T, 0.99, 0.95, S) == ERR_ALIAS
