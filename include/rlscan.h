@@ -245,8 +245,8 @@ rlscan_status rlscan_linear_scan_segmented(const float *a, const float *b, const
                                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Storage format and layout.  The seven estimators and the generic scan
- * again, each with two more leading arguments; every other argument means
+ * Storage format and layout.  The seven estimators, the two-output pass and
+ * the generic scan again, each with two more leading arguments; every other argument means
  * what it means for the float32 entry of the same name.
  *
  * fmt     The type of every value array (inputs, bootstraps, init and
@@ -292,6 +292,13 @@ rlscan_status rlscan_td_lambda_ex(rlscan_format fmt, rlscan_layout layout, const
                                   const uint8_t *terminated, const uint8_t *truncated, const void *bootstrap_value,
                                   const void *trunc_bootstrap, void *returns, int64_t E, int64_t T, float gamma,
                                   float lambda, hipStream_t stream);
+
+/* (16-bit or time-major calls run the two single-output kernels in turn.) */
+rlscan_status rlscan_returns_and_td_lambda_ex(rlscan_format fmt, rlscan_layout layout, const void *rewards,
+                                             const void *values, const uint8_t *terminated,
+                                             const uint8_t *truncated, const void *bootstrap_value,
+                                             const void *trunc_bootstrap, void *returns, void *td_returns, int64_t E,
+                                             int64_t T, float gamma, float lambda, hipStream_t stream);
 
 rlscan_status rlscan_gae_ex(rlscan_format fmt, rlscan_layout layout, const void *rewards, const void *values,
                             const uint8_t *terminated, const uint8_t *truncated, const void *bootstrap_value,

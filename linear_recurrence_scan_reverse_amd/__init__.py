@@ -56,8 +56,8 @@ _SIGNATURES = {
 }
 # The _ex entries take the storage format and the layout first, then the float32
 # entry's arguments.
-_EX = ("rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_gae", "rlscan_vtrace", "rlscan_retrace",
-       "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum")
+_EX = ("rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_returns_and_td_lambda", "rlscan_gae",
+       "rlscan_vtrace", "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum")
 for _n in _EX + ("rlscan_linear_scan_segmented",):
     _SIGNATURES[_n + "_ex"] = [_int, _int] + _SIGNATURES[_n]
 del _n
@@ -258,24 +258,25 @@ def td_lambda(rewards, values, terminated=None, truncated=None, bootstrap_value=
 
 
 def returns_and_td_lambda(rewards, values, terminated=None, truncated=None, bootstrap_value=None,
-                          trunc_bootstrap=None, *, gamma=0.99, lam=0.95, returns=None, td_returns=None,
-                          stream=None):
+                          trunc_bootstrap=None, *, time_major=False, gamma=0.99, lam=0.95, returns=None,
+                          td_returns=None, stream=None):
     """Discounted returns and TD(lambda) returns of one rollout in one pass.
 
     Returns (returns, td_returns), equal to ``discounted_returns`` and
     ``td_lambda`` with the same arguments."""
     shape, dev = _prep(rewards, "rewards")
-    E, T = shape
-    r = _check_f32(rewards, "rewards", shape, dev)
-    v = _check_f32(values, "values", shape, dev)
+    E, T = _dims(shape, time_major)
+    dt = _storage(rewards, "rewards")
+    r = _check_val(rewards, "rewards", shape, dev, dt)
+    v = _check_val(values, "values", shape, dev, dt)
     te = _check_flags(terminated, "terminated", shape, dev)
     tr = _check_flags(truncated, "truncated", shape, dev)
-    bv = _check_f32(bootstrap_value, "bootstrap_value", (E,), dev)
-    tb = _check_f32(trunc_bootstrap, "trunc_bootstrap", shape, dev)
-    returns = _out(returns, "returns", shape, dev)
-    td_returns = _out(td_returns, "td_returns", shape, dev)
-    _call("rlscan_returns_and_td_lambda", _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(tb),
-          _ptr(returns), _ptr(td_returns), E, T, float(gamma), float(lam), _stream(dev, stream))
+    bv = _check_val(bootstrap_value, "bootstrap_value", (E,), dev, dt)
+    tb = _check_val(trunc_bootstrap, "trunc_bootstrap", shape, dev, dt)
+    returns = _out(returns, "returns", shape, dev, dt)
+    td_returns = _out(td_returns, "td_returns", shape, dev, dt)
+    _entry("rlscan_returns_and_td_lambda", dt, time_major, _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv),
+           _ptr(tb), _ptr(returns), _ptr(td_returns), E, T, float(gamma), float(lam), _stream(dev, stream))
     return returns, td_returns
 
 

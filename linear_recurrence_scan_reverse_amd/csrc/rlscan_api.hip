@@ -182,6 +182,50 @@ rlscan_status impl_td_lambda(rlscan_format f, rlscan_layout l, const void* rewar
   return launched(launch_fmt<rlscan::TdLambda>(f, l, a, stream));
 }
 
+// Discounted and TD(lambda) returns: one fused pass for float32 [E,T] rows the
+// streaming kernel takes, else the two single-output calls in turn.
+rlscan_status impl_returns_td_lambda(rlscan_format f, rlscan_layout l, const void* rewards, const void* values,
+                                     const uint8_t* terminated, const uint8_t* truncated, const void* bootstrap_value,
+                                     const void* trunc_bootstrap, void* returns, void* td_returns, int64_t E, int64_t T,
+                                     float gamma, float lambda, hipStream_t stream) {
+  const int es = elem_size(f);
+  rlscan_status st = check_shape(E, T);
+  if (st != RLSCAN_OK) return st;
+  if (!in_unit(gamma) || !in_unit(lambda) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
+  if (E * T == 0) return RLSCAN_OK;
+  if (!rewards || !values || !returns || !td_returns) return RLSCAN_ERR_NULL;
+  if (misaligned(rewards, es) || misaligned(values, es)) return RLSCAN_ERR_ALIGN;
+  Io io;
+  io.add_in(rewards, es * E * T);
+  io.add_in(values, es * E * T);
+  if ((st = common_backward(io, terminated, truncated, bootstrap_value, trunc_bootstrap, E, T, es)) != RLSCAN_OK)
+    return st;
+  io.add_out(returns);
+  io.add_out(td_returns);
+  if ((st = check_io(io, E, T, es)) != RLSCAN_OK) return st;
+  KernelArgs a = blank(E, T);
+  a.r = fp(rewards);
+  a.v = fp(values);
+  a.term = terminated;
+  a.trunc = truncated;
+  a.row = fp(bootstrap_value);
+  a.tboot = fp(trunc_bootstrap);
+  a.out0 = fp(returns);
+  a.out1 = fp(td_returns);
+  a.gamma = gamma;
+  a.lam = lambda;
+  if (f == RLSCAN_FORMAT_F32 && l == RLSCAN_LAYOUT_ENV_MAJOR) return launched(rlscan::launch_returns_td_lambda(a, stream));
+  KernelArgs dr = a;
+  dr.v = nullptr;
+  dr.out1 = nullptr;
+  const hipError_t e = launch_fmt<rlscan::DiscountedReturn>(f, l, dr, stream);
+  if (e != hipSuccess) return launched(e);
+  KernelArgs td = a;
+  td.out0 = a.out1;
+  td.out1 = nullptr;
+  return launched(launch_fmt<rlscan::TdLambda>(f, l, td, stream));
+}
+
 rlscan_status impl_gae(rlscan_format f, rlscan_layout l, const void* rewards, const void* values, const uint8_t* terminated,
                        const uint8_t* truncated, const void* bootstrap_value, const void* trunc_bootstrap,
                        void* advantages, void* returns, int64_t E, int64_t T, float gamma, float lambda,
@@ -390,32 +434,8 @@ rlscan_status rlscan_returns_and_td_lambda(const float* rewards, const float* va
                                           const float* bootstrap_value, const float* trunc_bootstrap,
                                           float* returns, float* td_returns, int64_t E, int64_t T, float gamma,
                                           float lambda, hipStream_t stream) {
-  rlscan_status st = check_shape(E, T);
-  if (st != RLSCAN_OK) return st;
-  if (!in_unit(gamma) || !in_unit(lambda)) return RLSCAN_ERR_PARAM;
-  if (E * T == 0) return RLSCAN_OK;
-  if (!rewards || !values || !returns || !td_returns) return RLSCAN_ERR_NULL;
-  if (misaligned(rewards) || misaligned(values)) return RLSCAN_ERR_ALIGN;
-  Io io;
-  io.add_in(rewards, 4 * E * T);
-  io.add_in(values, 4 * E * T);
-  if ((st = common_backward(io, terminated, truncated, bootstrap_value, trunc_bootstrap, E, T)) != RLSCAN_OK)
-    return st;
-  io.add_out(returns);
-  io.add_out(td_returns);
-  if ((st = check_io(io, E, T)) != RLSCAN_OK) return st;
-  KernelArgs a = blank(E, T);
-  a.r = rewards;
-  a.v = values;
-  a.term = terminated;
-  a.trunc = truncated;
-  a.row = bootstrap_value;
-  a.tboot = trunc_bootstrap;
-  a.out0 = returns;
-  a.out1 = td_returns;
-  a.gamma = gamma;
-  a.lam = lambda;
-  return launched(rlscan::launch_returns_td_lambda(a, stream));
+  return impl_returns_td_lambda(RLSCAN_FORMAT_F32, RLSCAN_LAYOUT_ENV_MAJOR, rewards, values, terminated, truncated,
+                                bootstrap_value, trunc_bootstrap, returns, td_returns, E, T, gamma, lambda, stream);
 }
 
 rlscan_status rlscan_gae(const float* rewards, const float* values, const uint8_t* terminated,
@@ -473,6 +493,15 @@ rlscan_status rlscan_td_lambda_ex(rlscan_format fmt, rlscan_layout layout, const
                                   float lambda, hipStream_t stream) {
   return impl_td_lambda(fmt, layout, rewards, values, terminated, truncated, bootstrap_value, trunc_bootstrap,
                         returns, E, T, gamma, lambda, stream);
+}
+
+rlscan_status rlscan_returns_and_td_lambda_ex(rlscan_format fmt, rlscan_layout layout, const void* rewards,
+                                             const void* values, const uint8_t* terminated, const uint8_t* truncated,
+                                             const void* bootstrap_value, const void* trunc_bootstrap, void* returns,
+                                             void* td_returns, int64_t E, int64_t T, float gamma, float lambda,
+                                             hipStream_t stream) {
+  return impl_returns_td_lambda(fmt, layout, rewards, values, terminated, truncated, bootstrap_value,
+                                trunc_bootstrap, returns, td_returns, E, T, gamma, lambda, stream);
 }
 
 rlscan_status rlscan_gae_ex(rlscan_format fmt, rlscan_layout layout, const void* rewards, const void* values,

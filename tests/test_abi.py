@@ -42,7 +42,7 @@ def test_header_declares_the_expected_entry_points():
               "rlscan_gae", "rlscan_vtrace",
               "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum",
               "rlscan_linear_scan", "rlscan_linear_scan_segmented", "rlscan_eligibility_traces_vec",
-              "rlscan_discounted_returns_ex", "rlscan_td_lambda_ex", "rlscan_gae_ex",
+              "rlscan_discounted_returns_ex", "rlscan_td_lambda_ex", "rlscan_returns_and_td_lambda_ex", "rlscan_gae_ex",
               "rlscan_vtrace_ex", "rlscan_retrace_ex", "rlscan_eligibility_traces_ex",
               "rlscan_episodic_prefix_sum_ex", "rlscan_linear_scan_segmented_ex", "rlscan_status_string",
               "rlscan_version"]:
@@ -218,6 +218,11 @@ def test_ex_entries_validation(lib, lay):
                                      S) == ERR_NULL
         assert lib.rlscan_eligibility_traces_ex(fmt, lay, A, None, None, F + 1, C, E, T, 0.9, 0.9, S) == ERR_ALIGN
         assert lib.rlscan_episodic_prefix_sum_ex(fmt, lay, A, None, None, None, A + 2, E, T, S) == ERR_ALIAS
+    rtx = lib.rlscan_returns_and_td_lambda_ex
+    assert rtx(5, lay, A, B, None, None, None, None, C, D, E, T, 0.9, 0.9, S) == ERR_PARAM
+    assert rtx(BF16, lay, A, B, None, None, None, None, C, None, E, T, 0.9, 0.9, S) == ERR_NULL
+    assert rtx(F16, lay, A + 1, B, None, None, None, None, C, D, E, T, 0.9, 0.9, S) == ERR_ALIGN
+    assert rtx(BF16, lay, A, B, None, None, None, None, C, C + 2 * E * T - 2, E, T, 0.9, 0.9, S) == ERR_ALIAS
     lsx = lib.rlscan_linear_scan_segmented_ex
     assert lsx(9, lay, A, B, None, None, C, E, T, 1, S) == ERR_PARAM
     assert lsx(BF16, 3, A, B, None, None, C, E, T, 1, S) == ERR_PARAM

@@ -30,8 +30,9 @@ from tests.estimators import check_storage
 
 pytestmark = pytest.mark.gpu
 
+# the seven estimators and the two-output pass
 SEVEN = ("discounted_returns", "td_lambda", "gae", "vtrace", "retrace", "eligibility_traces",
-         "episodic_prefix_sum")
+         "episodic_prefix_sum", "returns_and_td_lambda")
 
 
 def _say(*a):

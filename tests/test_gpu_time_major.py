@@ -21,8 +21,9 @@ from tests.estimators import TOL, check_storage, parity_err
 
 pytestmark = pytest.mark.gpu
 
+# the seven estimators and the two-output pass
 SEVEN = ("discounted_returns", "td_lambda", "gae", "vtrace", "retrace", "eligibility_traces",
-         "episodic_prefix_sum")
+         "episodic_prefix_sum", "returns_and_td_lambda")
 FORMATS = ("float32", "bfloat16", "float16")
 
 
