@@ -421,22 +421,26 @@ def run_grid(torch, device, args):
     names = list(base.estimators)
     grid_e = [int(x) for x in args.grid_e.split(",")] if args.grid_e else GRID_E
     grid_t = [int(x) for x in args.grid_t.split(",")] if args.grid_t else GRID_T
+    st, tm = args.grid_storage, args.grid_time_major
+    vb = 2 if st != "f32" else 4
+    max_set = int(args.grid_max_gib * (1 << 30))
     for T in grid_t:
         for E in grid_e:
-            set_bytes = E * T * (4 * 8 + 2 + 4 * 8) + 4 * E
-            if set_bytes > (1 << 30):
-                log("grid %6d x %4d: buffer set %.2f GiB > 1 GiB, skipped" % (E, T, set_bytes / 2**30))
+            set_bytes = E * T * (vb * 8 + 2 + vb * 8) + vb * E
+            if set_bytes > max_set:
+                log("grid %6d x %4d: buffer set %.2f GiB > %g GiB, skipped" % (E, T, set_bytes / 2**30,
+                                                                               args.grid_max_gib))
                 continue
             w = dataclasses.replace(base, name="all7_%dx%d" % (E, T), E=E, T=T)
             d = synth.workload_inputs(w)
             if args.no_trunc:
                 d = drop_truncation(d)
             nsets = int(min(64, max(2, -(-(1 << 30) // set_bytes) + 1)))
-            runner = Runner(w, d, nsets, device)
+            runner = Runner(w, d, nsets, device, storage=st, time_major=tm)
             per = time_estimators(runner, names, d, w, max(args.steps, 20))
             log("grid %6d x %4d: " % (E, T) + "  ".join("%s %.2f us %.1f%%" % (
                 n[:6], per[n]["us_per_launch"], 100 * per[n]["frac_of_peak"]) for n in names))
-            print(json.dumps({"grid": True, "workload": w.name, "E": E, "T": T,
+            print(json.dumps({"grid": True, "workload": w.name, "E": E, "T": T, "storage": st, "time_major": tm,
                               "truncation": not args.no_trunc, "buffer_sets": nsets,
                               "per_estimator": per}), flush=True)
             del runner
@@ -481,6 +485,9 @@ def main():
     ap.add_argument("--grid-t", default=None, help="comma-separated T values for --grid")
     ap.add_argument("--no-16", action="store_true", help="skip the 16-bit storage and time-major timings")
     ap.add_argument("--configs", action="store_true", help="the smaller named workloads, one line each")
+    ap.add_argument("--grid-storage", default="f32", choices=list(FORMATS), help="value storage for --grid")
+    ap.add_argument("--grid-time-major", action="store_true", help="time-major [T, E] arrays for --grid")
+    ap.add_argument("--grid-max-gib", type=float, default=1.0, help="largest buffer set --grid runs (GiB)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
