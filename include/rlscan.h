@@ -245,8 +245,9 @@ rlscan_status rlscan_linear_scan_segmented(const float *a, const float *b, const
                                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Storage format and layout.  The seven estimators, the two-output pass and
- * the generic scan again, each with two more leading arguments; every other argument means
+ * Storage format and layout.  The seven estimators, the two-output pass, the
+ * vector traces and the generic scan again, each with two more leading
+ * arguments; every other argument means
  * what it means for the float32 entry of the same name.
  *
  * fmt     The type of every value array (inputs, bootstraps, init and
@@ -325,6 +326,15 @@ rlscan_status rlscan_eligibility_traces_ex(rlscan_format fmt, rlscan_layout layo
 rlscan_status rlscan_episodic_prefix_sum_ex(rlscan_format fmt, rlscan_layout layout, const void *x,
                                             const uint8_t *terminated, const uint8_t *truncated, const void *init,
                                             void *sums, int64_t E, int64_t T, hipStream_t stream);
+
+/* Vector traces (rlscan_eligibility_traces_vec) in a storage format and
+ * layout: x, init and traces in format fmt; time-major takes x and traces as
+ * [T,E,D] ((e,t,d) at (t*E + e)*D + d) and the flags as [T,E]; init stays
+ * [E,D]. */
+rlscan_status rlscan_eligibility_traces_vec_ex(rlscan_format fmt, rlscan_layout layout, const void *x,
+                                               const uint8_t *terminated, const uint8_t *truncated,
+                                               const void *init, void *traces, int64_t E, int64_t T, int64_t D,
+                                               float gamma, float lambda, hipStream_t stream);
 
 /* The generic recurrence with episode cuts (rlscan_linear_scan_segmented;
  * done = NULL gives rlscan_linear_scan) in a storage format and layout: a, b,

@@ -58,7 +58,7 @@ _SIGNATURES = {
 # entry's arguments.
 _EX = ("rlscan_discounted_returns", "rlscan_td_lambda", "rlscan_returns_and_td_lambda", "rlscan_gae",
        "rlscan_vtrace", "rlscan_retrace", "rlscan_eligibility_traces", "rlscan_episodic_prefix_sum")
-for _n in _EX + ("rlscan_linear_scan_segmented",):
+for _n in _EX + ("rlscan_linear_scan_segmented", "rlscan_eligibility_traces_vec"):
     _SIGNATURES[_n + "_ex"] = [_int, _int] + _SIGNATURES[_n]
 del _n
 
@@ -408,21 +408,28 @@ def linear_scan_segmented(a, b, done=None, carry=None, *, reverse=True, time_maj
 
 
 def eligibility_traces_vec(x, terminated=None, truncated=None, init=None, *, gamma=0.99, lam=0.95,
-                           out=None, stream=None):
-    """Eligibility traces of feature vectors: x [E, T, D], flags [E, T], init [E, D];
-    every column follows the scalar trace with the row's flags."""
+                           time_major=False, out=None, stream=None):
+    """Eligibility traces of feature vectors: x [E, T, D] (time_major: [T, E, D]),
+    flags [E, T] ([T, E]), init [E, D]; every column follows the scalar trace
+    with the row's flags.  float32, bfloat16 or float16 (the dtype of x)."""
     torch = _torch()
     if not isinstance(x, torch.Tensor) or x.dim() != 3:
         raise ValueError("x must be a [E, T, D] tensor")
     if x.device.type != "cuda":
         raise ValueError("x must be on a GPU device, got %s" % x.device)
-    E, T, D = x.shape
+    if time_major:
+        T, E, D = x.shape
+    else:
+        E, T, D = x.shape
     dev = x.device
-    xx = _check_f32(x, "x", (E, T, D), dev)
-    te = _check_flags(terminated, "terminated", (E, T), dev)
-    tr = _check_flags(truncated, "truncated", (E, T), dev)
-    it = _check_f32(init, "init", (E, D), dev)
-    out = _out(out, "out", (E, T, D), dev)
-    _call("rlscan_eligibility_traces_vec", _ptr(xx), _ptr(te), _ptr(tr), _ptr(it), _ptr(out), E, T, D,
-          float(gamma), float(lam), _stream(dev, stream))
+    dt = _storage(x, "x")
+    fshape = (T, E) if time_major else (E, T)
+    xx = _check_val(x, "x", tuple(x.shape), dev, dt)
+    te = _check_flags(terminated, "terminated", fshape, dev)
+    tr = _check_flags(truncated, "truncated", fshape, dev)
+    it = _check_val(init, "init", (E, D), dev, dt)
+    out = _out(out, "out", tuple(x.shape), dev, dt)
+    args = (_ptr(xx), _ptr(te), _ptr(tr), _ptr(it), _ptr(out), E, T, D, float(gamma), float(lam),
+            _stream(dev, stream))
+    _entry("rlscan_eligibility_traces_vec", dt, time_major, *args)
     return out

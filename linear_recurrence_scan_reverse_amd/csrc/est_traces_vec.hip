@@ -16,19 +16,24 @@
 // that e_t = A_t * c + y_t once the entering value c is known.  The 4
 // chunk maps (A, y_last) meet in LDS; each wave composes those of the waves
 // before it to get its c, then stores.  The super-tile's outgoing value is the
-// next one's entering value.  All arithmetic is fp64; outputs are rounded once.
+// next one's entering value.  All arithmetic is fp64; outputs are rounded
+// once (to float32, then to the 16-bit storage format when there is one).
 // Block and chunk sizes measured at 1024 x 256 x 64: 4 x 16 (27 us) beat 16 x 8
 // (38 us), 8 x 16 (30 us) and 4 x 8 (29 us).
+//
+// Layouts: env-major x[e][t][d] with flags [E, T] (a row's steps are D apart,
+// rows T*D apart), or time-major x[t][e][d] with flags [T, E] (steps E*D apart,
+// rows D apart).  Either way one step of a row is D contiguous values.
 #include "rlscan_launch.hpp"
 
 namespace rlscan {
 
 struct TraceVecArgs {
-  const float* x;        // [E, T, D]
-  const uint8_t* term;   // [E, T] or NULL
-  const uint8_t* trunc;  // [E, T] or NULL
+  const float* x;        // [E, T, D] or [T, E, D], values in the storage format
+  const uint8_t* term;   // [E, T] or [T, E], or NULL
+  const uint8_t* trunc;  // [E, T] or [T, E], or NULL
   const float* init;     // [E, D] or NULL
-  float* out;            // [E, T, D]
+  float* out;            // as x
   int64_t E, T, D;
   double decay;          // gamma * lambda
 };
@@ -36,6 +41,7 @@ struct TraceVecArgs {
 constexpr int kTvWaves = 4;   // waves per block: time chunks of a super-tile
 constexpr int kTvChunk = 16;  // steps per wave chunk
 
+template <class S, bool TM>
 __global__ void __launch_bounds__(64 * kTvWaves)
 trace_vec_kernel(const TraceVecArgs p) {
   __shared__ double s_a[kTvWaves];
@@ -48,15 +54,20 @@ trace_vec_kernel(const TraceVecArgs p) {
   const int64_t d = (blockIdx.x - e * ntile_d) * 64 + lane;
   const bool col_ok = d < D;
   const int64_t dc = col_ok ? d : D - 1;  // clamped column: loads stay inside the row
-  // row bases are wave-uniform; a lane addresses its column with a 32-bit
-  // element offset (T * D < 2^30 is checked by the C ABI)
-  const float* xr = p.x + e * T * D;
-  float* orow = p.out + e * T * D;
-  const uint32_t D32 = (uint32_t)D, dc32 = (uint32_t)dc;
-  const uint8_t* te = p.term ? p.term + e * T : nullptr;
-  const uint8_t* tr = p.trunc ? p.trunc + e * T : nullptr;
+  // element index of (row e, step t, column dc): a wave-uniform step base plus
+  // the lane's 32-bit column offset
+  const int64_t row_base = TM ? e * D : e * T * D;
+  const int64_t step = TM ? p.E * D : D;
+  auto step_base = [&](int64_t t) { return row_base + t * step; };
+  const uint32_t dc32 = (uint32_t)dc;
+  // flags of (row e, step t)
+  const int64_t f_base = TM ? e : e * T;
+  const int64_t f_step = TM ? p.E : 1;
+  const uint8_t* te = p.term;
+  const uint8_t* tr = p.trunc;
 
-  double carry = p.init ? (double)p.init[e * D + dc] : 0.0;  // value entering the super-tile
+  // value entering the super-tile
+  double carry = p.init ? (double)load1<S>(p.init, e * D, (uint32_t)dc) : 0.0;
   for (int64_t t0 = 0; t0 < T; t0 += (int64_t)kTvWaves * kTvChunk) {
     const int64_t c0 = t0 + (int64_t)w * kTvChunk;  // this wave's first step
     // ---- loads: the chunk's feature rows, and the done flags of steps c0-1 .. c0+14
@@ -64,13 +75,13 @@ trace_vec_kernel(const TraceVecArgs p) {
 #pragma unroll
     for (int k = 0; k < kTvChunk; ++k) {
       const int64_t t = c0 + k < T ? c0 + k : T - 1;
-      xv[k] = __builtin_nontemporal_load(at(xr, (uint32_t)t * D32 + dc32));
+      xv[k] = load1<S>(p.x, step_base(t), dc32);
     }
     // lane j < 16 reads the flags of step c0 + j - 1 (the step before each chunk step)
     bool dn = false;
     if (lane < kTvChunk) {
       const int64_t t = c0 + lane - 1;
-      if (t >= 0 && t < T) dn = (te && te[t] != 0) || (tr && tr[t] != 0);
+      if (t >= 0 && t < T) dn = (te && te[f_base + t * f_step] != 0) || (tr && tr[f_base + t * f_step] != 0);
     }
     const unsigned long long reset = __builtin_amdgcn_ballot_w64(dn);  // bit k: step c0+k restarts
 
@@ -102,22 +113,35 @@ trace_vec_kernel(const TraceVecArgs p) {
       const double a = ((reset >> k) & 1ull) ? 0.0 : p.decay;
       At = a * At;
       yk = __builtin_fma(a, yk, (double)xv[k]);
-      if (col_ok && c0 + k < T)
-        __builtin_nontemporal_store((float)__builtin_fma(At, c, yk), at(orow, (uint32_t)(c0 + k) * D32 + dc32));
+      if (col_ok && c0 + k < T) {
+        const float v = (float)__builtin_fma(At, c, yk);
+        const int64_t sb = step_base(c0 + k);
+        if constexpr (__is_same(S, F32S)) __builtin_nontemporal_store(v, at(p.out + sb, dc32));
+        else __builtin_nontemporal_store(f32_to_s<S>(v), reinterpret_cast<uint16_t*>(p.out) + sb + dc32);
+      }
     }
     carry = cout;
     __syncthreads();  // the LDS maps are rewritten by the next super-tile
   }
 }
 
-hipError_t launch_traces_vec(const float* x, const uint8_t* term, const uint8_t* trunc, const float* init,
-                             float* out, int64_t E, int64_t T, int64_t D, double gamma, double lam,
-                             hipStream_t s) {
+template <class S>
+static const void* trace_vec_fn(bool time_major) {
+  return time_major ? reinterpret_cast<const void*>(&trace_vec_kernel<S, true>)
+                    : reinterpret_cast<const void*>(&trace_vec_kernel<S, false>);
+}
+
+hipError_t launch_traces_vec(int fmt, bool time_major, const float* x, const uint8_t* term, const uint8_t* trunc,
+                             const float* init, float* out, int64_t E, int64_t T, int64_t D, double gamma,
+                             double lam, hipStream_t s) {
   TraceVecArgs a{x, term, trunc, init, out, E, T, D, gamma * lam};
   const int64_t blocks = E * ((D + 63) / 64);
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const void* fn = fmt == 1   ? trace_vec_fn<Bf16S>(time_major)
+                   : fmt == 2 ? trace_vec_fn<F16S>(time_major)
+                              : trace_vec_fn<F32S>(time_major);
   void* params[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&trace_vec_kernel), dim3((unsigned)blocks),
-                         dim3(64 * kTvWaves), params, 0, s);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(64 * kTvWaves), params, 0, s);
 }
 
 }  // namespace rlscan

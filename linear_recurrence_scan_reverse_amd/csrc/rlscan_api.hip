@@ -394,6 +394,30 @@ rlscan_status impl_linear_scan(rlscan_format f, rlscan_layout l, const void* a_c
                  : launched(launch_fmt<rlscan::LinearScanForward>(f, l, a, stream));
 }
 
+// Vector traces over [E,T,D] (or [T,E,D]) features.
+rlscan_status impl_traces_vec(rlscan_format f, rlscan_layout l, const void* x, const uint8_t* terminated,
+                              const uint8_t* truncated, const void* init, void* traces, int64_t E, int64_t T,
+                              int64_t D, float gamma, float lambda, hipStream_t stream) {
+  const int es = elem_size(f);
+  if (D < 0 || (D > 0 && T >= RLSCAN_MAX_T / D)) return RLSCAN_ERR_SHAPE;  // T*D < 2^30
+  rlscan_status st = check_shape(E, T);
+  if (st != RLSCAN_OK) return st;
+  if ((st = check_shape(E, T * D)) != RLSCAN_OK) return st;
+  if (!in_unit(gamma) || !in_unit(lambda) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
+  if (E * T * D == 0) return RLSCAN_OK;
+  if (!x || !traces) return RLSCAN_ERR_NULL;
+  if (misaligned(x, es) || misaligned(init, es)) return RLSCAN_ERR_ALIGN;
+  Io io;
+  io.add_in(x, es * E * T * D);
+  io.add_in(terminated, E * T);
+  io.add_in(truncated, E * T);
+  io.add_in(init, es * E * D);
+  io.add_out(traces);
+  if ((st = check_io(io, E, T * D, es)) != RLSCAN_OK) return st;
+  return launched(rlscan::launch_traces_vec((int)f, l == RLSCAN_LAYOUT_TIME_MAJOR, fp(x), terminated, truncated,
+                                            fp(init), fp(traces), E, T, D, gamma, lambda, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -565,23 +589,15 @@ rlscan_status rlscan_linear_scan_segmented_ex(rlscan_format fmt, rlscan_layout l
 rlscan_status rlscan_eligibility_traces_vec(const float* x, const uint8_t* terminated, const uint8_t* truncated,
                                             const float* init, float* traces, int64_t E, int64_t T, int64_t D,
                                             float gamma, float lambda, hipStream_t stream) {
-  if (D < 0 || (D > 0 && T >= RLSCAN_MAX_T / D)) return RLSCAN_ERR_SHAPE;  // T*D < 2^30
-  rlscan_status st = check_shape(E, T);
-  if (st != RLSCAN_OK) return st;
-  if ((st = check_shape(E, T * D)) != RLSCAN_OK) return st;
-  if (!in_unit(gamma) || !in_unit(lambda)) return RLSCAN_ERR_PARAM;
-  if (E * T * D == 0) return RLSCAN_OK;
-  if (!x || !traces) return RLSCAN_ERR_NULL;
-  if (misaligned(x) || misaligned(init)) return RLSCAN_ERR_ALIGN;
-  Io io;
-  io.add_in(x, 4 * E * T * D);
-  io.add_in(terminated, E * T);
-  io.add_in(truncated, E * T);
-  io.add_in(init, 4 * E * D);
-  io.add_out(traces);
-  if ((st = check_io(io, E, T * D)) != RLSCAN_OK) return st;
-  return launched(rlscan::launch_traces_vec(x, terminated, truncated, init, traces, E, T, D, gamma, lambda,
-                                            stream));
+  return impl_traces_vec(RLSCAN_FORMAT_F32, RLSCAN_LAYOUT_ENV_MAJOR, x, terminated, truncated, init, traces, E, T,
+                         D, gamma, lambda, stream);
+}
+
+rlscan_status rlscan_eligibility_traces_vec_ex(rlscan_format fmt, rlscan_layout layout, const void* x,
+                                               const uint8_t* terminated, const uint8_t* truncated, const void* init,
+                                               void* traces, int64_t E, int64_t T, int64_t D, float gamma,
+                                               float lambda, hipStream_t stream) {
+  return impl_traces_vec(fmt, layout, x, terminated, truncated, init, traces, E, T, D, gamma, lambda, stream);
 }
 
 }  // extern "C"

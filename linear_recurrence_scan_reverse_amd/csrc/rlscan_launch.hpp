@@ -388,10 +388,11 @@ hipError_t launch_tm(const KernelArgs& in, hipStream_t s) {
 // streaming pass where the rows allow it, else the two single-output kernels.
 hipError_t launch_returns_td_lambda(const KernelArgs& in, hipStream_t s);
 
-// Vector-valued eligibility traces over [E, T, D] features (one kernel).
-hipError_t launch_traces_vec(const float* x, const uint8_t* term, const uint8_t* trunc, const float* init,
-                             float* out, int64_t E, int64_t T, int64_t D, double gamma, double lam,
-                             hipStream_t s);
+// Vector-valued eligibility traces over [E, T, D] (or [T, E, D]) features,
+// one kernel; fmt: 0 float32, 1 bfloat16, 2 float16.
+hipError_t launch_traces_vec(int fmt, bool time_major, const float* x, const uint8_t* term, const uint8_t* trunc,
+                             const float* init, float* out, int64_t E, int64_t T, int64_t D, double gamma,
+                             double lam, hipStream_t s);
 
 // One translation unit per estimator instantiates launch<Est>.
 extern template hipError_t launch<DiscountedReturn>(const KernelArgs&, hipStream_t);

@@ -44,7 +44,8 @@ def test_header_declares_the_expected_entry_points():
               "rlscan_linear_scan", "rlscan_linear_scan_segmented", "rlscan_eligibility_traces_vec",
               "rlscan_discounted_returns_ex", "rlscan_td_lambda_ex", "rlscan_returns_and_td_lambda_ex", "rlscan_gae_ex",
               "rlscan_vtrace_ex", "rlscan_retrace_ex", "rlscan_eligibility_traces_ex",
-              "rlscan_episodic_prefix_sum_ex", "rlscan_linear_scan_segmented_ex", "rlscan_status_string",
+              "rlscan_episodic_prefix_sum_ex", "rlscan_linear_scan_segmented_ex", "rlscan_eligibility_traces_vec_ex",
+              "rlscan_status_string",
               "rlscan_version"]:
         assert n in names
 
@@ -223,6 +224,13 @@ def test_ex_entries_validation(lib, lay):
     assert rtx(BF16, lay, A, B, None, None, None, None, C, None, E, T, 0.9, 0.9, S) == ERR_NULL
     assert rtx(F16, lay, A + 1, B, None, None, None, None, C, D, E, T, 0.9, 0.9, S) == ERR_ALIGN
     assert rtx(BF16, lay, A, B, None, None, None, None, C, C + 2 * E * T - 2, E, T, 0.9, 0.9, S) == ERR_ALIAS
+    tvx = lib.rlscan_eligibility_traces_vec_ex
+    assert tvx(4, lay, A, None, None, None, C, E, T, 8, 0.9, 0.9, S) == ERR_PARAM
+    assert tvx(BF16, 7, A, None, None, None, C, E, T, 8, 0.9, 0.9, S) == ERR_PARAM
+    assert tvx(BF16, lay, A + 1, None, None, None, C, E, T, 8, 0.9, 0.9, S) == ERR_ALIGN
+    assert tvx(F16, lay, A, None, None, None, A + 2 * E * T * 8 - 2, E, T, 8, 0.9, 0.9, S) == ERR_ALIAS
+    assert tvx(F16, lay, A, None, None, None, C, E, T, -1, 0.9, 0.9, S) == ERR_SHAPE
+    assert tvx(BF16, lay, None, None, None, None, None, E, T, 0, 0.9, 0.9, S) == OK
     lsx = lib.rlscan_linear_scan_segmented_ex
     assert lsx(9, lay, A, B, None, None, C, E, T, 1, S) == ERR_PARAM
     assert lsx(BF16, 3, A, B, None, None, C, E, T, 1, S) == ERR_PARAM

@@ -51,3 +51,31 @@ def test_vector_traces_full_size_and_deterministic():
     a = rl.eligibility_traces_vec(dev["x"], dev["terminated"], dev["truncated"], dev["init"])
     b = rl.eligibility_traces_vec(dev["x"], dev["terminated"], dev["truncated"], dev["init"])
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("fmt", ["float32", "bfloat16", "float16"])
+@pytest.mark.parametrize("time_major", [False, True])
+@pytest.mark.parametrize("E,T,D", [(1, 1, 1), (3, 7, 5), (5, 256, 64), (17, 33, 70), (64, 100, 3)])
+def test_vector_traces_formats_and_layouts(fmt, time_major, E, T, D):
+    # values rounded to the format (the oracle runs on them, widened); time-major
+    # takes x as [T, E, D] and flags as [T, E]
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    from tests.estimators import check_rounded
+    dt = getattr(torch, fmt)
+    f = synth.draw_features(E, T, D, seed=80 + T + D, p_term=0.03, p_trunc=0.03)
+    x = torch.from_numpy(f["x"]).to(dt)
+    init = torch.from_numpy(f["init"]).to(dt)
+    hx, hi = x.float().numpy(), init.float().numpy()
+    te, tr = (torch.from_numpy(f[k]) for k in ("terminated", "truncated"))
+    if time_major:
+        xd, ted, trd = x.transpose(0, 1).contiguous(), te.t().contiguous(), tr.t().contiguous()
+    else:
+        xd, ted, trd = x, te, tr
+    got = rl.eligibility_traces_vec(xd.cuda(), ted.cuda(), trd.cuda(), init.cuda(), gamma=0.99, lam=0.95,
+                                    time_major=time_major)
+    torch.cuda.synchronize()
+    if time_major:
+        got = got.transpose(0, 1).contiguous()
+    ref = oracle.eligibility_traces_vec(hx, f["terminated"], f["truncated"], hi, gamma=0.99, lam=0.95)
+    check_rounded(got, ref, fmt, "traces_vec %s tm=%s E=%d T=%d D=%d" % (fmt, time_major, E, T, D))
