@@ -54,15 +54,22 @@ trace_vec_kernel(const TraceVecArgs p) {
   const int64_t d = (blockIdx.x - e * ntile_d) * 64 + lane;
   const bool col_ok = d < D;
   const int64_t dc = col_ok ? d : D - 1;  // clamped column: loads stay inside the row
-  // element index of (row e, step t, column dc): a wave-uniform step base plus
-  // the lane's 32-bit column offset
-  const int64_t row_base = TM ? e * D : e * T * D;
-  const int64_t step = TM ? p.E * D : D;
-  auto step_base = [&](int64_t t) { return row_base + t * step; };
-  const uint32_t dc32 = (uint32_t)dc;
-  // flags of (row e, step t)
-  const int64_t f_base = TM ? e : e * T;
-  const int64_t f_step = TM ? p.E : 1;
+  // element (row e, step t, column dc) = base + off: env-major, the row's base
+  // and a 32-bit in-row offset t*D + dc (T*D < 2^30 is checked by the C ABI);
+  // time-major, the step's wave-uniform base and the column
+  const uint32_t D32 = (uint32_t)D, dc32 = (uint32_t)dc;
+  auto elem = [&](int64_t t, int64_t& base, uint32_t& off) __attribute__((always_inline)) {
+    if constexpr (TM) {
+      base = (t * p.E + e) * D;
+      off = dc32;
+    } else {
+      base = e * T * D;
+      off = (uint32_t)t * D32 + dc32;
+    }
+  };
+  // flags of (row e, step t) at fb + t * fs
+  const int64_t fb = TM ? e : e * T;
+  const int64_t fs = TM ? p.E : 1;
   const uint8_t* te = p.term;
   const uint8_t* tr = p.trunc;
 
@@ -75,13 +82,16 @@ trace_vec_kernel(const TraceVecArgs p) {
 #pragma unroll
     for (int k = 0; k < kTvChunk; ++k) {
       const int64_t t = c0 + k < T ? c0 + k : T - 1;
-      xv[k] = load1<S>(p.x, step_base(t), dc32);
+      int64_t base;
+      uint32_t off;
+      elem(t, base, off);
+      xv[k] = load1<S>(p.x, base, off);
     }
     // lane j < 16 reads the flags of step c0 + j - 1 (the step before each chunk step)
     bool dn = false;
     if (lane < kTvChunk) {
       const int64_t t = c0 + lane - 1;
-      if (t >= 0 && t < T) dn = (te && te[f_base + t * f_step] != 0) || (tr && tr[f_base + t * f_step] != 0);
+      if (t >= 0 && t < T) dn = (te && te[fb + t * fs] != 0) || (tr && tr[fb + t * fs] != 0);
     }
     const unsigned long long reset = __builtin_amdgcn_ballot_w64(dn);  // bit k: step c0+k restarts
 
@@ -115,9 +125,11 @@ trace_vec_kernel(const TraceVecArgs p) {
       yk = __builtin_fma(a, yk, (double)xv[k]);
       if (col_ok && c0 + k < T) {
         const float v = (float)__builtin_fma(At, c, yk);
-        const int64_t sb = step_base(c0 + k);
-        if constexpr (__is_same(S, F32S)) __builtin_nontemporal_store(v, at(p.out + sb, dc32));
-        else __builtin_nontemporal_store(f32_to_s<S>(v), reinterpret_cast<uint16_t*>(p.out) + sb + dc32);
+        int64_t base;
+        uint32_t off;
+        elem(c0 + k, base, off);
+        if constexpr (__is_same(S, F32S)) __builtin_nontemporal_store(v, at(p.out + base, off));
+        else __builtin_nontemporal_store(f32_to_s<S>(v), reinterpret_cast<uint16_t*>(p.out) + base + off);
       }
     }
     carry = cout;
