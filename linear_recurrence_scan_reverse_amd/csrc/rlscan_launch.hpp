@@ -35,12 +35,13 @@ inline LaunchShape pick_shape(int64_t T) {
 // Team shape for 16-bit storage: rows of 65 to 512 steps take 8 steps per
 // lane (one 16-byte access per lane and stream, as 4 float32 steps are), so
 // half as many lanes per row.  Measured at 16384 x 256 (bfloat16): TD(lambda)
-// and GAE 13.0 -> 11.7 us, traces and prefix sums 10.1 -> 9.5 us; V-trace
-// unchanged; Retrace 17.4 -> 18.1 us and discounted returns 11.0 -> 15.3 us
-// (its 8 blocks per CU no longer fit), so those three keep 4 steps per lane.
+// and GAE 13.0 -> 11.7 us, traces and prefix sums 10.1 -> 9.5 us, discounted
+// returns 11.0 -> 10.5 us (with 4 blocks per CU: its usual 8 do not fit at 8
+// steps per lane; 65536 x 256: 32.0 -> 28.6 us); V-trace unchanged and Retrace
+// 17.4 -> 18.1 us, so those two keep 4 steps per lane.
 template <class Est>
 inline LaunchShape pick_shape_16(int64_t T) {
-  if (__is_same(Est, DiscountedReturn) || __is_same(Est, Vtrace) || __is_same(Est, Retrace)) return pick_shape(T);
+  if (__is_same(Est, Vtrace) || __is_same(Est, Retrace)) return pick_shape(T);
   if (T <= 64) return pick_shape(T);
   if (T <= 128) return {16, 8, 1};
   if (T <= 256) return {32, 8, 1};
@@ -50,9 +51,9 @@ inline LaunchShape pick_shape_16(int64_t T) {
 
 // Resident blocks per CU the persistent grid aims for (discounted returns, the
 // lightest kernel, measured faster with more waves in flight: 11.4 vs 11.9 us
-// at 16384 x 256).
+// at 16384 x 256; at 8 steps per lane its registers allow only 4).
 template <class Est>
-inline int blocks_per_cu(const LaunchShape&) { return __is_same(Est, DiscountedReturn) ? 8 : 4; }
+inline int blocks_per_cu(const LaunchShape& sh) { return (__is_same(Est, DiscountedReturn) && sh.K != 8) ? 8 : 4; }
 
 // Rows a team scans per work item: one on this path (the kernel keeps the
 // count as a template parameter, R).
