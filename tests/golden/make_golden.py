@@ -38,6 +38,18 @@ def compute(d):
                                     gamma=g, lam=l)
     out["eligibility_traces"] = oracle.eligibility_traces(d["r"], te, tr, bv, gamma=g, lam=l)
     out["episodic_prefix_sum"] = oracle.episodic_prefix_sum(d["r"], te, tr, bv)
+    # the generic recurrence with cuts at the terminated steps: a = the
+    # probabilities pi (in (0.05, 1)), b = rewards, carry = bootstrap_value
+    for rev in (True, False):
+        out["linear_scan_segmented_%s" % ("reverse" if rev else "forward")] = oracle.linear_scan_segmented(
+            d["pi"], d["r"], te, bv, reverse=rev)
+    # vector traces: features v (column 0), q (column 1), exp_q (column 2)
+    import numpy as np
+    x = np.ascontiguousarray(np.stack([d["v"], d["q"], d["exp_q"]], axis=-1))
+    init = np.ascontiguousarray(np.stack([bv, bv, bv], axis=-1))
+    tv = oracle.eligibility_traces_vec(x, te, tr, init, gamma=g, lam=l)
+    for c in range(3):
+        out["eligibility_traces_vec_col%d" % c] = np.ascontiguousarray(tv[:, :, c])
     return out
 
 
