@@ -247,19 +247,19 @@ rlscan_status rlscan_linear_scan_segmented(const float *a, const float *b, const
 /* ------------------------------------------------------------------------
  * Storage format and layout.  The seven estimators, the two-output pass, the
  * vector traces and the generic scan again, each with two more leading
- * arguments; every other argument means
- * what it means for the float32 entry of the same name.
+ * arguments; every other argument means what it means for the float32 entry
+ * of the same name.
  *
  * fmt     The type of every value array (inputs, bootstraps, init and
  *         outputs): float32, bfloat16 or float16.  16-bit storage halves the
  *         HBM bytes per step; the pages fix no precision, so this is an
  *         extension for rollouts already kept in 16 bits (the gist.science
  *         summary's plain-language part names specialised data formats as
- *         work still to do).  Inputs are widened exactly on load, the scan runs in float64
- *         as above, and each output is rounded to float32 and then to the
- *         format (round to nearest even both times; float16 overflow gives
- *         +-inf).  Flags stay uint8.  Value pointers must be aligned to the
- *         element size (2 bytes for the 16-bit formats).
+ *         work still to do).  Inputs are widened exactly on load, the scan
+ *         runs in float64 as above, and each output is rounded to float32 and
+ *         then to the format (round to nearest even both times; float16
+ *         overflow gives +-inf).  Flags stay uint8.  Value pointers must be
+ *         aligned to the element size (2 bytes for the 16-bit formats).
  * layout  RLSCAN_LAYOUT_ENV_MAJOR: [E,T] arrays as above, (e,t) at e*T + t.
  *         RLSCAN_LAYOUT_TIME_MAJOR: [T,E] arrays, (e,t) at t*E + e, the order
  *         of rollout buffers that append one step for all environments (the
