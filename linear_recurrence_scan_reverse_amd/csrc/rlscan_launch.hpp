@@ -360,20 +360,58 @@ constexpr int tm_waves() { return 16; }
 template <class Est>
 constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 
+// Few column groups and long columns: blocks of MODE 0 would leave most CUs
+// idle and walk thousands of steps each, so time is cut into segments (see
+// tm_kernel) giving about two blocks per CU, of at least 256 steps and a
+// multiple of 256 (whole super-tiles; the parked float64 pair needs at most 8
+// rows); the last segment takes the remainder.  At most kTmMaxSeg segments
+// per column (the carry kernel's 16 waves x kTmCarrySeg).  Returns the
+// segment length, or 0 to scan whole columns.
+constexpr int64_t kTmSegStep = 256;
+constexpr int64_t kTmMaxSeg = 16 * kTmCarrySeg;
+inline int64_t tm_segment_length(const KernelArgs& a) {
+  const int64_t groups = (a.E + 63) / 64;
+  const int64_t cus = cu_count();
+  if (groups >= cus || a.T < 2 * kTmSegStep) return 0;
+  int64_t nseg = (2 * cus + groups - 1) / groups;
+  if (nseg > kTmMaxSeg) nseg = kTmMaxSeg;
+  int64_t len = (a.T + nseg - 1) / nseg;
+  len = (len + kTmSegStep - 1) / kTmSegStep * kTmSegStep;
+  return a.T / len >= 2 ? len : 0;
+}
+
 template <class Est, int OPT, class S>
 inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
   constexpr int W = tm_waves<Est>(), K = tm_chunk<Est>();
-  const int64_t blocks = (a.E + 63) / 64;
-  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const int64_t groups = (a.E + 63) / 64;
+  int64_t seg_len = tm_segment_length(a);
+  int64_t nseg = seg_len ? a.T / seg_len : 1;  // the last segment takes the remainder
+  if (groups * nseg > INT32_MAX || nseg > kTmMaxSeg) return hipErrorInvalidConfiguration;
   KernelArgs arg = a;
-  void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&tm_kernel<Est, W, K, OPT, S>), dim3((unsigned)blocks),
-                         dim3(64 * W), params, 0, s);
+  void* params[] = {&arg, &seg_len, &nseg};
+  const dim3 block(64 * W);
+  if (nseg == 1)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&tm_kernel<Est, W, K, OPT, S, 0>), dim3((unsigned)groups),
+                           block, params, 0, s);
+  const dim3 grid((unsigned)(groups * nseg));
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&tm_kernel<Est, W, K, OPT, S, 1>), grid, block,
+                                 params, 0, s);
+  if (e != hipSuccess) return e;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&tm_carry_kernel<Est, S>), dim3((unsigned)groups), dim3(1024),
+                      params, 0, s);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&tm_kernel<Est, W, K, OPT, S, 2>), grid, block, params, 0, s);
 }
 
 template <class Est, class S = F32S>
 hipError_t launch_tm(const KernelArgs& in, hipStream_t s) {
   using Tr = Traits<Est>;
+  // one environment: [T, 1] is laid out as [1, T], so the row-major path
+  // (whose long rows are split into segments) takes it
+  if (in.E == 1) {
+    if constexpr (__is_same(S, F32S)) return launch<Est>(in, s);
+    else return launch_typed<Est, S>(in, s);
+  }
   const KernelArgs a = resolve_optional(in);
   const bool flags = a.has_term || a.has_trunc;
   if constexpr (Tr::kHasOut1) {

@@ -64,7 +64,7 @@ def test_generic_scan_formats(fmt, E, T, p_cut):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("E,T", [(1, 1), (63, 17), (64, 128), (65, 257), (1000, 300)])
+@pytest.mark.parametrize("E,T", [(1, 1), (63, 17), (64, 128), (65, 257), (1000, 300), (4, 5000), (70, 3000)])
 @pytest.mark.parametrize("p_cut", [0.0, 0.02])
 def test_generic_scan_time_major(fmt, E, T, p_cut):
     _run(fmt, E, T, 200 + E, p_cut, time_major=True)

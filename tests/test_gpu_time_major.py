@@ -101,3 +101,43 @@ def test_time_major_exact_integer_sums():
                                  None, torch.from_numpy(init).cuda(), time_major=True)
     assert tuple(got.shape) == (T, E)
     assert np.array_equal(got.cpu().numpy().T.astype(np.float64), ref)
+
+
+# Few column groups and long columns: time is cut into segments scanned in
+# three launches (segment maps parked in the first output, a carry pass, a
+# rescan).  Shapes: two segments, a ragged last segment, two column groups,
+# a 512-step segment length with over a hundred segments, many groups with
+# few steps each; one environment (laid out like one row, scanned by the
+# row-major path, whose long rows are segmented too).
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("E,T", [(2, 512), (3, 4097), (65, 2000), (5, 70000), (130, 8192), (1, 262144)])
+def test_time_major_segmented_columns(fmt, E, T):
+    _say("time-major segmented %s E=%d T=%d" % (fmt, E, T))
+    d = synth.draw(E, T, seed=86 + E, p_term=0.001, p_trunc=0.001)
+    for name in SEVEN:
+        check_storage(name, d, fmt, time_major=True)
+
+
+@pytest.mark.parametrize("variant", [dict(term=False, trunc=False), dict(boot=False, tboot=False),
+                                     dict(trunc=False), dict(tboot=False)])
+def test_time_major_segmented_optional_inputs(variant):
+    d = synth.draw(40, 3000, seed=87, p_term=0.002, p_trunc=0.002)
+    for name in SEVEN:
+        check_storage(name, d, "float32", time_major=True, **variant)
+        check_storage(name, d, "bfloat16", time_major=True, misalign=True, **variant)
+
+
+def test_time_major_segmented_no_cuts_and_deterministic():
+    # no episode ends: every segment's carry crosses into the next one
+    import torch
+    from tests.estimators import run_gpu, storage_inputs
+    d = synth.draw(7, 20000, seed=88, p_term=0.0, p_trunc=0.0)
+    for name in SEVEN:
+        check_storage(name, d, "float32", time_major=True)
+    _, tm = storage_inputs(d, time_major=True)
+    for name in SEVEN:
+        a = {k: v.cpu().numpy() for k, v in run_gpu(name, tm, time_major=True).items()}
+        b = {k: v.cpu().numpy() for k, v in run_gpu(name, tm, time_major=True).items()}
+        torch.cuda.synchronize()
+        for k in a:
+            assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), (name, k)
