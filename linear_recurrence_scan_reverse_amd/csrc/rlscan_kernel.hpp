@@ -32,6 +32,11 @@
 //     branch-free: out-of-range elements read a clamped in-row address and
 //     are masked in registers, so the compiler can count outstanding loads
 //     exactly.
+//   * One-item form (ONE = true, rows of one tile): the grid holds a team for
+//     every row group; a team issues its flags and inputs together, gathers
+//     the truncation bootstraps once the flags land, scans, stores and exits,
+//     and the hardware refills the slot with the next block.  Nothing is
+//     fetched ahead, so no pipeline has to fill or drain.
 // All scan arithmetic is float64; inputs are float32 (or bfloat16 / float16,
 // widened exactly) and each output is rounded to float32 once (then to the
 // 16-bit format).  The per-lane code below (pairs, fold, re-walk, epilogue)
@@ -673,7 +678,7 @@ template <class Est, int K> struct RowData : LaneIn<Est, K> {
 // tile is whole; otherwise every element is loaded at a clamped column), OPT
 // (bit 0: a flag array is present; bit 1: the second output is written).
 // The C ABI guarantees T < 2^30, so every in-row byte offset fits 32 bits.
-template <class Est, int L, int K, int W, int R, bool VEC, int OPT, class S = F32S>
+template <class Est, int L, int K, int W, int R, bool VEC, int OPT, class S = F32S, bool ONE = false>
 __global__ void __launch_bounds__(BlockShape<W>::kThreads)
 scan_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
@@ -793,8 +798,7 @@ scan_kernel(const KernelArgs p) {
     }
   };
 
-  auto issue_data = [&](const Cursor& c, const unsigned (&tbits)[R], const unsigned (&rbits)[R],
-                        RowData<Est, K> (&dd)[R]) __attribute__((always_inline)) {
+  auto issue_dense = [&](const Cursor& c, RowData<Est, K> (&dd)[R]) __attribute__((always_inline)) {
     const TilePos q = tile_pos(c);
     const ItemRows<R> ir = item_rows(c);
     const int64_t eb = ir.wb * T;  // element index of the base row
@@ -823,9 +827,22 @@ scan_kernel(const KernelArgs p) {
         d.nbf[1] = __builtin_nontemporal_load(at(p.trunc + eb, noff));
       }
       d.rowv = load1<S>(p.row, ir.wb, ir.rsel[rr]);
-      // Truncation bootstraps of this lane's chunk; lanes without a truncated
-      // step read the array's first chunk instead (one line shared by all waves).
-      if constexpr (GATHER_TB) {
+    }
+  };
+
+  // Truncation bootstraps of each lane's chunk; lanes without a truncated step
+  // read the array's first chunk instead (one line shared by all waves).
+  auto issue_gather = [&](const Cursor& c, const unsigned (&tbits)[R], const unsigned (&rbits)[R],
+                          RowData<Est, K> (&dd)[R]) __attribute__((always_inline)) {
+    if constexpr (GATHER_TB) {
+      const TilePos q = tile_pos(c);
+      const ItemRows<R> ir = item_rows(c);
+      const int64_t eb = ir.wb * T;
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        RowData<Est, K>& d = dd[rr];
+        const uint32_t off = ir.roff[rr] + q.cs;
+        const uint32_t last = ir.roff[rr] + T32 - 1;
         const unsigned need = rbits[rr] & ~tbits[rr];
         if constexpr (VEC) {
           load_s<S, K, true>(p.tboot, need ? eb : 0, need ? off : 0u, 0u, d.tb);
@@ -839,6 +856,12 @@ scan_kernel(const KernelArgs p) {
         }
       }
     }
+  };
+
+  auto issue_data = [&](const Cursor& c, const unsigned (&tbits)[R], const unsigned (&rbits)[R],
+                        RowData<Est, K> (&dd)[R]) __attribute__((always_inline)) {
+    issue_dense(c, dd);
+    issue_gather(c, tbits, rbits, dd);
   };
 
   const ScanScalars sc{gamma, lam, gl, (float)p.rho_bar, (float)p.c_bar, p.has_row != 0, p.has_tboot != 0};
@@ -920,6 +943,30 @@ scan_kernel(const KernelArgs p) {
       }
     }
   };
+
+  // ---------------------------------------------------------------- one item per team
+  // The grid holds a team for every row group, so a team scans the tiles of
+  // one row group and exits; the hardware refills its slot with a new block.
+  // Flags and inputs go out together, the bootstrap gather as soon as the
+  // flags land, and nothing is fetched for a later item.
+  if constexpr (ONE) {
+    double C[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) C[rr] = 0.0;
+    Cursor c{0, 0, 0};
+    for (int64_t ts = 0; ts < ntiles; ++ts) {
+      FlagRaw<K> F[R];
+      RowData<Est, K> D[R];
+      unsigned bt[R], br[R];
+      issue_flags(c, F);
+      issue_dense(c, D);
+      decode(F, bt, br);
+      issue_gather(c, bt, br, D);
+      compute(c.k, c, D, bt, br, C);
+      c = advance(c);
+    }
+    return;
+  }
 
   // ---------------------------------------------------------------- the pipeline
   // Two register sets (X: even items, Y: odd items) swap roles each step, so no

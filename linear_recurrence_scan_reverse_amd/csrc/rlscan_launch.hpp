@@ -1,6 +1,7 @@
 // rlscan_launch.hpp -- host-side launch of the scan kernels: resolves optional
-// inputs, routes a call to one of the kernels (streaming, pipelined,
-// segmented for long rows, time-major), picks its team shape, sizes its grid
+// inputs, routes a call to one of the kernels (streaming, pipelined with a
+// persistent grid or one item per team, segmented for long rows, time-major),
+// picks its team shape, sizes its grid
 // and launches it on the caller's stream (one kernel; three for the
 // segmented path).
 #pragma once
@@ -15,7 +16,8 @@
 namespace rlscan {
 
 struct LaunchShape {
-  int L, K, W;  // lanes per team (W == 1), steps per lane per tile, waves per row
+  int L, K, W;       // lanes per team (W == 1), steps per lane per tile, waves per row
+  bool one = false;  // one item per team (a grid covering every row group)
 };
 
 // Team shape by row length.  Short rows share a wave (16 or 32 lanes each) so
@@ -54,6 +56,37 @@ inline LaunchShape pick_shape_16(int64_t T) {
 // at 16384 x 256; at 8 steps per lane its registers allow only 4).
 template <class Est>
 inline int blocks_per_cu(const LaunchShape& sh) { return (__is_same(Est, DiscountedReturn) && sh.K != 8) ? 8 : 4; }
+
+// Estimators with a one-item-per-team form of the pipelined kernel (see
+// prefer_oneshot).
+template <class Est>
+constexpr bool kOneShotEst = __is_same(Est, Retrace) || __is_same(Est, Vtrace);
+
+// Whether a call takes the pipelined kernel with one item per team: a grid
+// that holds a team for every row group, each team loading its row's flags
+// and inputs at once and exiting after one store, instead of the persistent
+// grid that prefetches a team's next item.  Measured with flags present over
+// E in {4096, 16384, 65536} x T in {64 .. 1024} against the routing below:
+// Retrace faster at every point (16384 x 256: 22.6 -> 20.6 us; 4096 x 256:
+// 11.4 -> 7.5 us; 2048 x 1024: 13.4 -> 12.1 us), V-trace faster up to 512
+// steps (16384 x 256: 19.9 -> 19.1 us; 8192 x 128: 9.3 -> 7.3 us) but not at
+// 1024 (4096 x 1024: 20.5 -> 21.3 us).  With 16-bit storage (bfloat16, same
+// grid) Retrace again gained at every point (4096 x 256: 10.5 -> 6.6 us;
+// 65536 x 256: 61.1 -> 56.1 us) and V-trace up to 256 steps (65536 x 256:
+// 56.6 -> 51.8 us) but lost from 512 (16384 x 512: 29.6 -> 31.2 us).  The
+// five lighter estimators ran slower or no faster than on the streaming
+// kernel.  Rows up to 1024 steps are one tile of one team.  esize: bytes per
+// stored value.
+template <class Est>
+inline bool prefer_oneshot(const KernelArgs& a, int esize) {
+  if constexpr (!kOneShotEst<Est>) {
+    return false;
+  } else {
+    if (!a.has_term && !a.has_trunc) return false;
+    if constexpr (__is_same(Est, Retrace)) return a.T <= 1024;
+    return a.T <= (esize == 4 ? 512 : 256);
+  }
+}
 
 // Rows a team scans per work item: one on this path (the kernel keeps the
 // count as a template parameter, R).
@@ -113,10 +146,15 @@ inline hipError_t launch_one(const KernelArgs& a, hipStream_t s, const LaunchSha
   constexpr int R = rows_per_item<Est, K>();
   const int64_t groups = (a.E + R - 1) / R;
   int64_t blocks = (groups + TEAMS - 1) / TEAMS;
-  const int64_t resident = (int64_t)cu_count() * blocks_per_cu<Est>(sh);
-  if (blocks > resident) blocks = resident;
   KernelArgs arg = a;
   void* params[] = {&arg};
+  if constexpr (kOneShotEst<Est>) {
+    if (sh.one)
+      return hipLaunchKernel(reinterpret_cast<const void*>(&scan_kernel<Est, L, K, W, R, VEC, OPT, S, true>),
+                             dim3((unsigned)blocks), dim3(BLOCK), params, 0, s);
+  }
+  const int64_t resident = (int64_t)cu_count() * blocks_per_cu<Est>(sh);
+  if (blocks > resident) blocks = resident;
   return hipLaunchKernel(reinterpret_cast<const void*>(&scan_kernel<Est, L, K, W, R, VEC, OPT, S>),
                          dim3((unsigned)blocks), dim3(BLOCK), params, 0, s);
 }
@@ -291,14 +329,16 @@ template <class Est>
 hipError_t launch(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const int64_t len = segment_length(a)) return launch_segmented<Est>(a, s, len);
-  const int team = stream_team<F32S>(a);
+  const bool one = prefer_oneshot<Est>(a, 4);
+  const int team = one ? 0 : stream_team<F32S>(a);
   switch ((team != 0 && prefer_stream<Est>(a, team)) ? team : 0) {
     case 16: return launch_stream<Est, 16>(a, s);
     case 32: return launch_stream<Est, 32>(a, s);
     case 64: return launch_stream<Est, 64>(a, s);
     default: break;
   }
-  const LaunchShape sh = pick_shape(a.T);
+  LaunchShape sh = pick_shape(a.T);
+  sh.one = one;
   switch (sh.W * 1000 + sh.L * 10 + sh.K) {
     case 1000 + 160 + 1: return launch_shape<Est, 16, 1, 1>(a, s, sh);
     case 1000 + 160 + 2: return launch_shape<Est, 16, 2, 1>(a, s, sh);
@@ -332,7 +372,8 @@ hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
       default: break;
     }
   }
-  const LaunchShape sh = pick_shape_16<Est>(a.T);
+  LaunchShape sh = pick_shape_16<Est>(a.T);
+  sh.one = prefer_oneshot<Est>(a, (int)sizeof(typename S::T));
   switch (sh.W * 1000 + sh.L * 10 + sh.K) {
     case 1000 + 160 + 8: return launch_shape<Est, 16, 8, 1, S>(a, s, sh);
     case 1000 + 320 + 8: return launch_shape<Est, 32, 8, 1, S>(a, s, sh);
