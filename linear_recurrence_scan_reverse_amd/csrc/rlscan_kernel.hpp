@@ -714,7 +714,14 @@ scan_kernel(const KernelArgs p) {
   const int64_t my_team = (int64_t)blockIdx.x * TEAMS + team;
   // Block-uniform item count: the block's first team has the most row groups.
   const int64_t first_team = (int64_t)blockIdx.x * TEAMS;
-  const int64_t groups_first = first_team < groups ? (groups - first_team + teams_total - 1) / teams_total : 0;
+  // In Retrace's one-item form the grid holds a team for every row group, so a
+  // comparison gives the count.  Measured on one MI355X at 16384 x 256 (two
+  // runs each): Retrace 20.7 -> 20.2 us without the 64-bit division, while
+  // V-trace's one-item form ran 0.15 us slower without it and keeps it.
+  constexpr bool kCountByCompare = ONE && Tr::kRetrace;
+  const int64_t groups_first =
+      first_team >= groups ? 0
+                           : (kCountByCompare ? 1 : (groups - first_team + teams_total - 1) / teams_total);
   const int64_t n_items = groups_first * ntiles;
 
   const double gamma = p.gamma;

@@ -84,7 +84,8 @@ inline bool prefer_oneshot(const KernelArgs& a, int esize) {
   } else {
     if (!a.has_term && !a.has_trunc) return false;
     if constexpr (__is_same(Est, Retrace)) return a.T <= 1024;
-    return a.T <= (esize == 4 ? 512 : 256);
+    if constexpr (__is_same(Est, Vtrace)) return a.T <= (esize == 4 ? 512 : 256);
+    return false;
   }
 }
 
