@@ -299,3 +299,22 @@ def test_concurrent_host_threads():
     for i, (r, g) in enumerate(zip(ref, results)):
         for k in r:
             assert torch.equal(r[k], g[k]), (jobs[i], k)
+
+
+@pytest.mark.parametrize("T", [128, 256, 512, 1024])
+def test_zero_flag_arrays_match_absent_flags(T):
+    """All-zero flag arrays and absent (NULL) flags describe the same episodes, but
+    they route Retrace and V-trace to different kernels (the pipelined kernel's
+    one-item form with flags, the streaming or persistent kernel without), and
+    the other estimators to different template instances.  Each pair must agree
+    to fp32 rounding of the same fp64 result; no oracle is involved."""
+    E = 2048
+    d = synth.draw(E, T, seed=500 + T, p_term=0.0, p_trunc=0.0)
+    assert not d["terminated"].any() and not d["truncated"].any()
+    dd = to_dev(d)
+    for name in NAMES:
+        with_flags = _np(run_gpu(name, dd))
+        without = _np(run_gpu(name, dd, term=False, trunc=False))
+        for k in with_flags:
+            err = parity_err(with_flags[k], without[k])
+            assert err <= 1e-6, "%s %s T=%d: zero flags vs no flags differ by %.3g" % (name, k, T, err)
