@@ -251,6 +251,63 @@ def copy_same_bytes(torch, device, nbytes, reps=50):
     return 2 * half * reps / secs / 1e9
 
 
+# Arrays one estimator call streams per step: float32 inputs, one-byte flag
+# arrays, float32 outputs.  The [E] row values and the sparse truncation
+# bootstraps are left out (under 0.2% of the bytes at 256 steps).
+PROBE_MIX = {
+    "discounted_returns": (1, 2, 1), "td_lambda": (2, 2, 1), "gae": (2, 2, 1), "vtrace": (3, 2, 2),
+    "retrace": (5, 2, 1), "eligibility_traces": (1, 2, 1), "episodic_prefix_sum": (1, 2, 1),
+}
+PROBE_LIB = os.path.join(ROOT, "linear_recurrence_scan_reverse_amd", "libstreamprobe.so")
+
+
+def probe_same_mix(torch, device, n, mix, reps=50):
+    """Per-launch us of the plain streaming probe (libstreamprobe.so) moving one
+    estimator call's arrays (mix = float inputs, flag arrays, float outputs; n
+    elements each), over rotating buffer sets above 1 GiB with HIP events on the
+    launch stream; None when the probe library is not built."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        return None
+    fn = ctypes.CDLL(PROBE_LIB).stream_probe
+    P = ctypes.POINTER(ctypes.c_void_p)
+    fn.restype = ctypes.c_int
+    fn.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
+    nr, nf, nw = mix
+    set_bytes = n * (4 * nr + nf + 4 * nw)
+    nsets = int(min(64, max(2, -(-(1 << 30) // set_bytes) + 1)))
+    keep, calls = [], []
+    for _ in range(nsets):
+        ins = [torch.ones(n, dtype=torch.float32, device=device) for _ in range(nr)]
+        fls = [torch.zeros(n, dtype=torch.uint8, device=device) for _ in range(nf)]
+        outs = [torch.empty(n, dtype=torch.float32, device=device) for _ in range(nw)]
+        keep.append((ins, fls, outs))
+        calls.append(((ctypes.c_void_p * 5)(*[t.data_ptr() for t in ins]),
+                      (ctypes.c_void_p * 2)(*[t.data_ptr() for t in fls]),
+                      (ctypes.c_void_p * 2)(*[t.data_ptr() for t in outs])))
+    st = torch.cuda.current_stream(device)
+
+    def launch(i):
+        a, f, o = calls[i % nsets]
+        rc = fn(a, nr, f, nf, o, nw, n, ctypes.c_void_p(st.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("stream_probe failed with %d" % rc)
+
+    for i in range(nsets):
+        launch(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(st)
+    for i in range(reps):
+        launch(i)
+    e.record(st)
+    e.synchronize()
+    us = s.elapsed_time(e) * 1e3 / reps
+    del keep, calls
+    return us
+
+
 def read_traffic(est, workload):
     """HBM bytes per launch of one estimator's kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a calibration copy), or None
@@ -546,8 +603,15 @@ def main():
     for n in names:
         per[n]["copy_same_bytes_GBps"] = round(copy_same_bytes(torch, device, per[n]["alg_bytes"]), 1)
         per[n]["frac_of_copy"] = round(per[n]["GBps"] / per[n]["copy_same_bytes_GBps"], 4)
-        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  %5.1f%% of a same-size copy" % (
-            n, per[n]["us_per_launch"], per[n]["GBps"], 100 * per[n]["frac_of_peak"], 100 * per[n]["frac_of_copy"]))
+        pu = probe_same_mix(torch, device, w.E * w.T, PROBE_MIX[n]) if n in PROBE_MIX else None
+        probe_txt = ""
+        if pu is not None:
+            per[n]["stream_probe_us"] = round(pu, 3)
+            per[n]["frac_of_stream_probe"] = round(pu / per[n]["us_per_launch"], 4)
+            probe_txt = "  %5.1f%% of a same-mix stream (%.2f us)" % (100 * per[n]["frac_of_stream_probe"], pu)
+        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  %5.1f%% of a same-size copy%s" % (
+            n, per[n]["us_per_launch"], per[n]["GBps"], 100 * per[n]["frac_of_peak"], 100 * per[n]["frac_of_copy"],
+            probe_txt))
 
     # ---- the other entry points (not part of the step): the one-pass returns + TD(lambda)
     # entry and the generic episode-cut recurrence

@@ -21,6 +21,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "librlscan.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# the bench's streaming-ceiling probe: a library of its own, not part of librlscan
+PROBE_SRC = os.path.join(CSRC, "probe", "stream_probe.hip")
+PROBE_PATH = os.path.join(PKG, "libstreamprobe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("RLSCAN_OFFLOAD_ARCH", "gfx950")
 
@@ -69,9 +72,22 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (res.stdout, res.stderr))
     os.replace(tmp, LIB_PATH)
+    build_probe()
     if verbose:
-        print("built %s from %d sources" % (LIB_PATH, len(srcs)), file=sys.stderr)
+        print("built %s from %d sources (and %s)" % (LIB_PATH, len(srcs), os.path.basename(PROBE_PATH)),
+              file=sys.stderr)
     return LIB_PATH
+
+
+def build_probe() -> str:
+    """Compile the bench's streaming-ceiling probe into its own shared library."""
+    tmp = PROBE_PATH + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBE_SRC, res.stdout, res.stderr))
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
 
 
 if __name__ == "__main__":
