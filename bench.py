@@ -603,7 +603,11 @@ def main():
     for n in names:
         per[n]["copy_same_bytes_GBps"] = round(copy_same_bytes(torch, device, per[n]["alg_bytes"]), 1)
         per[n]["frac_of_copy"] = round(per[n]["GBps"] / per[n]["copy_same_bytes_GBps"], 4)
-        pu = probe_same_mix(torch, device, w.E * w.T, PROBE_MIX[n]) if n in PROBE_MIX else None
+        mix = None
+        if n in PROBE_MIX:  # as many flag arrays as the call reads
+            nflags = int("terminated" in d) + int("truncated" in d)
+            mix = (PROBE_MIX[n][0], min(PROBE_MIX[n][1], nflags), PROBE_MIX[n][2])
+        pu = probe_same_mix(torch, device, w.E * w.T, mix) if mix else None
         probe_txt = ""
         if pu is not None:
             per[n]["stream_probe_us"] = round(pu, 3)

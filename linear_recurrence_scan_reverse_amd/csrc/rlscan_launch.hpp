@@ -65,7 +65,9 @@ constexpr bool kOneShotEst = __is_same(Est, Retrace) || __is_same(Est, Vtrace);
 // Whether a call takes the pipelined kernel with one item per team: a grid
 // that holds a team for every row group, each team loading its row's flags
 // and inputs at once and exiting after one store, instead of the persistent
-// grid that prefetches a team's next item.  Measured with flags present over
+// grid that prefetches a team's next item (or the streaming kernel).  Without
+// flag arrays (16384 x 256: Retrace 22.6 -> 19.0 us, V-trace 20.0 -> 17.9 us;
+// 4096 x 256: 9.3 -> 6.8 and 7.5 -> 6.7 us) and with them, measured over
 // E in {4096, 16384, 65536} x T in {64 .. 1024} against the routing below:
 // Retrace faster at every point (16384 x 256: 22.6 -> 20.6 us; 4096 x 256:
 // 11.4 -> 7.5 us; 2048 x 1024: 13.4 -> 12.1 us), V-trace faster up to 512
@@ -82,7 +84,6 @@ inline bool prefer_oneshot(const KernelArgs& a, int esize) {
   if constexpr (!kOneShotEst<Est>) {
     return false;
   } else {
-    if (!a.has_term && !a.has_trunc) return false;
     if constexpr (__is_same(Est, Retrace)) return a.T <= 1024;
     if constexpr (__is_same(Est, Vtrace)) return a.T <= (esize == 4 ? 512 : 256);
     return false;
