@@ -45,3 +45,27 @@ def test_rejects_null_and_misaligned_pointers(fn):
     assert fn(_ptrs(8), 1, None, 0, good_out, 1, 16, None) == -1      # input not 16-byte aligned
     assert fn(good_in, 1, _ptrs(2), 1, good_out, 1, 16, None) == -1  # flags not 4-byte aligned
     assert fn(good_in, 1, None, 0, _ptrs(4), 1, 16, None) == -1       # output not 16-byte aligned
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nr,nf,nw", [(1, 2, 1), (2, 2, 1), (3, 2, 2), (5, 2, 1), (1, 0, 1), (4, 1, 2)])
+def test_probe_moves_every_array(fn, nr, nf, nw):
+    """The probe reads every input and flag array and writes every output: output k
+    is the elementwise sum of the inputs plus k, plus 1 in lane x of a 4-element
+    group whose flag bytes are not all zero."""
+    import torch
+    n = 4 * 1000
+    g = torch.Generator(device="cpu").manual_seed(nr * 100 + nf * 10 + nw)
+    ins = [torch.randn(n, generator=g).cuda() for _ in range(nr)]
+    fls = [(torch.rand(n, generator=g) < 0.05).to(torch.uint8).cuda() for _ in range(nf)]
+    outs = [torch.full((n,), float("nan"), device="cuda") for _ in range(nw)]
+    rc = fn(_ptrs(*[t.data_ptr() for t in ins]), nr, _ptrs(*[t.data_ptr() for t in fls]), nf,
+            _ptrs(*[t.data_ptr() for t in outs]), nw, n, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    ref = torch.stack([t.cpu() for t in ins]).sum(0).view(-1, 4)
+    if nf:
+        any_flag = torch.stack([t.cpu() for t in fls]).amax(0).view(-1, 4).amax(1) > 0
+        ref[:, 0] += any_flag.float()
+    for k, o in enumerate(outs):
+        assert torch.allclose(o.cpu().view(-1, 4), ref + k, rtol=1e-6, atol=1e-5), "output %d" % k
