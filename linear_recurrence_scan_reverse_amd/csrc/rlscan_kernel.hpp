@@ -185,6 +185,22 @@ __device__ __forceinline__ unsigned shift_up_u32(unsigned v) {
 }
 
 // Broadcast of lane (group start + L - 1) to the group.
+// Retrace trace coefficient c = lam * min(1, pi / mu) without an fp64
+// division: the fp32 reciprocal of mu (good to about 1e-7) refined by one
+// Newton step in fp64, which squares its error (about 1e-14), times pi.  Used
+// by the 16-bit storage formats, where the pipelined kernel is bound by vector
+// instructions: at 16384 x 256 Retrace in bfloat16 ran 16.4 -> 15.3 us.  In
+// float32 the kernel streams at its byte mix's speed and the fp64 division
+// measured 0.15-0.7 us faster, so float32 keeps it.  mu = 0 (or a denormal)
+// gives a NaN quotient and so c = lam, as pi / 0 = inf does with the division.
+__device__ __forceinline__ double retrace_c_fast(double lam, float pi, float mu) {
+  const double m = (double)mu;
+  const double r0 = (double)__builtin_amdgcn_rcpf(mu);
+  const double r1 = __builtin_fma(r0, __builtin_fma(-m, r0, 1.0), r0);
+  const double ratio = (double)pi * r1;
+  return lam * (ratio < 1.0 ? ratio : 1.0);
+}
+
 template <int L>
 __device__ __forceinline__ double group_last_f64(double v, int lane) {
   if constexpr (L == 64) {
@@ -474,7 +490,9 @@ template <int K> struct LanePairs {
 // Build the K pairs of one lane.  cs: column of the lane's lowest-addressed
 // step; nv: steps inside the row (VEC: always K); tbits / rbits: terminated /
 // truncated bit masks (bit m = memory index m).
-template <class Est, int K, bool VEC>
+// FASTDIV: Retrace's quotient pi / mu by retrace_c_fast instead of an fp64
+// division.
+template <class Est, int K, bool VEC, bool FASTDIV = false>
 __device__ __forceinline__ LanePairs<K> build_pairs(const LaneIn<Est, K>& d, const ScanScalars& sc, unsigned tbits,
                                                     unsigned rbits, uint32_t cs, int64_t T, int nv,
                                                     bool team_first_lane, const PredIn& pred) {
@@ -502,8 +520,12 @@ __device__ __forceinline__ LanePairs<K> build_pairs(const LaneIn<Est, K>& d, con
   if constexpr (Tr::kRetrace) {
 #pragma unroll
     for (int m = 0; m < K; ++m) {
-      const double ratio = (double)d.s[3][m] / (double)d.s[4][m];
-      cown[m] = lam * (ratio < 1.0 ? ratio : 1.0);
+      if constexpr (FASTDIV) {
+        cown[m] = retrace_c_fast(lam, d.s[3][m], d.s[4][m]);
+      } else {
+        const double ratio = (double)d.s[3][m] / (double)d.s[4][m];
+        cown[m] = lam * (ratio < 1.0 ? ratio : 1.0);
+      }
     }
   }
   float nb_v = 0.0f;
@@ -887,15 +909,19 @@ scan_kernel(const KernelArgs p) {
     PredIn pred{0.0f, 0.0, 0u};
     if constexpr (Tr::kRetrace) {
       pred.v = d.nb[0];
-      const double ratio = (double)d.nb[1] / (double)d.nb[2];
-      pred.c = q.nb_ok ? lam * (ratio < 1.0 ? ratio : 1.0) : 0.0;
+      if constexpr (!__is_same(S, F32S)) {
+        pred.c = q.nb_ok ? retrace_c_fast(lam, d.nb[1], d.nb[2]) : 0.0;
+      } else {
+        const double ratio = (double)d.nb[1] / (double)d.nb[2];
+        pred.c = q.nb_ok ? lam * (ratio < 1.0 ? ratio : 1.0) : 0.0;
+      }
     } else if constexpr (Tr::kNbValue) {
       pred.v = d.nb[0];
     } else if constexpr (Tr::kNbDone && USE_FLAGS) {
       const unsigned dn = ((unsigned)(d.nbf[0] != 0) & tmask) | ((unsigned)(d.nbf[1] != 0) & rmask);
       pred.done = (q.nb_ok && dn) ? 1u : 0u;
     }
-    const LanePairs<K> lp = build_pairs<Est, K, VEC>(d, sc, tbits, rbits, q.cs, T, nv, team_first_lane, pred);
+    const LanePairs<K> lp = build_pairs<Est, K, VEC, !__is_same(S, F32S)>(d, sc, tbits, rbits, q.cs, T, nv, team_first_lane, pred);
 
     // ---- (a3) serial fold, (a4) wave scan over lanes
     const AB incl = lane_scan<(W > 1 ? 64 : L)>(fold_lane<K>(lp.e));
