@@ -490,8 +490,8 @@ template <int K> struct LanePairs {
 // Build the K pairs of one lane.  cs: column of the lane's lowest-addressed
 // step; nv: steps inside the row (VEC: always K); tbits / rbits: terminated /
 // truncated bit masks (bit m = memory index m).
-// FASTDIV: Retrace's quotient pi / mu by retrace_c_fast instead of an fp64
-// division.
+// FASTDIV (16-bit storage formats): Retrace's quotient pi / mu by
+// retrace_c_fast instead of an fp64 division, and V-trace's exp by __expf.
 template <class Est, int K, bool VEC, bool FASTDIV = false>
 __device__ __forceinline__ LanePairs<K> build_pairs(const LaneIn<Est, K>& d, const ScanScalars& sc, unsigned tbits,
                                                     unsigned rbits, uint32_t cs, int64_t T, int nv,
@@ -578,7 +578,10 @@ __device__ __forceinline__ LanePairs<K> build_pairs(const LaneIn<Est, K>& d, con
         c.a = is_cut ? 0.0 : gl;
         c.b = __builtin_fma(gamma, nu, r) - (double)d.s[1][m];
       } else if constexpr (Tr::kVtrace) {
-        const float ratio = expf(d.s[2][m]);
+        // 16-bit formats (FASTDIV): the hardware exp2 of x log2(e), about 1e-7
+        // relative, far below a 16-bit unit (bfloat16 V-trace 16.4 -> 15.6 us at
+        // 16384 x 256); float32 keeps the libm expf
+        const float ratio = FASTDIV ? __expf(d.s[2][m]) : expf(d.s[2][m]);
         const double rh = (double)fminf(ratio, sc.rho_bar);
         const double ct = (double)fminf(ratio, sc.c_bar);
         c.a = is_cut ? 0.0 : gl * ct;

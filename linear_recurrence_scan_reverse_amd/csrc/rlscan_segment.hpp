@@ -152,7 +152,8 @@ __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t se
       }
     }
 
-    const LanePairs<K> lp = build_pairs<Est, K, VEC>(d, sc, tbits, rbits, cs, T, nv, first_lane, pred);
+    // 16-bit formats: the fast Retrace quotient and V-trace exp (build_pairs)
+    const LanePairs<K> lp = build_pairs<Est, K, VEC, !__is_same(S, F32S)>(d, sc, tbits, rbits, cs, T, nv, first_lane, pred);
     const AB incl = lane_scan<64>(fold_lane<K>(lp.e));
     if constexpr (AGG) {
       const double at_ = group_last_f64<64>(incl.a, lane);

@@ -179,7 +179,8 @@ __global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p, int64_t 
       }
     }
 
-    const LanePairs<K> lp = build_pairs<Est, K, false>(d, sc, tbits, rbits, cs, T, nv, true, pred);
+    // 16-bit formats: the fast Retrace quotient and V-trace exp (build_pairs)
+    const LanePairs<K> lp = build_pairs<Est, K, false, !__is_same(S, F32S)>(d, sc, tbits, rbits, cs, T, nv, true, pred);
     const AB agg = fold_lane<K>(lp.e);
     s_a[w][lane] = agg.a;
     s_b[w][lane] = agg.b;
