@@ -40,10 +40,12 @@ inline LaunchShape pick_shape(int64_t T) {
 // and GAE 13.0 -> 11.7 us, traces and prefix sums 10.1 -> 9.5 us, discounted
 // returns 11.0 -> 10.5 us (with 4 blocks per CU: its usual 8 do not fit at 8
 // steps per lane; 65536 x 256: 32.0 -> 28.6 us); V-trace unchanged and Retrace
-// 17.4 -> 18.1 us, so those two keep 4 steps per lane.
+// 17.4 -> 18.1 us, so those two keep 4 steps per lane -- except V-trace in the
+// one-item form (one: the call takes it), where 8 measured faster at
+// 16384 x 256 (bfloat16 15.3 -> 14.8 us; Retrace there 15.4 -> 16.4 us).
 template <class Est>
-inline LaunchShape pick_shape_16(int64_t T) {
-  if (__is_same(Est, Vtrace) || __is_same(Est, Retrace)) return pick_shape(T);
+inline LaunchShape pick_shape_16(int64_t T, bool one) {
+  if (__is_same(Est, Retrace) || (__is_same(Est, Vtrace) && !one)) return pick_shape(T);
   if (T <= 64) return pick_shape(T);
   if (T <= 128) return {16, 8, 1};
   if (T <= 256) return {32, 8, 1};
@@ -374,8 +376,9 @@ hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
       default: break;
     }
   }
-  LaunchShape sh = pick_shape_16<Est>(a.T);
-  sh.one = prefer_oneshot<Est>(a, (int)sizeof(typename S::T));
+  const bool one = prefer_oneshot<Est>(a, (int)sizeof(typename S::T));
+  LaunchShape sh = pick_shape_16<Est>(a.T, one);
+  sh.one = one;
   switch (sh.W * 1000 + sh.L * 10 + sh.K) {
     case 1000 + 160 + 8: return launch_shape<Est, 16, 8, 1, S>(a, s, sh);
     case 1000 + 320 + 8: return launch_shape<Est, 32, 8, 1, S>(a, s, sh);
