@@ -62,7 +62,8 @@ inline int blocks_per_cu(const LaunchShape& sh) { return (__is_same(Est, Discoun
 // Estimators with a one-item-per-team form of the pipelined kernel (see
 // prefer_oneshot).
 template <class Est>
-constexpr bool kOneShotEst = __is_same(Est, Retrace) || __is_same(Est, Vtrace);
+constexpr bool kOneShotEst = __is_same(Est, Retrace) || __is_same(Est, Vtrace) || __is_same(Est, DiscountedReturn) ||
+                             __is_same(Est, TdLambda) || __is_same(Est, Gae);
 
 // Whether a call takes the pipelined kernel with one item per team: a grid
 // that holds a team for every row group, each team loading its row's flags
@@ -77,10 +78,16 @@ constexpr bool kOneShotEst = __is_same(Est, Retrace) || __is_same(Est, Vtrace);
 // 1024 (4096 x 1024: 20.5 -> 21.3 us).  With 16-bit storage (bfloat16, same
 // grid) Retrace again gained at every point (4096 x 256: 10.5 -> 6.6 us;
 // 65536 x 256: 61.1 -> 56.1 us) and V-trace up to 256 steps (65536 x 256:
-// 56.6 -> 51.8 us) but lost from 512 (16384 x 512: 29.6 -> 31.2 us).  The
-// five lighter estimators ran slower or no faster than on the streaming
-// kernel.  Rows up to 1024 steps are one tile of one team.  esize: bytes per
-// stored value.
+// 56.6 -> 51.8 us) but lost from 512 (16384 x 512: 29.6 -> 31.2 us).  In
+// float32 the five lighter estimators ran slower or no faster than on the
+// streaming kernel.  In 16-bit storage (where they run on the persistent
+// pipelined kernel, not the streaming one; bfloat16 grid over E in
+// {4096, 16384, 65536} x T in {64 .. 512}) TD(lambda) and GAE gained at every
+// point but 4096 x 64 (16384 x 128: 10.2 -> 6.9 us; 4096 x 512: 11.9 ->
+// 7.3 us; 65536 x 256: 32.7 -> 28.8 us), and discounted returns gained only
+// with rows of 257 to 512 steps (4096 x 512: 11.0 -> 7.3 us; 16384 x 512:
+// 17.2 -> 14.9 us; 4096 x 256: 7.2 -> 9.3 us).  Rows up to 1024 steps are one
+// tile of one team.  esize: bytes per stored value.
 template <class Est>
 inline bool prefer_oneshot(const KernelArgs& a, int esize) {
   if constexpr (!kOneShotEst<Est>) {
@@ -88,7 +95,9 @@ inline bool prefer_oneshot(const KernelArgs& a, int esize) {
   } else {
     if constexpr (__is_same(Est, Retrace)) return a.T <= 1024;
     if constexpr (__is_same(Est, Vtrace)) return a.T <= (esize == 4 ? 512 : 256);
-    return false;
+    if (esize != 2) return false;
+    if constexpr (__is_same(Est, DiscountedReturn)) return a.T > 256 && a.T <= 512;
+    return a.T <= 512;  // TD(lambda), GAE
   }
 }
 
