@@ -676,6 +676,9 @@ def main():
         "traffic_source": traffic_src,
         "alg_bytes_per_launch": per[dom]["alg_bytes"],
         "us_per_launch": per[dom]["us_per_launch"],
+        # the same kernel against a plain stream of its own arrays (practical ceiling)
+        "stream_probe_us": per[dom].get("stream_probe_us"),
+        "frac_of_stream_probe": per[dom].get("frac_of_stream_probe"),
     }
 
     ceiling = copy_ceiling(torch, device)
