@@ -63,7 +63,8 @@ inline int blocks_per_cu(const LaunchShape& sh) { return (__is_same(Est, Discoun
 // prefer_oneshot).
 template <class Est>
 constexpr bool kOneShotEst = __is_same(Est, Retrace) || __is_same(Est, Vtrace) || __is_same(Est, DiscountedReturn) ||
-                             __is_same(Est, TdLambda) || __is_same(Est, Gae);
+                             __is_same(Est, TdLambda) || __is_same(Est, Gae) || __is_same(Est, EligibilityTrace) ||
+                             __is_same(Est, EpisodicPrefixSum);
 
 // Whether a call takes the pipelined kernel with one item per team: a grid
 // that holds a team for every row group, each team loading its row's flags
@@ -86,8 +87,11 @@ constexpr bool kOneShotEst = __is_same(Est, Retrace) || __is_same(Est, Vtrace) |
 // point but 4096 x 64 (16384 x 128: 10.2 -> 6.9 us; 4096 x 512: 11.9 ->
 // 7.3 us; 65536 x 256: 32.7 -> 28.8 us), and discounted returns gained only
 // with rows of 257 to 512 steps (4096 x 512: 11.0 -> 7.3 us; 16384 x 512:
-// 17.2 -> 14.9 us; 4096 x 256: 7.2 -> 9.3 us).  Rows up to 1024 steps are one
-// tile of one team.  esize: bytes per stored value.
+// 17.2 -> 14.9 us; 4096 x 256: 7.2 -> 9.3 us).  The 16-bit eligibility traces
+// and prefix sums, against the streaming kernel, gained from 16384 rows up
+// (65536 x 256: 26.3 -> 21.1 us; 16384 x 512: 14.6 -> 12.8 us) and lost
+// 0.3 us at 4096 x 64.  Rows up to 1024 steps are one tile of one team.
+// esize: bytes per stored value.
 template <class Est>
 inline bool prefer_oneshot(const KernelArgs& a, int esize) {
   if constexpr (!kOneShotEst<Est>) {
@@ -97,7 +101,7 @@ inline bool prefer_oneshot(const KernelArgs& a, int esize) {
     if constexpr (__is_same(Est, Vtrace)) return a.T <= (esize == 4 ? 512 : 256);
     if (esize != 2) return false;
     if constexpr (__is_same(Est, DiscountedReturn)) return a.T > 256 && a.T <= 512;
-    return a.T <= 512;  // TD(lambda), GAE
+    return a.T <= 512;  // TD(lambda), GAE, eligibility traces, prefix sums
   }
 }
 
@@ -376,8 +380,9 @@ template <class Est, class S>
 hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const int64_t len = segment_length(a)) return launch_segmented<Est, S>(a, s, len);
+  const bool one = prefer_oneshot<Est>(a, (int)sizeof(typename S::T));
   if constexpr (Traits<Est>::kForwardRl) {
-    const int team = stream_team<S>(a);
+    const int team = one ? 0 : stream_team<S>(a);
     switch ((team != 0 && prefer_stream<Est>(a, team)) ? team : 0) {
       case 16: return launch_stream<Est, 16, S>(a, s);
       case 32: return launch_stream<Est, 32, S>(a, s);
@@ -385,7 +390,6 @@ hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
       default: break;
     }
   }
-  const bool one = prefer_oneshot<Est>(a, (int)sizeof(typename S::T));
   LaunchShape sh = pick_shape_16<Est>(a.T, one);
   sh.one = one;
   switch (sh.W * 1000 + sh.L * 10 + sh.K) {
