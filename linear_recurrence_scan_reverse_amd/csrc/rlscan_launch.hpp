@@ -166,7 +166,9 @@ inline hipError_t launch_one(const KernelArgs& a, hipStream_t s, const LaunchSha
   KernelArgs arg = a;
   void* params[] = {&arg};
   if constexpr (kOneShotEst<Est>) {
-    if (sh.one)
+    // the one-item grid is not capped: past 2^31 work-items (e.g. 2^27 rows of
+    // 64 steps) the persistent grid below takes the call
+    if (sh.one && blocks * BLOCK < (int64_t(1) << 31))
       return hipLaunchKernel(reinterpret_cast<const void*>(&scan_kernel<Est, L, K, W, R, VEC, OPT, S, true>),
                              dim3((unsigned)blocks), dim3(BLOCK), params, 0, s);
   }
