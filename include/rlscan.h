@@ -206,7 +206,8 @@ rlscan_status rlscan_eligibility_traces(const float *x, const uint8_t *terminate
  * waves covers 64 columns of a row; full speed needs E*ceil(D/64) blocks in
  * the thousands.
  * Errors as above, with D < 0, T*D >= RLSCAN_MAX_T or E*T*D overflowing
- * reported as RLSCAN_ERR_SHAPE. */
+ * reported as RLSCAN_ERR_SHAPE; a grid past 2^32 - 1 work-items
+ * (E*ceil(D/64) >= 2^24 blocks) is refused with RLSCAN_ERR_HIP. */
 rlscan_status rlscan_eligibility_traces_vec(const float *x, const uint8_t *terminated,
                                             const uint8_t *truncated, const float *init, float *traces,
                                             int64_t E, int64_t T, int64_t D, float gamma, float lambda,
@@ -267,9 +268,12 @@ rlscan_status rlscan_linear_scan_segmented(const float *a, const float *b, const
  *         Workflow" step 2, lists contiguous and strided layouts).  This
  *         applies to rewards, values and every other [E,T] input or output,
  *         flags and trunc_bootstrap included; [E] arrays are unchanged.  E and
- *         T keep their meaning (environments, steps).  Time-major calls are
- *         one kernel whose blocks each cover 64 environments; full speed
- *         needs E in the thousands.
+ *         T keep their meaning (environments, steps).  Time-major calls run
+ *         blocks that each cover 64 environments (one launch; three when
+ *         there are fewer groups of 64 than compute units and the columns are
+ *         long); full speed needs E in the thousands.  A time-major grid past
+ *         2^32 - 1 work-items (about 2^28 environments) is refused with
+ *         RLSCAN_ERR_HIP.
  * An unknown fmt or layout is RLSCAN_ERR_PARAM.  (RLSCAN_FORMAT_F32,
  * RLSCAN_LAYOUT_ENV_MAJOR) is exactly the float32 entry.
  * ------------------------------------------------------------------------ */

@@ -447,7 +447,8 @@ inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
   const int64_t groups = (a.E + 63) / 64;
   int64_t seg_len = tm_segment_length(a);
   int64_t nseg = seg_len ? a.T / seg_len : 1;  // the last segment takes the remainder
-  if (groups * nseg > INT32_MAX || nseg > kTmMaxSeg) return hipErrorInvalidConfiguration;
+  // grids of at most 2^32 - 1 work-items (about 2^28 environments); larger calls are refused
+  if (groups * nseg * 64 * W > (int64_t)UINT32_MAX || nseg > kTmMaxSeg) return hipErrorInvalidConfiguration;
   KernelArgs arg = a;
   void* params[] = {&arg, &seg_len, &nseg};
   const dim3 block(64 * W);
