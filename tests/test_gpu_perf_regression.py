@@ -37,3 +37,33 @@ def test_per_estimator_time_at_16384x256():
     torch.cuda.empty_cache()
     slow = {n: round(per[n]["us_per_launch"], 2) for n in CEILING_US if per[n]["us_per_launch"] > CEILING_US[n]}
     assert not slow, "slower than the ceiling (us): %s" % slow
+
+
+# bfloat16 storage, same workload and method; 1.5x above the current kernels
+# (discounted returns 10.8 us, TD(lambda) / GAE 10.3 us, V-trace 14.8 us,
+# Retrace 15.5 us, traces / prefix sums 8.4 us), which include the one-item
+# routing of the 16-bit formats.
+CEILING_BF16_US = {
+    "discounted_returns": 16.5,
+    "td_lambda": 15.5,
+    "gae": 15.5,
+    "vtrace": 22.0,
+    "retrace": 23.5,
+    "eligibility_traces": 12.5,
+    "episodic_prefix_sum": 12.5,
+}
+
+
+def test_per_estimator_time_at_16384x256_bfloat16():
+    import torch
+    import bench
+    from linear_recurrence_scan_reverse_amd import synth
+    w = synth.WORKLOADS["all7_16384x256"]
+    d = synth.workload_inputs(w)
+    runner = bench.Runner(w, d, 9, torch.device("cuda", 0), storage="bf16")
+    per = bench.time_estimators(runner, list(CEILING_BF16_US), d, w, 100)
+    del runner
+    torch.cuda.empty_cache()
+    slow = {n: round(per[n]["us_per_launch"], 2) for n in CEILING_BF16_US
+            if per[n]["us_per_launch"] > CEILING_BF16_US[n]}
+    assert not slow, "slower than the ceiling (us): %s" % slow
