@@ -51,8 +51,12 @@
  *             must not be read or shared before the stream reaches the end of
  *             the call, which the rule above already implies).
  * Errors      Validation happens before any HIP call and returns:
- *               RLSCAN_ERR_SHAPE  E < 0, T < 0, T >= RLSCAN_MAX_T (2^30), or
- *                                 E*T overflows int64;
+ *               RLSCAN_ERR_SHAPE  E < 0, T < 0, T >= RLSCAN_MAX_T (2^30),
+ *                                 E*T overflows int64, or the launch grid
+ *                                 would pass 2^32 - 1 work-items: time-major
+ *                                 calls with ceil(E/64) > 4194303 (about
+ *                                 2^28 environments), vector traces with
+ *                                 E*ceil(D/64) > 16777215;
  *               RLSCAN_ERR_PARAM  a parameter is non-finite or out of range;
  *               RLSCAN_ERR_NULL   a required pointer is NULL while E*T > 0;
  *               RLSCAN_ERR_ALIGN  a value pointer is not aligned to its element
@@ -94,7 +98,9 @@ const char *rlscan_status_string(rlscan_status status);
 /* Static version string, e.g. "librlscan 0.1.0 gfx950". */
 const char *rlscan_version(void);
 
-/* Discounted return (Monte-Carlo return with bootstrap at cuts):
+/* Discounted return (Monte-Carlo return with bootstrap at cuts; the
+ * discounted return of Sutton & Barto 2018, eq. 3.9, truncated at episode
+ * ends and bootstrapped as in section 3 of gist.science's "Methodologie"):
  *   G_t = r_t + gamma * (G_{t+1} while the episode continues, else the
  *         successor value of the cut).
  * Recurrence: a_t = gamma*k_t, b_t = r_t + gamma*(1-k_t)*boot_t, with k_t = 1
@@ -206,8 +212,8 @@ rlscan_status rlscan_eligibility_traces(const float *x, const uint8_t *terminate
  * waves covers 64 columns of a row; full speed needs E*ceil(D/64) blocks in
  * the thousands.
  * Errors as above, with D < 0, T*D >= RLSCAN_MAX_T or E*T*D overflowing
- * reported as RLSCAN_ERR_SHAPE; a grid past 2^32 - 1 work-items
- * (E*ceil(D/64) >= 2^24 blocks) is refused with RLSCAN_ERR_HIP. */
+ * reported as RLSCAN_ERR_SHAPE, and so is a grid past 2^32 - 1 work-items
+ * (E*ceil(D/64) >= 2^24 blocks), before any HIP call. */
 rlscan_status rlscan_eligibility_traces_vec(const float *x, const uint8_t *terminated,
                                             const uint8_t *truncated, const float *init, float *traces,
                                             int64_t E, int64_t T, int64_t D, float gamma, float lambda,
@@ -272,8 +278,9 @@ rlscan_status rlscan_linear_scan_segmented(const float *a, const float *b, const
  *         blocks that each cover 64 environments (one launch; three when
  *         there are fewer groups of 64 than compute units and the columns are
  *         long); full speed needs E in the thousands.  A time-major grid past
- *         2^32 - 1 work-items (about 2^28 environments) is refused with
- *         RLSCAN_ERR_HIP.
+ *         2^32 - 1 work-items (ceil(E/64) > 4194303, about 2^28
+ *         environments) is refused with RLSCAN_ERR_SHAPE before any HIP
+ *         call.
  * An unknown fmt or layout is RLSCAN_ERR_PARAM.  (RLSCAN_FORMAT_F32,
  * RLSCAN_LAYOUT_ENV_MAJOR) is exactly the float32 entry.
  * ------------------------------------------------------------------------ */

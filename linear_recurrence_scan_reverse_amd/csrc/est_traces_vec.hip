@@ -38,7 +38,6 @@ struct TraceVecArgs {
   double decay;          // gamma * lambda
 };
 
-constexpr int kTvWaves = 4;   // waves per block: time chunks of a super-tile
 constexpr int kTvChunk = 16;  // steps per wave chunk
 
 template <class S, bool TM>
@@ -148,8 +147,8 @@ hipError_t launch_traces_vec(int fmt, bool time_major, const float* x, const uin
                              double lam, hipStream_t s) {
   TraceVecArgs a{x, term, trunc, init, out, E, T, D, gamma * lam};
   const int64_t blocks = E * ((D + 63) / 64);
-  // a grid of at most 2^32 - 1 work-items (launches past that are refused)
-  if (blocks * 64 * kTvWaves > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+  // a grid of at most 2^32 - 1 work-items (the C ABI refuses larger shapes first)
+  if (!tv_grid_ok(E, D)) return hipErrorInvalidConfiguration;
   const void* fn = fmt == 1   ? trace_vec_fn<Bf16S>(time_major)
                    : fmt == 2 ? trace_vec_fn<F16S>(time_major)
                               : trace_vec_fn<F32S>(time_major);

@@ -105,6 +105,10 @@ float* fp(void* p) { return static_cast<float*>(p); }
 
 bool layout_ok(rlscan_layout l) { return l == RLSCAN_LAYOUT_ENV_MAJOR || l == RLSCAN_LAYOUT_TIME_MAJOR; }
 
+// Shapes whose grid would pass 2^32 - 1 work-items: time-major calls take one
+// block of 16 waves per 64 environments (about 2^28 environments at most).
+bool grid_fits(rlscan_layout l, int64_t E) { return l != RLSCAN_LAYOUT_TIME_MAJOR || rlscan::tm_grid_ok(E); }
+
 // One estimator, one storage format, one layout.
 template <class Est>
 hipError_t launch_fmt(rlscan_format f, rlscan_layout l, const KernelArgs& a, hipStream_t s) {
@@ -133,6 +137,7 @@ rlscan_status impl_discounted_returns(rlscan_format f, rlscan_layout l, const vo
   if (st != RLSCAN_OK) return st;
   if (!in_unit(gamma) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
   if (E * T == 0) return RLSCAN_OK;
+  if (!grid_fits(l, E)) return RLSCAN_ERR_SHAPE;
   if (!rewards || !returns) return RLSCAN_ERR_NULL;
   if (misaligned(rewards, es)) return RLSCAN_ERR_ALIGN;
   Io io;
@@ -160,6 +165,7 @@ rlscan_status impl_td_lambda(rlscan_format f, rlscan_layout l, const void* rewar
   if (st != RLSCAN_OK) return st;
   if (!in_unit(gamma) || !in_unit(lambda) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
   if (E * T == 0) return RLSCAN_OK;
+  if (!grid_fits(l, E)) return RLSCAN_ERR_SHAPE;
   if (!rewards || !values || !returns) return RLSCAN_ERR_NULL;
   if (misaligned(rewards, es) || misaligned(values, es)) return RLSCAN_ERR_ALIGN;
   Io io;
@@ -193,6 +199,7 @@ rlscan_status impl_returns_td_lambda(rlscan_format f, rlscan_layout l, const voi
   if (st != RLSCAN_OK) return st;
   if (!in_unit(gamma) || !in_unit(lambda) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
   if (E * T == 0) return RLSCAN_OK;
+  if (!grid_fits(l, E)) return RLSCAN_ERR_SHAPE;
   if (!rewards || !values || !returns || !td_returns) return RLSCAN_ERR_NULL;
   if (misaligned(rewards, es) || misaligned(values, es)) return RLSCAN_ERR_ALIGN;
   Io io;
@@ -235,6 +242,7 @@ rlscan_status impl_gae(rlscan_format f, rlscan_layout l, const void* rewards, co
   if (st != RLSCAN_OK) return st;
   if (!in_unit(gamma) || !in_unit(lambda) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
   if (E * T == 0) return RLSCAN_OK;
+  if (!grid_fits(l, E)) return RLSCAN_ERR_SHAPE;
   if (!rewards || !values || !advantages) return RLSCAN_ERR_NULL;
   if (misaligned(rewards, es) || misaligned(values, es)) return RLSCAN_ERR_ALIGN;
   Io io;
@@ -269,6 +277,7 @@ rlscan_status impl_vtrace(rlscan_format f, rlscan_layout l, const void* rewards,
   if (!in_unit(gamma) || !in_unit(lambda) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
   if (!finite(rho_bar) || !finite(c_bar) || !(rho_bar > 0.0f) || !(c_bar > 0.0f)) return RLSCAN_ERR_PARAM;
   if (E * T == 0) return RLSCAN_OK;
+  if (!grid_fits(l, E)) return RLSCAN_ERR_SHAPE;
   if (!rewards || !values || !log_rhos || !vs) return RLSCAN_ERR_NULL;
   if (misaligned(rewards, es) || misaligned(values, es) || misaligned(log_rhos, es)) return RLSCAN_ERR_ALIGN;
   Io io;
@@ -306,6 +315,7 @@ rlscan_status impl_retrace(rlscan_format f, rlscan_layout l, const void* rewards
   if (st != RLSCAN_OK) return st;
   if (!in_unit(gamma) || !in_unit(lambda) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
   if (E * T == 0) return RLSCAN_OK;
+  if (!grid_fits(l, E)) return RLSCAN_ERR_SHAPE;
   if (!rewards || !q_values || !expected_q || !pi_prob || !mu_prob || !q_ret) return RLSCAN_ERR_NULL;
   if (misaligned(rewards, es) || misaligned(q_values, es) || misaligned(expected_q, es) ||
       misaligned(pi_prob, es) || misaligned(mu_prob, es))
@@ -344,6 +354,7 @@ rlscan_status impl_forward(rlscan_format f, rlscan_layout l, bool traces, const 
   if (st != RLSCAN_OK) return st;
   if (!in_unit(gamma) || !in_unit(lambda) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
   if (E * T == 0) return RLSCAN_OK;
+  if (!grid_fits(l, E)) return RLSCAN_ERR_SHAPE;
   if (!x || !out) return RLSCAN_ERR_NULL;
   if (misaligned(x, es) || misaligned(init, es)) return RLSCAN_ERR_ALIGN;
   Io io;
@@ -375,6 +386,7 @@ rlscan_status impl_linear_scan(rlscan_format f, rlscan_layout l, const void* a_c
   if (st != RLSCAN_OK) return st;
   if (es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
   if (E * T == 0) return RLSCAN_OK;
+  if (!grid_fits(l, E)) return RLSCAN_ERR_SHAPE;
   if (!a_coef || !b_coef || !x) return RLSCAN_ERR_NULL;
   if (misaligned(a_coef, es) || misaligned(b_coef, es) || misaligned(carry, es)) return RLSCAN_ERR_ALIGN;
   Io io;
@@ -405,6 +417,7 @@ rlscan_status impl_traces_vec(rlscan_format f, rlscan_layout l, const void* x, c
   if ((st = check_shape(E, T * D)) != RLSCAN_OK) return st;
   if (!in_unit(gamma) || !in_unit(lambda) || es == 0 || !layout_ok(l)) return RLSCAN_ERR_PARAM;
   if (E * T * D == 0) return RLSCAN_OK;
+  if (!rlscan::tv_grid_ok(E, D)) return RLSCAN_ERR_SHAPE;  // one block per row and 64 columns
   if (!x || !traces) return RLSCAN_ERR_NULL;
   if (misaligned(x, es) || misaligned(init, es)) return RLSCAN_ERR_ALIGN;
   Io io;
@@ -426,7 +439,7 @@ const char* rlscan_status_string(rlscan_status s) {
   switch (s) {
     case RLSCAN_OK: return "ok";
     case RLSCAN_ERR_NULL: return "a required pointer is NULL";
-    case RLSCAN_ERR_SHAPE: return "invalid shape: E or T negative, T >= 2^30, or E*T too large";
+    case RLSCAN_ERR_SHAPE: return "invalid shape: E or T negative, T >= 2^30, E*T too large, or a grid past 2^32 - 1 work-items";
     case RLSCAN_ERR_PARAM: return "invalid parameter: non-finite, or outside its range";
     case RLSCAN_ERR_HIP: return "HIP kernel launch failed";
     case RLSCAN_ERR_ALIGN: return "a value pointer is not aligned to its element size";

@@ -9,6 +9,7 @@
 #include <atomic>
 
 #include "rlscan_kernel.hpp"
+#include "rlscan_plan.hpp"
 #include "rlscan_segment.hpp"
 #include "rlscan_stream.hpp"
 #include "rlscan_timemajor.hpp"
@@ -290,27 +291,17 @@ inline bool prefer_stream(const KernelArgs& a, int L) {
 
 // ----------------------------------------------------------------- segmented path
 // Rows of at least kSegMinT steps, kSegMaxE rows or fewer, are cut into
-// segments so that passes 1 and 3 run about 32 waves per CU; segments hold at
-// least four tiles.  Returns the segment length, or 0 to scan whole rows.
+// segments (row_segments) so that passes 1 and 3 run about 32 waves per CU;
+// segments hold at least four tiles and the last one takes the remainder.
 // Measured: 1 x 262144 steps 12-14x faster than whole rows, 16 x 65536 3-4x;
 // at 256 rows whole-row teams already fill the GPU and win (the segmented
 // path reads its inputs twice).
-constexpr int64_t kSegMinT = 16384;
-constexpr int64_t kSegMaxE = 64;
-inline int64_t segment_length(const KernelArgs& a) {
-  if (a.T < kSegMinT || a.E > kSegMaxE) return 0;
-  const int64_t target = (int64_t)cu_count() * 32;
-  const int64_t nseg = (target + a.E - 1) / a.E;
-  int64_t len = (a.T + nseg - 1) / nseg;
-  len = (len + kSegTile - 1) / kSegTile * kSegTile;
-  if (len < 4 * kSegTile) len = 4 * kSegTile;
-  return len < a.T ? len : 0;
-}
+inline SegPlan segment_plan(const KernelArgs& a) { return row_segments(a.E, a.T, cu_count()); }
 
 template <class Est, int OPT, class S = F32S>
-inline hipError_t launch_segmented_opt(const KernelArgs& a, hipStream_t s, int64_t len) {
-  int64_t seg_len = len;
-  int64_t nseg = (a.T + len - 1) / len;
+inline hipError_t launch_segmented_opt(const KernelArgs& a, hipStream_t s, const SegPlan& plan) {
+  int64_t seg_len = plan.len;
+  int64_t nseg = plan.nseg;  // the last segment takes the remainder
   KernelArgs arg = a;
   void* params[] = {&arg, &seg_len, &nseg};
   const bool vec = vector_ok(a, 4, kSegTile, (int)sizeof(typename S::T));
@@ -329,25 +320,25 @@ inline hipError_t launch_segmented_opt(const KernelArgs& a, hipStream_t s, int64
 }
 
 template <class Est, class S = F32S>
-inline hipError_t launch_segmented(const KernelArgs& a, hipStream_t s, int64_t len) {
+inline hipError_t launch_segmented(const KernelArgs& a, hipStream_t s, const SegPlan& plan) {
   using Tr = Traits<Est>;
   const bool flags = a.has_term || a.has_trunc;
   if constexpr (Tr::kHasOut1) {
     const bool out1 = a.out1 != nullptr;
     if (flags)
-      return out1 ? launch_segmented_opt<Est, 3, S>(a, s, len) : launch_segmented_opt<Est, 1, S>(a, s, len);
-    return out1 ? launch_segmented_opt<Est, 2, S>(a, s, len) : launch_segmented_opt<Est, 0, S>(a, s, len);
+      return out1 ? launch_segmented_opt<Est, 3, S>(a, s, plan) : launch_segmented_opt<Est, 1, S>(a, s, plan);
+    return out1 ? launch_segmented_opt<Est, 2, S>(a, s, plan) : launch_segmented_opt<Est, 0, S>(a, s, plan);
   } else if constexpr (Tr::kUsesFlags) {
-    return flags ? launch_segmented_opt<Est, 1, S>(a, s, len) : launch_segmented_opt<Est, 0, S>(a, s, len);
+    return flags ? launch_segmented_opt<Est, 1, S>(a, s, plan) : launch_segmented_opt<Est, 0, S>(a, s, plan);
   } else {
-    return launch_segmented_opt<Est, 0, S>(a, s, len);
+    return launch_segmented_opt<Est, 0, S>(a, s, plan);
   }
 }
 
 template <class Est>
 hipError_t launch(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
-  if (const int64_t len = segment_length(a)) return launch_segmented<Est>(a, s, len);
+  if (const SegPlan plan = segment_plan(a); plan.len) return launch_segmented<Est>(a, s, plan);
   const bool one = prefer_oneshot<Est>(a, 4);
   const int team = one ? 0 : stream_team<F32S>(a);
   switch ((team != 0 && prefer_stream<Est>(a, team)) ? team : 0) {
@@ -381,7 +372,7 @@ hipError_t launch(const KernelArgs& in, hipStream_t s) {
 template <class Est, class S>
 hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
-  if (const int64_t len = segment_length(a)) return launch_segmented<Est, S>(a, s, len);
+  if (const SegPlan plan = segment_plan(a); plan.len) return launch_segmented<Est, S>(a, s, plan);
   const bool one = prefer_oneshot<Est>(a, (int)sizeof(typename S::T));
   if constexpr (Traits<Est>::kForwardRl) {
     const int team = one ? 0 : stream_team<S>(a);
@@ -422,33 +413,21 @@ template <class Est>
 constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 
 // Few column groups and long columns: blocks of MODE 0 would leave most CUs
-// idle and walk thousands of steps each, so time is cut into segments (see
-// tm_kernel) giving about two blocks per CU, of at least 256 steps and a
-// multiple of 256 (whole super-tiles; the parked float64 pair needs at most 8
-// rows); the last segment takes the remainder.  At most kTmMaxSeg segments
-// per column (the carry kernel's 16 waves x kTmCarrySeg).  Returns the
-// segment length, or 0 to scan whole columns.
-constexpr int64_t kTmSegStep = 256;
-constexpr int64_t kTmMaxSeg = 16 * kTmCarrySeg;
-inline int64_t tm_segment_length(const KernelArgs& a) {
-  const int64_t groups = (a.E + 63) / 64;
-  const int64_t cus = cu_count();
-  if (groups >= cus || a.T < 2 * kTmSegStep) return 0;
-  int64_t nseg = (2 * cus + groups - 1) / groups;
-  if (nseg > kTmMaxSeg) nseg = kTmMaxSeg;
-  int64_t len = (a.T + nseg - 1) / nseg;
-  len = (len + kTmSegStep - 1) / kTmSegStep * kTmSegStep;
-  return a.T / len >= 2 ? len : 0;
-}
-
+// idle and walk thousands of steps each, so time is cut into segments
+// (tm_segments; see tm_kernel) giving about two blocks per CU, of at least 256
+// steps and a multiple of 256 (whole super-tiles; the parked float64 pair
+// needs at most 8 rows); the last segment takes the remainder.  At most
+// kTmMaxSeg segments per column (the carry kernel's 16 waves x kTmCarrySeg).
 template <class Est, int OPT, class S>
 inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
   constexpr int W = tm_waves<Est>(), K = tm_chunk<Est>();
+  static_assert(W == kTmWaves, "the grid limit assumes kTmWaves waves per block");
   const int64_t groups = (a.E + 63) / 64;
-  int64_t seg_len = tm_segment_length(a);
-  int64_t nseg = seg_len ? a.T / seg_len : 1;  // the last segment takes the remainder
-  // grids of at most 2^32 - 1 work-items (about 2^28 environments); larger calls are refused
-  if (groups * nseg * 64 * W > (int64_t)UINT32_MAX || nseg > kTmMaxSeg) return hipErrorInvalidConfiguration;
+  const SegPlan plan = tm_segments(a.E, a.T, cu_count());
+  int64_t seg_len = plan.len;
+  int64_t nseg = plan.nseg;  // the last segment takes the remainder
+  // grids of at most 2^32 - 1 work-items (the C ABI refuses larger shapes first)
+  if (groups * nseg * 64 * W > kMaxWorkItems || nseg > kTmMaxSeg) return hipErrorInvalidConfiguration;
   KernelArgs arg = a;
   void* params[] = {&arg, &seg_len, &nseg};
   const dim3 block(64 * W);

@@ -22,10 +22,9 @@
 #pragma once
 
 #include "rlscan_kernel.hpp"
+#include "rlscan_plan.hpp"
 
 namespace rlscan {
-
-constexpr int kSegTile = 256;  // steps per tile (64 lanes x 4)
 
 // A double kept in the first 8 bytes at element `idx` of an output array in
 // storage format S (bit copies, element-aligned stores).
@@ -59,7 +58,9 @@ template <class S>
 constexpr int f64_elems() { return __is_same(S, F32S) ? 2 : 4; }
 
 // Passes 1 (AGG) and 3 (apply).  One wave per (row, segment); segments are
-// seg_len steps (a multiple of 256) and the last one of a row may be shorter.
+// seg_len steps (a multiple of 256), and the last one of a row takes the
+// remainder (seg_len to 2 seg_len - 1 steps), so the parked pair always lies
+// inside its own segment.
 // VEC: T % 256 == 0 and every array 16-byte aligned.
 template <class Est, bool AGG, bool VEC, int OPT, class S = F32S>
 __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t seg_len, int64_t nseg) {
@@ -77,8 +78,8 @@ __global__ void __launch_bounds__(256) seg_kernel(const KernelArgs p, int64_t se
   if (vrow >= p.E * nseg) return;  // (wave-uniform)
   const int64_t row = vrow / nseg;
   const int64_t seg = vrow - row * nseg;
-  const int64_t t_begin = seg * seg_len;
-  const int64_t t_end = (t_begin + seg_len < T) ? t_begin + seg_len : T;
+  const int64_t t_begin = seg_begin(seg, seg_len);
+  const int64_t t_end = seg_end(seg, seg_len, nseg, T);
   const int64_t ntl = (t_end - t_begin + kSegTile - 1) / kSegTile;
   const int64_t rb = row * T;  // element index of the row start
   const uint32_t last = (uint32_t)(T - 1);
@@ -200,7 +201,7 @@ __global__ void __launch_bounds__(256) seg_carry_kernel(const KernelArgs p, int6
     const int64_t k = k0 + lane;  // position in scan order
     const bool ok = k < nseg;
     const int64_t s = REV ? nseg - 1 - k : k;
-    const int64_t slot = base + (ok ? s : 0) * seg_len;
+    const int64_t slot = base + seg_begin(ok ? s : 0, seg_len);
     AB f{1.0, 0.0};
     if (ok) {
       f.a = get_f64<S>(p.out0, slot);

@@ -26,6 +26,7 @@
 #pragma once
 
 #include "rlscan_kernel.hpp"
+#include "rlscan_plan.hpp"
 
 namespace rlscan {
 
@@ -97,8 +98,8 @@ __global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p, int64_t 
   const int64_t grp = MODE == 0 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x % ngroups;
   const int64_t sidx = MODE == 0 ? 0 : (int64_t)blockIdx.x / ngroups;
   // this block's steps [t0, t1)
-  const int64_t t0 = MODE == 0 ? 0 : sidx * seg_len;
-  const int64_t t1 = (MODE == 0 || sidx == nseg - 1) ? T : t0 + seg_len;
+  const int64_t t0 = MODE == 0 ? 0 : seg_begin(sidx, seg_len);
+  const int64_t t1 = MODE == 0 ? T : seg_end(sidx, seg_len, nseg, T);
   // Addresses: a wave-uniform element index (step row + the block's first
   // column) plus a 32-bit lane offset, the lane's column clamped into the row
   // so every load stays inside the arrays.
@@ -232,7 +233,6 @@ __global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p, int64_t 
 // composes their maps, the wave maps meet in LDS, and every wave then walks
 // its segments from the value entering its first one, leaving each segment's
 // entering value in place of its map.  nseg <= 16 * kTmCarrySeg.
-constexpr int kTmCarrySeg = 16;
 template <class Est, class S = F32S>
 __global__ void __launch_bounds__(1024) tm_carry_kernel(const KernelArgs p, int64_t seg_len, int64_t nseg) {
   using Tr = Traits<Est>;
@@ -258,8 +258,8 @@ __global__ void __launch_bounds__(1024) tm_carry_kernel(const KernelArgs p, int6
     const int64_t k = k0 + j;
     if (j < q && k < nseg) {
       const int64_t sg = REV ? nseg - 1 - k : k;
-      a[j] = get_f64_col<S>(p.out0, sg * seg_len, E, e0, lo);
-      b[j] = get_f64_col<S>(p.out0, sg * seg_len + f64_rows<S>(), E, e0, lo);
+      a[j] = get_f64_col<S>(p.out0, seg_begin(sg, seg_len), E, e0, lo);
+      b[j] = get_f64_col<S>(p.out0, seg_begin(sg, seg_len) + f64_rows<S>(), E, e0, lo);
     }
   }
 #pragma unroll
@@ -279,7 +279,7 @@ __global__ void __launch_bounds__(1024) tm_carry_kernel(const KernelArgs p, int6
     const int64_t k = k0 + j;
     if (j < q && k < nseg) {
       const int64_t sg = REV ? nseg - 1 - k : k;
-      if (col_ok) put_f64_col<S>(p.out0, sg * seg_len, E, e0, lo, c);
+      if (col_ok) put_f64_col<S>(p.out0, seg_begin(sg, seg_len), E, e0, lo, c);
       c = __builtin_fma(a[j], c, b[j]);
     }
   }

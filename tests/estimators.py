@@ -73,9 +73,10 @@ def to_dev(d, device="cuda"):
             for k, v in d.items()}
 
 
-def run_gpu(name, dd, P=None, time_major=False, **variant):
+def run_gpu(name, dd, P=None, time_major=False, out0=None, **variant):
     """dd: dict of device tensors (to_dev).  Returns a dict of device tensors.
-    time_major: the per-step tensors in dd are [T, E] (outputs come back [T, E])."""
+    time_major: the per-step tensors in dd are [T, E] (outputs come back [T, E]).
+    out0: a caller-allocated tensor for the first output (None: allocated)."""
     import linear_recurrence_scan_reverse_amd as rl
     if time_major:
         rl = _TimeMajor(rl)
@@ -84,26 +85,26 @@ def run_gpu(name, dd, P=None, time_major=False, **variant):
     te, tr, bv, tb = o["terminated"], o["truncated"], o["bootstrap_value"], o["trunc_bootstrap"]
     g, l = P["gamma"], P["lam"]
     if name == "discounted_returns":
-        return {"out": rl.discounted_returns(dd["r"], te, tr, bv, tb, gamma=g)}
+        return {"out": rl.discounted_returns(dd["r"], te, tr, bv, tb, gamma=g, out=out0)}
     if name == "td_lambda":
-        return {"out": rl.td_lambda(dd["r"], dd["v"], te, tr, bv, tb, gamma=g, lam=l)}
+        return {"out": rl.td_lambda(dd["r"], dd["v"], te, tr, bv, tb, gamma=g, lam=l, out=out0)}
     if name == "returns_and_td_lambda":
-        ret, tdr = rl.returns_and_td_lambda(dd["r"], dd["v"], te, tr, bv, tb, gamma=g, lam=l)
+        ret, tdr = rl.returns_and_td_lambda(dd["r"], dd["v"], te, tr, bv, tb, gamma=g, lam=l, returns=out0)
         return {"out": ret, "out1": tdr}
     if name == "gae":
-        adv, ret = rl.gae(dd["r"], dd["v"], te, tr, bv, tb, gamma=g, lam=l, with_returns=True)
+        adv, ret = rl.gae(dd["r"], dd["v"], te, tr, bv, tb, gamma=g, lam=l, with_returns=True, advantages=out0)
         return {"out": adv, "out1": ret}
     if name == "vtrace":
         vs, pg = rl.vtrace(dd["r"], dd["v"], dd["log_rhos"], te, tr, bv, tb, gamma=g,
-                           lam=P["vtrace_lam"], rho_bar=P["rho_bar"], c_bar=P["c_bar"])
+                           lam=P["vtrace_lam"], rho_bar=P["rho_bar"], c_bar=P["c_bar"], vs=out0)
         return {"out": vs, "out1": pg}
     if name == "retrace":
         return {"out": rl.retrace(dd["r"], dd["q"], dd["exp_q"], dd["pi"], dd["mu"], te, tr, bv, tb,
-                                  gamma=g, lam=l)}
+                                  gamma=g, lam=l, out=out0)}
     if name == "eligibility_traces":
-        return {"out": rl.eligibility_traces(dd["r"], te, tr, bv, gamma=g, lam=l)}
+        return {"out": rl.eligibility_traces(dd["r"], te, tr, bv, gamma=g, lam=l, out=out0)}
     if name == "episodic_prefix_sum":
-        return {"out": rl.episodic_prefix_sum(dd["r"], te, tr, bv)}
+        return {"out": rl.episodic_prefix_sum(dd["r"], te, tr, bv, out=out0)}
     raise KeyError(name)
 
 

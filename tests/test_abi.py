@@ -264,3 +264,34 @@ def test_binding_rejects_cpu_tensors():
     r = torch.zeros(2, 3)
     with pytest.raises(ValueError, match="GPU"):
         rl.discounted_returns(r)
+
+
+def test_grid_limits_are_shape_errors(lib):
+    # launches whose grid would pass 2^32 - 1 work-items are refused in
+    # validation (before any HIP call), not at launch time
+    tm_max_e = 64 * (0xFFFFFFFF // (64 * 16))  # largest time-major E: one 16-wave block per 64 envs
+    for fmt in (F32, BF16):
+        big = tm_max_e + 1
+        assert lib.rlscan_gae_ex(fmt, TIME_MAJOR, A, B, None, None, None, None, C, None, big, 1, 0.99, 0.95,
+                                 S) == ERR_SHAPE
+        assert lib.rlscan_discounted_returns_ex(fmt, TIME_MAJOR, A, None, None, None, None, C, big, 2, 0.9,
+                                                S) == ERR_SHAPE
+        assert lib.rlscan_retrace_ex(fmt, TIME_MAJOR, A, B, C, D, F, None, None, None, None, G, big, 1, 0.9, 0.9,
+                                     S) == ERR_SHAPE
+        assert lib.rlscan_linear_scan_segmented_ex(fmt, TIME_MAJOR, A, B, None, None, C, big, 1, 1, S) == ERR_SHAPE
+        assert lib.rlscan_returns_and_td_lambda_ex(fmt, TIME_MAJOR, A, B, None, None, None, None, C, D, big, 1,
+                                                   0.9, 0.9, S) == ERR_SHAPE
+        # at the limit itself validation passes: with NULL outputs the next error is ERR_NULL
+        assert lib.rlscan_gae_ex(fmt, TIME_MAJOR, A, B, None, None, None, None, None, None, tm_max_e, 1, 0.99,
+                                 0.95, S) == ERR_NULL
+        # the same E row-major is not limited by this grid
+        assert lib.rlscan_gae_ex(fmt, ENV_MAJOR, A, B, None, None, None, None, None, None, big, 1, 0.99, 0.95,
+                                 S) == ERR_NULL
+    # vector traces: one 4-wave block per row and 64 feature columns
+    tv_max_blocks = 0xFFFFFFFF // (64 * 4)
+    f = lib.rlscan_eligibility_traces_vec
+    assert f(A, None, None, None, C, tv_max_blocks + 1, 1, 64, 0.9, 0.9, S) == ERR_SHAPE
+    assert f(A, None, None, None, C, tv_max_blocks // 2 + 1, 1, 65, 0.9, 0.9, S) == ERR_SHAPE
+    assert f(A, None, None, None, None, tv_max_blocks, 1, 64, 0.9, 0.9, S) == ERR_NULL
+    assert lib.rlscan_eligibility_traces_vec_ex(BF16, TIME_MAJOR, A, None, None, None, C, tv_max_blocks + 1, 1, 64,
+                                                0.9, 0.9, S) == ERR_SHAPE

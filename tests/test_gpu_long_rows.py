@@ -91,3 +91,62 @@ def test_long_rows_bitwise_deterministic():
         torch.cuda.synchronize()
         for k in a:
             assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), (name, k)
+
+
+# Rows whose length is a whole number of segments plus 1..7 steps: the last
+# segment takes the remainder, so its parked float64 pair (4 float32 or 8
+# 16-bit elements) stays inside it.  The first output sits at the start of a
+# larger buffer whose tail holds a sentinel that must survive the call.
+RAGGED = [(E, T) for E in (1, 2, 64) for T in (16385, 16387, 17409)]
+
+
+def _guarded(E, T, dtype):
+    import torch
+    guard = 64
+    buf = torch.full((E * T + guard,), -7.25, dtype=dtype, device="cuda")
+    return buf, buf[:E * T].view(E, T), guard
+
+
+def _guard_intact(buf, n, label):
+    import torch
+    tail = buf[n:].float().cpu()
+    assert torch.all(tail == -7.25), "%s: wrote past the end of the first output" % label
+
+
+@pytest.mark.parametrize("fmt", ["float32", "bfloat16"])
+@pytest.mark.parametrize("E,T", RAGGED + [(E, 16391) for E in (1, 2, 64)])
+def test_ragged_last_segment(fmt, E, T):
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    import oracle
+    from tests.estimators import check_rounded, run_gpu, run_oracle, storage_inputs
+    _say("ragged last segment %s E=%d T=%d" % (fmt, E, T))
+    dt = getattr(torch, fmt)
+    d = synth.draw(E, T, seed=45 + T % 97, p_term=0.001, p_trunc=0.001)
+    host, dev = storage_inputs(d, fmt)
+    for name in NAMES:
+        buf, out0, _ = _guarded(E, T, dt)
+        got = run_gpu(name, dev, out0=out0)
+        torch.cuda.synchronize()
+        ref = run_oracle(name, host)
+        label = "%s %s E=%d T=%d" % (name, fmt, E, T)
+        for k, r in ref.items():
+            check_rounded(got[k], r, fmt, label + " " + k)
+        _guard_intact(buf, E * T, label)
+    # the generic recurrence, both directions, without and with episode cuts
+    rng = np.random.default_rng(46)
+    a = rng.uniform(-1.0, 1.0, size=(E, T)).astype(np.float32)
+    b = rng.standard_normal((E, T)).astype(np.float32)
+    c = rng.standard_normal(E).astype(np.float32)
+    done = (rng.random((E, T)) < 0.001).astype(np.uint8)
+    ta, tb, tc = (torch.from_numpy(v).to(dt) for v in (a, b, c))
+    ha, hb, hc = (t.float().numpy() for t in (ta, tb, tc))
+    for rev in (True, False):
+        for cut in (None, done):
+            buf, out0, _ = _guarded(E, T, dt)
+            rl.linear_scan_segmented(ta.cuda(), tb.cuda(), None if cut is None else torch.from_numpy(cut).cuda(),
+                                     tc.cuda(), reverse=rev, out=out0)
+            torch.cuda.synchronize()
+            label = "linear scan %s rev=%s cuts=%s E=%d T=%d" % (fmt, rev, cut is not None, E, T)
+            check_rounded(out0, oracle.linear_scan_segmented(ha, hb, cut, hc, reverse=rev), fmt, label)
+            _guard_intact(buf, E * T, label)
