@@ -12,16 +12,22 @@ data.
 
 Printed (one JSON line on stdout):
   value          env-steps/s through the whole seven-estimator step
-  per_estimator  back-to-back launch time of each estimator, env-steps/s,
-                 algorithmic GB/s and fraction of the 8 TB/s HBM peak
-  roofline       the same for the dominant (slowest) kernel, plus the HBM
-                 traffic rocprofv3 counted for it (when the committed counter
-                 summary matches the current kernel sources)
+  per_estimator  back-to-back launch time of each estimator (200 calls or
+                 more), env-steps/s, algorithmic GB/s and fraction of the
+                 8 TB/s HBM peak
+  roofline       the same for the dominant (slowest) kernel, plus its kernel
+                 time and the HBM traffic rocprofv3 recorded for it (when the
+                 committed summaries match the current kernel sources)
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same workload
+  agreement      every output of the run (the seven estimators, the one-pass
+                 entries, the storage formats and layouts, the smaller
+                 workloads) against the oracle on the same inputs:
+                 max |gpu - oracle| / max(1, |oracle|) and max |oracle|; the
+                 line is marked failed (exit status 3) past the gate
   formats_and_layouts  the seven estimators with bfloat16 / float16 value
                  storage and in the time-major [T, E] layout (the _ex
                  entries), same workload, not part of the step
-  copy_ceiling   device-to-device copy bandwidth measured in the same run
+  configs        the four smaller workloads (latency and env-steps/s)
 Context only (not comparable): the rl-triton pages report 1.6-5.70x full-call
 speedups over a vectorized torch.compile scan on NVIDIA GPUs (H100 80GB HBM3
 and RTX 2000 Ada per the gist.science summary; the abstract does not name them).
@@ -125,10 +131,13 @@ class Runner:
         self.lib = rl.lib() if (fmt == 0 and not time_major) else _Ex(rl.lib(), fmt, 1 if time_major else 0)
         self.E, self.T = w.E, w.T
         self.w = w
+        self.time_major = time_major
         self.stream = torch.cuda.current_stream(device)
         self.sptr = self.stream.cuda_stream
         base = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in d.items()}
         base = {k: (v.to(vdt) if k in VALUE_KEYS else v) for k, v in base.items()}
+        # the values the kernels read, widened back to float32 (the oracle's inputs)
+        self.host_inputs = {k: (v.float().cpu().numpy() if k in VALUE_KEYS else d[k]) for k, v in base.items()}
         if time_major:  # [T, E] per-step arrays (E and T keep their meaning)
             base = {k: (v if k in ROW_KEYS else v.t().contiguous()) for k, v in base.items()}
         self.sets = []
@@ -184,6 +193,26 @@ class Runner:
         if rc != 0:
             raise RuntimeError("%s returned status %d" % (name, rc))
 
+    # output tensors each entry writes, by output key
+    OUTPUTS = {"vtrace": {"out": "out_vtrace", "out1": "out_vtrace_pg"},
+               "returns_and_td_lambda": {"out": "out_discounted_returns", "out1": "out_td_lambda"},
+               "linear_scan_segmented": {"out": "out_episodic_prefix_sum"}}
+
+    def outputs(self, name):
+        """One call of an entry on buffer set 0, its outputs copied to the host as
+        float32 [E, T] numpy arrays."""
+        torch = self.torch
+        s = self.sets[0]
+        self.call(name, s)
+        torch.cuda.synchronize()
+        res = {}
+        for k, key in self.OUTPUTS.get(name, {"out": "out_" + name}).items():
+            t = s["_keep"][key]
+            if self.time_major:
+                t = t.view(self.T, self.E).t()
+            res[k] = t.float().cpu().numpy()
+        return res
+
     def next_set(self):
         s = self.sets[self.counter % len(self.sets)]
         self.counter += 1
@@ -208,49 +237,6 @@ def time_region(runner, fn, reps):
     return start.elapsed_time(end) / 1e3  # seconds
 
 
-def copy_ceiling(torch, device, nbytes=1 << 30, reps=20):
-    """Device-to-device copy bandwidth (read + write bytes / time)."""
-    n = nbytes // 4
-    a = torch.empty(n, dtype=torch.float32, device=device).fill_(1.0)
-    bufs = [torch.empty_like(a) for _ in range(2)]
-    for b in bufs:
-        b.copy_(a)
-    torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(reps):
-        bufs[i % 2].copy_(a)
-    e.record()
-    e.synchronize()
-    secs = s.elapsed_time(e) / 1e3
-    del a, bufs
-    return 2 * nbytes * reps / secs / 1e9
-
-
-def copy_same_bytes(torch, device, nbytes, reps=50):
-    """Practical ceiling at one launch's size: device copies that move the same
-    bytes (half read, half written), rotating over > 1 GiB of buffers so the
-    256 MB MALL cannot serve them.  Returns GB/s."""
-    half = max(4, (nbytes // 2) // 4 * 4)
-    nsets = int(min(64, max(2, -(-(1 << 30) // (2 * half)) + 1)))
-    src = [torch.empty(half, dtype=torch.uint8, device=device).fill_(1) for _ in range(nsets)]
-    dst = [torch.empty(half, dtype=torch.uint8, device=device) for _ in range(nsets)]
-    for i in range(nsets):
-        dst[i].copy_(src[i])
-    torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(reps):
-        dst[i % nsets].copy_(src[i % nsets])
-    e.record()
-    e.synchronize()
-    secs = s.elapsed_time(e) / 1e3
-    del src, dst
-    return 2 * half * reps / secs / 1e9
-
-
 # Arrays one estimator call streams per step: float32 inputs, one-byte flag
 # arrays, float32 outputs.  The [E] row values and the sparse truncation
 # bootstraps are left out (under 0.2% of the bytes at 256 steps).
@@ -261,7 +247,7 @@ PROBE_MIX = {
 PROBE_LIB = os.path.join(ROOT, "linear_recurrence_scan_reverse_amd", "libstreamprobe.so")
 
 
-def probe_same_mix(torch, device, n, mix, reps=50):
+def probe_same_mix(torch, device, n, mix, reps=200, nsets=None):
     """Per-launch us of the plain streaming probe (libstreamprobe.so) moving one
     estimator call's arrays (mix = float inputs, flag arrays, float outputs; n
     elements each), over rotating buffer sets above 1 GiB with HIP events on the
@@ -275,7 +261,7 @@ def probe_same_mix(torch, device, n, mix, reps=50):
     fn.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
     nr, nf, nw = mix
     set_bytes = n * (4 * nr + nf + 4 * nw)
-    nsets = int(min(64, max(2, -(-(1 << 30) // set_bytes) + 1)))
+    nsets = nsets or int(min(64, max(2, -(-(1 << 30) // set_bytes) + 1)))
     keep, calls = [], []
     for _ in range(nsets):
         ins = [torch.ones(n, dtype=torch.float32, device=device) for _ in range(nr)]
@@ -329,25 +315,93 @@ def read_traffic(est, workload):
         return None, "malformed counter summary"
 
 
-# ----------------------------------------------------------------- CPU baseline (oracle)
-def cpu_baseline(w, d, budget_s=10.0):
-    """The fp64 oracle as it stands, all seven estimators, on a row sample."""
+def read_kernel_us(est, workload):
+    """Average kernel duration (us) of one estimator's back-to-back launches from the
+    committed rocprofv3 kernel-trace summary, or None when the summary is missing or
+    was taken on other kernel sources."""
+    path = os.path.join(PROFILES, "kernel_trace_rlscan_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None, "no kernel-trace summary"
+    rows, sha = {}, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("# kernel_source_sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.strip() and not line.startswith("#"):
+                tok = line.split()
+                if "avg" in tok:
+                    rows[tok[0]] = float(tok[tok.index("avg") + 1])
+    if sha != kernel_source_hash():
+        return None, "kernel sources changed since the kernel trace was taken"
+    if est not in rows:
+        return None, "estimator not in the kernel-trace summary"
+    return rows[est], os.path.relpath(path, ROOT)
+
+
+# ----------------------------------------------------------------- the oracle leg (CPU baseline)
+# The only part of the bench that runs the oracle: it times the unchanged fp64
+# oracle on the host cores (cpu_baseline), and its outputs on the inputs each GPU
+# call read are the reference of the agreement fields.
+TOL = 1e-5  # max |gpu - oracle| / max(1, |oracle|): relative where |oracle| >= 1, absolute below
+UNIT_ROUNDOFF = {"f32": 0.0, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}  # last rounding to the storage format
+
+
+def oracle_reference(name, d, w):
+    """The oracle's outputs of one GPU entry on host inputs d: {output: float64 array}."""
     import oracle
 
+    te, tr = d.get("terminated"), d.get("truncated")
+    bv, tb = d.get("bootstrap_value"), d.get("trunc_bootstrap")
+    g, lam = w.gamma, w.lam
+    if name == "discounted_returns":
+        return {"out": oracle.discounted_returns(d["r"], te, tr, bv, tb, gamma=g)}
+    if name == "td_lambda":
+        return {"out": oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=g, lam=lam)}
+    if name == "returns_and_td_lambda":
+        return {"out": oracle.discounted_returns(d["r"], te, tr, bv, tb, gamma=g),
+                "out1": oracle.td_lambda(d["r"], d["v"], te, tr, bv, tb, gamma=g, lam=lam)}
+    if name == "gae":
+        return {"out": oracle.gae(d["r"], d["v"], te, tr, bv, tb, gamma=g, lam=lam)}
+    if name == "vtrace":
+        vs, pg = oracle.vtrace(d["r"], d["v"], d["log_rhos"], te, tr, bv, tb, gamma=g, lam=w.vtrace_lam,
+                               rho_bar=w.rho_bar, c_bar=w.c_bar)
+        return {"out": vs, "out1": pg}
+    if name == "retrace":
+        return {"out": oracle.retrace(d["r"], d["q"], d["exp_q"], d["pi"], d["mu"], te, tr, bv, tb,
+                                      gamma=g, lam=lam)}
+    if name == "eligibility_traces":
+        return {"out": oracle.eligibility_traces(d["r"], te, tr, bv, gamma=g, lam=lam)}
+    if name == "episodic_prefix_sum":
+        return {"out": oracle.episodic_prefix_sum(d["r"], te, tr, bv)}
+    if name == "linear_scan_segmented":
+        return {"out": oracle.linear_scan_segmented(d["pi"], d["r"], te, None, reverse=True)}
+    raise KeyError(name)
+
+
+def agreement_of(gpu, d, w, fmt):
+    """Each output of each GPU entry (gpu: {name: {output: host array}}) against the
+    oracle on the same host inputs; gate TOL plus the storage format's last rounding."""
+    gate = TOL + UNIT_ROUNDOFF[fmt]
+    res = {}
+    for name, outs in gpu.items():
+        ref = oracle_reference(name, d, w)
+        for k, got in outs.items():
+            r = ref[k]
+            err = float(np.max(np.abs(got.astype(np.float64) - r) / np.maximum(1.0, np.abs(r)))) if r.size else 0.0
+            res[name if k == "out" else name + "." + k] = {
+                "max_err": err, "max_abs_ref": float(np.max(np.abs(r))) if r.size else 0.0,
+                "gate": gate, "pass": err <= gate}
+    return res
+
+
+def cpu_baseline(w, d, budget_s=10.0):
+    """The fp64 oracle as it stands, all seven estimators, on a row sample."""
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
 
     def run_rows(lo, hi):
         sl = {k: (v[lo:hi] if v.ndim >= 1 else v) for k, v in d.items()}
-        te, tr, bv, tb = sl["terminated"], sl["truncated"], sl["bootstrap_value"], sl["trunc_bootstrap"]
-        oracle.discounted_returns(sl["r"], te, tr, bv, tb, gamma=w.gamma)
-        oracle.td_lambda(sl["r"], sl["v"], te, tr, bv, tb, gamma=w.gamma, lam=w.lam)
-        oracle.gae(sl["r"], sl["v"], te, tr, bv, tb, gamma=w.gamma, lam=w.lam)
-        oracle.vtrace(sl["r"], sl["v"], sl["log_rhos"], te, tr, bv, tb, gamma=w.gamma, lam=w.vtrace_lam,
-                      rho_bar=w.rho_bar, c_bar=w.c_bar)
-        oracle.retrace(sl["r"], sl["q"], sl["exp_q"], sl["pi"], sl["mu"], te, tr, bv, tb, gamma=w.gamma,
-                       lam=w.lam)
-        oracle.eligibility_traces(sl["r"], te, tr, bv, gamma=w.gamma, lam=w.lam)
-        oracle.episodic_prefix_sum(sl["r"], te, tr, bv)
+        for n in ORDER:
+            oracle_reference(n, sl, w)
 
     # single-thread rate on one 256-row block (also warms the oracle library)
     t0 = time.perf_counter()
@@ -426,7 +480,7 @@ def time_estimators(runner, names, d, w, reps):
     return per
 
 
-def time_traces_vec(torch, device, args, E, T, D, p_term, p_trunc):
+def time_traces_vec(torch, device, reps, E, T, D, p_term, p_trunc):
     """Per-launch time of the vector traces entry on rotating [E, T, D] buffers."""
     import linear_recurrence_scan_reverse_amd as rl
     f = synth.draw_features(E, T, D, seed=0, p_term=p_term, p_trunc=p_trunc)
@@ -454,7 +508,6 @@ def time_traces_vec(torch, device, args, E, T, D, p_term, p_trunc):
 
     for _ in range(nsets + 2):
         call()
-    reps = max(args.steps, 20)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -494,7 +547,7 @@ def run_grid(torch, device, args):
                 d = drop_truncation(d)
             nsets = int(min(64, max(2, -(-(1 << 30) // set_bytes) + 1)))
             runner = Runner(w, d, nsets, device, storage=st, time_major=tm)
-            per = time_estimators(runner, names, d, w, max(args.steps, 20))
+            per = time_estimators(runner, names, d, w, max(200, args.reps))
             log("grid %6d x %4d: " % (E, T) + "  ".join("%s %.2f us %.1f%%" % (
                 n[:6], per[n]["us_per_launch"], 100 * per[n]["frac_of_peak"]) for n in names))
             print(json.dumps({"grid": True, "workload": w.name, "E": E, "T": T, "storage": st, "time_major": tm,
@@ -504,11 +557,13 @@ def run_grid(torch, device, args):
             torch.cuda.empty_cache()
 
 
-def run_configs(torch, device, args):
+def run_configs(torch, device, args, reps, collect=None):
     """The smaller named workloads (parity cases of the tests), each estimator's
-    per-launch time on rotating buffers: one JSON line per workload.  The
-    smallest are cache-resident, so their HBM fraction is not meaningful; their
-    figure is latency and env-steps/s."""
+    per-launch time on rotating buffers.  The smallest are cache-resident, so
+    their HBM fraction is not meaningful; their figure is latency and
+    env-steps/s.  collect: a dict that receives, per workload, the inputs and
+    the GPU outputs (for the agreement fields)."""
+    res = {}
     for name, w in synth.WORKLOADS.items():
         if name == "all7_16384x256":
             continue
@@ -517,13 +572,15 @@ def run_configs(torch, device, args):
         nsets = int(min(64, max(2, -(-(1 << 30) // set_bytes) + 1)))
         runner = Runner(w, d, nsets, device)
         names = [n for n in ORDER if n in w.estimators]
-        per = time_estimators(runner, names, d, w, max(args.steps, 100))
+        per = time_estimators(runner, names, d, w, reps)
         log("config %-18s " % name + "  ".join("%s %.2f us (%.3g env-steps/s)" % (
             n, per[n]["us_per_launch"], per[n]["env_steps_per_s"]) for n in names))
-        print(json.dumps({"config": True, "workload": name, "E": w.E, "T": w.T, "buffer_sets": nsets,
-                          "per_estimator": per}), flush=True)
+        res[name] = {"E": w.E, "T": w.T, "buffer_sets": nsets, "per_estimator": per}
+        if collect is not None:
+            collect[name] = (w, d, {n: runner.outputs(n) for n in names})
         del runner
         torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -531,21 +588,25 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--reps", type=int, default=200, help="back-to-back calls timed per estimator (at least 200)")
     ap.add_argument("--workload", default="all7_16384x256", choices=list(synth.WORKLOADS))
     ap.add_argument("--only", default=None, help="run only this estimator (profiling)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0 = enough for > 1 GiB)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--copy-only", action="store_true", help="only run the copy calibration kernel")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle (baseline and agreement)")
     ap.add_argument("--grid", action="store_true", help="every estimator over the E x T grid, one line each")
     ap.add_argument("--no-trunc", action="store_true", help="inputs without per-step truncation")
     ap.add_argument("--grid-e", default=None, help="comma-separated E values for --grid")
     ap.add_argument("--grid-t", default=None, help="comma-separated T values for --grid")
     ap.add_argument("--no-16", action="store_true", help="skip the 16-bit storage and time-major timings")
-    ap.add_argument("--configs", action="store_true", help="the smaller named workloads, one line each")
+    ap.add_argument("--no-configs", action="store_true", help="skip the smaller named workloads")
+    ap.add_argument("--configs", action="store_true", help="only the smaller named workloads, one line each")
     ap.add_argument("--grid-storage", default="f32", choices=list(FORMATS), help="value storage for --grid")
     ap.add_argument("--grid-time-major", action="store_true", help="time-major [T, E] arrays for --grid")
     ap.add_argument("--grid-max-gib", type=float, default=1.0, help="largest buffer set --grid runs (GiB)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="only the counter calibration: the stream probe copying 1 GiB to 1 GiB, 5 times")
     args = ap.parse_args()
+    reps = max(200, args.reps)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         log("bench.py: this build measures one GPU only (rows are independent; multi-GPU "
@@ -559,9 +620,9 @@ def main():
     device = torch.device("cuda", 0)
     torch.cuda.set_device(device)
 
-    if args.copy_only:
-        gbps = copy_ceiling(torch, device)
-        log("copy ceiling %.1f GB/s" % gbps)
+    if args.calibration_copy:
+        us = probe_same_mix(torch, device, 1 << 28, (1, 0, 1), reps=5, nsets=2)
+        log("calibration copy: 1 GiB read + 1 GiB written per launch, %.1f us (%.1f GB/s)" % (us, 2**31 / us / 1e3))
         return
 
     if args.grid:
@@ -569,7 +630,8 @@ def main():
         return
 
     if args.configs:
-        run_configs(torch, device, args)
+        for name, r in run_configs(torch, device, args, reps).items():
+            print(json.dumps({"config": True, "workload": name, **r}), flush=True)
         return
 
     w = synth.WORKLOADS[args.workload]
@@ -599,10 +661,8 @@ def main():
     log("step: %.3f ms  (%.3g env-steps/s through %d estimators)" % (ms_per_step, value, len(names)))
 
     # ---- per-estimator back-to-back launches (same rotation), HIP events on the launch stream
-    per = time_estimators(runner, names, d, w, max(args.steps, 20))
+    per = time_estimators(runner, names, d, w, reps)
     for n in names:
-        per[n]["copy_same_bytes_GBps"] = round(copy_same_bytes(torch, device, per[n]["alg_bytes"]), 1)
-        per[n]["frac_of_copy"] = round(per[n]["GBps"] / per[n]["copy_same_bytes_GBps"], 4)
         mix = None
         if n in PROBE_MIX:  # as many flag arrays as the call reads
             nflags = int("terminated" in d) + int("truncated" in d)
@@ -613,16 +673,19 @@ def main():
             per[n]["stream_probe_us"] = round(pu, 3)
             per[n]["frac_of_stream_probe"] = round(pu / per[n]["us_per_launch"], 4)
             probe_txt = "  %5.1f%% of a same-mix stream (%.2f us)" % (100 * per[n]["frac_of_stream_probe"], pu)
-        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  %5.1f%% of a same-size copy%s" % (
-            n, per[n]["us_per_launch"], per[n]["GBps"], 100 * per[n]["frac_of_peak"], 100 * per[n]["frac_of_copy"],
-            probe_txt))
+        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak%s" % (
+            n, per[n]["us_per_launch"], per[n]["GBps"], 100 * per[n]["frac_of_peak"], probe_txt))
+
+    # GPU outputs for the agreement fields: (workload, host inputs, {entry: outputs}, storage format)
+    checks = {"f32": (w, d, {n: runner.outputs(n) for n in names}, "f32")}
 
     # ---- the other entry points (not part of the step): the one-pass returns + TD(lambda)
     # entry and the generic episode-cut recurrence
     fused = None
     if "discounted_returns" in names and "td_lambda" in names:
-        fused = time_estimators(runner, ["returns_and_td_lambda", "linear_scan_segmented"], d, w,
-                                max(args.steps, 20))
+        extra = ["returns_and_td_lambda", "linear_scan_segmented"]
+        fused = time_estimators(runner, extra, d, w, reps)
+        checks["one_pass_entries"] = (w, d, {n: runner.outputs(n) for n in extra}, "f32")
         n = "returns_and_td_lambda"
         sep = per["discounted_returns"]["us_per_launch"] + per["td_lambda"]["us_per_launch"]
         fused[n]["separate_calls_us"] = round(sep, 3)
@@ -635,7 +698,7 @@ def main():
 
     # ---- vector-valued traces over [E, T, D] features (not part of the step)
     if "eligibility_traces" in names:
-        vt = time_traces_vec(torch, device, args, E=1024, T=w.T, D=64, p_term=w.p_term, p_trunc=w.p_trunc)
+        vt = time_traces_vec(torch, device, reps, E=1024, T=w.T, D=64, p_term=w.p_term, p_trunc=w.p_trunc)
         fused = dict(fused or {})
         fused["eligibility_traces_vec"] = vt
         log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  (%s)" % (
@@ -644,27 +707,37 @@ def main():
     # ---- the seven estimators with 16-bit storage and in the time-major layout
     # (not part of the step)
     variants = None
+    del runner
+    torch.cuda.empty_cache()
     if not args.only and not args.no_16:
         variants = {}
-        del runner
-        torch.cuda.empty_cache()
         for key, st, tm in (("bf16", "bf16", False), ("f16", "f16", False), ("time_major_f32", "f32", True),
                             ("time_major_bf16", "bf16", True)):
             vb = 2 if st != "f32" else 4
             nsets_v = int(min(64, max(2, -(-(1 << 30) // (set_bytes_est * vb // 4)) + 1)))
             rv = Runner(w, d, nsets_v, device, storage=st, time_major=tm)
-            pv = time_estimators(rv, names, d, w, max(args.steps, 20))
+            pv = time_estimators(rv, names, d, w, reps)
             for n in names:
                 pv[n]["f32_us_per_launch"] = per[n]["us_per_launch"]
                 pv[n]["speedup_vs_f32"] = round(per[n]["us_per_launch"] / pv[n]["us_per_launch"], 3)
             variants[key] = pv
+            checks[key] = (w, rv.host_inputs, {n: rv.outputs(n) for n in names}, st)
             log("  %-15s " % key + "  ".join("%s %.2f us %.1f%%" % (
                 n[:6], pv[n]["us_per_launch"], 100 * pv[n]["frac_of_peak"]) for n in names))
             del rv
             torch.cuda.empty_cache()
 
+    # ---- the smaller named workloads
+    configs = None
+    if not args.only and not args.no_configs and w.name == "all7_16384x256":
+        cfg_out = {}
+        configs = run_configs(torch, device, args, reps, collect=cfg_out)
+        for name, (cw, cd, outs) in cfg_out.items():
+            checks["config " + name] = (cw, cd, outs, "f32")
+
     dom = max(per, key=lambda k: per[k]["us_per_launch"])
     traffic, traffic_src = read_traffic(dom, w.name)
+    kus, kus_src = read_kernel_us(dom, w.name)
     roofline = {
         "bound": "hbm",
         "kernel": dom,
@@ -676,16 +749,29 @@ def main():
         "traffic_source": traffic_src,
         "alg_bytes_per_launch": per[dom]["alg_bytes"],
         "us_per_launch": per[dom]["us_per_launch"],
-        # the same kernel against a plain stream of its own arrays (practical ceiling)
+        "timing": "HIP events on the launch stream around %d back-to-back calls over rotating buffers" % reps,
+        # the same kernel's average duration in the committed rocprofv3 kernel trace
+        "rocprof_kernel_us": kus,
+        "rocprof_frac": (round(per[dom]["alg_bytes"] / (kus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+                         if kus else None),
+        "rocprof_source": kus_src,
+        # the same kernel against a plain stream of its own arrays
         "stream_probe_us": per[dom].get("stream_probe_us"),
         "frac_of_stream_probe": per[dom].get("frac_of_stream_probe"),
     }
 
-    ceiling = copy_ceiling(torch, device)
-    log("copy ceiling: %.1f GB/s" % ceiling)
-
-    cpu = None
+    # ---- the oracle leg: CPU baseline and the agreement of every output above
+    cpu, agreement, agree_ok = None, None, True
     if not args.no_cpu:
+        log("oracle: agreement of every output ...")
+        agreement = {}
+        for key, (cw, cd, outs, fmt) in checks.items():
+            agreement[key] = agreement_of(outs, cd, cw, fmt)
+            worst = max(v["max_err"] for v in agreement[key].values())
+            ok = all(v["pass"] for v in agreement[key].values())
+            agree_ok = agree_ok and ok
+            log("  %-28s worst %.3g  %s" % (key, worst, "ok" if ok else "FAILED"))
+        checks = None
         log("cpu baseline (oracle)...")
         cpu = cpu_baseline(w, d)
         log("cpu baseline: %.3g env-steps/s on %d threads" % (cpu["value"], cpu["cores"]))
@@ -709,20 +795,30 @@ def main():
             "p_term": w.p_term, "p_trunc": w.p_trunc, "gamma": w.gamma, "lambda": w.lam,
             "vtrace_lambda": w.vtrace_lam, "rho_bar": w.rho_bar, "c_bar": w.c_bar,
             "buffer_sets": nsets, "gae_returns_written": False, "vtrace_pg_written": True,
-            "truncation": not args.no_trunc,
+            "truncation": not args.no_trunc, "calls_timed_per_estimator": reps,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": None if agreement is None else {
+            "pass": agree_ok,
+            "metric": "max |gpu - oracle| / max(1, |oracle|) over every element (relative where "
+                      "|oracle| >= 1, absolute below); gate 1e-5, plus the storage format's unit "
+                      "roundoff for 16-bit storage",
+        },
+        "agreement": agreement,
         "per_estimator": per,
         "one_pass_entries": fused,
         "formats_and_layouts": variants,
-        "copy_ceiling_GBps": round(ceiling, 1),
+        "configs": configs,
         "kernel_source_sha256": kernel_source_hash(),
         "context": "rl-triton pages: 1.6-5.70x full-call speedup vs a vectorized torch.compile scan "
                    "on NVIDIA GPUs (H100 80GB HBM3, RTX 2000 Ada per the gist.science summary; the "
                    "abstract names none) - a different baseline and machine, context only",
     }
     print(json.dumps(line), flush=True)
+    if not agree_ok:
+        log("bench.py: GPU outputs disagree with the oracle beyond the gate")
+        sys.exit(3)
 
 
 if __name__ == "__main__":
