@@ -243,55 +243,73 @@ def time_region(runner, fn, reps):
 PROBE_MIX = {
     "discounted_returns": (1, 2, 1), "td_lambda": (2, 2, 1), "gae": (2, 2, 1), "vtrace": (3, 2, 2),
     "retrace": (5, 2, 1), "eligibility_traces": (1, 2, 1), "episodic_prefix_sum": (1, 2, 1),
+    "returns_and_td_lambda": (2, 2, 2), "linear_scan_segmented": (2, 1, 1),
 }
 PROBE_LIB = os.path.join(ROOT, "linear_recurrence_scan_reverse_amd", "libstreamprobe.so")
+PROBE_SHAPES = ("grid16", "grid32", "grid64", "grid16w", "persist", "grid32w")
+_probe = None
 
 
-def probe_same_mix(torch, device, n, mix, reps=200, nsets=None):
-    """Per-launch us of the plain streaming probe (libstreamprobe.so) moving one
-    estimator call's arrays (mix = float inputs, flag arrays, float outputs; n
-    elements each), over rotating buffer sets above 1 GiB with HIP events on the
-    launch stream; None when the probe library is not built."""
+def probe_lib():
+    """libstreamprobe.so with argument types set, or None when it is not built."""
+    global _probe
     import ctypes
-    if not os.path.exists(PROBE_LIB):
+    if _probe is None and os.path.exists(PROBE_LIB):
+        lib = ctypes.CDLL(PROBE_LIB)
+        P = ctypes.POINTER(ctypes.c_void_p)
+        lib.stream_probe_time.restype = ctypes.c_int
+        lib.stream_probe_time.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int64,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.POINTER(ctypes.c_float)]
+        lib.stream_probe_shapes.restype = ctypes.c_int
+        assert lib.stream_probe_shapes() == len(PROBE_SHAPES)
+        _probe = lib
+    return _probe
+
+
+def probe_sweep(torch, device, n, mix, reps=200, nsets=None, shapes=None):
+    """Per-launch us of every plain streaming shape (libstreamprobe.so) moving one
+    call's arrays (mix = float inputs, flag arrays, float outputs; n elements
+    each), over rotating buffer sets above 1 GiB, timed in the probe library with
+    HIP events on the launch stream: {shape name: us}, or None when the probe
+    library is not built."""
+    import ctypes
+    lib = probe_lib()
+    if lib is None:
         return None
-    fn = ctypes.CDLL(PROBE_LIB).stream_probe
-    P = ctypes.POINTER(ctypes.c_void_p)
-    fn.restype = ctypes.c_int
-    fn.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
     nr, nf, nw = mix
     set_bytes = n * (4 * nr + nf + 4 * nw)
     nsets = nsets or int(min(64, max(2, -(-(1 << 30) // set_bytes) + 1)))
-    keep, calls = [], []
+    keep, ins, fls, outs = [], [], [], []
     for _ in range(nsets):
-        ins = [torch.ones(n, dtype=torch.float32, device=device) for _ in range(nr)]
-        fls = [torch.zeros(n, dtype=torch.uint8, device=device) for _ in range(nf)]
-        outs = [torch.empty(n, dtype=torch.float32, device=device) for _ in range(nw)]
-        keep.append((ins, fls, outs))
-        calls.append(((ctypes.c_void_p * 5)(*[t.data_ptr() for t in ins]),
-                      (ctypes.c_void_p * 2)(*[t.data_ptr() for t in fls]),
-                      (ctypes.c_void_p * 2)(*[t.data_ptr() for t in outs])))
+        i_ = [torch.ones(n, dtype=torch.float32, device=device) for _ in range(nr)]
+        f_ = [torch.zeros(n, dtype=torch.uint8, device=device) for _ in range(nf)]
+        o_ = [torch.empty(n, dtype=torch.float32, device=device) for _ in range(nw)]
+        keep.append((i_, f_, o_))
+        ins += [t.data_ptr() for t in i_]
+        fls += [t.data_ptr() for t in f_]
+        outs += [t.data_ptr() for t in o_]
     st = torch.cuda.current_stream(device)
-
-    def launch(i):
-        a, f, o = calls[i % nsets]
-        rc = fn(a, nr, f, nf, o, nw, n, ctypes.c_void_p(st.cuda_stream))
+    pi = (ctypes.c_void_p * len(ins))(*ins)
+    pf = (ctypes.c_void_p * max(1, len(fls)))(*fls) if fls else None
+    po = (ctypes.c_void_p * len(outs))(*outs)
+    res = {}
+    for k in (shapes if shapes is not None else range(len(PROBE_SHAPES))):
+        us = ctypes.c_float(0.0)
+        rc = lib.stream_probe_time(pi, nr, pf, nf, po, nw, n, nsets, k, reps, ctypes.c_void_p(st.cuda_stream),
+                                   ctypes.byref(us))
         if rc != 0:
-            raise RuntimeError("stream_probe failed with %d" % rc)
-
-    for i in range(nsets):
-        launch(i)
+            raise RuntimeError("stream_probe_time failed with %d" % rc)
+        res[PROBE_SHAPES[k]] = round(us.value, 3)
+    del keep
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record(st)
-    for i in range(reps):
-        launch(i)
-    e.record(st)
-    e.synchronize()
-    us = s.elapsed_time(e) * 1e3 / reps
-    del keep, calls
-    return us
+    return res
+
+
+def ceiling_of(sweep):
+    """The fastest shape of a probe sweep: (name, us)."""
+    k = min(sweep, key=sweep.get)
+    return k, sweep[k]
 
 
 def read_traffic(est, workload):
@@ -467,6 +485,24 @@ def drop_truncation(d):
     return {k: v for k, v in d.items() if k not in ("truncated", "trunc_bootstrap")}
 
 
+def add_ceiling(entry, sweep, mix):
+    """Attach the probe sweep of an entry's byte mix and its fastest shape."""
+    if sweep is None:
+        entry["ceiling"] = None
+        return
+    k, us = ceiling_of(sweep)
+    entry["ceiling"] = {"mix": "%d float inputs, %d flag arrays, %d float outputs" % mix, "best_shape": k,
+                        "us": us, "frac_of_ceiling": round(us / entry["us_per_launch"], 4), "by_shape": sweep}
+
+
+def log_estimator(n, e):
+    c = e.get("ceiling")
+    txt = "  %5.1f%% of the best plain stream of its bytes (%s, %.2f us)" % (
+        100 * c["frac_of_ceiling"], c["best_shape"], c["us"]) if c else ""
+    log("  %-22s %8.2f us  %7.1f GB/s  %5.1f%% of peak%s" % (
+        n, e["us_per_launch"], e["GBps"], 100 * e["frac_of_peak"], txt))
+
+
 def time_estimators(runner, names, d, w, reps):
     per = {}
     for n in names:
@@ -621,7 +657,7 @@ def main():
     torch.cuda.set_device(device)
 
     if args.calibration_copy:
-        us = probe_same_mix(torch, device, 1 << 28, (1, 0, 1), reps=5, nsets=2)
+        us = probe_sweep(torch, device, 1 << 28, (1, 0, 1), reps=5, nsets=2, shapes=[0])["grid16"]
         log("calibration copy: 1 GiB read + 1 GiB written per launch, %.1f us (%.1f GB/s)" % (us, 2**31 / us / 1e3))
         return
 
@@ -662,19 +698,14 @@ def main():
 
     # ---- per-estimator back-to-back launches (same rotation), HIP events on the launch stream
     per = time_estimators(runner, names, d, w, reps)
+    sweeps = {}
+    nflags = int("terminated" in d) + int("truncated" in d)
     for n in names:
-        mix = None
-        if n in PROBE_MIX:  # as many flag arrays as the call reads
-            nflags = int("terminated" in d) + int("truncated" in d)
-            mix = (PROBE_MIX[n][0], min(PROBE_MIX[n][1], nflags), PROBE_MIX[n][2])
-        pu = probe_same_mix(torch, device, w.E * w.T, mix) if mix else None
-        probe_txt = ""
-        if pu is not None:
-            per[n]["stream_probe_us"] = round(pu, 3)
-            per[n]["frac_of_stream_probe"] = round(pu / per[n]["us_per_launch"], 4)
-            probe_txt = "  %5.1f%% of a same-mix stream (%.2f us)" % (100 * per[n]["frac_of_stream_probe"], pu)
-        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak%s" % (
-            n, per[n]["us_per_launch"], per[n]["GBps"], 100 * per[n]["frac_of_peak"], probe_txt))
+        mix = (PROBE_MIX[n][0], min(PROBE_MIX[n][1], nflags), PROBE_MIX[n][2])
+        if mix not in sweeps:
+            sweeps[mix] = probe_sweep(torch, device, w.E * w.T, mix, reps)
+        add_ceiling(per[n], sweeps[mix], mix)
+        log_estimator(n, per[n])
 
     # GPU outputs for the agreement fields: (workload, host inputs, {entry: outputs}, storage format)
     checks = {"f32": (w, d, {n: runner.outputs(n) for n in names}, "f32")}
@@ -686,22 +717,26 @@ def main():
         extra = ["returns_and_td_lambda", "linear_scan_segmented"]
         fused = time_estimators(runner, extra, d, w, reps)
         checks["one_pass_entries"] = (w, d, {n: runner.outputs(n) for n in extra}, "f32")
+        for n in extra:
+            mix = (PROBE_MIX[n][0], min(PROBE_MIX[n][1], 1 if n == "linear_scan_segmented" else nflags),
+                   PROBE_MIX[n][2])
+            if mix not in sweeps:
+                sweeps[mix] = probe_sweep(torch, device, w.E * w.T, mix, reps)
+            add_ceiling(fused[n], sweeps[mix], mix)
         n = "returns_and_td_lambda"
         sep = per["discounted_returns"]["us_per_launch"] + per["td_lambda"]["us_per_launch"]
         fused[n]["separate_calls_us"] = round(sep, 3)
         fused[n]["speedup_vs_separate"] = round(sep / fused[n]["us_per_launch"], 3)
-        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  (separate calls: %.2f us)" % (
-            "returns+td_lambda", fused[n]["us_per_launch"], fused[n]["GBps"], 100 * fused[n]["frac_of_peak"], sep))
-        n = "linear_scan_segmented"
-        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak" % (
-            "generic, with cuts", fused[n]["us_per_launch"], fused[n]["GBps"], 100 * fused[n]["frac_of_peak"]))
+        for n in extra:
+            log_estimator(n, fused[n])
+        log("  (returns + td_lambda as separate calls: %.2f us)" % sep)
 
     # ---- vector-valued traces over [E, T, D] features (not part of the step)
     if "eligibility_traces" in names:
         vt = time_traces_vec(torch, device, reps, E=1024, T=w.T, D=64, p_term=w.p_term, p_trunc=w.p_trunc)
         fused = dict(fused or {})
         fused["eligibility_traces_vec"] = vt
-        log("  %-20s %8.2f us  %7.1f GB/s  %5.1f%% of peak  (%s)" % (
+        log("  %-22s %8.2f us  %7.1f GB/s  %5.1f%% of peak  (%s)" % (
             "traces, D=64", vt["us_per_launch"], vt["GBps"], 100 * vt["frac_of_peak"], vt["shape"]))
 
     # ---- the seven estimators with 16-bit storage and in the time-major layout
@@ -755,9 +790,8 @@ def main():
         "rocprof_frac": (round(per[dom]["alg_bytes"] / (kus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
                          if kus else None),
         "rocprof_source": kus_src,
-        # the same kernel against a plain stream of its own arrays
-        "stream_probe_us": per[dom].get("stream_probe_us"),
-        "frac_of_stream_probe": per[dom].get("frac_of_stream_probe"),
+        # the same kernel against the fastest plain stream of its own arrays
+        "ceiling": per[dom].get("ceiling"),
     }
 
     # ---- the oracle leg: CPU baseline and the agreement of every output above

@@ -69,3 +69,36 @@ def test_probe_moves_every_array(fn, nr, nf, nw):
         ref[:, 0] += any_flag.float()
     for k, o in enumerate(outs):
         assert torch.allclose(o.cpu().view(-1, 4), ref + k, rtol=1e-6, atol=1e-5), "output %d" % k
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape", range(6))
+@pytest.mark.parametrize("nr,nf,nw", [(1, 2, 1), (5, 2, 1), (3, 2, 2)])
+def test_every_probe_shape_moves_every_array(shape, nr, nf, nw):
+    """Each shape of the bench's ceiling sweep, run through the timing entry point
+    on one buffer set, writes what the single-shape probe writes (ragged n: the
+    last block and tile are partial)."""
+    import torch
+    lib = ctypes.CDLL(PROBE)
+    f = lib.stream_probe_time
+    P = ctypes.POINTER(ctypes.c_void_p)
+    f.restype = ctypes.c_int
+    f.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
+    assert lib.stream_probe_shapes() == 6
+    n = 4 * 70001
+    g = torch.Generator(device="cpu").manual_seed(shape * 1000 + nr * 100 + nf * 10 + nw)
+    ins = [torch.randn(n, generator=g).cuda() for _ in range(nr)]
+    fls = [(torch.rand(n, generator=g) < 0.05).to(torch.uint8).cuda() for _ in range(nf)]
+    outs = [torch.full((n,), float("nan"), device="cuda") for _ in range(nw)]
+    us = ctypes.c_float(0.0)
+    rc = f(_ptrs(*[t.data_ptr() for t in ins]), nr, _ptrs(*[t.data_ptr() for t in fls]), nf,
+           _ptrs(*[t.data_ptr() for t in outs]), nw, n, 1, shape, 3,
+           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), ctypes.byref(us))
+    assert rc == 0 and us.value > 0
+    torch.cuda.synchronize()
+    ref = torch.stack([t.cpu() for t in ins]).sum(0).view(-1, 4)
+    any_flag = torch.stack([t.cpu() for t in fls]).amax(0).view(-1, 4).amax(1) > 0
+    ref[:, 0] += any_flag.float()
+    for k, o in enumerate(outs):
+        assert torch.allclose(o.cpu().view(-1, 4), ref + k, rtol=1e-6, atol=1e-5), "shape %d output %d" % (shape, k)
