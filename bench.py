@@ -639,6 +639,10 @@ def main():
     ap.add_argument("--grid-storage", default="f32", choices=list(FORMATS), help="value storage for --grid")
     ap.add_argument("--grid-time-major", action="store_true", help="time-major [T, E] arrays for --grid")
     ap.add_argument("--grid-max-gib", type=float, default=1.0, help="largest buffer set --grid runs (GiB)")
+    ap.add_argument("--storage", default="f32", choices=list(FORMATS),
+                    help="value storage of the main run (profiling one format; the line's value is float32)")
+    ap.add_argument("--time-major", action="store_true", help="time-major [T, E] arrays in the main run (profiling)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the plain-stream ceiling sweep (profiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only the counter calibration: the stream probe copying 1 GiB to 1 GiB, 5 times")
     args = ap.parse_args()
@@ -681,8 +685,10 @@ def main():
     if args.no_trunc:
         d = drop_truncation(d)
     set_bytes_est = sum(v.nbytes for v in d.values()) + 8 * 4 * w.E * w.T
-    nsets = args.sets or int(min(64, max(2, -(-(1 << 30) // set_bytes_est) + 1)))
-    runner = Runner(w, d, nsets, device)
+    main_vb = 2 if args.storage != "f32" else 4
+    nsets = args.sets or int(min(64, max(2, -(-(1 << 30) // (set_bytes_est * main_vb // 4)) + 1)))
+    runner = Runner(w, d, nsets, device, storage=args.storage, time_major=args.time_major)
+    main_fmt = args.storage + (" time-major" if args.time_major else "")
     log("buffer sets: %d x %.1f MiB = %.2f GiB" % (nsets, runner.set_bytes / 2**20,
                                                     nsets * runner.set_bytes / 2**30))
 
@@ -703,12 +709,12 @@ def main():
     for n in names:
         mix = (PROBE_MIX[n][0], min(PROBE_MIX[n][1], nflags), PROBE_MIX[n][2])
         if mix not in sweeps:
-            sweeps[mix] = probe_sweep(torch, device, w.E * w.T, mix, reps)
+            sweeps[mix] = None if args.no_ceiling else probe_sweep(torch, device, w.E * w.T, mix, reps)
         add_ceiling(per[n], sweeps[mix], mix)
         log_estimator(n, per[n])
 
     # GPU outputs for the agreement fields: (workload, host inputs, {entry: outputs}, storage format)
-    checks = {"f32": (w, d, {n: runner.outputs(n) for n in names}, "f32")}
+    checks = {main_fmt: (w, runner.host_inputs, {n: runner.outputs(n) for n in names}, args.storage)}
 
     # ---- the other entry points (not part of the step): the one-pass returns + TD(lambda)
     # entry and the generic episode-cut recurrence
@@ -716,12 +722,12 @@ def main():
     if "discounted_returns" in names and "td_lambda" in names:
         extra = ["returns_and_td_lambda", "linear_scan_segmented"]
         fused = time_estimators(runner, extra, d, w, reps)
-        checks["one_pass_entries"] = (w, d, {n: runner.outputs(n) for n in extra}, "f32")
+        checks["one_pass_entries"] = (w, runner.host_inputs, {n: runner.outputs(n) for n in extra}, args.storage)
         for n in extra:
             mix = (PROBE_MIX[n][0], min(PROBE_MIX[n][1], 1 if n == "linear_scan_segmented" else nflags),
                    PROBE_MIX[n][2])
             if mix not in sweeps:
-                sweeps[mix] = probe_sweep(torch, device, w.E * w.T, mix, reps)
+                sweeps[mix] = None if args.no_ceiling else probe_sweep(torch, device, w.E * w.T, mix, reps)
             add_ceiling(fused[n], sweeps[mix], mix)
         n = "returns_and_td_lambda"
         sep = per["discounted_returns"]["us_per_launch"] + per["td_lambda"]["us_per_launch"]
@@ -822,7 +828,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f64",
-        "storage_dtype": "f32 values, u8 flags",
+        "storage_dtype": "%s values, u8 flags%s" % (args.storage, ", time-major" if args.time_major else ""),
         "data": "synthetic (seeded numpy draws; no dataset)",
         "config": {
             "workload": w.name, "E": w.E, "T": w.T, "estimators": names,

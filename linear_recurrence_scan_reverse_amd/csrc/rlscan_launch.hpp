@@ -8,6 +8,7 @@
 
 #include <atomic>
 
+#include "rlscan_duo.hpp"
 #include "rlscan_kernel.hpp"
 #include "rlscan_plan.hpp"
 #include "rlscan_segment.hpp"
@@ -289,6 +290,56 @@ inline bool prefer_stream(const KernelArgs& a, int L) {
   return true;
 }
 
+// ----------------------------------------------------------------- two items per wave
+// Rows of 64, 128 or 256 steps in float32 with every dense array 16-byte
+// aligned (and the flag arrays 4-byte aligned) can take the kernel that gives
+// each wave two 256-element items, the second staged through LDS (duo_kernel).
+// Measured against the routes below (flags present, E in {1024, 4096, 16384,
+// 65536} x T in {64, 128, 256}): discounted returns gained or tied at every
+// point (16384 x 256: 10.8 -> 10.2 us; 16384 x 128: 7.9 -> 6.7 us; 65536 x 256:
+// 36.2 -> 29.7 us); TD(lambda), eligibility traces and prefix sums gained at
+// 65536 x 256 (TD(lambda) 46.1 -> 40.2 us, traces 31.7 -> 26.5 us) but lost
+// 1.0-1.1 us at 16384 x 256; V-trace gained 0.1-0.5 us at 4096 and 16384 rows
+// of 256 steps and lost at 65536; Retrace lost from 16384 rows up.  Returns
+// the team width, or 0 when the call does not take this kernel.
+template <class Est>
+inline int duo_team(const KernelArgs& a) {
+  if (a.T != 64 && a.T != 128 && a.T != 256) return 0;
+  const int L = (int)(a.T / 4);
+  const int64_t items = (a.E + (64 / L) - 1) / (64 / L);
+  if ((items + 7) / 8 * 256 > kMaxWorkItems) return 0;
+  if (!vector_ok(a, 4, (int)a.T)) return 0;
+  bool take = false;
+  if constexpr (__is_same(Est, DiscountedReturn)) take = true;
+  if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae) || __is_same(Est, EligibilityTrace) ||
+                __is_same(Est, EpisodicPrefixSum))
+    take = a.T == 256 && a.E >= 32768;
+  if constexpr (__is_same(Est, Vtrace)) take = a.T == 256 && a.E >= 4096 && a.E < 32768;
+  return take ? L : 0;
+}
+
+template <class Est, int L, int OPT>
+inline hipError_t launch_duo_opt(const KernelArgs& a, hipStream_t s) {
+  const int64_t items = (a.E + (64 / L) - 1) / (64 / L);
+  KernelArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT>), dim3((unsigned)((items + 7) / 8)),
+                         dim3(256), params, 0, s);
+}
+
+template <class Est, int L>
+inline hipError_t launch_duo(const KernelArgs& a, hipStream_t s) {
+  using Tr = Traits<Est>;
+  const bool flags = a.has_term || a.has_trunc;
+  if constexpr (Tr::kHasOut1) {
+    const bool out1 = a.out1 != nullptr;
+    if (flags) return out1 ? launch_duo_opt<Est, L, 3>(a, s) : launch_duo_opt<Est, L, 1>(a, s);
+    return out1 ? launch_duo_opt<Est, L, 2>(a, s) : launch_duo_opt<Est, L, 0>(a, s);
+  } else {
+    return flags ? launch_duo_opt<Est, L, 1>(a, s) : launch_duo_opt<Est, L, 0>(a, s);
+  }
+}
+
 // ----------------------------------------------------------------- segmented path
 // Rows of at least kSegMinT steps, kSegMaxE rows or fewer, are cut into
 // segments (row_segments) so that passes 1 and 3 run about 32 waves per CU;
@@ -339,6 +390,14 @@ template <class Est>
 hipError_t launch(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const SegPlan plan = segment_plan(a); plan.len) return launch_segmented<Est>(a, s, plan);
+  if constexpr (!Traits<Est>::kDual && !Traits<Est>::kLinear) {
+    switch (duo_team<Est>(a)) {
+      case 16: return launch_duo<Est, 16>(a, s);
+      case 32: return launch_duo<Est, 32>(a, s);
+      case 64: return launch_duo<Est, 64>(a, s);
+      default: break;
+    }
+  }
   const bool one = prefer_oneshot<Est>(a, 4);
   const int team = one ? 0 : stream_team<F32S>(a);
   switch ((team != 0 && prefer_stream<Est>(a, team)) ? team : 0) {

@@ -189,7 +189,9 @@ struct alignas(16) FlagTick {
 // One lane's part of one tile of one row: pairs, wave scan, re-walk and
 // outputs.  C is the row's running value (in: beyond this tile; out: beyond
 // the next one), `carry` the boundary inputs handed between tiles of the row.
-template <class E2, int L, int K>
+// CARRY: hand the boundary inputs to the next tile of the row (rows of one
+// tile need none).
+template <class E2, int L, int K, bool CARRY = true>
 __device__ __forceinline__ void stream_tile(const LaneIn<E2, K>& d, const ScanScalars& sc, unsigned tbits,
                                             unsigned rbits, uint32_t cs, int64_t T, bool team_first_lane, int lane,
                                             double& C, PredIn& carry, float (&o0)[K], float (&o1)[K]) {
@@ -206,7 +208,7 @@ __device__ __forceinline__ void stream_tile(const LaneIn<E2, K>& d, const ScanSc
   epilogue<E2, K>(d, lp, sc, x_in, xs, o0, o1);
 
   // boundary inputs for the next tile of this row (held by the scan-last lane, 63)
-  if constexpr (L == 64) {
+  if constexpr (CARRY && L == 64) {
     if constexpr (Tr::kRetrace) {
       const double ratio = (double)d.s[3][MLAST] / (double)d.s[4][MLAST];
       const double cl = sc.lam * (ratio < 1.0 ? ratio : 1.0);

@@ -1,0 +1,58 @@
+"""The two-items-per-wave kernel (rows of 64, 128 or 256 float32 steps, each
+wave scanning a second 256-element item staged through LDS) against the
+oracle, at the shapes the launcher routes to it: discounted returns at every
+E; V-trace with 4096 to 32767 rows of 256 steps; TD(lambda), GAE, eligibility
+traces and prefix sums from 32768 rows of 256 steps.  Row counts that leave
+the last block with waves that have no second item, or the last item with
+fewer than 64 / L rows, are included, as are absent optional inputs."""
+from __future__ import annotations
+
+import sys
+
+import pytest
+
+from linear_recurrence_scan_reverse_amd import synth
+from tests.estimators import TOL, compare
+
+pytestmark = pytest.mark.gpu
+
+CASES = (
+    [("discounted_returns", E, T) for (E, T) in [(1, 64), (3, 64), (13, 64), (5, 128), (9, 256), (1000, 128),
+                                                 (1001, 256), (4099, 64), (16385, 256)]]
+    + [("vtrace", E, 256) for E in (4096, 4099, 20001)]
+    + [(n, E, 256) for n in ("td_lambda", "gae", "eligibility_traces", "episodic_prefix_sum") for E in (32768, 32771)]
+)
+
+
+@pytest.mark.parametrize("name,E,T", CASES)
+def test_duo_kernel_matches_oracle(name, E, T):
+    print("duo %s E=%d T=%d" % (name, E, T), file=sys.stderr, flush=True)
+    d = synth.draw(E, T, seed=90 + E % 13, p_term=0.01, p_trunc=0.01)
+    for k, (err, mx) in compare(name, d).items():
+        assert err <= TOL, "%s %s E=%d T=%d: err %.3g (max|ref| %.3g)" % (name, k, E, T, err, mx)
+
+
+@pytest.mark.parametrize("variant", [dict(term=False, trunc=False), dict(boot=False, tboot=False), dict(trunc=False),
+                                     dict(tboot=False)])
+@pytest.mark.parametrize("name", ["discounted_returns", "vtrace"])
+def test_duo_kernel_optional_inputs(name, variant):
+    d = synth.draw(4101, 256, seed=97, p_term=0.02, p_trunc=0.02)
+    for k, (err, mx) in compare(name, d, **variant).items():
+        assert err <= TOL, "%s %s %s: err %.3g" % (name, variant, k, err)
+
+
+def test_duo_kernel_dense_flags_and_exact_sums():
+    import numpy as np
+    import torch
+    import linear_recurrence_scan_reverse_amd as rl
+    import oracle
+    d = synth.draw(33001, 256, seed=98, p_term=0.3, p_trunc=0.3)
+    for name in ("discounted_returns", "td_lambda", "eligibility_traces"):
+        for k, (err, mx) in compare(name, d).items():
+            assert err <= TOL, (name, k, err)
+    # small-integer prefix sums are exact on this path too
+    rng = np.random.default_rng(99)
+    x = rng.integers(-20, 21, size=(32768, 256)).astype(np.float32)
+    term = (rng.random((32768, 256)) < 0.01).astype(np.uint8)
+    got = rl.episodic_prefix_sum(torch.from_numpy(x).cuda(), torch.from_numpy(term).cuda()).cpu().numpy()
+    assert np.array_equal(got.astype(np.float64), oracle.episodic_prefix_sum(x, term))
