@@ -8,9 +8,11 @@
 // items in flight, and the rows the first round of waves does not cover wait
 // for slots to free before their loads start.  A plain streaming kernel moving
 // the same arrays ran fastest with two items per wave (every item requested at
-// once).  Here the second item costs no registers: its input streams land in
-// the wave's own LDS slot (4 KiB per float32 stream), so occupancy stays that
-// of the one-item kernel while twice the bytes are requested.  The per-lane
+// once).  Here the second item costs few registers: up to three of its input
+// streams land in the wave's own LDS slot (1 KiB per stream and wave; 12 KiB
+// per block at most, so eight blocks fit a CU) and the rest in registers, so
+// occupancy stays that of the one-item kernel while twice the bytes are
+// requested.  The per-lane
 // scan code is the one every kernel of the library shares (stream_tile:
 // pairs, fold, lane scan, re-walk, epilogue).
 //
@@ -38,6 +40,12 @@ constexpr int kDuoItem = 256;  // elements of every array in one item
 // (T == 4 L), OPT (bit 0 flags, bit 1 second output).  Float32 storage; every
 // dense array 16-byte aligned, flag arrays 4-byte aligned (checked by the
 // launcher).  Blocks of 4 waves take items 8 b + w and 8 b + 4 + w.
+// Retrace forms its trace quotient pi / mu from the fp32 reciprocal of mu
+// refined by one fp64 Newton step (retrace_c_fast, relative error about
+// 1e-14) instead of an fp64 division: this kernel computes two items per wave
+// after both have landed, so its vector instructions count.  Measured at
+// 16384 x 256 on one MI355X: 20.0 -> 19.75 us (the one-item form measured
+// slower with it and keeps the division).
 template <class Est, int L, int OPT>
 __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
@@ -52,7 +60,10 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   static_assert(!Tr::kDual, "one recurrence per pass");
   static_assert(G * SPAN == kDuoItem, "an item is whole rows");
 
-  __shared__ float s_b[4][NS][kDuoItem];  // each wave's second item, memory order
+  // B's first NL streams go through LDS (at most three: 12 KiB per block, so
+  // eight blocks fit a CU's LDS with room to spare); the rest -> registers
+  constexpr int NL = NS < 3 ? NS : 3;
+  __shared__ float s_b[4][NL][kDuoItem];  // each wave's second item, memory order
 
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -97,10 +108,12 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
     int64_t e = item_bc * kDuoItem + 4 * lane;
     if (e > E * T - 4) e = E * T - 4;
 #pragma unroll
-    for (int st = 0; st < NS; ++st)
+    for (int st = 0; st < NL; ++st)
       __builtin_amdgcn_global_load_lds((gbl_void_ptr)(srcs[st] + e), (lds_void_ptr)&s_b[w][st][0], 16, 0, 0);
   }
   LaneIn<Est, K> db;
+#pragma unroll
+  for (int st = NL; st < NS; ++st) load_s<F32S, K, true>(srcs[st], rb * T, cs, 0u, db.s[st]);
   unsigned ftb[K], frb[K];
   if constexpr (USE_FLAGS) {
     load_flag_raw<K, true>(p.term + rb * T, cs, 0u, ftb);
@@ -137,7 +150,7 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
     if constexpr (!Tr::kBackwardRl) C = (ok_a && p.has_row) ? (double)da.rowv : 0.0;
     PredIn carry{0.0f, 0.0, 0u};  // a row is one tile: no scan predecessor
     float o0[K], o1[K];
-    stream_tile<Est, L, K, false>(da, sc, tba, rba, cs, T, team_first_lane, lane, C, carry, o0, o1);
+    stream_tile<Est, L, K, false, Tr::kRetrace>(da, sc, tba, rba, cs, T, team_first_lane, lane, C, carry, o0, o1);
     if (G == 1 || ok_a) {
       store_s<F32S, K, true>(p.out0, ra * T, cs, K, o0);
       if constexpr (OUT1) store_s<F32S, K, true>(p.out1, ra * T, cs, K, o1);
@@ -147,13 +160,13 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   // ---- 6. item B
   if (!has_b) return;
 #pragma unroll
-  for (int st = 0; st < NS; ++st) lds_read4<F32S>(&s_b[w][st][lds_idx], db.s[st]);
+  for (int st = 0; st < NL; ++st) lds_read4<F32S>(&s_b[w][st][lds_idx], db.s[st]);
   {
     double C = 0.0;
     if constexpr (!Tr::kBackwardRl) C = (ok_b && p.has_row) ? (double)db.rowv : 0.0;
     PredIn carry{0.0f, 0.0, 0u};
     float o0[K], o1[K];
-    stream_tile<Est, L, K, false>(db, sc, tbb, rbb, cs, T, team_first_lane, lane, C, carry, o0, o1);
+    stream_tile<Est, L, K, false, Tr::kRetrace>(db, sc, tbb, rbb, cs, T, team_first_lane, lane, C, carry, o0, o1);
     if (G == 1 || ok_b) {
       store_s<F32S, K, true>(p.out0, rb * T, cs, K, o0);
       if constexpr (OUT1) store_s<F32S, K, true>(p.out1, rb * T, cs, K, o1);

@@ -294,14 +294,23 @@ inline bool prefer_stream(const KernelArgs& a, int L) {
 // Rows of 64, 128 or 256 steps in float32 with every dense array 16-byte
 // aligned (and the flag arrays 4-byte aligned) can take the kernel that gives
 // each wave two 256-element items, the second staged through LDS (duo_kernel).
-// Measured against the routes below (flags present, E in {1024, 4096, 16384,
-// 65536} x T in {64, 128, 256}): discounted returns gained or tied at every
-// point (16384 x 256: 10.8 -> 10.2 us; 16384 x 128: 7.9 -> 6.7 us; 65536 x 256:
-// 36.2 -> 29.7 us); TD(lambda), eligibility traces and prefix sums gained at
-// 65536 x 256 (TD(lambda) 46.1 -> 40.2 us, traces 31.7 -> 26.5 us) but lost
-// 1.0-1.1 us at 16384 x 256; V-trace gained 0.1-0.5 us at 4096 and 16384 rows
-// of 256 steps and lost at 65536; Retrace lost from 16384 rows up.  Returns
-// the team width, or 0 when the call does not take this kernel.
+// Routing from an A/B on one MI355X with flags present, over E in {1024, 4096,
+// 16384, 32768, 65536} x T in {64, 128, 256}, against the one-item pipelined
+// kernel (Retrace, V-trace) or the streaming kernel (the others):
+//  * discounted returns: faster or within 0.1 us everywhere (16384 x 256:
+//    10.4 -> 10.2 us; 32768 x 64: 7.7 -> 6.5 us; 65536 x 256: 33.7 -> 29.7 us);
+//  * Retrace: faster with rows of 256 steps up to 32768 rows (16384 x 256:
+//    20.4 -> 20.1 us; 32768 x 256: 37.4 -> 36.1 us) and up to 4096 rows of 64
+//    or 128 steps; slower at 65536 x 256 and from 16384 rows of 64 or 128;
+//  * V-trace: faster from 4096 rows of 256 steps (16384 x 256: 19.3 -> 18.9
+//    us; 32768 x 256: 34.0 -> 31.8 us) and at 65536 x 128; slower elsewhere;
+//  * TD(lambda) and GAE: faster from 32768 rows of 256 steps (TD(lambda)
+//    23.8 -> 20.9 us, 65536 x 256: 46.1 -> 40.3 us) and at 65536 x 128, but
+//    about 1 us slower at 16384 x 256;
+//  * traces and prefix sums: faster up to 4096 rows, up to 16384 rows of 64
+//    or 128 steps, and at 65536 x 256 (32.2 -> 26.4 us); about 0.9 us slower
+//    at 16384 and 32768 rows of 256 steps.
+// Returns the team width, or 0 when the call does not take this kernel.
 template <class Est>
 inline int duo_team(const KernelArgs& a) {
   if (a.T != 64 && a.T != 128 && a.T != 256) return 0;
@@ -309,12 +318,15 @@ inline int duo_team(const KernelArgs& a) {
   const int64_t items = (a.E + (64 / L) - 1) / (64 / L);
   if ((items + 7) / 8 * 256 > kMaxWorkItems) return 0;
   if (!vector_ok(a, 4, (int)a.T)) return 0;
+  const int64_t E = a.E, T = a.T;
   bool take = false;
   if constexpr (__is_same(Est, DiscountedReturn)) take = true;
-  if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae) || __is_same(Est, EligibilityTrace) ||
-                __is_same(Est, EpisodicPrefixSum))
-    take = a.T == 256 && a.E >= 32768;
-  if constexpr (__is_same(Est, Vtrace)) take = a.T == 256 && a.E >= 4096 && a.E < 32768;
+  if constexpr (__is_same(Est, Retrace)) take = (T == 256 && E <= 32768) || E <= 4096;
+  if constexpr (__is_same(Est, Vtrace)) take = (T == 256 && E >= 4096) || (T == 128 && E >= 65536);
+  if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae))
+    take = (T == 256 && E >= 32768) || (T == 128 && E >= 65536);
+  if constexpr (__is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum))
+    take = E <= 4096 || (T <= 128 && E <= 16384) || (T == 256 && E >= 65536);
   return take ? L : 0;
 }
 

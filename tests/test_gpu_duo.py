@@ -1,10 +1,13 @@
 """The two-items-per-wave kernel (rows of 64, 128 or 256 float32 steps, each
 wave scanning a second 256-element item staged through LDS) against the
-oracle, at the shapes the launcher routes to it: discounted returns at every
-E; V-trace with 4096 to 32767 rows of 256 steps; TD(lambda), GAE, eligibility
-traces and prefix sums from 32768 rows of 256 steps.  Row counts that leave
-the last block with waves that have no second item, or the last item with
-fewer than 64 / L rows, are included, as are absent optional inputs."""
+oracle, at shapes the launcher routes to it for every estimator that takes it
+(discounted returns at every E; Retrace with rows of 256 steps up to 32768
+rows and any row up to 4096 rows; V-trace from 4096 rows of 256 steps and
+from 65536 rows of 128; TD(lambda) and GAE from 32768 rows of 256 steps and
+65536 rows of 128; traces and prefix sums up to 4096 rows, up to 16384 rows of
+64 or 128 steps and from 65536 rows of 256).  Row counts that leave the last
+block with waves that have no second item, or the last item with fewer than
+64 / L rows, are included, as are absent optional inputs."""
 from __future__ import annotations
 
 import sys
@@ -19,8 +22,11 @@ pytestmark = pytest.mark.gpu
 CASES = (
     [("discounted_returns", E, T) for (E, T) in [(1, 64), (3, 64), (13, 64), (5, 128), (9, 256), (1000, 128),
                                                  (1001, 256), (4099, 64), (16385, 256)]]
-    + [("vtrace", E, 256) for E in (4096, 4099, 20001)]
-    + [(n, E, 256) for n in ("td_lambda", "gae", "eligibility_traces", "episodic_prefix_sum") for E in (32768, 32771)]
+    + [("retrace", E, T) for (E, T) in [(3, 64), (1001, 128), (4096, 128), (9, 256), (16385, 256)]]
+    + [("vtrace", E, T) for (E, T) in [(4096, 256), (4099, 256), (20001, 256), (65537, 128)]]
+    + [(n, E, T) for n in ("td_lambda", "gae") for (E, T) in [(32768, 256), (32771, 256), (65536, 128)]]
+    + [(n, E, T) for n in ("eligibility_traces", "episodic_prefix_sum")
+       for (E, T) in [(5, 64), (1001, 128), (4096, 256), (16383, 64), (65537, 256)]]
 )
 
 
@@ -34,7 +40,7 @@ def test_duo_kernel_matches_oracle(name, E, T):
 
 @pytest.mark.parametrize("variant", [dict(term=False, trunc=False), dict(boot=False, tboot=False), dict(trunc=False),
                                      dict(tboot=False)])
-@pytest.mark.parametrize("name", ["discounted_returns", "vtrace"])
+@pytest.mark.parametrize("name", ["discounted_returns", "vtrace", "retrace"])
 def test_duo_kernel_optional_inputs(name, variant):
     d = synth.draw(4101, 256, seed=97, p_term=0.02, p_trunc=0.02)
     for k, (err, mx) in compare(name, d, **variant).items():
