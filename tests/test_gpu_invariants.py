@@ -304,10 +304,10 @@ def test_concurrent_host_threads():
 @pytest.mark.parametrize("T", [128, 256, 512, 1024])
 def test_zero_flag_arrays_match_absent_flags(T):
     """All-zero flag arrays and absent (NULL) flags describe the same episodes, but
-    they route Retrace and V-trace to different kernels (the pipelined kernel's
-    one-item form with flags, the streaming or persistent kernel without), and
-    the other estimators to different template instances.  Each pair must agree
-    to fp32 rounding of the same fp64 result; no oracle is involved."""
+    a call with flag arrays runs other template instances than one without
+    (they read and decode the flag bytes, and the backward estimators gather
+    truncation bootstraps).  Each pair must agree to fp32 rounding of the same
+    fp64 result; no oracle is involved."""
     E = 2048
     d = synth.draw(E, T, seed=500 + T, p_term=0.0, p_trunc=0.0)
     assert not d["terminated"].any() and not d["truncated"].any()

@@ -55,7 +55,7 @@ EDGE_T = [1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128
 @pytest.mark.parametrize("T", EDGE_T)
 def test_edge_lengths_all_estimators(T):
     """Ragged tails, tile/wave/team boundaries and multi-tile rows."""
-    for E in (1, 3, 65):
+    for E in (1, 3, 64, 65):
         d = synth.draw(E, T, seed=1000 + T + E, p_term=0.05, p_trunc=0.05)
         for name in NAMES:
             _assert_ok(name, compare(name, d), "E=%d T=%d" % (E, T))
