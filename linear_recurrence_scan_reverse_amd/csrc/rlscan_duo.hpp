@@ -1,7 +1,7 @@
-// rlscan_duo.hpp -- rows of 64, 128 or 256 steps (one 256-element item of
-// every [E,T] array holds G = 64 / L whole rows): each wave scans two items,
-// the first loaded into registers and the second into LDS by DMA, both
-// requested before either is scanned.
+// rlscan_duo.hpp -- rows of 64 to 512 steps, whose items (1 KiB of every
+// array: 256 float32 or 512 16-bit elements) hold G = 64 / L whole rows: each
+// wave scans two items, the first loaded into registers and the second into
+// LDS by DMA, both requested before either is scanned.
 //
 // A kernel that gives each wave one item (the pipelined kernel's one-item
 // form) holds its inputs in registers; at full occupancy a CU then has 32
@@ -12,9 +12,9 @@
 // streams land in the wave's own LDS slot (1 KiB per stream and wave; 12 KiB
 // per block at most, so eight blocks fit a CU) and the rest in registers, so
 // occupancy stays that of the one-item kernel while twice the bytes are
-// requested.  The per-lane
-// scan code is the one every kernel of the library shares (stream_tile:
-// pairs, fold, lane scan, re-walk, epilogue).
+// requested.  The per-lane scan code is the one every kernel of the library
+// shares (stream_tile: pairs, fold, lane scan, re-walk, epilogue); a lane
+// holds K = 4 float32 or K = 8 16-bit steps (16 bytes of each array).
 //
 // Order inside a wave (the flag-dependent bootstrap gather of each item is
 // issued as soon as its flags are known):
@@ -34,36 +34,59 @@
 
 namespace rlscan {
 
-constexpr int kDuoItem = 256;  // elements of every array in one item
+constexpr int kDuoItemBytes = 1024;  // bytes of every array in one item
+
+// K stored values at an LDS byte address (16-byte aligned), widened.
+template <class S, int K>
+__device__ __forceinline__ void lds_read_chunk(const char* q, float (&o)[K]) {
+  if constexpr (__is_same(S, F32S)) {
+    static_assert(K == 4, "four float32 values");
+    const f32x4 v = *reinterpret_cast<const f32x4*>(q);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  } else {
+    static_assert(K == 8, "eight 16-bit values");
+    const u32x4 v = *reinterpret_cast<const u32x4*>(q);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = s_to_f32<S>((uint16_t)w[i]);
+      o[2 * i + 1] = s_to_f32<S>((uint16_t)(w[i] >> 16));
+    }
+  }
+}
 
 // Template parameters: estimator tag (not the two-output pass), team width L
-// (T == 4 L), OPT (bit 0 flags, bit 1 second output).  Float32 storage; every
-// dense array 16-byte aligned, flag arrays 4-byte aligned (checked by the
-// launcher).  Blocks of 4 waves take items 8 b + w and 8 b + 4 + w.
+// (T == K L), OPT (bit 0 flags, bit 1 second output), storage format S.
+// Every dense array 16-byte aligned, flag arrays K-byte aligned (checked by
+// the launcher).  Blocks of 4 waves take items 8 b + w and 8 b + 4 + w.
 // Retrace forms its trace quotient pi / mu from the fp32 reciprocal of mu
 // refined by one fp64 Newton step (retrace_c_fast, relative error about
 // 1e-14) instead of an fp64 division: this kernel computes two items per wave
 // after both have landed, so its vector instructions count.  Measured at
 // 16384 x 256 on one MI355X: 20.0 -> 19.75 us (the one-item form measured
-// slower with it and keeps the division).
-template <class Est, int L, int OPT>
+// slower with it and keeps the division).  The 16-bit formats also take the
+// fast exp of V-trace, as every kernel does for them.
+template <class Est, int L, int OPT, class S = F32S>
 __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
-  constexpr int K = 4;
+  constexpr int ES = (int)sizeof(typename S::T);  // bytes per stored value
+  constexpr int K = 16 / ES;                      // steps per lane
+  constexpr int ITEM = kDuoItemBytes / ES;        // elements per item
   constexpr bool REV = Est::kReverse;
   constexpr int NS = Tr::kStreams;
   constexpr bool USE_FLAGS = (OPT & 1) && Tr::kUsesFlags;
   constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
   constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
+  constexpr bool FAST = Tr::kRetrace || !__is_same(S, F32S);
   constexpr int G = 64 / L;   // rows per item
   constexpr int SPAN = L * K;  // row length
   static_assert(!Tr::kDual, "one recurrence per pass");
-  static_assert(G * SPAN == kDuoItem, "an item is whole rows");
+  static_assert(G * SPAN == ITEM, "an item is whole rows");
 
   // B's first NL streams go through LDS (at most three: 12 KiB per block, so
   // eight blocks fit a CU's LDS with room to spare); the rest -> registers
   constexpr int NL = NS < 3 ? NS : 3;
-  __shared__ float s_b[4][NL][kDuoItem];  // each wave's second item, memory order
+  __shared__ __attribute__((aligned(16))) char s_b[4][NL][kDuoItemBytes];  // each wave's second item, memory order
 
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -71,7 +94,7 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   const int g = lane & (L - 1);
   const bool team_first_lane = g == 0;
   const uint32_t cs = REV ? (uint32_t)(SPAN - (g + 1) * K) : (uint32_t)(g * K);  // column of the lane's chunk
-  const uint32_t lds_idx = (uint32_t)(team * SPAN) + cs;
+  const uint32_t lds_off = (uint32_t)((team * SPAN + (int)cs) * ES);             // its byte offset in the item
   const int64_t E = p.E, T = p.T;
   const int64_t items = (E + G - 1) / G;
   const int64_t item_a = (int64_t)blockIdx.x * 8 + w;
@@ -95,31 +118,32 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   LaneIn<Est, K> da;
   unsigned fta[K], fra[K];
 #pragma unroll
-  for (int st = 0; st < NS; ++st) load_s<F32S, K, true>(srcs[st], ra * T, cs, 0u, da.s[st]);
+  for (int st = 0; st < NS; ++st) load_s<S, K, true>(srcs[st], ra * T, cs, 0u, da.s[st]);
   if constexpr (USE_FLAGS) {
     load_flag_raw<K, true>(p.term + ra * T, cs, 0u, fta);
     load_flag_raw<K, true>(p.trunc + ra * T, cs, 0u, fra);
   }
-  da.rowv = load1<F32S>(p.row, ra, 0u);
+  da.rowv = load1<S>(p.row, ra, 0u);
 
-  // ---- 2. item B: streams -> LDS (lane l moves elements 4 l .. 4 l + 3 of the
-  // item, clamped into the array), flags and row value -> registers
+  // ---- 2. item B: streams -> LDS (lane l moves bytes 16 l .. 16 l + 15 of
+  // the item, clamped into the array), flags and row value -> registers
   {
-    int64_t e = item_bc * kDuoItem + 4 * lane;
-    if (e > E * T - 4) e = E * T - 4;
+    int64_t bo = item_bc * kDuoItemBytes + 16 * lane;
+    if (bo > E * T * ES - 16) bo = E * T * ES - 16;
 #pragma unroll
     for (int st = 0; st < NL; ++st)
-      __builtin_amdgcn_global_load_lds((gbl_void_ptr)(srcs[st] + e), (lds_void_ptr)&s_b[w][st][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_ptr)(reinterpret_cast<const char*>(srcs[st]) + bo),
+                                       (lds_void_ptr)&s_b[w][st][0], 16, 0, 0);
   }
   LaneIn<Est, K> db;
 #pragma unroll
-  for (int st = NL; st < NS; ++st) load_s<F32S, K, true>(srcs[st], rb * T, cs, 0u, db.s[st]);
+  for (int st = NL; st < NS; ++st) load_s<S, K, true>(srcs[st], rb * T, cs, 0u, db.s[st]);
   unsigned ftb[K], frb[K];
   if constexpr (USE_FLAGS) {
     load_flag_raw<K, true>(p.term + rb * T, cs, 0u, ftb);
     load_flag_raw<K, true>(p.trunc + rb * T, cs, 0u, frb);
   }
-  db.rowv = load1<F32S>(p.row, rb, 0u);
+  db.rowv = load1<S>(p.row, rb, 0u);
 
   // ---- 3. A's flags and bootstrap gather
   unsigned tba = 0, rba = 0, tbb = 0, rbb = 0;
@@ -130,7 +154,7 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
     rba = flag_bits<K, true>(fra) & rmask;
   }
   if constexpr (GATHER_TB) {
-    if ((rba & ~tba) != 0u && p.has_tboot) load_chunk<K, true>(p.tboot + ra * T, cs, 0u, da.tb);
+    if ((rba & ~tba) != 0u && p.has_tboot) load_s<S, K, true>(p.tboot, ra * T, cs, 0u, da.tb);
   }
 
   // ---- 4. everything landed (B's DMA included); B's flags and gather
@@ -141,7 +165,7 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
     rbb = flag_bits<K, true>(frb) & rmask;
   }
   if constexpr (GATHER_TB) {
-    if ((rbb & ~tbb) != 0u && p.has_tboot) load_chunk<K, true>(p.tboot + rb * T, cs, 0u, db.tb);
+    if ((rbb & ~tbb) != 0u && p.has_tboot) load_s<S, K, true>(p.tboot, rb * T, cs, 0u, db.tb);
   }
 
   // ---- 5. item A
@@ -150,28 +174,201 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
     if constexpr (!Tr::kBackwardRl) C = (ok_a && p.has_row) ? (double)da.rowv : 0.0;
     PredIn carry{0.0f, 0.0, 0u};  // a row is one tile: no scan predecessor
     float o0[K], o1[K];
-    stream_tile<Est, L, K, false, Tr::kRetrace>(da, sc, tba, rba, cs, T, team_first_lane, lane, C, carry, o0, o1);
+    stream_tile<Est, L, K, false, FAST>(da, sc, tba, rba, cs, T, team_first_lane, lane, C, carry, o0, o1);
     if (G == 1 || ok_a) {
-      store_s<F32S, K, true>(p.out0, ra * T, cs, K, o0);
-      if constexpr (OUT1) store_s<F32S, K, true>(p.out1, ra * T, cs, K, o1);
+      store_s<S, K, true>(p.out0, ra * T, cs, K, o0);
+      if constexpr (OUT1) store_s<S, K, true>(p.out1, ra * T, cs, K, o1);
     }
   }
 
   // ---- 6. item B
   if (!has_b) return;
 #pragma unroll
-  for (int st = 0; st < NL; ++st) lds_read4<F32S>(&s_b[w][st][lds_idx], db.s[st]);
+  for (int st = 0; st < NL; ++st) lds_read_chunk<S, K>(&s_b[w][st][lds_off], db.s[st]);
   {
     double C = 0.0;
     if constexpr (!Tr::kBackwardRl) C = (ok_b && p.has_row) ? (double)db.rowv : 0.0;
     PredIn carry{0.0f, 0.0, 0u};
     float o0[K], o1[K];
-    stream_tile<Est, L, K, false, Tr::kRetrace>(db, sc, tbb, rbb, cs, T, team_first_lane, lane, C, carry, o0, o1);
+    stream_tile<Est, L, K, false, FAST>(db, sc, tbb, rbb, cs, T, team_first_lane, lane, C, carry, o0, o1);
     if (G == 1 || ok_b) {
-      store_s<F32S, K, true>(p.out0, rb * T, cs, K, o0);
-      if constexpr (OUT1) store_s<F32S, K, true>(p.out1, rb * T, cs, K, o1);
+      store_s<S, K, true>(p.out0, rb * T, cs, K, o0);
+      if constexpr (OUT1) store_s<S, K, true>(p.out1, rb * T, cs, K, o1);
     }
   }
+}
+
+// ----------------------------------------------------------------- both items in registers
+// The same two items per wave with item B held in registers too, as the raw
+// 16 bytes per stream and lane (converted only when B is scanned), so no LDS
+// DMA mixes with the ordinary loads and the compiler's waits stay exact: A is
+// scanned as soon as its own loads have landed, while B's are still in
+// flight.  In the LDS form every wave waits for both items, so the waves of a
+// CU, whose requests all went out at once, mostly start computing together at
+// the end of the load phase; here half of that work moves into it.  Measured
+// at 16384 x 256 on one MI355X: bfloat16 discounted returns 9.1 -> 7.9 us,
+// V-trace 14.1 -> 12.2 us against the LDS form; float32 discounted returns
+// 10.3 -> 9.4 us, Retrace 19.5 -> 20.1 us (Retrace keeps the LDS form there).  Request order: A's flags, A's streams, B's flags, A's bootstraps
+// (once A's flags are in), B's streams, B's bootstraps (once B's flags are
+// in); then A is scanned and stored, then B.  Bootstraps and stores go
+// through buffer resources over the item (lanes without a bootstrap to fetch,
+// and rows past E, fall outside the resource and touch no memory), so no
+// branch surrounds a request.
+constexpr uint32_t kDuoOff = 0x80000000u;  // past every item resource
+
+template <class S>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t duo_item_rs(const void* base, int64_t item, int64_t total_bytes) {
+  const int64_t b0 = item * kDuoItemBytes;
+  const int64_t n = total_bytes - b0 < kDuoItemBytes ? total_bytes - b0 : kDuoItemBytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + b0, 0, (int)n,
+                                           0x00020000);
+}
+
+// K values of format S from 16 raw bytes.
+template <class S, int K>
+__device__ __forceinline__ void unpack16(const u32x4 v, float (&o)[K]) {
+  if constexpr (__is_same(S, F32S)) {
+    static_assert(K == 4, "four float32 values");
+    const f32x4 f = __builtin_bit_cast(f32x4, v);
+    o[0] = f.x; o[1] = f.y; o[2] = f.z; o[3] = f.w;
+  } else {
+    static_assert(K == 8, "eight 16-bit values");
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = s_to_f32<S>((uint16_t)w[i]);
+      o[2 * i + 1] = s_to_f32<S>((uint16_t)(w[i] >> 16));
+    }
+  }
+}
+// K values of format S packed into 16 bytes.
+template <class S, int K>
+__device__ __forceinline__ u32x4 pack16(const float (&o)[K]) {
+  if constexpr (__is_same(S, F32S)) {
+    return __builtin_bit_cast(u32x4, f32x4{o[0], o[1], o[2], o[3]});
+  } else {
+    u32x4 q;
+    q.x = (uint32_t)f32_to_s<S>(o[0]) | ((uint32_t)f32_to_s<S>(o[1]) << 16);
+    q.y = (uint32_t)f32_to_s<S>(o[2]) | ((uint32_t)f32_to_s<S>(o[3]) << 16);
+    q.z = (uint32_t)f32_to_s<S>(o[4]) | ((uint32_t)f32_to_s<S>(o[5]) << 16);
+    q.w = (uint32_t)f32_to_s<S>(o[6]) | ((uint32_t)f32_to_s<S>(o[7]) << 16);
+    return q;
+  }
+}
+
+template <class Est, int L, int OPT, class S = F32S>
+__global__ void __launch_bounds__(256) duo_reg_kernel(const KernelArgs p) {
+  using Tr = Traits<Est>;
+  constexpr int ES = (int)sizeof(typename S::T);
+  constexpr int K = 16 / ES;
+  constexpr int ITEM = kDuoItemBytes / ES;
+  constexpr bool REV = Est::kReverse;
+  constexpr int NS = Tr::kStreams;
+  constexpr bool USE_FLAGS = (OPT & 1) && Tr::kUsesFlags;
+  constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
+  constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
+  constexpr bool FAST = Tr::kRetrace || !__is_same(S, F32S);
+  constexpr int G = 64 / L;
+  constexpr int SPAN = L * K;
+  static_assert(!Tr::kDual, "one recurrence per pass");
+  static_assert(G * SPAN == ITEM, "an item is whole rows");
+
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int team = lane / L;
+  const int g = lane & (L - 1);
+  const bool team_first_lane = g == 0;
+  const uint32_t cs = REV ? (uint32_t)(SPAN - (g + 1) * K) : (uint32_t)(g * K);
+  const uint32_t boff = (uint32_t)((team * SPAN + (int)cs) * ES);  // lane's byte offset in its item
+  const int64_t E = p.E, T = p.T;
+  const int64_t total = E * T * ES;
+  const int64_t items = (E + G - 1) / G;
+  const int64_t item_a = (int64_t)blockIdx.x * 8 + w;
+  const int64_t item_b = item_a + 4;
+  if (item_a >= items) return;  // (wave-uniform; the kernel has no block barrier)
+  const bool has_b = item_b < items;
+  const int64_t item_bc = has_b ? item_b : item_a;
+
+  const double gamma = p.gamma, lam = p.lam;
+  const ScanScalars sc{gamma, lam, gamma * lam, (float)p.rho_bar, (float)p.c_bar, p.has_row != 0, p.has_tboot != 0};
+  const unsigned tmask = p.has_term ? ~0u : 0u;
+  const unsigned rmask = p.has_trunc ? ~0u : 0u;
+  const float* srcs[5] = {p.r, p.v, p.aux, p.pi, p.mu};
+
+  const int64_t row_a = item_a * G + team, row_b = item_bc * G + team;
+  const bool ok_a = row_a < E, ok_b = has_b && row_b < E;
+  const int64_t ra = ok_a ? row_a : E - 1, rb = row_b < E ? row_b : E - 1;
+  auto raw_at = [&](const float* base, int64_t row) -> u32x4 {
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + (row * T + cs) * ES));
+  };
+
+  // A's flags and streams, B's flags
+  unsigned fta[K], fra[K], ftb[K], frb[K];
+  if constexpr (USE_FLAGS) {
+    load_flag_raw<K, true>(p.term + ra * T, cs, 0u, fta);
+    load_flag_raw<K, true>(p.trunc + ra * T, cs, 0u, fra);
+  }
+  const float rowa = load1<S>(p.row, ra, 0u);
+  u32x4 xa[NS], xb[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) xa[st] = raw_at(srcs[st], ra);
+  if constexpr (USE_FLAGS) {
+    load_flag_raw<K, true>(p.term + rb * T, cs, 0u, ftb);
+    load_flag_raw<K, true>(p.trunc + rb * T, cs, 0u, frb);
+  }
+  const float rowb = load1<S>(p.row, rb, 0u);
+  asm volatile("" ::: "memory");
+
+  // A's bootstraps (waits for A's flags only)
+  unsigned tba = 0, rba = 0, tbb = 0, rbb = 0;
+  if constexpr (USE_FLAGS) {
+    tba = flag_bits<K, true>(fta) & tmask;
+    rba = flag_bits<K, true>(fra) & rmask;
+  }
+  u32x4 ga = u32x4{0u, 0u, 0u, 0u}, gb = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (GATHER_TB) {
+    const bool need = ok_a && (rba & ~tba) != 0u && p.has_tboot;
+    ga = __builtin_amdgcn_raw_buffer_load_b128(duo_item_rs<S>(p.tboot, item_a, total), need ? boff : kDuoOff, 0, 2);
+  }
+  // B's streams, then B's bootstraps (waits for B's flags only).  The empty
+  // asm takes B's flag words after B's streams are requested, so the compiler
+  // cannot decode them (and wait for them, and so for A's streams) earlier.
+#pragma unroll
+  for (int st = 0; st < NS; ++st) xb[st] = raw_at(srcs[st], rb);
+  if constexpr (USE_FLAGS) {
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) asm volatile("" : "+v"(ftb[i]), "+v"(frb[i])::"memory");
+  }
+  if constexpr (USE_FLAGS) {
+    tbb = flag_bits<K, true>(ftb) & tmask;
+    rbb = flag_bits<K, true>(frb) & rmask;
+  }
+  if constexpr (GATHER_TB) {
+    const bool need = ok_b && (rbb & ~tbb) != 0u && p.has_tboot;
+    gb = __builtin_amdgcn_raw_buffer_load_b128(duo_item_rs<S>(p.tboot, item_bc, total), need ? boff : kDuoOff, 0, 2);
+  }
+
+  // one item: unpack, scan, store (rows past E fall outside the output resource)
+  auto item = [&](int64_t it, const u32x4 (&x)[NS], const u32x4 gt, float rowv, unsigned tbits, unsigned rbits,
+                  bool ok) {
+    LaneIn<Est, K> d;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) unpack16<S, K>(x[st], d.s[st]);
+    unpack16<S, K>(gt, d.tb);
+    d.rowv = rowv;
+    double C = 0.0;
+    if constexpr (!Tr::kBackwardRl) C = (ok && p.has_row) ? (double)rowv : 0.0;
+    PredIn carry{0.0f, 0.0, 0u};
+    float o0[K], o1[K];
+    stream_tile<Est, L, K, false, FAST>(d, sc, tbits, rbits, cs, T, team_first_lane, lane, C, carry, o0, o1);
+    __builtin_amdgcn_raw_buffer_store_b128(pack16<S, K>(o0), duo_item_rs<S>(p.out0, it, total), boff, 0, 2);
+    if constexpr (OUT1)
+      __builtin_amdgcn_raw_buffer_store_b128(pack16<S, K>(o1), duo_item_rs<S>(p.out1, it, total), boff, 0, 2);
+  };
+  item(item_a, xa, ga, rowa, tba, rba, ok_a);
+  if (!has_b) return;
+  item(item_b, xb, gb, rowb, tbb, rbb, ok_b);
 }
 
 }  // namespace rlscan

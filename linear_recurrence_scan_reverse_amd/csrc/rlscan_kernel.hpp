@@ -481,8 +481,8 @@ struct PredIn {
 // Per-lane result of building the pairs.
 template <int K> struct LanePairs {
   AB e[K];           // pairs in scan order (j = 0 nearest the carry)
-  double rho[K];     // V-trace: rho_t
-  double succv[K];   // V-trace: the cut's successor value
+  float rho[K];      // V-trace: rho_t (a float32 value; widened where used)
+  float succv[K];    // V-trace: the cut's successor value (a float32 input)
   unsigned cut;      // K-bit mask of steps after which the episode chain stops
   float nb_v;        // value handed in for the innermost step (V-trace epilogue)
 };
@@ -548,8 +548,8 @@ __device__ __forceinline__ LanePairs<K> build_pairs(const LaneIn<Est, K>& d, con
   for (int j = 0; j < K; ++j) {
     const int m = REV ? (K - 1 - j) : j;
     AB c;
-    out.rho[j] = 0.0;
-    out.succv[j] = 0.0;
+    out.rho[j] = 0.0f;
+    out.succv[j] = 0.0f;
     if constexpr (Tr::kBackwardRl) {
       const bool is_cut = (cut >> m) & 1u;
       // successor value at a cut (0 terminated / trunc bootstrap / row bootstrap)
@@ -582,12 +582,13 @@ __device__ __forceinline__ LanePairs<K> build_pairs(const LaneIn<Est, K>& d, con
         // relative, far below a 16-bit unit (bfloat16 V-trace 16.4 -> 15.6 us at
         // 16384 x 256); float32 keeps the libm expf
         const float ratio = FASTDIV ? __expf(d.s[2][m]) : expf(d.s[2][m]);
-        const double rh = (double)fminf(ratio, sc.rho_bar);
+        const float rhf = fminf(ratio, sc.rho_bar);
+        const double rh = (double)rhf;
         const double ct = (double)fminf(ratio, sc.c_bar);
         c.a = is_cut ? 0.0 : gl * ct;
         c.b = rh * (__builtin_fma(gamma, nu, r) - (double)d.s[1][m]);
-        out.rho[j] = rh;
-        out.succv[j] = (double)bvf;
+        out.rho[j] = rhf;
+        out.succv[j] = bvf;
       } else if constexpr (Tr::kRetrace) {
         c.a = is_cut ? 0.0 : gamma * cn;
         c.b = __builtin_fma(gamma, nu, r) - (double)d.s[1][m];
@@ -659,8 +660,8 @@ __device__ __forceinline__ void epilogue(const LaneIn<Est, K>& d, const LanePair
       const double xprev = (j == 0) ? x_in : xs[j - 1];
       const int mp = REV ? m + 1 : m - 1;
       const float vnx = (j == 0) ? lp.nb_v : d.s[1][(mp < 0 || mp >= K) ? 0 : mp];
-      const double succ = ((lp.cut >> m) & 1u) ? lp.succv[j] : ((double)vnx + xprev);
-      y1 = lp.rho[j] * (__builtin_fma(sc.gamma, succ, (double)d.s[0][m]) - (double)d.s[1][m]);
+      const double succ = ((lp.cut >> m) & 1u) ? (double)lp.succv[j] : ((double)vnx + xprev);
+      y1 = (double)lp.rho[j] * (__builtin_fma(sc.gamma, succ, (double)d.s[0][m]) - (double)d.s[1][m]);
       y = (double)d.s[1][m] + y;
     } else if constexpr (Tr::kRetrace) {
       y = (double)d.s[1][m] + y;

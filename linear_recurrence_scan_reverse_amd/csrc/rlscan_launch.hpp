@@ -291,26 +291,32 @@ inline bool prefer_stream(const KernelArgs& a, int L) {
 }
 
 // ----------------------------------------------------------------- two items per wave
-// Rows of 64, 128 or 256 steps in float32 with every dense array 16-byte
-// aligned (and the flag arrays 4-byte aligned) can take the kernel that gives
-// each wave two 256-element items, the second staged through LDS (duo_kernel).
-// Routing from an A/B on one MI355X with flags present, over E in {1024, 4096,
-// 16384, 32768, 65536} x T in {64, 128, 256}, against the one-item pipelined
-// kernel (Retrace, V-trace) or the streaming kernel (the others):
-//  * discounted returns: faster or within 0.1 us everywhere (16384 x 256:
-//    10.4 -> 10.2 us; 32768 x 64: 7.7 -> 6.5 us; 65536 x 256: 33.7 -> 29.7 us);
-//  * Retrace: faster with rows of 256 steps up to 32768 rows (16384 x 256:
-//    20.4 -> 20.1 us; 32768 x 256: 37.4 -> 36.1 us) and up to 4096 rows of 64
-//    or 128 steps; slower at 65536 x 256 and from 16384 rows of 64 or 128;
-//  * V-trace: faster from 4096 rows of 256 steps (16384 x 256: 19.3 -> 18.9
-//    us; 32768 x 256: 34.0 -> 31.8 us) and at 65536 x 128; slower elsewhere;
-//  * TD(lambda) and GAE: faster from 32768 rows of 256 steps (TD(lambda)
-//    23.8 -> 20.9 us, 65536 x 256: 46.1 -> 40.3 us) and at 65536 x 128, but
-//    about 1 us slower at 16384 x 256;
-//  * traces and prefix sums: faster up to 4096 rows, up to 16384 rows of 64
-//    or 128 steps, and at 65536 x 256 (32.2 -> 26.4 us); about 0.9 us slower
-//    at 16384 and 32768 rows of 256 steps.
-// Returns the team width, or 0 when the call does not take this kernel.
+// Rows of 64, 128 or 256 float32 steps (128, 256 or 512 16-bit steps) with
+// every dense array 16-byte aligned (and the flag arrays 4-byte aligned) can
+// take a kernel that gives each wave two items of 1 KiB per array: duo_kernel
+// (the second item staged through LDS) or duo_reg_kernel (both in registers,
+// each scanned as soon as its own loads land).  Routing from A/B runs on one
+// MI355X with flags present over E in {4096, 16384, 65536} x T in {64, 128,
+// 256, 512} (and E in {1024, 32768} for the float32 rules), each against the
+// one-item pipelined kernel or the streaming kernel the call took before:
+//  * discounted returns: faster or within noise everywhere (float32 16384 x
+//    256: 10.3 -> 9.4 us; bfloat16: 10.6 -> 7.9 us);
+//  * Retrace: float32 rows of 256 steps up to 32768 rows and any row up to
+//    4096 rows, the LDS form from 16384 rows of 256 steps (19.5-19.7 us
+//    against 20.1 with both items in registers), the register form below
+//    (4096 x 256: 7.4 -> 6.7 us); 16-bit: everywhere (bfloat16 16384 x 256
+//    14.8 -> 12.8 us, 65536 x 256 49.5 -> 41.6 us);
+//  * V-trace: float32 from 4096 rows of 256 steps and at 65536 x 128 (34.2 ->
+//    32.7 us); 16-bit: all but 4096 x 128 (bfloat16 16384 x 256: 14.5 ->
+//    12.2 us);
+//  * TD(lambda) and GAE: float32 from 32768 rows of 256 steps, at 65536 x 128
+//    (22.3 -> 20.8 us) and up to 4096 rows (4096 x 256: 5.7 -> 4.8-4.9 us;
+//    below 4096 rows within the 5-10% run-to-run spread of these 4 us
+//    calls); 16-bit: everywhere (bfloat16 16384 x 256: 10.1 -> 8.8 us);
+//  * traces and prefix sums: float32 up to 4096 rows, up to 16384 rows of 64
+//    or 128 steps, and at 65536 x 256; 16-bit: all but 4096 x 256 (bfloat16
+//    16384 x 256: 8.1 -> 6.7 us).
+// Returns the team width, or 0 when the call does not take these kernels.
 template <class Est>
 inline int duo_team(const KernelArgs& a) {
   if (a.T != 64 && a.T != 128 && a.T != 256) return 0;
@@ -324,31 +330,57 @@ inline int duo_team(const KernelArgs& a) {
   if constexpr (__is_same(Est, Retrace)) take = (T == 256 && E <= 32768) || E <= 4096;
   if constexpr (__is_same(Est, Vtrace)) take = (T == 256 && E >= 4096) || (T == 128 && E >= 65536);
   if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae))
-    take = (T == 256 && E >= 32768) || (T == 128 && E >= 65536);
+    take = (T == 256 && E >= 32768) || (T == 128 && E >= 65536) || E <= 4096;
   if constexpr (__is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum))
     take = E <= 4096 || (T <= 128 && E <= 16384) || (T == 256 && E >= 65536);
   return take ? L : 0;
 }
 
-template <class Est, int L, int OPT>
-inline hipError_t launch_duo_opt(const KernelArgs& a, hipStream_t s) {
+// float32: the LDS form only for Retrace from 16384 rows of 256 steps
+template <class Est>
+inline bool duo_in_registers(const KernelArgs& a) {
+  return !(__is_same(Est, Retrace) && a.T == 256 && a.E > 4096);
+}
+
+// 16-bit storage: items of 512 elements, eight steps per lane, so rows of
+// 128, 256 or 512 steps (team width T / 8); always the register form.
+template <class Est>
+inline int duo_team_16(const KernelArgs& a) {
+  if (a.T != 128 && a.T != 256 && a.T != 512) return 0;
+  const int L = (int)(a.T / 8);
+  const int64_t items = (a.E + (64 / L) - 1) / (64 / L);
+  if ((items + 7) / 8 * 256 > kMaxWorkItems) return 0;
+  if (!vector_ok(a, 8, (int)a.T, 2)) return 0;
+  const int64_t E = a.E, T = a.T;
+  bool take = true;
+  if constexpr (__is_same(Est, Vtrace)) take = !(E <= 4096 && T == 128);
+  if constexpr (__is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum))
+    take = !(E <= 4096 && T == 256);
+  return take ? L : 0;
+}
+
+template <class Est, int L, int OPT, class S = F32S>
+inline hipError_t launch_duo_opt(const KernelArgs& a, hipStream_t s, bool reg) {
   const int64_t items = (a.E + (64 / L) - 1) / (64 / L);
   KernelArgs arg = a;
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT>), dim3((unsigned)((items + 7) / 8)),
-                         dim3(256), params, 0, s);
+  const void* k = reinterpret_cast<const void*>(&duo_reg_kernel<Est, L, OPT, S>);
+  if constexpr (__is_same(S, F32S)) {
+    if (!reg) k = reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT>);
+  }
+  return hipLaunchKernel(k, dim3((unsigned)((items + 7) / 8)), dim3(256), params, 0, s);
 }
 
-template <class Est, int L>
-inline hipError_t launch_duo(const KernelArgs& a, hipStream_t s) {
+template <class Est, int L, class S = F32S>
+inline hipError_t launch_duo(const KernelArgs& a, hipStream_t s, bool reg) {
   using Tr = Traits<Est>;
   const bool flags = a.has_term || a.has_trunc;
   if constexpr (Tr::kHasOut1) {
     const bool out1 = a.out1 != nullptr;
-    if (flags) return out1 ? launch_duo_opt<Est, L, 3>(a, s) : launch_duo_opt<Est, L, 1>(a, s);
-    return out1 ? launch_duo_opt<Est, L, 2>(a, s) : launch_duo_opt<Est, L, 0>(a, s);
+    if (flags) return out1 ? launch_duo_opt<Est, L, 3, S>(a, s, reg) : launch_duo_opt<Est, L, 1, S>(a, s, reg);
+    return out1 ? launch_duo_opt<Est, L, 2, S>(a, s, reg) : launch_duo_opt<Est, L, 0, S>(a, s, reg);
   } else {
-    return flags ? launch_duo_opt<Est, L, 1>(a, s) : launch_duo_opt<Est, L, 0>(a, s);
+    return flags ? launch_duo_opt<Est, L, 1, S>(a, s, reg) : launch_duo_opt<Est, L, 0, S>(a, s, reg);
   }
 }
 
@@ -403,10 +435,11 @@ hipError_t launch(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const SegPlan plan = segment_plan(a); plan.len) return launch_segmented<Est>(a, s, plan);
   if constexpr (!Traits<Est>::kDual && !Traits<Est>::kLinear) {
+    const bool reg = duo_in_registers<Est>(a);
     switch (duo_team<Est>(a)) {
-      case 16: return launch_duo<Est, 16>(a, s);
-      case 32: return launch_duo<Est, 32>(a, s);
-      case 64: return launch_duo<Est, 64>(a, s);
+      case 16: return launch_duo<Est, 16>(a, s, reg);
+      case 32: return launch_duo<Est, 32>(a, s, reg);
+      case 64: return launch_duo<Est, 64>(a, s, reg);
       default: break;
     }
   }
@@ -433,7 +466,8 @@ hipError_t launch(const KernelArgs& in, hipStream_t s) {
 }
 
 // Values stored as 16-bit bf16 / fp16 (S = Bf16S, F16S): the segmented path
-// for long rows; the streaming kernel for traces and prefix sums where the
+// for long rows; the two-item register kernel for rows of 128-512 steps
+// (duo_team_16); the streaming kernel for traces and prefix sums where the
 // rows allow it and the float32 routing rule prefers it; else the pipelined
 // kernel.  At 16384 x 256 (bfloat16) the streaming kernel ran traces and
 // prefix sums in 8.7-9.3 us against 9.6-9.9 pipelined, but the five backward
@@ -444,6 +478,14 @@ template <class Est, class S>
 hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const SegPlan plan = segment_plan(a); plan.len) return launch_segmented<Est, S>(a, s, plan);
+  if constexpr (!Traits<Est>::kDual && !Traits<Est>::kLinear) {
+    switch (duo_team_16<Est>(a)) {
+      case 16: return launch_duo<Est, 16, S>(a, s, true);
+      case 32: return launch_duo<Est, 32, S>(a, s, true);
+      case 64: return launch_duo<Est, 64, S>(a, s, true);
+      default: break;
+    }
+  }
   const bool one = prefer_oneshot<Est>(a, (int)sizeof(typename S::T));
   if constexpr (Traits<Est>::kForwardRl) {
     const int team = one ? 0 : stream_team<S>(a);

@@ -1,13 +1,16 @@
-"""The two-items-per-wave kernel (rows of 64, 128 or 256 float32 steps, each
-wave scanning a second 256-element item staged through LDS) against the
-oracle, at shapes the launcher routes to it for every estimator that takes it
-(discounted returns at every E; Retrace with rows of 256 steps up to 32768
-rows and any row up to 4096 rows; V-trace from 4096 rows of 256 steps and
-from 65536 rows of 128; TD(lambda) and GAE from 32768 rows of 256 steps and
-65536 rows of 128; traces and prefix sums up to 4096 rows, up to 16384 rows of
-64 or 128 steps and from 65536 rows of 256).  Row counts that leave the last
-block with waves that have no second item, or the last item with fewer than
-64 / L rows, are included, as are absent optional inputs."""
+"""The two-items-per-wave kernels (rows of 64, 128 or 256 float32 steps; each
+wave scans two 256-element items, the second staged through LDS or, in the
+register form, held in registers too) against the oracle, at shapes the
+launcher routes to them for every estimator that takes them (discounted
+returns at every E; Retrace with rows of 256 steps up to 32768 rows, in the
+LDS form from 4097 rows, and any row up to 4096 rows; V-trace from 4096 rows
+of 256 steps and from 65536 rows of 128; TD(lambda) and GAE up to 4096 rows,
+from 32768 rows of 256 steps and 65536 rows of 128; traces and prefix sums up
+to 4096 rows, up to 16384 rows of 64 or 128 steps and from 65536 rows of 256).
+Row counts that leave the last block with waves that have no second item, or
+the last item with fewer than 64 / L rows, are included, as are absent
+optional inputs.  The 16-bit formats' register form is covered in
+test_gpu_storage16.py."""
 from __future__ import annotations
 
 import sys
@@ -24,7 +27,8 @@ CASES = (
                                                  (1001, 256), (4099, 64), (16385, 256)]]
     + [("retrace", E, T) for (E, T) in [(3, 64), (1001, 128), (4096, 128), (9, 256), (16385, 256)]]
     + [("vtrace", E, T) for (E, T) in [(4096, 256), (4099, 256), (20001, 256), (65537, 128)]]
-    + [(n, E, T) for n in ("td_lambda", "gae") for (E, T) in [(32768, 256), (32771, 256), (65536, 128)]]
+    + [(n, E, T) for n in ("td_lambda", "gae") for (E, T) in [(7, 64), (1001, 128), (4096, 256), (32768, 256),
+                                                                 (32771, 256), (65536, 128)]]
     + [(n, E, T) for n in ("eligibility_traces", "episodic_prefix_sum")
        for (E, T) in [(5, 64), (1001, 128), (4096, 256), (16383, 64), (65537, 256)]]
 )

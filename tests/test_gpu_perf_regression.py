@@ -3,8 +3,8 @@
 Each estimator's per-launch time, measured as the bench measures it (rotating
 buffer sets over 1 GiB, 200 back-to-back calls, HIP events on the launch
 stream), must stay under a ceiling set 1.2x above what the current kernels
-measure on one MI355X (discounted returns 10.6 us, TD(lambda) / GAE 12.2 us,
-V-trace 19.1 us, Retrace 19.9 us, traces / prefix sums 8.7 us).  Times move by
+measure on one MI355X (discounted returns 9.4 us, TD(lambda) / GAE 12.1 us,
+V-trace 19.0 us, Retrace 19.6 us, traces / prefix sums 8.1 us).  Times move by
 up to about 5% from one GPU to the next; a routing or occupancy mistake has
 cost 1.3-2x here.
 """
@@ -15,13 +15,13 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 CEILING_US = {
-    "discounted_returns": 12.7,
-    "td_lambda": 14.6,
-    "gae": 14.6,
-    "vtrace": 22.9,
-    "retrace": 23.9,
-    "eligibility_traces": 10.4,
-    "episodic_prefix_sum": 10.4,
+    "discounted_returns": 11.3,
+    "td_lambda": 14.5,
+    "gae": 14.5,
+    "vtrace": 22.8,
+    "retrace": 23.5,
+    "eligibility_traces": 9.8,
+    "episodic_prefix_sum": 9.8,
 }
 
 
@@ -40,16 +40,16 @@ def test_per_estimator_time_at_16384x256():
 
 
 # bfloat16 storage, same workload and method; 1.2x above the current kernels
-# (discounted returns 10.7 us, TD(lambda) / GAE 10.2 us, V-trace 14.6 us,
-# Retrace 15.1 us, traces / prefix sums 8.2 us).
+# (discounted returns 8.0 us, TD(lambda) / GAE 8.8 us, V-trace 12.4 us,
+# Retrace 12.8 us, traces / prefix sums 6.7 us).
 CEILING_BF16_US = {
-    "discounted_returns": 12.9,
-    "td_lambda": 12.3,
-    "gae": 12.3,
-    "vtrace": 17.5,
-    "retrace": 18.1,
-    "eligibility_traces": 9.8,
-    "episodic_prefix_sum": 9.8,
+    "discounted_returns": 9.6,
+    "td_lambda": 10.6,
+    "gae": 10.6,
+    "vtrace": 14.9,
+    "retrace": 15.4,
+    "eligibility_traces": 8.0,
+    "episodic_prefix_sum": 8.0,
 }
 
 

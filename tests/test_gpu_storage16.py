@@ -109,3 +109,16 @@ def test_float16_overflow_gives_inf():
         exp = ref.astype(np.float32).astype(np.float16).astype(np.float32)
     assert np.isposinf(exp[:, -1]).all() and np.isfinite(exp[:, 31]).all()
     assert np.array_equal(got, exp)
+
+
+@pytest.mark.parametrize("fmt", ["bfloat16", "float16"])
+@pytest.mark.parametrize("E,T", [(1, 512), (5, 128), (9, 256), (1001, 512), (4099, 128), (16385, 256)])
+def test_storage16_two_items_per_wave(fmt, E, T):
+    # rows of 128, 256 or 512 steps with 16-byte aligned arrays: the kernel
+    # that gives each wave two 512-element items (the second through LDS)
+    # where the launcher routes them there; row counts leave the last block
+    # with waves that have no second item and the last item with fewer rows
+    _say("16-bit storage two items per wave %s E=%d T=%d" % (fmt, E, T))
+    d = synth.draw(E, T, seed=74 + E % 7, p_term=0.01, p_trunc=0.01)
+    for name in SEVEN:
+        check_storage(name, d, fmt)
