@@ -475,6 +475,254 @@ def host_info():
     return {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "model": model}
 
 
+# ----------------------------------------------------------------- profile summaries
+# The rocprofv3 runs behind the summaries under profiles/, and the summaries
+# themselves (written from the runs' CSV output; no GPU needed):
+#   python3 bench.py --profile-commands OUT > run.sh   (then: bash run.sh)
+#   python3 bench.py --summarize OUT                   (writes profiles/*.txt)
+# A main run's per-estimator timing is 200 or more back-to-back calls of one
+# kernel; the summaries average each estimator's kernel over the longest such
+# run of consecutive dispatches, so warm-up and step calls do not enter.
+PROFILE_MAIN = {  # main runs profiled: name -> bench.py arguments
+    "f32": [],
+    "bf16": ["--storage", "bf16"],
+    "tm_f32": ["--time-major"],
+}
+PMC_PASSES = {  # one rocprofv3 --pmc run each (within the per-block counter limits)
+    "A": "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+         "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VMEM GRBM_GUI_ACTIVE",
+    "B": "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_SMEM "
+         "SQ_ACTIVE_INST_LDS SQ_WAVES GRBM_GUI_ACTIVE",
+    "C": "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_WRREQ_sum",
+    "F": "FETCH_SIZE",
+    "W": "WRITE_SIZE",
+}
+PROFILE_RUN_ARGS = ["--steps", "2", "--warmup", "1", "--no-cpu", "--no-ceiling", "--no-16", "--no-configs"]
+KERNEL_TAGS = {"DiscountedReturn": "discounted_returns", "TdLambda": "td_lambda", "Gae": "gae", "Vtrace": "vtrace",
+               "Retrace": "retrace", "EligibilityTrace": "eligibility_traces",
+               "EpisodicPrefixSum": "episodic_prefix_sum", "ReturnsTdLambda": "returns_and_td_lambda"}
+CLOCK_GHZ = 2.4   # MI355X peak engine clock
+SIMDS = 256 * 4   # compute units x SIMDs
+
+
+def profile_commands(out):
+    """Shell commands (one GPU step each, bounded) that produce every rocprofv3
+    output the summaries read, under directory `out`."""
+    bench = os.path.join(ROOT, "bench.py")
+    run = "python3 %s --steps 5 --warmup 2 --no-cpu --no-configs --no-ceiling" % bench
+    lines = ["set -o pipefail", "cd /tmp && export TMPDIR=/tmp", "mkdir -p %s" % out,
+             "timeout -k 10 600 %s > %s/bench_plain.json" % (run, out),
+             "timeout -k 10 600 rocprofv3 --kernel-trace --stats --output-format csv -d %s/kt -o kt -- %s > "
+             "%s/bench.json" % (out, run, out)]
+    for m, extra in PROFILE_MAIN.items():
+        for ps, counters in PMC_PASSES.items():
+            lines.append("timeout -s KILL 180 rocprofv3 --pmc %s --output-format csv -d %s/pmc/%s/%s -o pmc -- "
+                         "python3 %s %s" % (counters, out, m, ps, bench, " ".join(PROFILE_RUN_ARGS + extra)))
+    for ps in ("F", "W"):
+        lines.append("timeout -s KILL 120 rocprofv3 --pmc %s --output-format csv -d %s/cal/%s -o pmc -- "
+                     "python3 %s --calibration-copy" % (PMC_PASSES[ps], out, ps, bench))
+    return "\n".join(l + (" &&" if i < len(lines) - 1 and i >= 1 else "") for i, l in enumerate(lines))
+
+
+def _kernel_short(name):
+    """A kernel's name without return type, namespace and argument list."""
+    name = name.strip().replace("rlscan::", "").replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            name = name[:i]
+            break
+    return name.strip()
+
+
+def _read_dispatches(pattern):
+    """Dispatches of one rocprofv3 CSV output (kernel trace or counter
+    collection): list of {name, us, counters}, in dispatch order."""
+    import csv
+    import glob
+    files = sorted(glob.glob(pattern, recursive=True))
+    if len(files) != 1:
+        raise SystemExit("expected one file for %s, found %d" % (pattern, len(files)))
+    disp = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            k = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            e = disp.setdefault(k, {"name": _kernel_short(r["Kernel_Name"]), "counters": {},
+                                    "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0})
+            if "Counter_Name" in r:
+                e["counters"][r["Counter_Name"]] = e["counters"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [disp[k] for k in sorted(disp)]
+
+
+def _timed_runs(disp, min_len=100):
+    """{kernel: dispatches of its longest run of consecutive calls} for runs of
+    at least min_len calls (the bench's back-to-back timing)."""
+    best, i = {}, 0
+    while i < len(disp):
+        j = i
+        while j < len(disp) and disp[j]["name"] == disp[i]["name"]:
+            j += 1
+        if j - i >= min_len and j - i > len(best.get(disp[i]["name"], [])):
+            best[disp[i]["name"]] = disp[i:j]
+        i = j
+    return best
+
+
+def _estimator_of(kernel):
+    import re
+    m = re.search(r"<(\w+)", kernel)
+    return KERNEL_TAGS.get(m.group(1)) if m else None
+
+
+def _bench_json(path):
+    for line in reversed(open(path).read().splitlines()):
+        if line.startswith("{"):
+            return json.loads(line)
+    raise SystemExit("no bench line in %s" % path)
+
+
+def summarize_profiles(out):
+    """Write the profiles/ summaries from the rocprofv3 output under `out`."""
+    sha = kernel_source_hash()
+    cmd_note = ["# commands (repository root, one MI355X; OUT an empty directory):",
+                "#   python3 bench.py --profile-commands OUT > run.sh && bash run.sh",
+                "#   python3 bench.py --summarize OUT",
+                "# (run.sh: the rocprofv3 runs listed by --profile-commands; each averages an estimator's",
+                "#  kernel over its longest run of back-to-back calls, the bench's 200-call timing)"]
+    # HIP-event times of an unprofiled run of the same bench command (under the
+    # profiler, launches are spaced by its per-dispatch work, so events there
+    # time the host, not the kernels)
+    bl = _bench_json(os.path.join(out, "bench_plain.json"))
+    if bl.get("kernel_source_sha256") != sha or _bench_json(os.path.join(out, "bench.json")).get(
+            "kernel_source_sha256") != sha:
+        raise SystemExit("the profiled runs used other kernel sources")
+    runs = _timed_runs(_read_dispatches(os.path.join(out, "kt", "**", "*kernel_trace.csv")))
+    events = {("f32", n): e["us_per_launch"] for n, e in bl["per_estimator"].items()}
+    for n, e in (bl.get("one_pass_entries") or {}).items():
+        if "us_per_launch" in e:
+            events[("f32", n)] = e["us_per_launch"]
+    for fmt, per in (bl.get("formats_and_layouts") or {}).items():
+        for n, e in per.items():
+            events[(fmt, n)] = e["us_per_launch"]
+
+    def fmt_of(k):
+        s = "bf16" if "Bf16S" in k else "f16" if "F16S" in k else "f32"
+        return ("time_major_" + s) if k.startswith(("tm_kernel", "tm_carry")) else s
+
+    rows = {}
+    for k, v in runs.items():
+        n = _estimator_of(k)
+        if n:
+            rows.setdefault(fmt_of(k), []).append((n, k, v))
+    head = ["# kernel_source_sha256: %s" % sha,
+            "# columns: estimator, kernel (template arguments), calls averaged, average / min / max",
+            "#   duration (us), and the per-launch time HIP events measured for the same 200 calls",
+            "#   in an unprofiled run of the same command (the bench's timing)"] + cmd_note + [""]
+    order = list(ORDER) + ["returns_and_td_lambda"]
+    main = ["# rocprofv3 kernel trace: librlscan kernels, workload all7_16384x256 (E=16384, T=256), float32"] + head
+    other = ["# rocprofv3 kernel trace: librlscan kernels, workload all7_16384x256 (E=16384, T=256),",
+             "# 16-bit storage and the time-major layout (first column: format:estimator)"] + head
+    for fmt in ["f32", "bf16", "f16", "time_major_f32", "time_major_bf16"]:
+        for n, k, v in sorted(rows.get(fmt, []), key=lambda r: order.index(r[0]) if r[0] in order else 99):
+            us = [x["us"] for x in v]
+            ev = events.get((fmt, n))
+            line = "%-34s %-46s calls %4d  avg %7.2f  min %7.2f  max %7.2f   events %s" % (
+                n if fmt == "f32" else "%s:%s" % (fmt, n), k, len(us), sum(us) / len(us), min(us), max(us),
+                "%7.2f" % ev if ev else "   -")
+            (main if fmt == "f32" else other).append(line)
+    wl = "all7_16384x256"
+    with open(os.path.join(PROFILES, "kernel_trace_rlscan_%s.txt" % wl), "w") as f:
+        f.write("\n".join(main) + "\n")
+    with open(os.path.join(PROFILES, "kernel_trace_rlscan_formats_layouts_%s.txt" % wl), "w") as f:
+        f.write("\n".join(other) + "\n")
+
+    # counters: calibration (a plain copy of known size) for the traffic counters
+    cal = {}
+    for ps, cname in (("F", "FETCH_SIZE"), ("W", "WRITE_SIZE")):
+        d = [x for x in _read_dispatches(os.path.join(out, "cal", ps, "**", "*counter_collection.csv"))
+             if "grid_kernel" in x["name"]]
+        cal[ps] = sum(x["counters"][cname] for x in d) / len(d)
+    moved_kib = float(1 << 20)  # the calibration copy reads and writes 1 GiB per launch
+    scale = {"F": moved_kib / cal["F"], "W": moved_kib / cal["W"]}
+
+    w = synth.WORKLOADS[wl]
+    d = synth.workload_inputs(w)
+    traffic = ["# HBM traffic per launch of the librlscan kernels, workload %s (E=%d, T=%d), float32" % (wl, w.E, w.T),
+               "# hbm bytes = FETCH_SIZE * 1024 * read_scale + WRITE_SIZE * 1024 * write_scale (per-dispatch",
+               "#   averages over each estimator's back-to-back calls); the scales make the same counters",
+               "#   read 1 GiB each way for a plain copy kernel of 1 GiB (%s KiB fetched, %s KiB written" % (
+                   "%.1f" % cal["F"], "%.1f" % cal["W"]),
+               "#   per copy launch)"] + cmd_note + [
+               "kernel_source_sha256: %s" % sha, "read_scale: %.4f" % scale["F"], "write_scale: %.4f" % scale["W"]]
+    ctr = ["# rocprofv3 counters of the librlscan kernels, workload %s (E=%d, T=%d)" % (wl, w.E, w.T),
+           "# per launch, averaged over each estimator's back-to-back calls:",
+           "#   waves            SQ_WAVES",
+           "#   valu/wave ...    SQ_INSTS_VALU, _VMEM_RD, _VMEM_WR, _LDS, _SALU per wave",
+           "#   valu_us          SQ_INSTS_VALU x 4 cycles / %d SIMDs / %.1f GHz: the time every SIMD spends" % (
+               SIMDS, CLOCK_GHZ),
+           "#                    issuing vector instructions if the work spreads evenly (a wave64 VALU",
+           "#                    instruction occupies its SIMD for 4 cycles or more)",
+           "#   valu_active      SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES: share of resident wave time issuing VALU",
+           "#   wait_mem         SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES: share of resident wave time waiting at a",
+           "#                    s_waitcnt for memory",
+           "#   waves/CU         SQ_WAVE_CYCLES x 4 / (256 CUs x kernel cycles at %.1f GHz): mean resident waves" % CLOCK_GHZ,
+           "#   l2_hit           TCC_HIT / (TCC_HIT + TCC_MISS)",
+           "#   hbm/alg          HBM bytes (FETCH_SIZE, WRITE_SIZE as in the traffic summary) / algorithmic bytes",
+           "# kernel_us is the profiled dispatch duration (counter collection serializes and slows",
+           "# dispatches; the kernel-trace summary has the unperturbed times)"] + cmd_note + [
+           "kernel_source_sha256: %s" % sha, ""]
+    hdr = "%-30s %-44s %6s %7s %6s %6s %6s %6s %7s %7s %7s %7s %7s %7s %7s" % (
+        "format:estimator", "kernel", "waves", "valu/w", "vmrd/w", "vmwr/w", "lds/w", "salu/w", "valu_us",
+        "valu_act", "wait_mem", "waves/CU", "l2_hit", "hbm/alg", "kernel_us")
+    ctr.append(hdr)
+    for m in PROFILE_MAIN:
+        per_pass = {}
+        for ps in PMC_PASSES:
+            per_pass[ps] = _timed_runs(_read_dispatches(os.path.join(out, "pmc", m, ps, "**",
+                                                                     "*counter_collection.csv")))
+        kernels = sorted(set().union(*[set(r) for r in per_pass.values()]))
+        vb = 2 if m == "bf16" else 4
+        for k in kernels:
+            n = _estimator_of(k)
+            if not n or n not in ORDER:
+                continue
+
+            def avg(ps, c):
+                v = per_pass[ps].get(k)
+                return sum(x["counters"].get(c, 0.0) for x in v) / len(v) if v else float("nan")
+            waves = avg("B", "SQ_WAVES")
+            wc = avg("A", "SQ_WAVE_CYCLES")
+            durs = [x["us"] for x in per_pass["A"].get(k, [])]
+            dur = sum(durs) / len(durs) if durs else float("nan")
+            hbm = avg("F", "FETCH_SIZE") * 1024 * scale["F"] + avg("W", "WRITE_SIZE") * 1024 * scale["W"]
+            alg = alg_bytes(n, d, w.E, w.T, vb=vb)
+            hit, miss = avg("C", "TCC_HIT_sum"), avg("C", "TCC_MISS_sum")
+            ctr.append("%-30s %-44s %6d %7.0f %6.1f %6.1f %6.1f %6.0f %7.2f %7.3f %7.3f %7.1f %7.3f %7.3f %7.2f" % (
+                "%s:%s" % (m, n), k[:44], waves, avg("B", "SQ_INSTS_VALU") / waves, avg("B", "SQ_INSTS_VMEM_RD") / waves,
+                avg("B", "SQ_INSTS_VMEM_WR") / waves, avg("B", "SQ_INSTS_LDS") / waves,
+                avg("B", "SQ_INSTS_SALU") / waves, avg("B", "SQ_INSTS_VALU") * 4 / SIMDS / (CLOCK_GHZ * 1e3),
+                avg("A", "SQ_ACTIVE_INST_VALU") / wc, avg("A", "SQ_WAIT_INST_ANY") / wc,
+                wc * 4 / (256 * dur * CLOCK_GHZ * 1e3), hit / (hit + miss) if hit + miss else float("nan"),
+                hbm / alg, dur))
+            if m == "f32":
+                traffic += ["%s.kernel: %s" % (n, k), "%s.fetch_kib: %.1f" % (n, avg("F", "FETCH_SIZE")),
+                            "%s.write_kib: %.1f" % (n, avg("W", "WRITE_SIZE")),
+                            "%s.hbm_bytes_per_launch: %d" % (n, round(hbm)),
+                            "%s.alg_bytes_per_launch: %d" % (n, alg),
+                            "%s.traffic_over_alg: %.3f" % (n, hbm / alg)]
+    with open(os.path.join(PROFILES, "hbm_traffic_rlscan_%s.txt" % wl), "w") as f:
+        f.write("\n".join(traffic) + "\n")
+    with open(os.path.join(PROFILES, "counters_rlscan_%s.txt" % wl), "w") as f:
+        f.write("\n".join(ctr) + "\n")
+    log("wrote the kernel-trace, traffic and counter summaries under profiles/")
+
+
 # ----------------------------------------------------------------- main
 GRID_E = (256, 1024, 4096, 16384, 65536)
 GRID_T = (64, 128, 256, 512, 1024, 2048, 4096)
@@ -645,8 +893,18 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the plain-stream ceiling sweep (profiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only the counter calibration: the stream probe copying 1 GiB to 1 GiB, 5 times")
+    ap.add_argument("--profile-commands", metavar="OUT", default=None,
+                    help="print the rocprofv3 runs behind the profiles/ summaries (output under OUT)")
+    ap.add_argument("--summarize", metavar="OUT", default=None,
+                    help="write the profiles/ summaries from the rocprofv3 output under OUT (no GPU)")
     args = ap.parse_args()
     reps = max(200, args.reps)
+    if args.profile_commands:
+        print(profile_commands(os.path.abspath(args.profile_commands)))
+        return
+    if args.summarize:
+        summarize_profiles(os.path.abspath(args.summarize))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         log("bench.py: this build measures one GPU only (rows are independent; multi-GPU "
