@@ -371,4 +371,141 @@ __global__ void __launch_bounds__(256) duo_reg_kernel(const KernelArgs p) {
   item(item_b, xb, gb, rowb, tbb, rbb, ok_b);
 }
 
+// ----------------------------------------------------------------- NI items per wave, in registers
+// Wave w of block b scans items b * 4 NI + 4 i + w, i = 0 .. NI - 1, as a
+// software pipeline: while item i is scanned, the streams of items i + 1 and
+// i + 2, the bootstraps of item i + 1 and the flags of i + 2 and i + 3 are in
+// flight.  Per iteration i the wave requests bootstraps(i + 1) (its flags
+// landed with the streams of item i, which were requested before them),
+// streams(i + 2) and flags(i + 3), then scans and stores item i; the only
+// waits are for what item i uses.  Items past the last are scanned on a
+// clamped item's data and not stored (their store offset falls outside the
+// output resource), so no branch surrounds a request.
+template <class Est, int L, int OPT, class S, int NI>
+__global__ void __launch_bounds__(256) multi_reg_kernel(const KernelArgs p) {
+  using Tr = Traits<Est>;
+  constexpr int ES = (int)sizeof(typename S::T);
+  constexpr int K = 16 / ES;
+  constexpr int ITEM = kDuoItemBytes / ES;
+  constexpr bool REV = Est::kReverse;
+  constexpr int NS = Tr::kStreams;
+  constexpr bool USE_FLAGS = (OPT & 1) && Tr::kUsesFlags;
+  constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
+  constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
+  constexpr bool FAST = Tr::kRetrace || !__is_same(S, F32S);
+  constexpr int G = 64 / L;
+  constexpr int SPAN = L * K;
+  static_assert(!Tr::kDual, "one recurrence per pass");
+  static_assert(G * SPAN == ITEM, "an item is whole rows");
+  static_assert(NI >= 2 && NI <= 4, "items per wave");
+
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int team = lane / L;
+  const int g = lane & (L - 1);
+  const bool team_first_lane = g == 0;
+  const uint32_t cs = REV ? (uint32_t)(SPAN - (g + 1) * K) : (uint32_t)(g * K);
+  const uint32_t boff = (uint32_t)((team * SPAN + (int)cs) * ES);
+  const int64_t E = p.E, T = p.T;
+  const int64_t total = E * T * ES;
+  const int64_t items = (E + G - 1) / G;
+  const int64_t first = (int64_t)blockIdx.x * (4 * NI) + w;
+  if (first >= items) return;  // (wave-uniform; the kernel has no block barrier)
+
+  const double gamma = p.gamma, lam = p.lam;
+  const ScanScalars sc{gamma, lam, gamma * lam, (float)p.rho_bar, (float)p.c_bar, p.has_row != 0, p.has_tboot != 0};
+  const unsigned tmask = p.has_term ? ~0u : 0u;
+  const unsigned rmask = p.has_trunc ? ~0u : 0u;
+  const float* srcs[5] = {p.r, p.v, p.aux, p.pi, p.mu};
+
+  int64_t it[NI], rr[NI];
+  bool ok[NI], has[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int64_t t = first + 4 * i;
+    has[i] = t < items;
+    it[i] = has[i] ? t : first;  // a valid item for the requests
+    const int64_t row = it[i] * G + team;
+    ok[i] = has[i] && row < E;
+    rr[i] = row < E ? row : E - 1;
+  }
+  unsigned ft[NI][K], fr[NI][K];
+  float rowv[NI];
+  u32x4 x[NI][NS], gt[NI];
+  unsigned tb[NI], rb[NI];
+
+  auto req_flags = [&](int i) {
+    if constexpr (USE_FLAGS) {
+      load_flag_raw<K, true>(p.term + rr[i] * T, cs, 0u, ft[i]);
+      load_flag_raw<K, true>(p.trunc + rr[i] * T, cs, 0u, fr[i]);
+    }
+    rowv[i] = load1<S>(p.row, rr[i], 0u);
+  };
+  auto req_streams = [&](int i) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      x[i][st] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(srcs[st]) + (rr[i] * T + cs) * ES));
+  };
+  // decode item i's flags (the empty asm pins the wait for them here) and
+  // request its bootstraps
+  auto req_gather = [&](int i) {
+    tb[i] = rb[i] = 0u;
+    if constexpr (USE_FLAGS) {
+#pragma unroll
+      for (int j = 0; j < K / 4; ++j) asm volatile("" : "+v"(ft[i][j]), "+v"(fr[i][j])::"memory");
+      tb[i] = flag_bits<K, true>(ft[i]) & tmask;
+      rb[i] = flag_bits<K, true>(fr[i]) & rmask;
+    }
+    gt[i] = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (GATHER_TB) {
+      const bool need = ok[i] && (rb[i] & ~tb[i]) != 0u && p.has_tboot;
+      gt[i] = __builtin_amdgcn_raw_buffer_load_b128(duo_item_rs<S>(p.tboot, it[i], total), need ? boff : kDuoOff,
+                                                    0, 2);
+    }
+  };
+  auto scan_item = [&](int i) {
+    LaneIn<Est, K> d;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) unpack16<S, K>(x[i][st], d.s[st]);
+    unpack16<S, K>(gt[i], d.tb);
+    d.rowv = rowv[i];
+    double C = 0.0;
+    if constexpr (!Tr::kBackwardRl) C = (ok[i] && p.has_row) ? (double)rowv[i] : 0.0;
+    PredIn carry{0.0f, 0.0, 0u};
+    float o0[K], o1[K];
+    stream_tile<Est, L, K, false, FAST>(d, sc, tb[i], rb[i], cs, T, team_first_lane, lane, C, carry, o0, o1);
+    const uint32_t so = has[i] ? boff : kDuoOff;
+    __builtin_amdgcn_raw_buffer_store_b128(pack16<S, K>(o0), duo_item_rs<S>(p.out0, it[i], total), so, 0, 2);
+    if constexpr (OUT1)
+      __builtin_amdgcn_raw_buffer_store_b128(pack16<S, K>(o1), duo_item_rs<S>(p.out1, it[i], total), so, 0, 2);
+  };
+
+  // prologue: flags and streams of items 0 and 1, flags of item 2, then the
+  // bootstraps of item 0
+  // (each empty asm keeps the compiler from reordering requests across it)
+  req_flags(0);
+  asm volatile("" ::: "memory");
+  req_streams(0);
+  asm volatile("" ::: "memory");
+  req_flags(1);
+  asm volatile("" ::: "memory");
+  req_streams(1);
+  asm volatile("" ::: "memory");
+  if constexpr (NI > 2) req_flags(2);
+  asm volatile("" ::: "memory");
+  req_gather(0);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    asm volatile("" ::: "memory");
+    if (i + 1 < NI) req_gather(i + 1);
+    asm volatile("" ::: "memory");
+    if (i + 2 < NI) req_streams(i + 2);
+    asm volatile("" ::: "memory");
+    if (i + 3 < NI) req_flags(i + 3);
+    asm volatile("" ::: "memory");
+    scan_item(i);
+  }
+}
+
 }  // namespace rlscan

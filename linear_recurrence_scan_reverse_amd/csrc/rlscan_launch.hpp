@@ -290,60 +290,75 @@ inline bool prefer_stream(const KernelArgs& a, int L) {
   return true;
 }
 
-// ----------------------------------------------------------------- two items per wave
+// ----------------------------------------------------------------- items of 1 KiB per array
 // Rows of 64, 128 or 256 float32 steps (128, 256 or 512 16-bit steps) with
-// every dense array 16-byte aligned (and the flag arrays 4-byte aligned) can
-// take a kernel that gives each wave two items of 1 KiB per array: duo_kernel
-// (the second item staged through LDS) or duo_reg_kernel (both in registers,
-// each scanned as soon as its own loads land).  Routing from A/B runs on one
-// MI355X with flags present over E in {4096, 16384, 65536} x T in {64, 128,
-// 256, 512} (and E in {1024, 32768} for the float32 rules), each against the
-// one-item pipelined kernel or the streaming kernel the call took before:
-//  * discounted returns: faster or within noise everywhere (float32 16384 x
-//    256: 10.3 -> 9.4 us; bfloat16: 10.6 -> 7.9 us);
-//  * Retrace: float32 rows of 256 steps up to 32768 rows and any row up to
-//    4096 rows, the LDS form from 16384 rows of 256 steps (19.5-19.7 us
-//    against 20.1 with both items in registers), the register form below
-//    (4096 x 256: 7.4 -> 6.7 us); 16-bit: everywhere (bfloat16 16384 x 256
-//    14.8 -> 12.8 us, 65536 x 256 49.5 -> 41.6 us);
-//  * V-trace: float32 from 4096 rows of 256 steps and at 65536 x 128 (34.2 ->
-//    32.7 us); 16-bit: all but 4096 x 128 (bfloat16 16384 x 256: 14.5 ->
-//    12.2 us);
-//  * TD(lambda) and GAE: float32 from 32768 rows of 256 steps, at 65536 x 128
-//    (22.3 -> 20.8 us) and up to 4096 rows (4096 x 256: 5.7 -> 4.8-4.9 us;
-//    below 4096 rows within the 5-10% run-to-run spread of these 4 us
-//    calls); 16-bit: everywhere (bfloat16 16384 x 256: 10.1 -> 8.8 us);
-//  * traces and prefix sums: float32 up to 4096 rows, up to 16384 rows of 64
-//    or 128 steps, and at 65536 x 256; 16-bit: all but 4096 x 256 (bfloat16
-//    16384 x 256: 8.1 -> 6.7 us).
-// Returns the team width, or 0 when the call does not take these kernels.
+// every dense array 16-byte aligned (and the flag arrays K-byte aligned) can
+// take a kernel whose items are 1 KiB of every array (whole rows): duo_kernel
+// (two items per wave, the second staged through LDS), duo_reg_kernel (two
+// items per wave, both in registers, each scanned as soon as its own loads
+// land) or multi_reg_kernel with four items per wave (a software pipeline
+// keeping two items ahead in flight).
+enum DuoForm { kDuoNone = 0, kDuoLds = 1, kDuoReg = 2, kDuoReg4 = 4 };
+
+// Float32 routing, from A/B runs on one MI355X with flags present (each form
+// forced for every estimator, two interleaved rounds over E in {4096, 16384,
+// 32768, 65536} x T in {64, 128, 256}; us, against the streaming or one-item
+// pipelined kernel the call takes otherwise):
+//  * discounted returns: two in registers everywhere (16384 x 64: 5.9 -> 4.5;
+//    16384 x 256: 11.0 -> 9.4; 32768 x 256: 19.7 -> 16.2);
+//  * TD(lambda), GAE: two in registers (16384 x 64: 5.9 -> 4.8; 16384 x 128:
+//    8.1 -> 7.2; 65536 x 128: 22.4 -> 20.8), four at 16384 x 256 (12.0 ->
+//    11.7);
+//  * V-trace: four at 16384-32768 rows of 128 or 256 steps and 65536 x 64
+//    (16384 x 256: 18.8 -> 18.1; 16384 x 128: 11.4 -> 10.2; 65536 x 64:
+//    18.9 -> 17.8), two in registers at 32768 x 64, 65536 x 128 and 4096 x
+//    256, LDS from 32768 rows of 256 steps (33.5 -> 31.7);
+//  * Retrace: two in registers up to 16384 rows of 64 and up to 4096 rows
+//    (4096 x 128: 5.5 -> 4.4), four at 32768 rows of 64 and 16384-32768 rows
+//    of 128 (16384 x 128: 11.9 -> 10.8), LDS at 65536 x 128 and 16384-32768
+//    rows of 256 (16384 x 256: 20.2 -> 19.6);
+//  * traces and prefix sums: LDS for rows of 64 steps up to 16384 rows
+//    (16384 x 64: 4.3 -> 4.0) and at 65536 x 256 (an earlier sweep: 32.2 ->
+//    26.4), two in registers up to 4096 rows and at 16384 x 128 and 32768 x
+//    64 (5.7 -> 5.4), the streaming kernel elsewhere (16384 x 256: 8.6 against
+//    8.7 in registers).
+// Row counts between the measured ones take the form of the next smaller one.
 template <class Est>
-inline int duo_team(const KernelArgs& a) {
-  if (a.T != 64 && a.T != 128 && a.T != 256) return 0;
+inline int duo_form(const KernelArgs& a) {
+  if (a.T != 64 && a.T != 128 && a.T != 256) return kDuoNone;
   const int L = (int)(a.T / 4);
   const int64_t items = (a.E + (64 / L) - 1) / (64 / L);
-  if ((items + 7) / 8 * 256 > kMaxWorkItems) return 0;
-  if (!vector_ok(a, 4, (int)a.T)) return 0;
+  if ((items + 7) / 8 * 256 > kMaxWorkItems) return kDuoNone;
+  if (!vector_ok(a, 4, (int)a.T)) return kDuoNone;
   const int64_t E = a.E, T = a.T;
-  bool take = false;
-  if constexpr (__is_same(Est, DiscountedReturn)) take = true;
-  if constexpr (__is_same(Est, Retrace)) take = (T == 256 && E <= 32768) || E <= 4096;
-  if constexpr (__is_same(Est, Vtrace)) take = (T == 256 && E >= 4096) || (T == 128 && E >= 65536);
+  if constexpr (__is_same(Est, DiscountedReturn)) return kDuoReg;
   if constexpr (__is_same(Est, TdLambda) || __is_same(Est, Gae))
-    take = (T == 256 && E >= 32768) || (T == 128 && E >= 65536) || E <= 4096;
-  if constexpr (__is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum))
-    take = E <= 4096 || (T <= 128 && E <= 16384) || (T == 256 && E >= 65536);
-  return take ? L : 0;
-}
-
-// float32: the LDS form only for Retrace from 16384 rows of 256 steps
-template <class Est>
-inline bool duo_in_registers(const KernelArgs& a) {
-  return !(__is_same(Est, Retrace) && a.T == 256 && a.E > 4096);
+    return (T == 256 && E >= 16384 && E < 32768) ? kDuoReg4 : kDuoReg;
+  if constexpr (__is_same(Est, Vtrace)) {
+    if (T == 64) return E >= 65536 ? kDuoReg4 : E >= 32768 ? kDuoReg : kDuoNone;
+    if (T == 128) return E >= 65536 ? kDuoReg : E >= 16384 ? kDuoReg4 : kDuoNone;
+    return E >= 32768 ? kDuoLds : E >= 16384 ? kDuoReg4 : E >= 4096 ? kDuoReg : kDuoNone;
+  }
+  if constexpr (__is_same(Est, Retrace)) {
+    if (T == 64) return E >= 32768 ? kDuoReg4 : kDuoReg;
+    if (T == 128) return E >= 65536 ? kDuoLds : E >= 16384 ? kDuoReg4 : E <= 4096 ? kDuoReg : kDuoNone;
+    return E > 32768 ? kDuoNone : E > 4096 ? kDuoLds : kDuoReg;
+  }
+  if constexpr (__is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum)) {
+    if ((T == 256 && E >= 65536) || (T == 64 && E <= 16384)) return kDuoLds;
+    return (E <= 4096 || (T == 128 && E <= 16384) || (T == 64 && E <= 32768)) ? kDuoReg : kDuoNone;
+  }
+  return kDuoNone;
 }
 
 // 16-bit storage: items of 512 elements, eight steps per lane, so rows of
-// 128, 256 or 512 steps (team width T / 8); always the register form.
+// 128, 256 or 512 steps (team width T / 8); two items per wave in registers.
+// From bfloat16 A/B runs over E in {4096, 16384, 65536} x T in {128, 256,
+// 512} against the kernels the calls took before: taken everywhere but
+// V-trace at 4096 x 128 and traces / prefix sums at 4096 x 256 (16384 x 256:
+// discounted returns 10.6 -> 8.0 us, TD(lambda) 10.1 -> 8.7, V-trace 14.5 ->
+// 12.2, Retrace 14.8 -> 12.8, traces 8.1 -> 6.7); the LDS form was 0.2-1.9 us
+// slower at 16384 x 256, four items per wave slower at most shapes.
 template <class Est>
 inline int duo_team_16(const KernelArgs& a) {
   if (a.T != 128 && a.T != 256 && a.T != 512) return 0;
@@ -360,27 +375,32 @@ inline int duo_team_16(const KernelArgs& a) {
 }
 
 template <class Est, int L, int OPT, class S = F32S>
-inline hipError_t launch_duo_opt(const KernelArgs& a, hipStream_t s, bool reg) {
+inline hipError_t launch_duo_opt(const KernelArgs& a, hipStream_t s, int form) {
   const int64_t items = (a.E + (64 / L) - 1) / (64 / L);
   KernelArgs arg = a;
   void* params[] = {&arg};
   const void* k = reinterpret_cast<const void*>(&duo_reg_kernel<Est, L, OPT, S>);
+  int per_block = 8;  // items per block of 4 waves
   if constexpr (__is_same(S, F32S)) {
-    if (!reg) k = reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT>);
+    if (form == kDuoLds) k = reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT>);
+    if (form == kDuoReg4) {
+      k = reinterpret_cast<const void*>(&multi_reg_kernel<Est, L, OPT, S, 4>);
+      per_block = 16;
+    }
   }
-  return hipLaunchKernel(k, dim3((unsigned)((items + 7) / 8)), dim3(256), params, 0, s);
+  return hipLaunchKernel(k, dim3((unsigned)((items + per_block - 1) / per_block)), dim3(256), params, 0, s);
 }
 
 template <class Est, int L, class S = F32S>
-inline hipError_t launch_duo(const KernelArgs& a, hipStream_t s, bool reg) {
+inline hipError_t launch_duo(const KernelArgs& a, hipStream_t s, int form) {
   using Tr = Traits<Est>;
   const bool flags = a.has_term || a.has_trunc;
   if constexpr (Tr::kHasOut1) {
     const bool out1 = a.out1 != nullptr;
-    if (flags) return out1 ? launch_duo_opt<Est, L, 3, S>(a, s, reg) : launch_duo_opt<Est, L, 1, S>(a, s, reg);
-    return out1 ? launch_duo_opt<Est, L, 2, S>(a, s, reg) : launch_duo_opt<Est, L, 0, S>(a, s, reg);
+    if (flags) return out1 ? launch_duo_opt<Est, L, 3, S>(a, s, form) : launch_duo_opt<Est, L, 1, S>(a, s, form);
+    return out1 ? launch_duo_opt<Est, L, 2, S>(a, s, form) : launch_duo_opt<Est, L, 0, S>(a, s, form);
   } else {
-    return flags ? launch_duo_opt<Est, L, 1, S>(a, s, reg) : launch_duo_opt<Est, L, 0, S>(a, s, reg);
+    return flags ? launch_duo_opt<Est, L, 1, S>(a, s, form) : launch_duo_opt<Est, L, 0, S>(a, s, form);
   }
 }
 
@@ -435,12 +455,12 @@ hipError_t launch(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const SegPlan plan = segment_plan(a); plan.len) return launch_segmented<Est>(a, s, plan);
   if constexpr (!Traits<Est>::kDual && !Traits<Est>::kLinear) {
-    const bool reg = duo_in_registers<Est>(a);
-    switch (duo_team<Est>(a)) {
-      case 16: return launch_duo<Est, 16>(a, s, reg);
-      case 32: return launch_duo<Est, 32>(a, s, reg);
-      case 64: return launch_duo<Est, 64>(a, s, reg);
-      default: break;
+    if (const int form = duo_form<Est>(a); form != kDuoNone) {
+      switch (a.T) {
+        case 64: return launch_duo<Est, 16>(a, s, form);
+        case 128: return launch_duo<Est, 32>(a, s, form);
+        default: return launch_duo<Est, 64>(a, s, form);
+      }
     }
   }
   const bool one = prefer_oneshot<Est>(a, 4);
@@ -480,9 +500,9 @@ hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
   if (const SegPlan plan = segment_plan(a); plan.len) return launch_segmented<Est, S>(a, s, plan);
   if constexpr (!Traits<Est>::kDual && !Traits<Est>::kLinear) {
     switch (duo_team_16<Est>(a)) {
-      case 16: return launch_duo<Est, 16, S>(a, s, true);
-      case 32: return launch_duo<Est, 32, S>(a, s, true);
-      case 64: return launch_duo<Est, 64, S>(a, s, true);
+      case 16: return launch_duo<Est, 16, S>(a, s, kDuoReg);
+      case 32: return launch_duo<Est, 32, S>(a, s, kDuoReg);
+      case 64: return launch_duo<Est, 64, S>(a, s, kDuoReg);
       default: break;
     }
   }

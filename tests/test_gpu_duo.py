@@ -1,16 +1,19 @@
-"""The two-items-per-wave kernels (rows of 64, 128 or 256 float32 steps; each
-wave scans two 256-element items, the second staged through LDS or, in the
-register form, held in registers too) against the oracle, at shapes the
-launcher routes to them for every estimator that takes them (discounted
-returns at every E; Retrace with rows of 256 steps up to 32768 rows, in the
-LDS form from 4097 rows, and any row up to 4096 rows; V-trace from 4096 rows
-of 256 steps and from 65536 rows of 128; TD(lambda) and GAE up to 4096 rows,
-from 32768 rows of 256 steps and 65536 rows of 128; traces and prefix sums up
-to 4096 rows, up to 16384 rows of 64 or 128 steps and from 65536 rows of 256).
-Row counts that leave the last block with waves that have no second item, or
-the last item with fewer than 64 / L rows, are included, as are absent
-optional inputs.  The 16-bit formats' register form is covered in
-test_gpu_storage16.py."""
+"""The kernels whose items are 1 KiB of every array (rows of 64, 128 or 256
+float32 steps; two items per wave with the second staged through LDS or held
+in registers, or four items per wave in registers) against the oracle, at
+shapes the launcher routes to each form: discounted returns at every E;
+TD(lambda) and GAE everywhere (four per wave at 16384-32767 rows of 256
+steps); V-trace four per wave at 16384-32767 rows of 128 or 256 steps and
+from 65536 rows of 64, two in registers at 32768 x 64, from 65536 rows of
+128 and from 4096 rows of 256, LDS from 32768 rows of 256; Retrace in
+registers up to 32767 rows of 64 and up to 4096 rows, four per wave from
+32768 rows of 64 and at 16384-65535 rows of 128, LDS at 4097-32768 rows of
+256 and from 65536 rows of 128; traces and prefix sums LDS for rows of 64 up
+to 16384 rows and from 65536 rows of 256, registers up to 4096 rows, at
+16384 x 128 and 32768 x 64.  Row counts that leave the last block with waves
+that have fewer items, or the last item with fewer than 64 / L rows, are
+included, as are absent optional inputs.  The 16-bit formats' register form
+is covered in test_gpu_storage16.py."""
 from __future__ import annotations
 
 import sys
@@ -25,12 +28,14 @@ pytestmark = pytest.mark.gpu
 CASES = (
     [("discounted_returns", E, T) for (E, T) in [(1, 64), (3, 64), (13, 64), (5, 128), (9, 256), (1000, 128),
                                                  (1001, 256), (4099, 64), (16385, 256)]]
-    + [("retrace", E, T) for (E, T) in [(3, 64), (1001, 128), (4096, 128), (9, 256), (16385, 256)]]
-    + [("vtrace", E, T) for (E, T) in [(4096, 256), (4099, 256), (20001, 256), (65537, 128)]]
-    + [(n, E, T) for n in ("td_lambda", "gae") for (E, T) in [(7, 64), (1001, 128), (4096, 256), (32768, 256),
-                                                                 (32771, 256), (65536, 128)]]
+    + [("retrace", E, T) for (E, T) in [(3, 64), (1001, 128), (4096, 128), (9, 256), (16385, 256), (16387, 128),
+                                        (32769, 64), (65536, 128)]]
+    + [("vtrace", E, T) for (E, T) in [(4096, 256), (4099, 256), (20001, 256), (65537, 128), (16385, 128),
+                                       (32768, 64), (65537, 64), (32769, 256)]]
+    + [(n, E, T) for n in ("td_lambda", "gae") for (E, T) in [(7, 64), (1001, 128), (4096, 256), (16385, 256),
+                                                                 (32768, 256), (32771, 256), (65536, 128)]]
     + [(n, E, T) for n in ("eligibility_traces", "episodic_prefix_sum")
-       for (E, T) in [(5, 64), (1001, 128), (4096, 256), (16383, 64), (65537, 256)]]
+       for (E, T) in [(5, 64), (1001, 128), (4096, 256), (16383, 64), (16384, 128), (32768, 64), (65537, 256)]]
 )
 
 
