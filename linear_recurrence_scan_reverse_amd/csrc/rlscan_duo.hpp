@@ -216,12 +216,46 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
 // branch surrounds a request.
 constexpr uint32_t kDuoOff = 0x80000000u;  // past every item resource
 
-template <class S>
+template <class S, int IB = kDuoItemBytes>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t duo_item_rs(const void* base, int64_t item, int64_t total_bytes) {
-  const int64_t b0 = item * kDuoItemBytes;
-  const int64_t n = total_bytes - b0 < kDuoItemBytes ? total_bytes - b0 : kDuoItemBytes;
+  const int64_t b0 = item * IB;
+  const int64_t n = total_bytes - b0 < IB ? total_bytes - b0 : IB;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + b0, 0, (int)n,
                                            0x00020000);
+}
+
+// A lane's raw bytes of one array in one item: 16 (u32x4) or 8 (u32x2).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int LB> struct RawOf;
+template <> struct RawOf<16> { typedef u32x4 T; };
+template <> struct RawOf<8> { typedef u32x2 T; };
+
+template <int LB>
+__device__ __forceinline__ typename RawOf<LB>::T raw_buffer_load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (LB == 16) return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2);
+  else return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 2);
+}
+template <int LB>
+__device__ __forceinline__ void raw_buffer_store(typename RawOf<LB>::T v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (LB == 16) __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 2);
+  else __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 2);
+}
+// K values of format S from 8 raw bytes (16-bit formats, K = 4).
+template <class S, int K>
+__device__ __forceinline__ void unpack8(const u32x2 v, float (&o)[K]) {
+  static_assert(!__is_same(S, F32S) && K == 4, "four 16-bit values");
+  o[0] = s_to_f32<S>((uint16_t)v.x);
+  o[1] = s_to_f32<S>((uint16_t)(v.x >> 16));
+  o[2] = s_to_f32<S>((uint16_t)v.y);
+  o[3] = s_to_f32<S>((uint16_t)(v.y >> 16));
+}
+template <class S, int K>
+__device__ __forceinline__ u32x2 pack8(const float (&o)[K]) {
+  static_assert(!__is_same(S, F32S) && K == 4, "four 16-bit values");
+  u32x2 q;
+  q.x = (uint32_t)f32_to_s<S>(o[0]) | ((uint32_t)f32_to_s<S>(o[1]) << 16);
+  q.y = (uint32_t)f32_to_s<S>(o[2]) | ((uint32_t)f32_to_s<S>(o[3]) << 16);
+  return q;
 }
 
 // K values of format S from 16 raw bytes.
@@ -256,12 +290,14 @@ __device__ __forceinline__ u32x4 pack16(const float (&o)[K]) {
   }
 }
 
-template <class Est, int L, int OPT, class S = F32S>
+template <class Est, int L, int OPT, class S = F32S, int LB = 16>
 __global__ void __launch_bounds__(256) duo_reg_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
+  using RawT = typename RawOf<LB>::T;
   constexpr int ES = (int)sizeof(typename S::T);
-  constexpr int K = 16 / ES;
-  constexpr int ITEM = kDuoItemBytes / ES;
+  constexpr int K = LB / ES;     // steps per lane
+  constexpr int IB = 64 * LB;    // bytes of every array in one item
+  constexpr int ITEM = IB / ES;  // elements per item
   constexpr bool REV = Est::kReverse;
   constexpr int NS = Tr::kStreams;
   constexpr bool USE_FLAGS = (OPT & 1) && Tr::kUsesFlags;
@@ -298,9 +334,17 @@ __global__ void __launch_bounds__(256) duo_reg_kernel(const KernelArgs p) {
   const int64_t row_a = item_a * G + team, row_b = item_bc * G + team;
   const bool ok_a = row_a < E, ok_b = has_b && row_b < E;
   const int64_t ra = ok_a ? row_a : E - 1, rb = row_b < E ? row_b : E - 1;
-  auto raw_at = [&](const float* base, int64_t row) -> u32x4 {
+  auto raw_at = [&](const float* base, int64_t row) -> RawT {
     return __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + (row * T + cs) * ES));
+        reinterpret_cast<const RawT*>(reinterpret_cast<const char*>(base) + (row * T + cs) * ES));
+  };
+  auto unpack = [&](const RawT v, float (&o)[K]) {
+    if constexpr (LB == 16) unpack16<S, K>(v, o);
+    else unpack8<S, K>(v, o);
+  };
+  auto pack = [&](const float (&o)[K]) -> RawT {
+    if constexpr (LB == 16) return pack16<S, K>(o);
+    else return pack8<S, K>(o);
   };
 
   // A's flags and streams, B's flags
@@ -310,7 +354,7 @@ __global__ void __launch_bounds__(256) duo_reg_kernel(const KernelArgs p) {
     load_flag_raw<K, true>(p.trunc + ra * T, cs, 0u, fra);
   }
   const float rowa = load1<S>(p.row, ra, 0u);
-  u32x4 xa[NS], xb[NS];
+  RawT xa[NS], xb[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) xa[st] = raw_at(srcs[st], ra);
   if constexpr (USE_FLAGS) {
@@ -320,16 +364,19 @@ __global__ void __launch_bounds__(256) duo_reg_kernel(const KernelArgs p) {
   const float rowb = load1<S>(p.row, rb, 0u);
   asm volatile("" ::: "memory");
 
-  // A's bootstraps (waits for A's flags only)
+  // A's bootstraps (waits for A's flags only; the empty asm takes A's flag
+  // words here, so their decode cannot move above B's requests)
   unsigned tba = 0, rba = 0, tbb = 0, rbb = 0;
   if constexpr (USE_FLAGS) {
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) asm volatile("" : "+v"(fta[i]), "+v"(fra[i])::"memory");
     tba = flag_bits<K, true>(fta) & tmask;
     rba = flag_bits<K, true>(fra) & rmask;
   }
-  u32x4 ga = u32x4{0u, 0u, 0u, 0u}, gb = u32x4{0u, 0u, 0u, 0u};
+  RawT ga = RawT(0u), gb = RawT(0u);
   if constexpr (GATHER_TB) {
     const bool need = ok_a && (rba & ~tba) != 0u && p.has_tboot;
-    ga = __builtin_amdgcn_raw_buffer_load_b128(duo_item_rs<S>(p.tboot, item_a, total), need ? boff : kDuoOff, 0, 2);
+    ga = raw_buffer_load<LB>(duo_item_rs<S, IB>(p.tboot, item_a, total), need ? boff : kDuoOff);
   }
   // B's streams, then B's bootstraps (waits for B's flags only).  The empty
   // asm takes B's flag words after B's streams are requested, so the compiler
@@ -346,25 +393,24 @@ __global__ void __launch_bounds__(256) duo_reg_kernel(const KernelArgs p) {
   }
   if constexpr (GATHER_TB) {
     const bool need = ok_b && (rbb & ~tbb) != 0u && p.has_tboot;
-    gb = __builtin_amdgcn_raw_buffer_load_b128(duo_item_rs<S>(p.tboot, item_bc, total), need ? boff : kDuoOff, 0, 2);
+    gb = raw_buffer_load<LB>(duo_item_rs<S, IB>(p.tboot, item_bc, total), need ? boff : kDuoOff);
   }
 
   // one item: unpack, scan, store (rows past E fall outside the output resource)
-  auto item = [&](int64_t it, const u32x4 (&x)[NS], const u32x4 gt, float rowv, unsigned tbits, unsigned rbits,
+  auto item = [&](int64_t it, const RawT (&x)[NS], const RawT gt, float rowv, unsigned tbits, unsigned rbits,
                   bool ok) {
     LaneIn<Est, K> d;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) unpack16<S, K>(x[st], d.s[st]);
-    unpack16<S, K>(gt, d.tb);
+    for (int st = 0; st < NS; ++st) unpack(x[st], d.s[st]);
+    unpack(gt, d.tb);
     d.rowv = rowv;
     double C = 0.0;
     if constexpr (!Tr::kBackwardRl) C = (ok && p.has_row) ? (double)rowv : 0.0;
     PredIn carry{0.0f, 0.0, 0u};
     float o0[K], o1[K];
     stream_tile<Est, L, K, false, FAST>(d, sc, tbits, rbits, cs, T, team_first_lane, lane, C, carry, o0, o1);
-    __builtin_amdgcn_raw_buffer_store_b128(pack16<S, K>(o0), duo_item_rs<S>(p.out0, it, total), boff, 0, 2);
-    if constexpr (OUT1)
-      __builtin_amdgcn_raw_buffer_store_b128(pack16<S, K>(o1), duo_item_rs<S>(p.out1, it, total), boff, 0, 2);
+    raw_buffer_store<LB>(pack(o0), duo_item_rs<S, IB>(p.out0, it, total), boff);
+    if constexpr (OUT1) raw_buffer_store<LB>(pack(o1), duo_item_rs<S, IB>(p.out1, it, total), boff);
   };
   item(item_a, xa, ga, rowa, tba, rba, ok_a);
   if (!has_b) return;

@@ -351,27 +351,41 @@ inline int duo_form(const KernelArgs& a) {
   return kDuoNone;
 }
 
-// 16-bit storage: items of 512 elements, eight steps per lane, so rows of
-// 128, 256 or 512 steps (team width T / 8); two items per wave in registers.
-// From bfloat16 A/B runs over E in {4096, 16384, 65536} x T in {128, 256,
-// 512} against the kernels the calls took before: taken everywhere but
-// V-trace at 4096 x 128 and traces / prefix sums at 4096 x 256 (16384 x 256:
-// discounted returns 10.6 -> 8.0 us, TD(lambda) 10.1 -> 8.7, V-trace 14.5 ->
-// 12.2, Retrace 14.8 -> 12.8, traces 8.1 -> 6.7); the LDS form was 0.2-1.9 us
-// slower at 16384 x 256, four items per wave slower at most shapes.
+// 16-bit storage: two items per wave in registers, a lane holding 16 bytes of
+// each array (8 steps; rows of 128, 256 or 512 steps, team width T / 8) or 8
+// bytes (4 steps; rows of 64, 128 or 256, team width T / 4).  From bfloat16
+// A/B runs over E in {4096, 16384, 32768, 65536} x T in {64 .. 512} against
+// the kernels the calls took before (us):
+//  * 16 bytes per lane: everywhere but V-trace at 4096 x 128 and traces /
+//    prefix sums at 4096 x 256 (16384 x 256: discounted returns 10.6 -> 8.0,
+//    TD(lambda) 10.1 -> 8.7, V-trace 14.5 -> 12.2, Retrace 14.8 -> 12.8,
+//    traces 8.1 -> 6.7); the LDS form was 0.2-1.9 us slower at 16384 x 256,
+//    four items per wave slower at most shapes;
+//  * 8 bytes per lane, where it beat that: rows of 64 steps from 16384 rows
+//    (TD(lambda) 32768 x 64: 6.7 -> 5.8; Retrace 65536 x 64: 14.8 -> 12.7),
+//    rows of 128 up to 4096 rows (Retrace 5.0 -> 4.3; discounted returns
+//    6.2 -> 4.4), and discounted returns, traces and prefix sums with rows
+//    of 256 up to 4096 rows (4.7 -> 4.2); slower with 256 steps from 16384
+//    rows (TD(lambda) 8.8 -> 9.6).
+struct Duo16 {
+  int L;   // team width (0: not taken)
+  int lb;  // bytes per lane and array
+};
 template <class Est>
-inline int duo_team_16(const KernelArgs& a) {
-  if (a.T != 128 && a.T != 256 && a.T != 512) return 0;
-  const int L = (int)(a.T / 8);
-  const int64_t items = (a.E + (64 / L) - 1) / (64 / L);
-  if ((items + 7) / 8 * 256 > kMaxWorkItems) return 0;
-  if (!vector_ok(a, 8, (int)a.T, 2)) return 0;
+inline Duo16 duo_form_16(const KernelArgs& a) {
   const int64_t E = a.E, T = a.T;
-  bool take = true;
-  if constexpr (__is_same(Est, Vtrace)) take = !(E <= 4096 && T == 128);
-  if constexpr (__is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum))
-    take = !(E <= 4096 && T == 256);
-  return take ? L : 0;
+  constexpr bool light = __is_same(Est, DiscountedReturn) || __is_same(Est, EligibilityTrace) ||
+                         __is_same(Est, EpisodicPrefixSum);
+  int lb = 16;
+  if ((T == 64 && E >= 16384) || (T == 128 && E <= 4096) || (T == 256 && E <= 4096 && light)) lb = 8;
+  else if (T != 128 && T != 256 && T != 512) return Duo16{0, 0};
+  const int L = (int)(T * 2 / lb);
+  const int64_t items = (E + (64 / L) - 1) / (64 / L);
+  if ((items + 7) / 8 * 256 > kMaxWorkItems) return Duo16{0, 0};
+  if (!vector_ok(a, lb / 2, (int)T, 2)) return Duo16{0, 0};
+  if (lb == 16 && (__is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum)) && E <= 4096 && T == 256)
+    return Duo16{0, 0};
+  return Duo16{L, lb};
 }
 
 template <class Est, int L, int OPT, class S = F32S>
@@ -380,6 +394,9 @@ inline hipError_t launch_duo_opt(const KernelArgs& a, hipStream_t s, int form) {
   KernelArgs arg = a;
   void* params[] = {&arg};
   const void* k = reinterpret_cast<const void*>(&duo_reg_kernel<Est, L, OPT, S>);
+  if constexpr (!__is_same(S, F32S)) {
+    if (a.T == 4 * L) k = reinterpret_cast<const void*>(&duo_reg_kernel<Est, L, OPT, S, 8>);  // 8 bytes per lane
+  }
   int per_block = 8;  // items per block of 4 waves
   if constexpr (__is_same(S, F32S)) {
     if (form == kDuoLds) k = reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT>);
@@ -487,7 +504,7 @@ hipError_t launch(const KernelArgs& in, hipStream_t s) {
 
 // Values stored as 16-bit bf16 / fp16 (S = Bf16S, F16S): the segmented path
 // for long rows; the two-item register kernel for rows of 128-512 steps
-// (duo_team_16); the streaming kernel for traces and prefix sums where the
+// (duo_form_16); the streaming kernel for traces and prefix sums where the
 // rows allow it and the float32 routing rule prefers it; else the pipelined
 // kernel.  At 16384 x 256 (bfloat16) the streaming kernel ran traces and
 // prefix sums in 8.7-9.3 us against 9.6-9.9 pipelined, but the five backward
@@ -499,7 +516,7 @@ hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const SegPlan plan = segment_plan(a); plan.len) return launch_segmented<Est, S>(a, s, plan);
   if constexpr (!Traits<Est>::kDual && !Traits<Est>::kLinear) {
-    switch (duo_team_16<Est>(a)) {
+    switch (duo_form_16<Est>(a).L) {
       case 16: return launch_duo<Est, 16, S>(a, s, kDuoReg);
       case 32: return launch_duo<Est, 32, S>(a, s, kDuoReg);
       case 64: return launch_duo<Est, 64, S>(a, s, kDuoReg);
