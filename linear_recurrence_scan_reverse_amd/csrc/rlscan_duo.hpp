@@ -66,7 +66,7 @@ __device__ __forceinline__ void lds_read_chunk(const char* q, float (&o)[K]) {
 // 16384 x 256 on one MI355X: 20.0 -> 19.75 us (the one-item form measured
 // slower with it and keeps the division).  The 16-bit formats also take the
 // fast exp of V-trace, as every kernel does for them.
-template <class Est, int L, int OPT, class S = F32S>
+template <class Est, int L, int OPT, class S = F32S, int NLMAX = 3>
 __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
   constexpr int ES = (int)sizeof(typename S::T);  // bytes per stored value
@@ -83,9 +83,10 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   static_assert(!Tr::kDual, "one recurrence per pass");
   static_assert(G * SPAN == ITEM, "an item is whole rows");
 
-  // B's first NL streams go through LDS (at most three: 12 KiB per block, so
-  // eight blocks fit a CU's LDS with room to spare); the rest -> registers
-  constexpr int NL = NS < 3 ? NS : 3;
+  // B's first NL streams go through LDS (at most NLMAX, 1 KiB each per wave:
+  // three take 12 KiB per block, so eight blocks fit a CU's LDS with room to
+  // spare); the rest -> registers
+  constexpr int NL = NS < NLMAX ? NS : NLMAX;
   __shared__ __attribute__((aligned(16))) char s_b[4][NL][kDuoItemBytes];  // each wave's second item, memory order
 
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));

@@ -298,7 +298,7 @@ inline bool prefer_stream(const KernelArgs& a, int L) {
 // items per wave, both in registers, each scanned as soon as its own loads
 // land) or multi_reg_kernel with four items per wave (a software pipeline
 // keeping two items ahead in flight).
-enum DuoForm { kDuoNone = 0, kDuoLds = 1, kDuoReg = 2, kDuoReg4 = 4 };
+enum DuoForm { kDuoNone = 0, kDuoLds = 1, kDuoReg = 2, kDuoReg4 = 4, kDuoLds4 = 5 };
 
 // Float32 routing, from A/B runs on one MI355X with flags present (each form
 // forced for every estimator, two interleaved rounds over E in {4096, 16384,
@@ -316,7 +316,9 @@ enum DuoForm { kDuoNone = 0, kDuoLds = 1, kDuoReg = 2, kDuoReg4 = 4 };
 //  * Retrace: two in registers up to 16384 rows of 64 and up to 4096 rows
 //    (4096 x 128: 5.5 -> 4.4), four at 32768 rows of 64 and 16384-32768 rows
 //    of 128 (16384 x 128: 11.9 -> 10.8), LDS at 65536 x 128 and 16384-32768
-//    rows of 256 (16384 x 256: 20.2 -> 19.6);
+//    rows of 256 (16384 x 256: 20.2 -> 19.6), there with four of item B's
+//    five streams in LDS up to 16384 rows (three interleaved rounds: 19.72 ->
+//    19.50; at 32768 x 256 four were 34.9-37.3 against 35.2 and stay three);
 //  * traces and prefix sums: LDS for rows of 64 steps up to 16384 rows
 //    (16384 x 64: 4.3 -> 4.0) and at 65536 x 256 (an earlier sweep: 32.2 ->
 //    26.4), two in registers up to 4096 rows and at 16384 x 128 and 32768 x
@@ -342,7 +344,7 @@ inline int duo_form(const KernelArgs& a) {
   if constexpr (__is_same(Est, Retrace)) {
     if (T == 64) return E >= 32768 ? kDuoReg4 : kDuoReg;
     if (T == 128) return E >= 65536 ? kDuoLds : E >= 16384 ? kDuoReg4 : E <= 4096 ? kDuoReg : kDuoNone;
-    return E > 32768 ? kDuoNone : E > 4096 ? kDuoLds : kDuoReg;
+    return E > 32768 ? kDuoNone : E > 16384 ? kDuoLds : E > 4096 ? kDuoLds4 : kDuoReg;
   }
   if constexpr (__is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum)) {
     if ((T == 256 && E >= 65536) || (T == 64 && E <= 16384)) return kDuoLds;
@@ -400,6 +402,7 @@ inline hipError_t launch_duo_opt(const KernelArgs& a, hipStream_t s, int form) {
   int per_block = 8;  // items per block of 4 waves
   if constexpr (__is_same(S, F32S)) {
     if (form == kDuoLds) k = reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT>);
+    if (form == kDuoLds4) k = reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT, S, 4>);
     if (form == kDuoReg4) {
       k = reinterpret_cast<const void*>(&multi_reg_kernel<Est, L, OPT, S, 4>);
       per_block = 16;

@@ -8,7 +8,8 @@ from 65536 rows of 64, two in registers at 32768 x 64, from 65536 rows of
 128 and from 4096 rows of 256, LDS from 32768 rows of 256; Retrace in
 registers up to 32767 rows of 64 and up to 4096 rows, four per wave from
 32768 rows of 64 and at 16384-65535 rows of 128, LDS at 4097-32768 rows of
-256 and from 65536 rows of 128; traces and prefix sums LDS for rows of 64 up
+256 (four of item B's five streams in LDS up to 16384 rows, three above) and
+from 65536 rows of 128; traces and prefix sums LDS for rows of 64 up
 to 16384 rows and from 65536 rows of 256, registers up to 4096 rows, at
 16384 x 128 and 32768 x 64.  Row counts that leave the last block with waves
 that have fewer items, or the last item with fewer than 64 / L rows, are
@@ -28,8 +29,8 @@ pytestmark = pytest.mark.gpu
 CASES = (
     [("discounted_returns", E, T) for (E, T) in [(1, 64), (3, 64), (13, 64), (5, 128), (9, 256), (1000, 128),
                                                  (1001, 256), (4099, 64), (16385, 256)]]
-    + [("retrace", E, T) for (E, T) in [(3, 64), (1001, 128), (4096, 128), (9, 256), (16385, 256), (16387, 128),
-                                        (32769, 64), (65536, 128)]]
+    + [("retrace", E, T) for (E, T) in [(3, 64), (1001, 128), (4096, 128), (9, 256), (9001, 256), (16384, 256),
+                                        (16385, 256), (16387, 128), (32769, 64), (65536, 128)]]
     + [("vtrace", E, T) for (E, T) in [(4096, 256), (4099, 256), (20001, 256), (65537, 128), (16385, 128),
                                        (32768, 64), (65537, 64), (32769, 256)]]
     + [(n, E, T) for n in ("td_lambda", "gae") for (E, T) in [(7, 64), (1001, 128), (4096, 256), (16385, 256),
