@@ -1,33 +1,21 @@
-// rlscan_duo.hpp -- rows of 64 to 512 steps, whose items (1 KiB of every
-// array: 256 float32 or 512 16-bit elements) hold G = 64 / L whole rows: each
-// wave scans two items, the first loaded into registers and the second into
-// LDS by DMA, both requested before either is scanned.
+// rlscan_duo.hpp -- the item kernels: rows of 64 to 512 steps, cut into items
+// of 1 KiB of every array (256 float32 or 512 16-bit elements; a variant of
+// 512 bytes for 16-bit rows of 64-256 steps), each item G = 64 / L whole rows
+// of L lanes.  A wave scans several items:
+//  * duo_kernel (float32): two items, the second with up to NLMAX of its input
+//    streams staged in the wave's own LDS slot by DMA;
+//  * duo_reg_kernel: two items, both held in registers as raw bytes;
+//  * multi_reg_kernel: four items in registers as a software pipeline.
 //
 // A kernel that gives each wave one item (the pipelined kernel's one-item
-// form) holds its inputs in registers; at full occupancy a CU then has 32
-// items in flight, and the rows the first round of waves does not cover wait
-// for slots to free before their loads start.  A plain streaming kernel moving
-// the same arrays ran fastest with two items per wave (every item requested at
-// once).  Here the second item costs few registers: up to three of its input
-// streams land in the wave's own LDS slot (1 KiB per stream and wave; 12 KiB
-// per block at most, so eight blocks fit a CU) and the rest in registers, so
-// occupancy stays that of the one-item kernel while twice the bytes are
-// requested.  The per-lane scan code is the one every kernel of the library
-// shares (stream_tile: pairs, fold, lane scan, re-walk, epilogue); a lane
-// holds K = 4 float32 or K = 8 16-bit steps (16 bytes of each array).
-//
-// Order inside a wave (the flag-dependent bootstrap gather of each item is
-// issued as soon as its flags are known):
-//   1. item A: flags, input streams, row value -> registers;
-//   2. item B: input streams -> LDS (DMA), flags and row value -> registers;
-//   3. A's flags decoded, A's truncation bootstraps gathered;
-//   4. wait for everything; B's flags decoded, B's bootstraps gathered;
-//   5. A scanned and stored (B's gather in flight);
-//   6. B read from LDS, scanned and stored.
-// A wave that mixes LDS DMA with ordinary loads gets no finer waits from the
-// compiler than "everything" (its counter tracking takes the two kinds as
-// unordered), so A is scanned once B has landed too: every item of the wave
-// is requested at once, as in the plain streaming kernel the design follows.
+// form) requests every item of a CU at once, so the waves reach their compute
+// together at the end of the load phase and the compute is exposed.  With
+// several items per wave a wave can scan one item while the next ones land.
+// gfx9 counts a wave's loads with one in-order counter, so the order in which
+// items and their flag-dependent bootstrap gathers are requested decides what
+// each wait covers; each kernel states its order below.  The per-lane scan
+// code is the one every kernel of the library shares (stream_tile: pairs,
+// fold, lane scan, re-walk, epilogue).
 #pragma once
 
 #include "rlscan_stream.hpp"
@@ -36,36 +24,39 @@ namespace rlscan {
 
 constexpr int kDuoItemBytes = 1024;  // bytes of every array in one item
 
-// K stored values at an LDS byte address (16-byte aligned), widened.
-template <class S, int K>
-__device__ __forceinline__ void lds_read_chunk(const char* q, float (&o)[K]) {
-  if constexpr (__is_same(S, F32S)) {
-    static_assert(K == 4, "four float32 values");
-    const f32x4 v = *reinterpret_cast<const f32x4*>(q);
-    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-  } else {
-    static_assert(K == 8, "eight 16-bit values");
-    const u32x4 v = *reinterpret_cast<const u32x4*>(q);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = s_to_f32<S>((uint16_t)w[i]);
-      o[2 * i + 1] = s_to_f32<S>((uint16_t)(w[i] >> 16));
-    }
-  }
+// Four float32 values at an LDS byte address (16-byte aligned).
+__device__ __forceinline__ void lds_read4f(const char* q, float (&o)[4]) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(q);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
 }
 
+// ----------------------------------------------------------------- two items, the second through LDS
+// Order inside a wave (the bootstrap gather of each item is issued as soon
+// as its flags are known):
+//   1. item A: flags, input streams, row value -> registers;
+//   2. item B: NL input streams -> LDS (DMA), the rest, flags, row value -> registers;
+//   3. A's flags decoded, A's truncation bootstraps gathered;
+//   4. wait for everything; B's flags decoded, B's bootstraps gathered;
+//   5. A scanned and stored (B's gather in flight);
+//   6. B read from LDS, scanned and stored.
+// A wave that mixes LDS DMA with ordinary loads gets no finer waits from the
+// compiler than "everything" (its counter tracking takes the two kinds as
+// unordered), so A is scanned once B has landed too.  The LDS slot costs no
+// registers, so occupancy stays that of a one-item kernel.
+//
 // Template parameters: estimator tag (not the two-output pass), team width L
-// (T == K L), OPT (bit 0 flags, bit 1 second output), storage format S.
-// Every dense array 16-byte aligned, flag arrays K-byte aligned (checked by
-// the launcher).  Blocks of 4 waves take items 8 b + w and 8 b + 4 + w.
+// (T == 4 L), OPT (bit 0 flags, bit 1 second output), storage format S
+// (float32 only), NLMAX.  Every dense array 16-byte aligned, flag arrays
+// 4-byte aligned (checked by the launcher).  Blocks of 4 waves take items
+// 8 b + w and 8 b + 4 + w.
 // Retrace forms its trace quotient pi / mu from the fp32 reciprocal of mu
 // refined by one fp64 Newton step (retrace_c_fast, relative error about
 // 1e-14) instead of an fp64 division: this kernel computes two items per wave
 // after both have landed, so its vector instructions count.  Measured at
 // 16384 x 256 on one MI355X: 20.0 -> 19.75 us (the one-item form measured
-// slower with it and keeps the division).  The 16-bit formats also take the
-// fast exp of V-trace, as every kernel does for them.
+// slower with it and keeps the division).  The register forms do the same,
+// and in 16-bit storage they also take the fast exp of V-trace, as every
+// kernel does for those formats.
 template <class Est, int L, int OPT, class S = F32S, int NLMAX = 3>
 __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
@@ -77,9 +68,10 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   constexpr bool USE_FLAGS = (OPT & 1) && Tr::kUsesFlags;
   constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
   constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
-  constexpr bool FAST = Tr::kRetrace || !__is_same(S, F32S);
+  constexpr bool FAST = Tr::kRetrace;
   constexpr int G = 64 / L;   // rows per item
   constexpr int SPAN = L * K;  // row length
+  static_assert(__is_same(S, F32S), "float32 storage (16-bit rows take the register forms)");
   static_assert(!Tr::kDual, "one recurrence per pass");
   static_assert(G * SPAN == ITEM, "an item is whole rows");
 
@@ -185,7 +177,7 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
   // ---- 6. item B
   if (!has_b) return;
 #pragma unroll
-  for (int st = 0; st < NL; ++st) lds_read_chunk<S, K>(&s_b[w][st][lds_off], db.s[st]);
+  for (int st = 0; st < NL; ++st) lds_read4f(&s_b[w][st][lds_off], db.s[st]);
   {
     double C = 0.0;
     if constexpr (!Tr::kBackwardRl) C = (ok_b && p.has_row) ? (double)db.rowv : 0.0;
@@ -201,7 +193,7 @@ __global__ void __launch_bounds__(256) duo_kernel(const KernelArgs p) {
 
 // ----------------------------------------------------------------- both items in registers
 // The same two items per wave with item B held in registers too, as the raw
-// 16 bytes per stream and lane (converted only when B is scanned), so no LDS
+// bytes of each stream and lane (converted only when B is scanned), so no LDS
 // DMA mixes with the ordinary loads and the compiler's waits stay exact: A is
 // scanned as soon as its own loads have landed, while B's are still in
 // flight.  In the LDS form every wave waits for both items, so the waves of a
