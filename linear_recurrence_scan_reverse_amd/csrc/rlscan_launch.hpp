@@ -14,6 +14,7 @@
 #include "rlscan_segment.hpp"
 #include "rlscan_stream.hpp"
 #include "rlscan_timemajor.hpp"
+#include "rlscan_tmitem.hpp"
 
 namespace rlscan {
 
@@ -571,6 +572,27 @@ constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 // steps and a multiple of 256 (whole super-tiles; the parked float64 pair
 // needs at most 8 rows); the last segment takes the remainder.  At most
 // kTmMaxSeg segments per column (the carry kernel's 16 waves x kTmCarrySeg).
+// The item form of the time-major path (tm_item_kernel): float32, one
+// recurrence of at most three streams, whole 64 x 64 chunks and 16-byte
+// aligned per-step arrays.  Columns of exactly one super-tile of tm_kernel
+// stay there: it has every load of such a column in flight at once and was
+// the faster one in the sweep (16384 x 256, float32: discounted returns 12.2
+// against 12.4 us, TD(lambda) 14.5 against 15.2; V-trace at 128 steps 12.5
+// against 13.0); at every other step count from 64 to 512 the item form was
+// (16384 x 320: TD(lambda) 23.6 -> 18.2 us, V-trace 34.2 -> 27.1; 16384 x 64:
+// 11.0 -> 6.8).
+template <class Est, class S>
+constexpr bool tm_item_ok() {
+  return __is_same(S, F32S) && !Traits<Est>::kDual && Traits<Est>::kStreams <= 3;
+}
+template <class Est>
+inline bool tm_item_fits(const KernelArgs& a) {
+  auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  return a.T != (int64_t)tm_waves<Est>() * tm_chunk<Est>() && a.E % kTiChunk == 0 && a.T % kTiChunk == 0 &&
+         a.E < ((int64_t)1 << 23) && al(a.r) && al(a.v) && al(a.aux) && al(a.term) && al(a.trunc) && al(a.out0) &&
+         al(a.out1);
+}
+
 template <class Est, int OPT, class S>
 inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
   constexpr int W = tm_waves<Est>(), K = tm_chunk<Est>();
@@ -582,6 +604,13 @@ inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
   // grids of at most 2^32 - 1 work-items (the C ABI refuses larger shapes first)
   if (groups * nseg * 64 * W > kMaxWorkItems || nseg > kTmMaxSeg) return hipErrorInvalidConfiguration;
   KernelArgs arg = a;
+  if constexpr (tm_item_ok<Est, S>()) {
+    if (nseg == 1 && tm_item_fits<Est>(a)) {
+      void* p1[] = {&arg};
+      return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT>), dim3((unsigned)groups),
+                             dim3(kTiThreads), p1, 0, s);
+    }
+  }
   void* params[] = {&arg, &seg_len, &nseg};
   const dim3 block(64 * W);
   if (nseg == 1)

@@ -195,9 +195,11 @@ struct alignas(16) FlagTick {
 // One lane's part of one tile of one row: pairs, wave scan, re-walk and
 // outputs.  C is the row's running value (in: beyond this tile; out: beyond
 // the next one), `carry` the boundary inputs handed between tiles of the row.
-// CARRY: hand the boundary inputs to the next tile of the row (rows of one
-// tile need none); FASTDIV as for build_pairs.
-template <class E2, int L, int K, bool CARRY = true, bool FASTDIV = false>
+// FASTDIV as for build_pairs.  CARRY: the next tile of the same rows follows (rows longer than one tile):
+// the boundary inputs it needs are taken from the scan-last lane of each team
+// (lane 63 with one team per wave; with several teams per wave only when
+// CARRY_TEAMS is set, where rows of L < 64 lanes span several tiles).
+template <class E2, int L, int K, bool CARRY = true, bool FASTDIV = false, bool CARRY_TEAMS = false>
 __device__ __forceinline__ void stream_tile(const LaneIn<E2, K>& d, const ScanScalars& sc, unsigned tbits,
                                             unsigned rbits, uint32_t cs, int64_t T, bool team_first_lane, int lane,
                                             double& C, PredIn& carry, float (&o0)[K], float (&o1)[K]) {
@@ -227,6 +229,18 @@ __device__ __forceinline__ void stream_tile(const LaneIn<E2, K>& d, const ScanSc
       carry.v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d.s[1][MLAST]), 63));
     } else if constexpr (Tr::kNbDone) {
       carry.done = (unsigned)__builtin_amdgcn_readlane((int)(((tbits | rbits) >> MLAST) & 1u), 63);
+    }
+  } else if constexpr (CARRY && CARRY_TEAMS) {
+    // several teams per wave: each team's scan-last lane (team start + L - 1)
+    const int src = (lane & ~(L - 1)) + L - 1;
+    if constexpr (Tr::kRetrace) {
+      const double ratio = (double)d.s[3][MLAST] / (double)d.s[4][MLAST];
+      carry.v = __shfl(d.s[2][MLAST], src, 64);
+      carry.c = __shfl(sc.lam * (ratio < 1.0 ? ratio : 1.0), src, 64);
+    } else if constexpr (Tr::kNbValue) {
+      carry.v = __shfl(d.s[1][MLAST], src, 64);
+    } else if constexpr (Tr::kNbDone) {
+      carry.done = (unsigned)__shfl((int)(((tbits | rbits) >> MLAST) & 1u), src, 64);
     }
   }
   C = C_next;

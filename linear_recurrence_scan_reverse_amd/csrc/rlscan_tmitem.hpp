@@ -1,0 +1,331 @@
+// rlscan_tmitem.hpp -- time-major [T, E] arrays scanned in the row-major item
+// layout: loader waves move chunks of 64 steps x 64 environments between HBM
+// and LDS, and compute waves read a chunk back as rows (4 environments x 64
+// steps per item, 16 lanes x 4 steps per row), run the per-lane code of the
+// row-major kernels on them, carrying each row across chunks, and leave the
+// outputs in LDS for the loaders to store.
+//
+// The time-major kernel in rlscan_timemajor.hpp maps lanes to environments
+// and splits time over the 16 waves of a block, so a block computes only once
+// all its waves' loads have landed, and at 16384 environments (one block per
+// CU) loads and compute never overlap.  Here a block owns 64 environments and
+// walks their time chunk by chunk, one chunk per tick, with the loads running
+// two chunks ahead of the compute.  Every environment's whole time range stays
+// with one compute wave, so no wave waits for another's result; the waves of
+// a block meet once per tick, at a barrier.
+//
+// Tick s (chunks in scan order; backward estimators walk time from the end):
+//   loaders  request chunk s+2's streams and chunk s+3's flags, store the
+//            outputs of chunk s-1 (read back from LDS), write chunk s+1's
+//            streams and chunk s+2's flags (requested a tick earlier) to LDS;
+//   compute  read chunk s+1's flags and request its truncation bootstraps,
+//            scan chunk s (its flags and bootstraps taken a tick earlier) and
+//            write its outputs over its streams in LDS.
+// Each wave only touches its own LDS cells of a slot (the loaders by step, the
+// compute waves by environment), and a slot changes hands only at a barrier.
+// Global accesses take whole runs of a step: 16 bytes a lane for streams and
+// outputs (scattered 16-byte stores of the compute waves' rows cost three
+// times the kernel's time), 4 bytes for flags, through buffer resources over
+// one chunk; requests of chunks before the first or past the last get a
+// resource of no records and touch no memory, so no branch surrounds a
+// request.  LDS holds every array environment-major (the loaders transpose on
+// the way in and out): a lane reads its 4 steps of a stream with two 8-byte
+// reads, and its 4 steps of both flags as one word (the loaders fold the two
+// flag bytes of a step into one, bit 0 terminated, bit 1 truncated).
+// Against step-major LDS rows read a step at a time, at 16384 x 256:
+// discounted returns 14.1 -> 12.5 us.
+#pragma once
+
+#include "rlscan_duo.hpp"
+#include "rlscan_stream.hpp"
+
+namespace rlscan {
+
+constexpr int kTiChunk = 64;   // steps per chunk (a row tile: 16 lanes x 4 steps)
+constexpr int kTiCompute = 8;  // compute waves, 8 environments (two items of 4 rows) each
+constexpr int kTiLoaders = 4;  // loader waves, 16 steps of every chunk each
+constexpr int kTiThreads = 64 * (kTiCompute + kTiLoaders);
+constexpr int kTiSlots = 2;    // chunks of streams in LDS (3 or 4, loads further ahead, measured slower)
+constexpr int kTiRow = 66;     // LDS words per environment and stream of a chunk (64 steps, padded)
+constexpr int kTiFlagRow = 17; // LDS words per environment of a chunk's flags (16 words of 4 steps, padded)
+
+// Wait until this wave's LDS accesses are done (lgkmcnt 0; the vector-memory
+// and export counters are left alone), so a barrier after it publishes them.
+__device__ __forceinline__ void lds_done() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Bit 0 of every byte of x: whether the byte is non-zero.
+__device__ __forceinline__ uint32_t bytes_nonzero(uint32_t x) {
+  return ((((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) >> 7) & 0x01010101u;
+}
+
+// Template parameters: estimator (one recurrence, at most three input
+// streams), OPT as for the other kernels.  Float32 storage; E and T
+// multiples of 64, every per-step array 16-byte aligned, 64 * E * 4 < 2^31
+// (checked by the launcher).  Block b: environments 64 b .. 64 b + 63.
+template <class Est, int OPT>
+__global__ void __launch_bounds__(kTiThreads) tm_item_kernel(const KernelArgs p) {
+  using Tr = Traits<Est>;
+  constexpr int L = 16, K = 4, SPAN = kTiChunk;
+  constexpr bool REV = Est::kReverse;
+  constexpr int NS = Tr::kStreams;
+  constexpr bool USE_FLAGS = (OPT & 1) && Tr::kUsesFlags;
+  constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
+  constexpr int NOUT = OUT1 ? 2 : 1;
+  constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
+  static_assert(!Tr::kDual && NS <= 3 && NOUT <= NS, "one recurrence, at most three streams, outputs over streams");
+  constexpr int NSL = kTiSlots, NFL = NSL + 1;
+
+  // streams (then outputs) of NSL chunks: [slot][stream][environment][step]
+  __shared__ __attribute__((aligned(16))) float s_d[NSL][NS][64][kTiRow];
+  // flags of NSL + 1 chunks, one byte per step (bit 0 terminated, bit 1
+  // truncated), four steps a word: [slot][environment][steps / 4]
+  __shared__ uint32_t s_f[USE_FLAGS ? NFL : 1][USE_FLAGS ? 64 : 1][kTiFlagRow];
+  // slots of chunk s (s >= -1)
+  auto dslot = [](int s) { return (s + NSL) % NSL; };
+  auto fslot = [](int s) { return s % NFL; };
+
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int64_t E = p.E, T = p.T;
+  const int ticks = (int)(T / SPAN);
+  const int64_t e0 = (int64_t)blockIdx.x * 64;
+  // resource over chunk s of an [T, E] array of esz-byte elements, from the
+  // block's first environment; no records for s outside [0, ticks)
+  auto chunk_rs = [&](const void* base, int s, int esz) {
+    const bool on = s >= 0 && s < ticks;
+    const int64_t t0 = on ? (REV ? (int64_t)(ticks - 1 - s) : (int64_t)s) * SPAN : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(base)) + (t0 * E + e0) * esz, 0, on ? (int)(SPAN * E * esz) : 0,
+        0x00020000);
+  };
+
+  if (wave >= kTiCompute) {
+    // ================================================================ loaders
+    const int lw = wave - kTiCompute;
+    const float* srcs[3] = {p.r, p.v, p.aux};
+    float* dsts[2] = {p.out0, p.out1};
+    // streams and outputs: access q of a lane covers step 4 (lw + 4 q) + lane / 16,
+    // environments 4 (lane % 16) .. + 3
+    const int scol = 4 * (lane & 15);
+    auto dstep = [&](int q) { return 4 * (lw + 4 * q) + (lane >> 4); };
+    auto doff = [&](int q) { return (uint32_t)(((int64_t)dstep(q) * E + scol) * 4); };
+    // flags: steps 16 lw + 4 (lane / 16) .. + 3, environments 4 (lane % 16) .. + 3,
+    // one 4-byte access per step and array
+    const int fword = 4 * lw + (lane >> 4);
+    auto foff = [&](int m) { return (uint32_t)((int64_t)(4 * fword + m) * E + scol); };
+
+    typedef u32x4 Chunk[NS][4];
+    typedef uint32_t Flags[2][4];
+    auto issue_data = [&](int s, Chunk& x) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const __amdgpu_buffer_rsrc_t rs = chunk_rs(srcs[st], s, 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[st][q] = raw_buffer_load<16>(rs, doff(q));
+      }
+    };
+    auto write_data = [&](int s, const Chunk& x) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 f = __builtin_bit_cast(f32x4, x[st][q]);
+          const int t = dstep(q);
+          s_d[dslot(s)][st][scol + 0][t] = f.x;
+          s_d[dslot(s)][st][scol + 1][t] = f.y;
+          s_d[dslot(s)][st][scol + 2][t] = f.z;
+          s_d[dslot(s)][st][scol + 3][t] = f.w;
+        }
+    };
+    auto issue_flags = [&](int s, Flags& f) {
+      if constexpr (USE_FLAGS) {
+        const __amdgpu_buffer_rsrc_t rt = chunk_rs(p.term, s, 1), rr = chunk_rs(p.trunc, s, 1);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f[0][m] = __builtin_amdgcn_raw_buffer_load_b32(rt, foff(m), 0, 2);
+          f[1][m] = __builtin_amdgcn_raw_buffer_load_b32(rr, foff(m), 0, 2);
+        }
+      }
+    };
+    // the lane's 4 steps x 4 environments of flags, combined and turned to
+    // one word of 4 steps per environment
+    auto write_flags = [&](int s, const Flags& f) {
+      if constexpr (USE_FLAGS) {
+        uint32_t c[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) c[m] = bytes_nonzero(f[0][m]) | (bytes_nonzero(f[1][m]) << 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = ((c[0] >> (8 * j)) & 0xffu) | (((c[1] >> (8 * j)) & 0xffu) << 8) |
+                             (((c[2] >> (8 * j)) & 0xffu) << 16) | (((c[3] >> (8 * j)) & 0xffu) << 24);
+          s_f[fslot(s)][scol + j][fword] = w;
+        }
+      }
+    };
+    // outputs of chunk s (left over its streams by the compute waves)
+    auto store_out = [&](int s) {
+#pragma unroll
+      for (int o = 0; o < NOUT; ++o) {
+        const __amdgpu_buffer_rsrc_t rs = chunk_rs(dsts[o], s, 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = dstep(q);
+          const f32x4 f = {s_d[dslot(s)][o][scol + 0][t], s_d[dslot(s)][o][scol + 1][t],
+                           s_d[dslot(s)][o][scol + 2][t], s_d[dslot(s)][o][scol + 3][t]};
+          raw_buffer_store<16>(__builtin_bit_cast(u32x4, f), rs, doff(q));
+        }
+      }
+    };
+    auto loaded = [] {
+      lds_done();
+      tick_barrier();
+    };
+    // one tick; X/F: the register sets written this tick (requested a tick
+    // earlier), Y/G: the ones requested now.  The streams of chunk s+NSL-1 go
+    // to the slot chunk s-1's outputs leave.
+    auto tick = [&](int s, Chunk& X, Chunk& Y, Flags& F, Flags& G) {
+      issue_data(s + NSL, Y);
+      issue_flags(s + NSL + 1, G);
+      asm volatile("" ::: "memory");
+      store_out(s - 1);
+      write_data(s + NSL - 1, X);
+      write_flags(s + NSL, F);
+      loaded();
+    };
+
+    Chunk x[NSL];
+    Flags f[NFL];
+    // before the first tick: the streams of chunks 0 .. NSL-1 and the flags of
+    // chunks 0 .. NSL requested at once; all but the last of each in LDS
+#pragma unroll
+    for (int k = 0; k < NFL; ++k) issue_flags(k, f[k]);
+#pragma unroll
+    for (int k = 0; k < NSL; ++k) issue_data(k, x[k]);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < NSL; ++k) write_flags(k, f[k]);
+#pragma unroll
+    for (int k = 0; k + 1 < NSL; ++k) write_data(k, x[k]);
+    loaded();
+    // from here two register sets of each kind take turns
+    tick(0, x[NSL - 1], x[0], f[NSL], f[0]);
+    for (int s = 1; s < ticks; s += 2) {
+      tick(s, x[0], x[NSL - 1], f[0], f[NSL]);
+      if (s + 1 < ticks) tick(s + 1, x[NSL - 1], x[0], f[NSL], f[0]);
+    }
+    store_out(ticks - 1);
+  } else {
+    // ================================================================ compute
+    const int c = wave;
+    const int team = lane / L;  // row (environment) of the item
+    const int g = lane & (L - 1);
+    const bool team_first_lane = g == 0;
+    const uint32_t cs_local = REV ? (uint32_t)(SPAN - (g + 1) * K) : (uint32_t)(g * K);
+    const double gamma = p.gamma, lam = p.lam;
+    const ScanScalars sc{gamma, lam, gamma * lam, (float)p.rho_bar, (float)p.c_bar, p.has_row != 0,
+                         p.has_tboot != 0};
+    const unsigned tmask = p.has_term ? ~0u : 0u;
+    const unsigned rmask = p.has_trunc ? ~0u : 0u;
+    constexpr bool FAST = Tr::kRetrace;
+
+    int col[2];     // environment offset inside the block, per item
+    float rowv[2];  // bootstrap value / init of the environment
+    double C[2];
+    PredIn carry[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      col[it] = 8 * c + 4 * it + team;
+      rowv[it] = p.has_row ? __builtin_nontemporal_load(p.row + e0 + col[it]) : 0.0f;
+      C[it] = 0.0;
+      if constexpr (!Tr::kBackwardRl) C[it] = p.has_row ? (double)rowv[it] : 0.0;
+      carry[it] = PredIn{0.0f, 0.0, 0u};
+    }
+
+    // what a chunk's scan takes besides its streams: the lane's flag bits and
+    // truncation bootstraps, per item (read a tick ahead)
+    struct Side {
+      unsigned tb[2], rb[2];
+      float boot[2][K];
+    };
+    // flags of chunk s from LDS, and its bootstraps requested (none past the
+    // last chunk; lanes and steps without one pass an offset outside the resource)
+    auto side_of = [&](int s, Side& o) {
+      const int sf = s < ticks ? s : ticks - 1;  // flags slot read (any valid one past the end)
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        o.tb[it] = o.rb[it] = 0u;
+        if constexpr (USE_FLAGS) {
+          const uint32_t w = s_f[fslot(sf)][col[it]][cs_local / 4];
+          o.tb[it] = ((w & 1u) | ((w >> 7) & 2u) | ((w >> 14) & 4u) | ((w >> 21) & 8u)) & tmask;
+          o.rb[it] = (((w >> 1) & 1u) | ((w >> 8) & 2u) | ((w >> 15) & 4u) | ((w >> 22) & 8u)) & rmask;
+        }
+#pragma unroll
+        for (int m = 0; m < K; ++m) o.boot[it][m] = 0.0f;
+      }
+      if constexpr (GATHER_TB) {
+        const __amdgpu_buffer_rsrc_t rs = chunk_rs(p.tboot, s, 4);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const unsigned need = p.has_tboot ? (o.rb[it] & ~o.tb[it]) : 0u;
+#pragma unroll
+          for (int m = 0; m < K; ++m) {
+            const uint32_t off = (uint32_t)(((int64_t)(cs_local + m) * E + col[it]) * 4);
+            o.boot[it][m] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((need >> m) & 1u) ? off : kDuoOff, 0, 2));
+          }
+        }
+      }
+    };
+    // one tick: chunk s+1's side inputs requested, chunk s scanned, its
+    // outputs written over its streams
+    auto tick = [&](int s, const Side& cur, Side& nxt) {
+      side_of(s + 1, nxt);
+      const int slot = dslot(s);
+      const int64_t t0 = (REV ? (int64_t)(ticks - 1 - s) : (int64_t)s) * SPAN;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        LaneIn<Est, K> d;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          const f32x2* q = reinterpret_cast<const f32x2*>(&s_d[slot][st][col[it]][cs_local]);
+          const f32x2 a = q[0], b = q[1];
+          d.s[st][0] = a.x;
+          d.s[st][1] = a.y;
+          d.s[st][2] = b.x;
+          d.s[st][3] = b.y;
+        }
+#pragma unroll
+        for (int m = 0; m < K; ++m) d.tb[m] = cur.boot[it][m];
+        d.rowv = rowv[it];
+        float o0[K], o1[K];
+        stream_tile<Est, L, K, true, FAST, true>(d, sc, cur.tb[it], cur.rb[it], (uint32_t)t0 + cs_local, T,
+                                                 team_first_lane, lane, C[it], carry[it], o0, o1);
+        f32x2* w0 = reinterpret_cast<f32x2*>(&s_d[slot][0][col[it]][cs_local]);
+        w0[0] = (f32x2){o0[0], o0[1]};
+        w0[1] = (f32x2){o0[2], o0[3]};
+        if constexpr (OUT1) {
+          f32x2* w1 = reinterpret_cast<f32x2*>(&s_d[slot][1][col[it]][cs_local]);
+          w1[0] = (f32x2){o1[0], o1[1]};
+          w1[1] = (f32x2){o1[2], o1[3]};
+        }
+      }
+      lds_done();
+      tick_barrier();
+    };
+
+    Side sa, sb;
+    tick_barrier();  // chunk 0 and the flags of chunks 0 and 1 are in LDS
+    side_of(0, sa);
+    // Tick 0 runs ahead of the loop, so the loop is entered from the same
+    // point of the pipeline its back edge returns to (the compiler's count of
+    // requests in flight then agrees on both, and its waits stay exact); the
+    // two side-input register sets swap roles from tick to tick.
+    tick(0, sa, sb);
+    for (int s = 1; s < ticks; s += 2) {
+      tick(s, sb, sa);
+      if (s + 1 < ticks) tick(s + 1, sa, sb);
+    }
+  }
+}
+
+}  // namespace rlscan

@@ -11,7 +11,8 @@ episodes) are checked against the oracle:
   array): discounted returns (streaming kernel), GAE (streaming), Retrace
   (pipelined kernel), rows sampled at the start, around element 2^31 and at
   the end;
-* the same shape time-major ([T, E]) for TD(lambda);
+* the same shape time-major ([T, E]) for TD(lambda), and [320, 2^23 - 64]
+  (the largest shape of the time-major item form);
 * two rows of 2^30 - 1 steps (the ABI's longest) on the segmented path,
   checked on whole episodes: a slice that ends with a terminated step
   (backward) or starts right after a done step (forward) does not depend on
@@ -118,6 +119,30 @@ def test_time_major_past_2pow31_elements():
     import torch
     g = torch.Generator(device="cuda")
     g.manual_seed(92)
+    bv = torch.randn(E, generator=g, device="cuda")
+    out = rl.td_lambda(d["r"], d["v"], d["terminated"], d["truncated"], bv, d["trunc_bootstrap"], gamma=0.99,
+                       lam=0.95, time_major=True)
+    rows = _sample_rows(E, T)
+    h = {k: _rows(v, rows, time_major=True) for k, v in d.items()}
+    hb = _rows(bv, rows)
+    got = _rows(out, rows, time_major=True)
+    del d, out, bv
+    _free()
+    ref = oracle.td_lambda(h["r"], h["v"], h["terminated"], h["truncated"], hb, h["trunc_bootstrap"], gamma=0.99,
+                           lam=0.95)
+    assert parity_err(got, ref) <= TOL
+
+
+def test_time_major_item_form_past_2pow31_elements():
+    # the largest environment count of the LDS-staged item form (a multiple of
+    # 64 below 2^23), with columns long enough to pass element 2^31
+    import linear_recurrence_scan_reverse_amd as rl
+    E, T = (1 << 23) - 64, 320
+    _say("max sizes time-major item form td_lambda E=%d T=%d" % (E, T))
+    d = _inputs((T, E), 93, ["r", "v", "trunc_bootstrap", "terminated", "truncated"])
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(94)
     bv = torch.randn(E, generator=g, device="cuda")
     out = rl.td_lambda(d["r"], d["v"], d["terminated"], d["truncated"], bv, d["trunc_bootstrap"], gamma=0.99,
                        lam=0.95, time_major=True)

@@ -103,6 +103,32 @@ def test_time_major_exact_integer_sums():
     assert np.array_equal(got.cpu().numpy().T.astype(np.float64), ref)
 
 
+# The item form of float32 time-major calls (chunks of 64 steps x 64
+# environments staged in LDS and scanned as rows; whole chunks, 16-byte
+# aligned arrays, one launch, columns other than one super-tile of the other
+# kernel): one chunk, odd and even chunk counts, one and many column groups,
+# 16384 environments at 64, 384 and 512 steps; dense flags; no episode ends
+# (every row's carry crosses every chunk).
+@pytest.mark.parametrize("E,T", [(64, 64), (128, 192), (192, 448), (256, 320), (1024, 128), (16384, 64),
+                                 (16384, 384), (16384, 512)])
+@pytest.mark.parametrize("p", [0.0, 0.01, 0.3])
+def test_time_major_item_form(E, T, p):
+    if p != 0.01 and E * T > (1 << 20):
+        pytest.skip("flag densities are covered at the smaller shapes")
+    _say("time-major item form E=%d T=%d p=%g" % (E, T, p))
+    d = synth.draw(E, T, seed=89 + E + T, p_term=p, p_trunc=p)
+    for name in SEVEN:
+        check_storage(name, d, "float32", time_major=True)
+
+
+@pytest.mark.parametrize("variant", [dict(term=False, trunc=False), dict(boot=False, tboot=False),
+                                     dict(trunc=False), dict(term=False), dict(tboot=False)])
+def test_time_major_item_form_optional_inputs(variant):
+    d = synth.draw(128, 320, seed=90, p_term=0.03, p_trunc=0.03)
+    for name in SEVEN:
+        check_storage(name, d, "float32", time_major=True, **variant)
+
+
 # Few column groups and long columns: time is cut into segments scanned in
 # three launches (segment maps parked in the first output, a carry pass, a
 # rescan).  Shapes: two segments, a ragged last segment, two column groups,
