@@ -573,24 +573,40 @@ constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 // needs at most 8 rows); the last segment takes the remainder.  At most
 // kTmMaxSeg segments per column (the carry kernel's 16 waves x kTmCarrySeg).
 // The item form of the time-major path (tm_item_kernel): float32, one
-// recurrence of at most three streams, whole 64 x 64 chunks and 16-byte
-// aligned per-step arrays.  Columns of exactly one super-tile of tm_kernel
-// stay there: it has every load of such a column in flight at once and was
-// the faster one in the sweep (16384 x 256, float32: discounted returns 12.2
-// against 12.4 us, TD(lambda) 14.5 against 15.2; V-trace at 128 steps 12.5
-// against 13.0); at every other step count from 64 to 512 the item form was
-// (16384 x 320: TD(lambda) 23.6 -> 18.2 us, V-trace 34.2 -> 27.1; 16384 x 64:
-// 11.0 -> 6.8).
+// recurrence of at most three streams, whole 64-step chunks, 16-byte aligned
+// per-step arrays.  Blocks of 64 environments when there are at least as many
+// such column groups as CUs, else of 32 (twice the blocks; with 32 at many
+// environments the arrays streamed more slowly: 16384 x 256 discounted
+// returns 12.5 us with 64, 16.4 with 32; 4096 x 256: 10.1 with 64, 8.9 with
+// 32).  Routing, from a sweep of 1024 to 32768 environments and 64 to 2048
+// steps (float32, one MI355X):
+//  * columns of exactly one super-tile of tm_kernel, with 64-environment
+//    blocks, stay there: it has every load of such a column in flight at once
+//    (16384 x 256: discounted returns 12.2 against 12.4 us, TD(lambda) 14.5
+//    against 15.2; V-trace at 128 steps 12.5 against 13.0);
+//  * a block walks its columns' chunks one after another, so long columns
+//    over few blocks go to the segmented path: the item form takes columns of
+//    up to 16 chunks, or any length with at least half as many blocks as CUs
+//    (TD(lambda) 2048 x 2048: 31.1 us segmented, 47.5 item form; 4096 x 2048:
+//    58.2 and 49.6; 4096 x 512: 26.4 and 15.6);
+//  * everywhere else it was the faster one (16384 x 320: TD(lambda) 23.6 ->
+//    18.2 us, V-trace 34.2 -> 27.1; 16384 x 64: 11.0 -> 6.8).
 template <class Est, class S>
 constexpr bool tm_item_ok() {
   return __is_same(S, F32S) && !Traits<Est>::kDual && Traits<Est>::kStreams <= 3;
 }
+// environments per block of the item form, or 0 where the other kernels take the call
 template <class Est>
-inline bool tm_item_fits(const KernelArgs& a) {
+inline int tm_item_envs(const KernelArgs& a, int cus) {
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  return a.T != (int64_t)tm_waves<Est>() * tm_chunk<Est>() && a.E % kTiChunk == 0 && a.T % kTiChunk == 0 &&
-         a.E < ((int64_t)1 << 23) && al(a.r) && al(a.v) && al(a.aux) && al(a.term) && al(a.trunc) && al(a.out0) &&
-         al(a.out1);
+  if (a.T % kTiChunk != 0 || a.E >= ((int64_t)1 << 23) || !al(a.r) || !al(a.v) || !al(a.aux) || !al(a.term) ||
+      !al(a.trunc) || !al(a.out0) || !al(a.out1))
+    return 0;
+  const int eb = (a.E + 63) / 64 >= cus ? 64 : 32;
+  if (a.E % eb != 0) return 0;
+  if (eb == 64 && a.T == (int64_t)tm_waves<Est>() * tm_chunk<Est>()) return 0;
+  if (a.T / kTiChunk > 16 && 2 * (a.E / eb) < cus) return 0;
+  return eb;
 }
 
 template <class Est, int OPT, class S>
@@ -605,10 +621,14 @@ inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
   if (groups * nseg * 64 * W > kMaxWorkItems || nseg > kTmMaxSeg) return hipErrorInvalidConfiguration;
   KernelArgs arg = a;
   if constexpr (tm_item_ok<Est, S>()) {
-    if (nseg == 1 && tm_item_fits<Est>(a)) {
+    if (const int eb = tm_item_envs<Est>(a, cu_count())) {
       void* p1[] = {&arg};
-      return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT>), dim3((unsigned)groups),
-                             dim3(kTiThreads), p1, 0, s);
+      const dim3 grid((unsigned)(a.E / eb));
+      if (eb == 64)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 64>), grid,
+                               dim3(ti_threads<64>()), p1, 0, s);
+      return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 32>), grid,
+                             dim3(ti_threads<32>()), p1, 0, s);
     }
   }
   void* params[] = {&arg, &seg_len, &nseg};

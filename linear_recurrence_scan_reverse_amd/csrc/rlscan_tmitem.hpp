@@ -1,16 +1,16 @@
 // rlscan_tmitem.hpp -- time-major [T, E] arrays scanned in the row-major item
-// layout: loader waves move chunks of 64 steps x 64 environments between HBM
-// and LDS, and compute waves read a chunk back as rows (4 environments x 64
-// steps per item, 16 lanes x 4 steps per row), run the per-lane code of the
-// row-major kernels on them, carrying each row across chunks, and leave the
-// outputs in LDS for the loaders to store.
+// layout: loader waves move chunks of 64 steps x 64 (or 32) environments
+// between HBM and LDS, and compute waves read a chunk back as rows (4
+// environments x 64 steps per item, 16 lanes x 4 steps per row), run the
+// per-lane code of the row-major kernels on them, carrying each row across
+// chunks, and leave the outputs in LDS for the loaders to store.
 //
 // The time-major kernel in rlscan_timemajor.hpp maps lanes to environments
 // and splits time over the 16 waves of a block, so a block computes only once
 // all its waves' loads have landed, and at 16384 environments (one block per
-// CU) loads and compute never overlap.  Here a block owns 64 environments and
-// walks their time chunk by chunk, one chunk per tick, with the loads running
-// two chunks ahead of the compute.  Every environment's whole time range stays
+// CU) loads and compute never overlap.  Here a block owns 64 or 32
+// environments and walks their time chunk by chunk, one chunk per tick, with
+// the loads running two chunks ahead of the compute.  Every environment's whole time range stays
 // with one compute wave, so no wave waits for another's result; the waves of
 // a block meet once per tick, at a barrier.
 //
@@ -42,12 +42,22 @@
 namespace rlscan {
 
 constexpr int kTiChunk = 64;   // steps per chunk (a row tile: 16 lanes x 4 steps)
-constexpr int kTiCompute = 8;  // compute waves, 8 environments (two items of 4 rows) each
-constexpr int kTiLoaders = 4;  // loader waves, 16 steps of every chunk each
-constexpr int kTiThreads = 64 * (kTiCompute + kTiLoaders);
 constexpr int kTiSlots = 2;    // chunks of streams in LDS (3 or 4, loads further ahead, measured slower)
 constexpr int kTiRow = 66;     // LDS words per environment and stream of a chunk (64 steps, padded)
-constexpr int kTiFlagRow = 17; // LDS words per environment of a chunk's flags (16 words of 4 steps, padded)
+// A block of EB environments (64 or 32): EB / 8 compute waves of two items
+// (4 environments each), EB / 16 loader waves, each 64 / (EB / 16) steps of
+// every chunk; 16-byte lane accesses cover a step's EB environments with
+// EB / 4 lanes.
+template <int EB>
+constexpr int ti_compute() { return EB / 8; }
+template <int EB>
+constexpr int ti_loaders() { return EB / 16; }
+template <int EB>
+constexpr int ti_threads() { return 64 * (ti_compute<EB>() + ti_loaders<EB>()); }
+// LDS words per environment of a chunk's flags (16 words of 4 steps, padded
+// so the loaders' writes spread over the banks)
+template <int EB>
+constexpr int ti_flag_row() { return EB == 64 ? 17 : 18; }
 
 // Wait until this wave's LDS accesses are done (lgkmcnt 0; the vector-memory
 // and export counters are left alone), so a barrier after it publishes them.
@@ -59,11 +69,12 @@ __device__ __forceinline__ uint32_t bytes_nonzero(uint32_t x) {
 }
 
 // Template parameters: estimator (one recurrence, at most three input
-// streams), OPT as for the other kernels.  Float32 storage; E and T
-// multiples of 64, every per-step array 16-byte aligned, 64 * E * 4 < 2^31
-// (checked by the launcher).  Block b: environments 64 b .. 64 b + 63.
-template <class Est, int OPT>
-__global__ void __launch_bounds__(kTiThreads) tm_item_kernel(const KernelArgs p) {
+// streams), OPT as for the other kernels, EB environments per block.
+// Float32 storage; E a multiple of EB, T of 64, every per-step array 16-byte
+// aligned, 64 * E * 4 < 2^31 (checked by the launcher).  Block b:
+// environments EB b .. EB b + EB - 1.
+template <class Est, int OPT, int EB>
+__global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
   constexpr int L = 16, K = 4, SPAN = kTiChunk;
   constexpr bool REV = Est::kReverse;
@@ -73,13 +84,17 @@ __global__ void __launch_bounds__(kTiThreads) tm_item_kernel(const KernelArgs p)
   constexpr int NOUT = OUT1 ? 2 : 1;
   constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
   static_assert(!Tr::kDual && NS <= 3 && NOUT <= NS, "one recurrence, at most three streams, outputs over streams");
+  static_assert(EB == 64 || EB == 32, "blocks of 64 or 32 environments");
   constexpr int NSL = kTiSlots, NFL = NSL + 1;
+  constexpr int NC = ti_compute<EB>(), NLD = ti_loaders<EB>(), FROW = ti_flag_row<EB>();
+  constexpr int LPR = EB / 4;      // lanes per step of a 16-byte access
+  constexpr int SPI = 64 / LPR;    // steps per loader instruction
 
   // streams (then outputs) of NSL chunks: [slot][stream][environment][step]
-  __shared__ __attribute__((aligned(16))) float s_d[NSL][NS][64][kTiRow];
+  __shared__ __attribute__((aligned(16))) float s_d[NSL][NS][EB][kTiRow];
   // flags of NSL + 1 chunks, one byte per step (bit 0 terminated, bit 1
   // truncated), four steps a word: [slot][environment][steps / 4]
-  __shared__ uint32_t s_f[USE_FLAGS ? NFL : 1][USE_FLAGS ? 64 : 1][kTiFlagRow];
+  __shared__ uint32_t s_f[USE_FLAGS ? NFL : 1][USE_FLAGS ? EB : 1][FROW];
   // slots of chunk s (s >= -1)
   auto dslot = [](int s) { return (s + NSL) % NSL; };
   auto fslot = [](int s) { return s % NFL; };
@@ -88,7 +103,7 @@ __global__ void __launch_bounds__(kTiThreads) tm_item_kernel(const KernelArgs p)
   const int lane = threadIdx.x & 63;
   const int64_t E = p.E, T = p.T;
   const int ticks = (int)(T / SPAN);
-  const int64_t e0 = (int64_t)blockIdx.x * 64;
+  const int64_t e0 = (int64_t)blockIdx.x * EB;
   // resource over chunk s of an [T, E] array of esz-byte elements, from the
   // block's first environment; no records for s outside [0, ticks)
   auto chunk_rs = [&](const void* base, int s, int esz) {
@@ -99,19 +114,19 @@ __global__ void __launch_bounds__(kTiThreads) tm_item_kernel(const KernelArgs p)
         0x00020000);
   };
 
-  if (wave >= kTiCompute) {
+  if (wave >= NC) {
     // ================================================================ loaders
-    const int lw = wave - kTiCompute;
+    const int lw = wave - NC;
     const float* srcs[3] = {p.r, p.v, p.aux};
     float* dsts[2] = {p.out0, p.out1};
-    // streams and outputs: access q of a lane covers step 4 (lw + 4 q) + lane / 16,
-    // environments 4 (lane % 16) .. + 3
-    const int scol = 4 * (lane & 15);
-    auto dstep = [&](int q) { return 4 * (lw + 4 * q) + (lane >> 4); };
+    // streams and outputs: access q of a lane covers step SPI (lw + NLD q) +
+    // lane / LPR, environments 4 (lane % LPR) .. + 3
+    const int scol = 4 * (lane % LPR);
+    auto dstep = [&](int q) { return SPI * (lw + NLD * q) + lane / LPR; };
     auto doff = [&](int q) { return (uint32_t)(((int64_t)dstep(q) * E + scol) * 4); };
-    // flags: steps 16 lw + 4 (lane / 16) .. + 3, environments 4 (lane % 16) .. + 3,
-    // one 4-byte access per step and array
-    const int fword = 4 * lw + (lane >> 4);
+    // flags: steps 4 fword .. + 3, environments 4 (lane % LPR) .. + 3, one
+    // 4-byte access per step and array
+    const int fword = (16 / NLD) * lw + lane / LPR;
     auto foff = [&](int m) { return (uint32_t)((int64_t)(4 * fword + m) * E + scol); };
 
     typedef u32x4 Chunk[NS][4];

@@ -103,14 +103,16 @@ def test_time_major_exact_integer_sums():
     assert np.array_equal(got.cpu().numpy().T.astype(np.float64), ref)
 
 
-# The item form of float32 time-major calls (chunks of 64 steps x 64
+# The item form of float32 time-major calls (chunks of 64 steps x 64 or 32
 # environments staged in LDS and scanned as rows; whole chunks, 16-byte
-# aligned arrays, one launch, columns other than one super-tile of the other
-# kernel): one chunk, odd and even chunk counts, one and many column groups,
-# 16384 environments at 64, 384 and 512 steps; dense flags; no episode ends
-# (every row's carry crosses every chunk).
-@pytest.mark.parametrize("E,T", [(64, 64), (128, 192), (192, 448), (256, 320), (1024, 128), (16384, 64),
-                                 (16384, 384), (16384, 512)])
+# aligned arrays, one launch): one chunk, odd and even chunk counts, blocks of
+# 32 environments (fewer than 16384; 96 is no multiple of 64) and of 64
+# (16384 at 64, 384 and 512 steps, not 256: one super-tile of the other
+# kernel), 4096 x 1088 (columns of 17 chunks, taken since the blocks are half
+# as many as the CUs); dense flags; no episode ends (every row's carry
+# crosses every chunk).
+@pytest.mark.parametrize("E,T", [(64, 64), (96, 128), (128, 192), (192, 448), (256, 320), (1024, 128), (4096, 256),
+                                 (4096, 1088), (16384, 64), (16384, 384), (16384, 512)])
 @pytest.mark.parametrize("p", [0.0, 0.01, 0.3])
 def test_time_major_item_form(E, T, p):
     if p != 0.01 and E * T > (1 << 20):
