@@ -589,11 +589,15 @@ constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 //    up to 16 chunks, or any length with at least half as many blocks as CUs
 //    (TD(lambda) 2048 x 2048: 31.1 us segmented, 47.5 item form; 4096 x 2048:
 //    58.2 and 49.6; 4096 x 512: 26.4 and 15.6);
+//  * Retrace's five streams fit in LDS only with 32-environment blocks; with
+//    at least one 64-environment column group per CU tm_kernel stays faster
+//    for it (16384 x 256: 25.4 us against 31.6), below that the item form
+//    (4096 x 512: 41.8 -> 20.9 us, 8192 x 1024: 95.4 -> 53.3);
 //  * everywhere else it was the faster one (16384 x 320: TD(lambda) 23.6 ->
 //    18.2 us, V-trace 34.2 -> 27.1; 16384 x 64: 11.0 -> 6.8).
 template <class Est, class S>
 constexpr bool tm_item_ok() {
-  return __is_same(S, F32S) && !Traits<Est>::kDual && Traits<Est>::kStreams <= 3;
+  return __is_same(S, F32S) && !Traits<Est>::kDual && (Traits<Est>::kStreams <= 3 || Traits<Est>::kStreams == 5);
 }
 // environments per block of the item form, or 0 where the other kernels take the call
 template <class Est>
@@ -602,7 +606,9 @@ inline int tm_item_envs(const KernelArgs& a, int cus) {
   if (a.T % kTiChunk != 0 || a.E >= ((int64_t)1 << 23) || !al(a.r) || !al(a.v) || !al(a.aux) || !al(a.term) ||
       !al(a.trunc) || !al(a.out0) || !al(a.out1))
     return 0;
-  const int eb = (a.E + 63) / 64 >= cus ? 64 : 32;
+  const bool wide = (a.E + 63) / 64 >= cus;  // a 64-environment column group per CU at least
+  if (wide && Traits<Est>::kStreams > 3) return 0;
+  const int eb = wide ? 64 : 32;
   if (a.E % eb != 0) return 0;
   if (eb == 64 && a.T == (int64_t)tm_waves<Est>() * tm_chunk<Est>()) return 0;
   if (a.T / kTiChunk > 16 && 2 * (a.E / eb) < cus) return 0;
@@ -624,9 +630,11 @@ inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
     if (const int eb = tm_item_envs<Est>(a, cu_count())) {
       void* p1[] = {&arg};
       const dim3 grid((unsigned)(a.E / eb));
-      if (eb == 64)
-        return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 64>), grid,
-                               dim3(ti_threads<64>()), p1, 0, s);
+      if constexpr (Traits<Est>::kStreams <= 3) {
+        if (eb == 64)
+          return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 64>), grid,
+                                 dim3(ti_threads<64>()), p1, 0, s);
+      }
       return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 32>), grid,
                              dim3(ti_threads<32>()), p1, 0, s);
     }

@@ -69,7 +69,9 @@ __device__ __forceinline__ uint32_t bytes_nonzero(uint32_t x) {
 }
 
 // Template parameters: estimator (one recurrence, at most three input
-// streams), OPT as for the other kernels, EB environments per block.
+// streams, or Retrace's five with 32 environments per block: the LDS holds
+// two chunks of them), OPT as for the other kernels, EB environments per
+// block.
 // Float32 storage; E a multiple of EB, T of 64, every per-step array 16-byte
 // aligned, 64 * E * 4 < 2^31 (checked by the launcher).  Block b:
 // environments EB b .. EB b + EB - 1.
@@ -83,7 +85,8 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
   constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
   constexpr int NOUT = OUT1 ? 2 : 1;
   constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
-  static_assert(!Tr::kDual && NS <= 3 && NOUT <= NS, "one recurrence, at most three streams, outputs over streams");
+  static_assert(!Tr::kDual && NOUT <= NS, "one recurrence, outputs over streams");
+  static_assert(NS <= 3 || (NS == 5 && EB == 32), "five streams (Retrace) in blocks of 32 environments");
   static_assert(EB == 64 || EB == 32, "blocks of 64 or 32 environments");
   constexpr int NSL = kTiSlots, NFL = NSL + 1;
   constexpr int NC = ti_compute<EB>(), NLD = ti_loaders<EB>(), FROW = ti_flag_row<EB>();
@@ -117,7 +120,7 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
   if (wave >= NC) {
     // ================================================================ loaders
     const int lw = wave - NC;
-    const float* srcs[3] = {p.r, p.v, p.aux};
+    const float* srcs[5] = {p.r, p.v, p.aux, p.pi, p.mu};
     float* dsts[2] = {p.out0, p.out1};
     // streams and outputs: access q of a lane covers step SPI (lw + NLD q) +
     // lane / LPR, environments 4 (lane % LPR) .. + 3
