@@ -572,9 +572,9 @@ constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 // steps and a multiple of 256 (whole super-tiles; the parked float64 pair
 // needs at most 8 rows); the last segment takes the remainder.  At most
 // kTmMaxSeg segments per column (the carry kernel's 16 waves x kTmCarrySeg).
-// The item form of the time-major path (tm_item_kernel): float32, one
-// recurrence of at most three streams, whole 64-step chunks, 16-byte aligned
-// per-step arrays.  Blocks of 64 environments when there are at least as many
+// The item form of the time-major path (tm_item_kernel): one recurrence of
+// at most three streams (or Retrace), whole 64-step chunks, 16-byte aligned
+// per-step arrays, every storage format.  Blocks of 64 environments when there are at least as many
 // such column groups as CUs, else of 32 (twice the blocks; with 32 at many
 // environments the arrays streamed more slowly: 16384 x 256 discounted
 // returns 12.5 us with 64, 16.4 with 32; 4096 x 256: 10.1 with 64, 8.9 with
@@ -582,8 +582,11 @@ constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 // steps (float32, one MI355X):
 //  * columns of exactly one super-tile of tm_kernel, with 64-environment
 //    blocks, stay there: it has every load of such a column in flight at once
-//    (16384 x 256: discounted returns 12.2 against 12.4 us, TD(lambda) 14.5
-//    against 15.2; V-trace at 128 steps 12.5 against 13.0);
+//    (float32 16384 x 256: discounted returns 12.2 against 12.4 us, TD(lambda)
+//    14.5 against 15.2; V-trace at 128 steps 12.5 against 13.0), except the
+//    16-bit discounted returns, TD(lambda) and GAE (bfloat16 16384 x 256:
+//    14.0 -> 12.8 us, 15.6 -> 13.9, 15.6 -> 14.1; traces there 9.4 against
+//    10.3 in the item form);
 //  * a block walks its columns' chunks one after another, so long columns
 //    over few blocks go to the segmented path: the item form takes columns of
 //    up to 16 chunks, or any length with at least half as many blocks as CUs
@@ -593,24 +596,28 @@ constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 //    at least one 64-environment column group per CU tm_kernel stays faster
 //    for it (16384 x 256: 25.4 us against 31.6), below that the item form
 //    (4096 x 512: 41.8 -> 20.9 us, 8192 x 1024: 95.4 -> 53.3);
-//  * everywhere else it was the faster one (16384 x 320: TD(lambda) 23.6 ->
-//    18.2 us, V-trace 34.2 -> 27.1; 16384 x 64: 11.0 -> 6.8).
+//  * everywhere else it was the faster one (float32 16384 x 320: TD(lambda)
+//    23.6 -> 18.2 us, V-trace 34.2 -> 27.1; 16384 x 64: 11.0 -> 6.8;
+//    bfloat16 32768 x 64 discounted returns 22.9 -> 8.3, 4096 x 512
+//    TD(lambda) 32.0 -> 16.8).
 template <class Est, class S>
 constexpr bool tm_item_ok() {
-  return __is_same(S, F32S) && !Traits<Est>::kDual && (Traits<Est>::kStreams <= 3 || Traits<Est>::kStreams == 5);
+  return !Traits<Est>::kDual && (Traits<Est>::kStreams <= 3 || Traits<Est>::kStreams == 5);
 }
 // environments per block of the item form, or 0 where the other kernels take the call
-template <class Est>
+template <class Est, class S>
 inline int tm_item_envs(const KernelArgs& a, int cus) {
+  using Tr = Traits<Est>;
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   if (a.T % kTiChunk != 0 || a.E >= ((int64_t)1 << 23) || !al(a.r) || !al(a.v) || !al(a.aux) || !al(a.term) ||
       !al(a.trunc) || !al(a.out0) || !al(a.out1))
     return 0;
   const bool wide = (a.E + 63) / 64 >= cus;  // a 64-environment column group per CU at least
-  if (wide && Traits<Est>::kStreams > 3) return 0;
+  if (wide && Tr::kStreams > 3) return 0;
   const int eb = wide ? 64 : 32;
   if (a.E % eb != 0) return 0;
-  if (eb == 64 && a.T == (int64_t)tm_waves<Est>() * tm_chunk<Est>()) return 0;
+  const bool bwd16 = !__is_same(S, F32S) && Tr::kBackwardRl && Tr::kStreams <= 2;
+  if (eb == 64 && a.T == (int64_t)tm_waves<Est>() * tm_chunk<Est>() && !bwd16) return 0;
   if (a.T / kTiChunk > 16 && 2 * (a.E / eb) < cus) return 0;
   return eb;
 }
@@ -627,15 +634,15 @@ inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
   if (groups * nseg * 64 * W > kMaxWorkItems || nseg > kTmMaxSeg) return hipErrorInvalidConfiguration;
   KernelArgs arg = a;
   if constexpr (tm_item_ok<Est, S>()) {
-    if (const int eb = tm_item_envs<Est>(a, cu_count())) {
+    if (const int eb = tm_item_envs<Est, S>(a, cu_count())) {
       void* p1[] = {&arg};
       const dim3 grid((unsigned)(a.E / eb));
       if constexpr (Traits<Est>::kStreams <= 3) {
         if (eb == 64)
-          return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 64>), grid,
+          return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 64, S>), grid,
                                  dim3(ti_threads<64>()), p1, 0, s);
       }
-      return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 32>), grid,
+      return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 32, S>), grid,
                              dim3(ti_threads<32>()), p1, 0, s);
     }
   }

@@ -71,11 +71,12 @@ __device__ __forceinline__ uint32_t bytes_nonzero(uint32_t x) {
 // Template parameters: estimator (one recurrence, at most three input
 // streams, or Retrace's five with 32 environments per block: the LDS holds
 // two chunks of them), OPT as for the other kernels, EB environments per
-// block.
-// Float32 storage; E a multiple of EB, T of 64, every per-step array 16-byte
-// aligned, 64 * E * 4 < 2^31 (checked by the launcher).  Block b:
-// environments EB b .. EB b + EB - 1.
-template <class Est, int OPT, int EB>
+// block, S the storage format (16-bit values are widened to float32 on the
+// way into LDS and rounded back, to nearest even, on the way out).  E a
+// multiple of EB, T of 64, every per-step array 16-byte aligned,
+// 64 * E * 4 < 2^31 (checked by the launcher).  Block b: environments
+// EB b .. EB b + EB - 1.
+template <class Est, int OPT, int EB, class S = F32S>
 __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
   constexpr int L = 16, K = 4, SPAN = kTiChunk;
@@ -90,7 +91,9 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
   static_assert(EB == 64 || EB == 32, "blocks of 64 or 32 environments");
   constexpr int NSL = kTiSlots, NFL = NSL + 1;
   constexpr int NC = ti_compute<EB>(), NLD = ti_loaders<EB>(), FROW = ti_flag_row<EB>();
-  constexpr int LPR = EB / 4;      // lanes per step of a 16-byte access
+  constexpr int ES = __is_same(S, F32S) ? 4 : 2;  // bytes per stored value
+  constexpr int LB = 4 * ES;       // bytes per lane access of values (4 environments)
+  constexpr int LPR = EB / 4;      // lanes per step of a value access
   constexpr int SPI = 64 / LPR;    // steps per loader instruction
 
   // streams (then outputs) of NSL chunks: [slot][stream][environment][step]
@@ -126,20 +129,20 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
     // lane / LPR, environments 4 (lane % LPR) .. + 3
     const int scol = 4 * (lane % LPR);
     auto dstep = [&](int q) { return SPI * (lw + NLD * q) + lane / LPR; };
-    auto doff = [&](int q) { return (uint32_t)(((int64_t)dstep(q) * E + scol) * 4); };
+    auto doff = [&](int q) { return (uint32_t)(((int64_t)dstep(q) * E + scol) * ES); };
     // flags: steps 4 fword .. + 3, environments 4 (lane % LPR) .. + 3, one
     // 4-byte access per step and array
     const int fword = (16 / NLD) * lw + lane / LPR;
     auto foff = [&](int m) { return (uint32_t)((int64_t)(4 * fword + m) * E + scol); };
 
-    typedef u32x4 Chunk[NS][4];
+    typedef typename RawOf<LB>::T Chunk[NS][4];
     typedef uint32_t Flags[2][4];
     auto issue_data = [&](int s, Chunk& x) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const __amdgpu_buffer_rsrc_t rs = chunk_rs(srcs[st], s, 4);
+        const __amdgpu_buffer_rsrc_t rs = chunk_rs(srcs[st], s, ES);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) x[st][q] = raw_buffer_load<16>(rs, doff(q));
+        for (int q = 0; q < 4; ++q) x[st][q] = raw_buffer_load<LB>(rs, doff(q));
       }
     };
     auto write_data = [&](int s, const Chunk& x) {
@@ -147,12 +150,12 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
       for (int st = 0; st < NS; ++st)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4 f = __builtin_bit_cast(f32x4, x[st][q]);
+          float f[4];
+          if constexpr (LB == 16) unpack16<S, 4>(x[st][q], f);
+          else unpack8<S, 4>(x[st][q], f);
           const int t = dstep(q);
-          s_d[dslot(s)][st][scol + 0][t] = f.x;
-          s_d[dslot(s)][st][scol + 1][t] = f.y;
-          s_d[dslot(s)][st][scol + 2][t] = f.z;
-          s_d[dslot(s)][st][scol + 3][t] = f.w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s_d[dslot(s)][st][scol + j][t] = f[j];
         }
     };
     auto issue_flags = [&](int s, Flags& f) {
@@ -184,13 +187,15 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
     auto store_out = [&](int s) {
 #pragma unroll
       for (int o = 0; o < NOUT; ++o) {
-        const __amdgpu_buffer_rsrc_t rs = chunk_rs(dsts[o], s, 4);
+        const __amdgpu_buffer_rsrc_t rs = chunk_rs(dsts[o], s, ES);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int t = dstep(q);
-          const f32x4 f = {s_d[dslot(s)][o][scol + 0][t], s_d[dslot(s)][o][scol + 1][t],
-                           s_d[dslot(s)][o][scol + 2][t], s_d[dslot(s)][o][scol + 3][t]};
-          raw_buffer_store<16>(__builtin_bit_cast(u32x4, f), rs, doff(q));
+          float f[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) f[j] = s_d[dslot(s)][o][scol + j][t];
+          if constexpr (LB == 16) raw_buffer_store<16>(__builtin_bit_cast(u32x4, (f32x4){f[0], f[1], f[2], f[3]}), rs, doff(q));
+          else raw_buffer_store<8>(pack8<S, 4>(f), rs, doff(q));
         }
       }
     };
@@ -244,7 +249,9 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
                          p.has_tboot != 0};
     const unsigned tmask = p.has_term ? ~0u : 0u;
     const unsigned rmask = p.has_trunc ? ~0u : 0u;
-    constexpr bool FAST = Tr::kRetrace;
+    // 16-bit formats: the fast Retrace quotient and V-trace exp, as in the
+    // other kernels of those formats
+    constexpr bool FAST = Tr::kRetrace || !__is_same(S, F32S);
 
     int col[2];     // environment offset inside the block, per item
     float rowv[2];  // bootstrap value / init of the environment
@@ -253,7 +260,7 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       col[it] = 8 * c + 4 * it + team;
-      rowv[it] = p.has_row ? __builtin_nontemporal_load(p.row + e0 + col[it]) : 0.0f;
+      rowv[it] = p.has_row ? load1<S>(p.row, e0, (uint32_t)col[it]) : 0.0f;
       C[it] = 0.0;
       if constexpr (!Tr::kBackwardRl) C[it] = p.has_row ? (double)rowv[it] : 0.0;
       carry[it] = PredIn{0.0f, 0.0, 0u};
@@ -281,15 +288,18 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
         for (int m = 0; m < K; ++m) o.boot[it][m] = 0.0f;
       }
       if constexpr (GATHER_TB) {
-        const __amdgpu_buffer_rsrc_t rs = chunk_rs(p.tboot, s, 4);
+        const __amdgpu_buffer_rsrc_t rs = chunk_rs(p.tboot, s, ES);
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
           const unsigned need = p.has_tboot ? (o.rb[it] & ~o.tb[it]) : 0u;
 #pragma unroll
           for (int m = 0; m < K; ++m) {
-            const uint32_t off = (uint32_t)(((int64_t)(cs_local + m) * E + col[it]) * 4);
-            o.boot[it][m] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((need >> m) & 1u) ? off : kDuoOff, 0, 2));
+            const uint32_t off = (uint32_t)(((int64_t)(cs_local + m) * E + col[it]) * ES);
+            const uint32_t at = ((need >> m) & 1u) ? off : kDuoOff;
+            if constexpr (ES == 4)
+              o.boot[it][m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, at, 0, 2));
+            else
+              o.boot[it][m] = s_to_f32<S>(__builtin_amdgcn_raw_buffer_load_b16(rs, at, 0, 2));
           }
         }
       }

@@ -123,6 +123,20 @@ def test_time_major_item_form(E, T, p):
         check_storage(name, d, "float32", time_major=True)
 
 
+# The item form with 16-bit storage (values widened on the way into LDS and
+# rounded to nearest even on the way out): both block sizes, one and several
+# chunks, dense flags, and 16384 x 256 (the item form for discounted returns,
+# TD(lambda) and GAE there, the other kernel for the rest).
+@pytest.mark.parametrize("fmt", ("bfloat16", "float16"))
+@pytest.mark.parametrize("E,T,p", [(64, 64, 0.01), (96, 128, 0.3), (256, 320, 0.01), (4096, 256, 0.01),
+                                   (16384, 256, 0.01), (16384, 384, 0.01)])
+def test_time_major_item_form_16bit(fmt, E, T, p):
+    _say("time-major item form %s E=%d T=%d p=%g" % (fmt, E, T, p))
+    d = synth.draw(E, T, seed=91 + E + T, p_term=p, p_trunc=p)
+    for name in SEVEN:
+        check_storage(name, d, fmt, time_major=True)
+
+
 @pytest.mark.parametrize("variant", [dict(term=False, trunc=False), dict(boot=False, tboot=False),
                                      dict(trunc=False), dict(term=False), dict(tboot=False)])
 def test_time_major_item_form_optional_inputs(variant):
