@@ -213,6 +213,20 @@ __device__ __forceinline__ double group_last_f64(double v, int lane) {
   }
 }
 
+// Column group of block b of n, for kernels whose neighbouring column groups
+// share 128-byte lines of the flag arrays (R groups per line: a flag row of a
+// group is 128 / R bytes).  Blocks go to the 8 XCDs of the chip round-robin,
+// and each XCD has its own L2, so groups g and g + 1 on different XCDs each
+// fetch their shared lines from HBM; here the R groups of a line go to the
+// same XCD.  Bijective on [0, n): blocks past the last whole set of 8 R keep
+// their own group.
+__device__ __forceinline__ int64_t xcd_group(int64_t b, int64_t n, int R) {
+  const int64_t span = 8 * (int64_t)R;
+  if (b >= n / span * span) return b;
+  const int64_t x = b % 8, i = b / 8;
+  return span * (i / R) + R * x + i % R;
+}
+
 // ----------------------------------------------------------------- streaming loads / stores
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -580,13 +580,18 @@ constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 // returns 12.5 us with 64, 16.4 with 32; 4096 x 256: 10.1 with 64, 8.9 with
 // 32).  Routing, from a sweep of 1024 to 32768 environments and 64 to 2048
 // steps (float32, one MI355X):
-//  * columns of exactly one super-tile of tm_kernel, with 64-environment
-//    blocks, stay there: it has every load of such a column in flight at once
-//    (float32 16384 x 256: discounted returns 12.2 against 12.4 us, TD(lambda)
-//    14.5 against 15.2; V-trace at 128 steps 12.5 against 13.0), except the
-//    16-bit discounted returns, TD(lambda) and GAE (bfloat16 16384 x 256:
-//    14.0 -> 12.8 us, 15.6 -> 13.9, 15.6 -> 14.1; traces there 9.4 against
-//    10.3 in the item form);
+//  * at columns of exactly one super-tile of tm_kernel (256 steps, 128 for
+//    V-trace), with 64-environment blocks, tm_kernel has every load of a
+//    column in flight at once and the two are close; each estimator and
+//    format takes the faster at 16384 and 32768 environments: V-trace, float32
+//    TD(lambda) and GAE, 16-bit traces and prefix sums stay with tm_kernel
+//    (V-trace 16384 x 128: 12.3 against 12.5 us; TD(lambda) 32768 x 256: 26.4
+//    against 27.1; bfloat16 traces 16384 x 256: 8.7 against 9.5), float32
+//    discounted returns, traces and prefix sums and 16-bit discounted
+//    returns, TD(lambda) and GAE take the item form (32768 x 256: float32
+//    discounted returns 22.1 -> 19.8, traces 19.2 -> 17.8; bfloat16
+//    TD(lambda) 16384 x 256 15.6 -> 13.0 before both kernels mapped blocks
+//    to XCDs by flag lines, about even after);
 //  * a block walks its columns' chunks one after another, so long columns
 //    over few blocks go to the segmented path: the item form takes columns of
 //    up to 16 chunks, or any length with at least half as many blocks as CUs
@@ -616,8 +621,10 @@ inline int tm_item_envs(const KernelArgs& a, int cus) {
   if (wide && Tr::kStreams > 3) return 0;
   const int eb = wide ? 64 : 32;
   if (a.E % eb != 0) return 0;
-  const bool bwd16 = !__is_same(S, F32S) && Tr::kBackwardRl && Tr::kStreams <= 2;
-  if (eb == 64 && a.T == (int64_t)tm_waves<Est>() * tm_chunk<Est>() && !bwd16) return 0;
+  // one super-tile of tm_kernel: the faster kernel measured per estimator and format
+  const bool keep_tm = Tr::kStreams == 3 || (__is_same(S, F32S) ? Tr::kBackwardRl && Tr::kStreams == 2
+                                                                 : !Tr::kBackwardRl);
+  if (eb == 64 && a.T == (int64_t)tm_waves<Est>() * tm_chunk<Est>() && keep_tm) return 0;
   if (a.T / kTiChunk > 16 && 2 * (a.E / eb) < cus) return 0;
   return eb;
 }

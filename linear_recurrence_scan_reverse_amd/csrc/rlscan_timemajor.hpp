@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(64 * W) tm_kernel(const KernelArgs p, int64_t 
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t E = p.E, T = p.T;
   const int64_t ngroups = (E + 63) / 64;
-  const int64_t grp = MODE == 0 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x % ngroups;
+  const int64_t grp = MODE == 0 ? xcd_group(blockIdx.x, ngroups, 2) : (int64_t)blockIdx.x % ngroups;
   const int64_t sidx = MODE == 0 ? 0 : (int64_t)blockIdx.x / ngroups;
   // this block's steps [t0, t1)
   const int64_t t0 = MODE == 0 ? 0 : seg_begin(sidx, seg_len);

@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
   const int lane = threadIdx.x & 63;
   const int64_t E = p.E, T = p.T;
   const int ticks = (int)(T / SPAN);
-  const int64_t e0 = (int64_t)blockIdx.x * EB;
+  const int64_t e0 = xcd_group(blockIdx.x, gridDim.x, 128 / EB) * EB;
   // resource over chunk s of an [T, E] array of esz-byte elements, from the
   // block's first environment; no records for s outside [0, ticks)
   auto chunk_rs = [&](const void* base, int s, int esz) {

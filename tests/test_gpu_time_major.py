@@ -107,12 +107,13 @@ def test_time_major_exact_integer_sums():
 # environments staged in LDS and scanned as rows; whole chunks, 16-byte
 # aligned arrays, one launch): one chunk, odd and even chunk counts, blocks of
 # 32 environments (fewer than 16384; 96 is no multiple of 64) and of 64
-# (16384 at 64, 384 and 512 steps, not 256: one super-tile of the other
-# kernel), 4096 x 1088 (columns of 17 chunks, taken since the blocks are half
+# (16384 at 64, 256, 384 and 512 steps; at 256, one super-tile of the other
+# kernel, only discounted returns, traces and prefix sums take the item
+# form), 4096 x 1088 (columns of 17 chunks, taken since the blocks are half
 # as many as the CUs); dense flags; no episode ends (every row's carry
 # crosses every chunk).
 @pytest.mark.parametrize("E,T", [(64, 64), (96, 128), (128, 192), (192, 448), (256, 320), (1024, 128), (4096, 256),
-                                 (4096, 1088), (16384, 64), (16384, 384), (16384, 512)])
+                                 (4096, 1088), (16384, 64), (16384, 256), (16384, 384), (16384, 512)])
 @pytest.mark.parametrize("p", [0.0, 0.01, 0.3])
 def test_time_major_item_form(E, T, p):
     if p != 0.01 and E * T > (1 << 20):
