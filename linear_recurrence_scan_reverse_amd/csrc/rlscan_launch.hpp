@@ -369,10 +369,18 @@ inline int duo_form(const KernelArgs& a) {
 //    rows of 128 up to 4096 rows (Retrace 5.0 -> 4.3; discounted returns
 //    6.2 -> 4.4), and discounted returns, traces and prefix sums with rows
 //    of 256 up to 4096 rows (4.7 -> 4.2); slower with 256 steps from 16384
-//    rows (TD(lambda) 8.8 -> 9.6).
+//    rows (TD(lambda) 8.8 -> 9.6);
+//  * four items per wave as a software pipeline (multi_reg_kernel) for rows
+//    of 512 steps from 16384 rows: traces and prefix sums (16384 x 512: 11.4
+//    -> 10.1; 32768 x 512: 19.5 -> 18.0), TD(lambda) and GAE below 32768
+//    rows (16384 x 512: 15.2 -> 14.2; even at 32768) -- the rows of the
+//    float32 rule for TD(lambda) and GAE, at half the bytes per step; at
+//    256 steps and below it was even or slower (TD(lambda) 4096 x 256: 4.7
+//    -> 6.0).
 struct Duo16 {
-  int L;   // team width (0: not taken)
-  int lb;  // bytes per lane and array
+  int L;     // team width (0: not taken)
+  int lb;    // bytes per lane and array
+  int form;  // kDuoReg or kDuoReg4
 };
 template <class Est>
 inline Duo16 duo_form_16(const KernelArgs& a) {
@@ -381,14 +389,17 @@ inline Duo16 duo_form_16(const KernelArgs& a) {
                          __is_same(Est, EpisodicPrefixSum);
   int lb = 16;
   if ((T == 64 && E >= 16384) || (T == 128 && E <= 4096) || (T == 256 && E <= 4096 && light)) lb = 8;
-  else if (T != 128 && T != 256 && T != 512) return Duo16{0, 0};
+  else if (T != 128 && T != 256 && T != 512) return Duo16{0, 0, 0};
   const int L = (int)(T * 2 / lb);
   const int64_t items = (E + (64 / L) - 1) / (64 / L);
-  if ((items + 7) / 8 * 256 > kMaxWorkItems) return Duo16{0, 0};
-  if (!vector_ok(a, lb / 2, (int)T, 2)) return Duo16{0, 0};
+  if ((items + 7) / 8 * 256 > kMaxWorkItems) return Duo16{0, 0, 0};
+  if (!vector_ok(a, lb / 2, (int)T, 2)) return Duo16{0, 0, 0};
   if (lb == 16 && (__is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum)) && E <= 4096 && T == 256)
-    return Duo16{0, 0};
-  return Duo16{L, lb};
+    return Duo16{0, 0, 0};
+  constexpr bool fwd = __is_same(Est, EligibilityTrace) || __is_same(Est, EpisodicPrefixSum);
+  constexpr bool td = __is_same(Est, TdLambda) || __is_same(Est, Gae);
+  const bool four = T == 512 && E >= 16384 && (fwd || (td && E < 32768));
+  return Duo16{L, lb, four ? kDuoReg4 : kDuoReg};
 }
 
 template <class Est, int L, int OPT, class S = F32S>
@@ -404,10 +415,10 @@ inline hipError_t launch_duo_opt(const KernelArgs& a, hipStream_t s, int form) {
   if constexpr (__is_same(S, F32S)) {
     if (form == kDuoLds) k = reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT>);
     if (form == kDuoLds4) k = reinterpret_cast<const void*>(&duo_kernel<Est, L, OPT, S, 4>);
-    if (form == kDuoReg4) {
-      k = reinterpret_cast<const void*>(&multi_reg_kernel<Est, L, OPT, S, 4>);
-      per_block = 16;
-    }
+  }
+  if (form == kDuoReg4) {
+    k = reinterpret_cast<const void*>(&multi_reg_kernel<Est, L, OPT, S, 4>);
+    per_block = 16;
   }
   return hipLaunchKernel(k, dim3((unsigned)((items + per_block - 1) / per_block)), dim3(256), params, 0, s);
 }
@@ -520,10 +531,11 @@ hipError_t launch_typed(const KernelArgs& in, hipStream_t s) {
   const KernelArgs a = resolve_optional(in);
   if (const SegPlan plan = segment_plan(a); plan.len) return launch_segmented<Est, S>(a, s, plan);
   if constexpr (!Traits<Est>::kDual && !Traits<Est>::kLinear) {
-    switch (duo_form_16<Est>(a).L) {
-      case 16: return launch_duo<Est, 16, S>(a, s, kDuoReg);
-      case 32: return launch_duo<Est, 32, S>(a, s, kDuoReg);
-      case 64: return launch_duo<Est, 64, S>(a, s, kDuoReg);
+    const Duo16 f = duo_form_16<Est>(a);
+    switch (f.L) {
+      case 16: return launch_duo<Est, 16, S>(a, s, f.form);
+      case 32: return launch_duo<Est, 32, S>(a, s, f.form);
+      case 64: return launch_duo<Est, 64, S>(a, s, f.form);
       default: break;
     }
   }

@@ -113,14 +113,15 @@ def test_float16_overflow_gives_inf():
 
 @pytest.mark.parametrize("fmt", ["bfloat16", "float16"])
 @pytest.mark.parametrize("E,T", [(1, 512), (5, 128), (9, 256), (1001, 512), (4099, 128), (16385, 256), (1001, 256),
-                                 (16385, 64), (32768, 64), (3, 64)])
+                                 (16385, 64), (32768, 64), (3, 64), (16387, 512)])
 def test_storage16_two_items_per_wave(fmt, E, T):
     # rows of 64-512 steps with aligned arrays: the kernel that gives each wave
     # two items held in registers, 16 bytes per lane and array (rows of
     # 128-512 steps) or 8 (rows of 64 from 16384 rows, of 128 up to 4096 rows,
     # of 256 up to 4096 rows for the light estimators), where the launcher
-    # routes them there; row counts leave the last block with waves that have
-    # no second item and the last item with fewer rows
+    # routes them there, or four items per wave (rows of 512 from 16384 rows:
+    # traces, prefix sums, TD(lambda), GAE); row counts leave the last block
+    # with waves that have no second item and the last item with fewer rows
     _say("16-bit storage two items per wave %s E=%d T=%d" % (fmt, E, T))
     d = synth.draw(E, T, seed=74 + E % 7, p_term=0.01, p_trunc=0.01)
     for name in SEVEN:
