@@ -213,9 +213,10 @@ def test_segmented_generic_scan_long_rows_and_exact_sums():
 
 def test_graph_capture_of_formats_layouts_and_long_rows():
     # a captured HIP graph holding a time-major bfloat16 call, a row-major
-    # float16 call and a segmented long-row call (three kernels), replayed
-    # several times with the program's own work between replays: every replay
-    # matches the eager result bit for bit
+    # float16 call, a segmented long-row call and a time-major float32 call in
+    # the item form (six kernels), replayed several times with the program's
+    # own work between replays: every replay matches the eager result bit for
+    # bit
     import torch
     import linear_recurrence_scan_reverse_amd as rl
     from tests.estimators import storage_inputs
@@ -224,6 +225,8 @@ def test_graph_capture_of_formats_layouts_and_long_rows():
     _, hf = storage_inputs(d1, "float16")
     d2 = synth.draw(2, 40000, seed=29, p_term=0.001, p_trunc=0.001)
     lr = to_dev(d2)
+    d3 = synth.draw(256, 320, seed=30, p_term=0.01, p_trunc=0.01)
+    _, ti = storage_inputs(d3, "float32", time_major=True)
 
     def calls(outs):
         rl.gae(tm["r"], tm["v"], tm["terminated"], tm["truncated"], tm["bootstrap_value"], tm["trunc_bootstrap"],
@@ -232,10 +235,12 @@ def test_graph_capture_of_formats_layouts_and_long_rows():
                    hf["bootstrap_value"], hf["trunc_bootstrap"], out=outs[2])
         rl.discounted_returns(lr["r"], lr["terminated"], lr["truncated"], lr["bootstrap_value"],
                               lr["trunc_bootstrap"], out=outs[3])
+        rl.vtrace(ti["r"], ti["v"], ti["log_rhos"], ti["terminated"], ti["truncated"], ti["bootstrap_value"],
+                  ti["trunc_bootstrap"], time_major=True, vs=outs[4], pg_advantages=outs[5])
 
     def fresh():
         return [torch.empty_like(tm["r"]), torch.empty_like(tm["r"]), torch.empty_like(hf["r"]),
-                torch.empty_like(lr["r"])]
+                torch.empty_like(lr["r"]), torch.empty_like(ti["r"]), torch.empty_like(ti["r"])]
 
     eager = fresh()
     calls(eager)
@@ -265,9 +270,9 @@ def test_concurrent_host_threads():
 
     import torch
     from tests.estimators import storage_inputs
-    d = synth.draw(700, 256, seed=31, p_term=0.01, p_trunc=0.01)
+    d = synth.draw(704, 256, seed=31, p_term=0.01, p_trunc=0.01)
     jobs = [("gae", "float32", False), ("retrace", "float32", False), ("vtrace", "bfloat16", False),
-            ("td_lambda", "float16", True)]
+            ("td_lambda", "float16", True)]  # the last in the time-major item form (704 = 22 x 32)
     inputs = [storage_inputs(d, fmt, time_major=tm)[1] for _, fmt, tm in jobs]
 
     def raw(outs):
