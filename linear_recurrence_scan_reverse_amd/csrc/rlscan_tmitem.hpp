@@ -10,14 +10,16 @@
 // all its waves' loads have landed, and at 16384 environments (one block per
 // CU) loads and compute never overlap.  Here a block owns 64 or 32
 // environments and walks their time chunk by chunk, one chunk per tick, with
-// the loads running two chunks ahead of the compute.  Every environment's whole time range stays
-// with one compute wave, so no wave waits for another's result; the waves of
-// a block meet once per tick, at a barrier.
+// the loads of the next three chunks in flight while one is scanned.  Every
+// environment's whole time range stays with one compute wave, so no wave
+// waits for another's result; the waves of a block meet once per tick, at a
+// barrier.
 //
 // Tick s (chunks in scan order; backward estimators walk time from the end):
-//   loaders  request chunk s+2's streams and chunk s+3's flags, store the
-//            outputs of chunk s-1 (read back from LDS), write chunk s+1's
-//            streams and chunk s+2's flags (requested a tick earlier) to LDS;
+//   loaders  store the outputs of chunk s-1 (read back from LDS), write chunk
+//            s+1's streams and chunk s+2's flags (requested two ticks earlier)
+//            to LDS and request chunk s+3's streams and s+4's flags into the
+//            registers those left;
 //   compute  read chunk s+1's flags and request its truncation bootstraps,
 //            scan chunk s (its flags and bootstraps taken a tick earlier) and
 //            write its outputs over its streams in LDS.
@@ -94,6 +96,11 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
   constexpr int ES = __is_same(S, F32S) ? 4 : 2;  // bytes per stored value
   constexpr int LB = 4 * ES;       // bytes per lane access of values (4 environments)
   constexpr int LPR = EB / 4;      // lanes per step of a value access
+  // chunks of loads in flight in a loader's registers; against one (chunk
+  // s+2 requested in tick s, written in tick s+1), two gave bfloat16
+  // TD(lambda) 16384 x 256 16.4 -> 13.5 us, float32 discounted returns 13.5
+  // -> 11.0; three needed twice the registers and was slower
+  constexpr int PD = 2;
   constexpr int SPI = 64 / LPR;    // steps per loader instruction
 
   // streams (then outputs) of NSL chunks: [slot][stream][environment][step]
@@ -203,39 +210,46 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
       lds_done();
       tick_barrier();
     };
-    // one tick; X/F: the register sets written this tick (requested a tick
-    // earlier), Y/G: the ones requested now.  The streams of chunk s+NSL-1 go
-    // to the slot chunk s-1's outputs leave.
-    auto tick = [&](int s, Chunk& X, Chunk& Y, Flags& F, Flags& G) {
-      issue_data(s + NSL, Y);
-      issue_flags(s + NSL + 1, G);
-      asm volatile("" ::: "memory");
+    // Register sets in flight: chunk k's streams and flags sit in set k % PD
+    // from their request until written to LDS.  Tick s writes chunk s+1's
+    // streams (into the slot chunk s-1's outputs just left) and chunk s+2's
+    // flags, and requests chunk s+1+PD's and s+2+PD's into the sets those
+    // free, so PD chunks of loads are in flight behind the one being scanned.
+    auto tick = [&](int s, Chunk& X, Flags& F) {
       store_out(s - 1);
-      write_data(s + NSL - 1, X);
-      write_flags(s + NSL, F);
+      write_data(s + 1, X);
+      issue_data(s + 1 + PD, X);
+      write_flags(s + 2, F);
+      issue_flags(s + 2 + PD, F);
       loaded();
     };
 
-    Chunk x[NSL];
-    Flags f[NFL];
-    // before the first tick: the streams of chunks 0 .. NSL-1 and the flags of
-    // chunks 0 .. NSL requested at once; all but the last of each in LDS
+    Chunk x[PD];
+    Flags f[PD];
+    // before the first tick: the streams and flags of chunks 0 .. PD-1
+    // requested at once; chunk 0's streams and chunks 0 and 1's flags in LDS
+    // (their sets refilled with chunks PD and PD+1)
 #pragma unroll
-    for (int k = 0; k < NFL; ++k) issue_flags(k, f[k]);
+    for (int k = 0; k < PD; ++k) issue_flags(k, f[k]);
 #pragma unroll
-    for (int k = 0; k < NSL; ++k) issue_data(k, x[k]);
+    for (int k = 0; k < PD; ++k) issue_data(k, x[k]);
     asm volatile("" ::: "memory");
-#pragma unroll
-    for (int k = 0; k < NSL; ++k) write_flags(k, f[k]);
-#pragma unroll
-    for (int k = 0; k + 1 < NSL; ++k) write_data(k, x[k]);
+    write_flags(0, f[0]);
+    issue_flags(PD, f[0]);
+    write_flags(1, f[1]);
+    issue_flags(PD + 1, f[1]);
+    write_data(0, x[0]);
+    issue_data(PD, x[0]);
     loaded();
-    // from here two register sets of each kind take turns
-    tick(0, x[NSL - 1], x[0], f[NSL], f[0]);
-    for (int s = 1; s < ticks; s += 2) {
-      tick(s, x[0], x[NSL - 1], f[0], f[NSL]);
-      if (s + 1 < ticks) tick(s + 1, x[NSL - 1], x[0], f[NSL], f[0]);
+    // whole rounds of PD ticks (static set indices), then the rest
+    int base = 0;
+    for (; base + PD <= ticks; base += PD) {
+#pragma unroll
+      for (int k = 0; k < PD; ++k) tick(base + k, x[(k + 1) % PD], f[(k + 2) % PD]);
     }
+#pragma unroll
+    for (int k = 0; k + 1 < PD; ++k)
+      if (base + k < ticks) tick(base + k, x[(k + 1) % PD], f[(k + 2) % PD]);
     store_out(ticks - 1);
   } else {
     // ================================================================ compute
