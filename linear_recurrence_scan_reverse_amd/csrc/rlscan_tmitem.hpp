@@ -97,9 +97,11 @@ __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelA
   constexpr int LB = 4 * ES;       // bytes per lane access of values (4 environments)
   constexpr int LPR = EB / 4;      // lanes per step of a value access
   // chunks of loads in flight in a loader's registers; against one (chunk
-  // s+2 requested in tick s, written in tick s+1), two gave bfloat16
-  // TD(lambda) 16384 x 256 16.4 -> 13.5 us, float32 discounted returns 13.5
-  // -> 11.0; three needed twice the registers and was slower
+  // s+2 requested in tick s, written in tick s+1), two gave float32 4096 x 512
+  // TD(lambda) 14.3 -> 13.2 us, 16384 x 512 discounted returns 19.7 -> 18.5,
+  // bfloat16 4096 x 256 V-trace 12.4 -> 11.5 (bfloat16 V-trace from 16384
+  // environments 2-4% slower); three or four needed more registers than the
+  // block allows and spilled
   constexpr int PD = 2;
   constexpr int SPI = 64 / LPR;    // steps per loader instruction
 
