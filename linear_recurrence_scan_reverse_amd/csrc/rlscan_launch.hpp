@@ -626,8 +626,11 @@ template <class Est, class S>
 inline int tm_item_envs(const KernelArgs& a, int cus) {
   using Tr = Traits<Est>;
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  if (a.T % kTiChunk != 0 || a.E >= ((int64_t)1 << 23) || !al(a.r) || !al(a.v) || !al(a.aux) || !al(a.term) ||
-      !al(a.trunc) || !al(a.out0) || !al(a.out1))
+  // (at least one chunk: the loader and compute waves meet at the same count of
+  // barriers only when the column has a first chunk)
+  if (a.T < kTiChunk || a.T % kTiChunk != 0 || a.E < 1 || a.E >= ((int64_t)1 << 23))
+    return 0;
+  if (!al(a.r) || !al(a.v) || !al(a.aux) || !al(a.term) || !al(a.trunc) || !al(a.out0) || !al(a.out1))
     return 0;
   const bool wide = (a.E + 63) / 64 >= cus;  // a 64-environment column group per CU at least
   if (wide && Tr::kStreams > 3) return 0;

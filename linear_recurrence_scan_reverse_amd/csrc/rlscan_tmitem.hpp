@@ -75,8 +75,8 @@ __device__ __forceinline__ uint32_t bytes_nonzero(uint32_t x) {
 // two chunks of them), OPT as for the other kernels, EB environments per
 // block, S the storage format (16-bit values are widened to float32 on the
 // way into LDS and rounded back, to nearest even, on the way out).  E a
-// multiple of EB, T of 64, every per-step array 16-byte aligned,
-// 64 * E * 4 < 2^31 (checked by the launcher).  Block b: environments
+// positive multiple of EB, T a positive multiple of 64, every per-step array
+// 16-byte aligned, 64 * E * 4 < 2^31 (checked by the launcher).  Block b: environments
 // EB b .. EB b + EB - 1.
 template <class Est, int OPT, int EB, class S = F32S>
 __global__ void __launch_bounds__(ti_threads<EB>()) tm_item_kernel(const KernelArgs p) {
