@@ -626,22 +626,13 @@ template <class Est, class S>
 inline int tm_item_envs(const KernelArgs& a, int cus) {
   using Tr = Traits<Est>;
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  // (at least one chunk: the loader and compute waves meet at the same count of
-  // barriers only when the column has a first chunk)
-  if (a.T < kTiChunk || a.T % kTiChunk != 0 || a.E < 1 || a.E >= ((int64_t)1 << 23))
-    return 0;
   if (!al(a.r) || !al(a.v) || !al(a.aux) || !al(a.term) || !al(a.trunc) || !al(a.out0) || !al(a.out1))
     return 0;
-  const bool wide = (a.E + 63) / 64 >= cus;  // a 64-environment column group per CU at least
-  if (wide && Tr::kStreams > 3) return 0;
-  const int eb = wide ? 64 : 32;
-  if (a.E % eb != 0) return 0;
   // one super-tile of tm_kernel: the faster kernel measured per estimator and format
-  const bool keep_tm = Tr::kStreams == 3 || (__is_same(S, F32S) ? Tr::kBackwardRl && Tr::kStreams == 2
-                                                                 : !Tr::kBackwardRl);
-  if (eb == 64 && a.T == (int64_t)tm_waves<Est>() * tm_chunk<Est>() && keep_tm) return 0;
-  if (a.T / kTiChunk > 16 && 2 * (a.E / eb) < cus) return 0;
-  return eb;
+  constexpr bool keep_tm = Tr::kStreams == 3 || (__is_same(S, F32S) ? Tr::kBackwardRl && Tr::kStreams == 2
+                                                                     : !Tr::kBackwardRl);
+  static_assert(kTiChunkSteps == kTiChunk, "one chunk size");
+  return tm_item_block_envs(a.E, a.T, cus, Tr::kStreams, (int64_t)tm_waves<Est>() * tm_chunk<Est>(), keep_tm);
 }
 
 template <class Est, int OPT, class S>

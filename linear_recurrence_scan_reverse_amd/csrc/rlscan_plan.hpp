@@ -78,6 +78,31 @@ inline SegPlan tm_segments(int64_t E, int64_t T, int64_t cus) {
   return SegPlan{len, nseg};
 }
 
+// ----------------------------------------------------------------- time-major item form
+// Shape part of the item form's routing (tm_item_envs in rlscan_launch.hpp
+// adds the pointer alignment and takes the measured rules from there):
+// environments per block, 64 or 32, or 0 where the other time-major kernels
+// take the call.  A routed shape always has at least one whole 64-step chunk
+// and whole blocks, which is what keeps the item kernel's loader and compute
+// waves at equal barrier counts, and 64 * E * 4 < 2^31, so chunk resources
+// and the out-of-range offset 2^31 stay apart.
+//   streams: input streams of the estimator (5: Retrace, 32-environment blocks
+//            only); supertile: the steps of one super-tile of tm_kernel;
+//   keep_tm: tm_kernel measured faster at exactly one super-tile.
+constexpr int64_t kTiChunkSteps = 64;
+constexpr int64_t kTiMaxE = (int64_t)1 << 23;
+inline int tm_item_block_envs(int64_t E, int64_t T, int64_t cus, int streams, int64_t supertile, bool keep_tm) {
+  if (T < kTiChunkSteps || T % kTiChunkSteps != 0 || E < 1 || E >= kTiMaxE || cus < 1) return 0;
+  const bool wide = (E + 63) / 64 >= cus;  // a 64-environment column group per CU at least
+  if (wide && streams > 3) return 0;
+  const int eb = wide ? 64 : 32;
+  if (E % eb != 0) return 0;
+  if (eb == 64 && T == supertile && keep_tm) return 0;
+  const int64_t chunks = T / kTiChunkSteps, blocks = E / eb;
+  if (chunks > 16 && 2 * blocks < cus) return 0;
+  return eb;
+}
+
 // ----------------------------------------------------------------- grid limits
 // A launch keeps its grid at or below 2^32 - 1 work-items.  The C ABI refuses
 // the shapes past these limits (RLSCAN_ERR_SHAPE) before any HIP call.

@@ -1,4 +1,5 @@
-// Host-only check of the segment plans and grid limits in rlscan_plan.hpp
+// Host-only check of the segment plans, the time-major item form's shape rule
+// and the grid limits in rlscan_plan.hpp
 // (compiled with a plain C++ compiler by tests/test_plan.py; no GPU).
 //
 // For every plan the launcher can make, each segment must hold at least the
@@ -115,6 +116,27 @@ static bool check_limits() {
   return true;
 }
 
+// The time-major item form: a routed shape has whole blocks and at least one
+// whole chunk (the kernel's loader and compute waves each meet 1 + T / 64
+// barriers, the compute side running its first chunk unconditionally), chunk
+// resources below the 2^31 out-of-range offset, five-stream calls in
+// 32-environment blocks only, and a grid within 2^32 - 1 work-items.
+static bool check_item(int64_t E, int64_t T, int64_t cus, int streams, bool keep_tm) {
+  ++g_checked;
+  const int64_t supertile = streams >= 3 ? 128 : 256;
+  const int eb = tm_item_block_envs(E, T, cus, streams, supertile, keep_tm);
+  if (eb == 0) return true;
+  if (eb != 32 && eb != 64) FAIL("item E=%lld T=%lld: %d environments per block", (long long)E, (long long)T, eb);
+  if (T < kTiChunkSteps || T % kTiChunkSteps != 0)
+    FAIL("item E=%lld T=%lld: not whole chunks", (long long)E, (long long)T);
+  if (E < 1 || E % eb != 0) FAIL("item E=%lld T=%lld: not whole blocks of %d", (long long)E, (long long)T, eb);
+  if (streams > 3 && eb != 32) FAIL("item E=%lld: five streams in blocks of %d", (long long)E, eb);
+  if (kTiChunkSteps * E * 4 >= ((int64_t)1 << 31)) FAIL("item E=%lld: a chunk resource reaches 2^31", (long long)E);
+  if (E / eb * 64 * (eb / 8 + eb / 16) > kMaxWorkItems) FAIL("item E=%lld: grid too large", (long long)E);
+  if (T / kTiChunkSteps > 0x7fffffff) FAIL("item T=%lld: chunk count", (long long)T);
+  return true;
+}
+
 int main(int argc, char** argv) {
   g_ceil_rule = argc > 1 && std::strcmp(argv[1], "--ceil-rule") == 0;
   const int64_t cus_list[] = {256, 304, 80, 8, 1};
@@ -142,6 +164,18 @@ int main(int argc, char** argv) {
     for (int64_t E : {int64_t(2), int64_t(63), int64_t(64), int64_t(65), int64_t(130), int64_t(4000), int64_t(16383)})
       for (int64_t T = 1; T < 70000; T += (T < 3000 ? 1 : 97))
         if (!check_tm_plan(E, T, cus)) return 1;
+  // time-major item form: environment counts around the block sizes and the
+  // limit, step counts around chunk multiples, every stream count
+  for (int64_t cus : cus_list)
+    for (int64_t E : {int64_t(1), int64_t(31), int64_t(32), int64_t(33), int64_t(64), int64_t(96), int64_t(4096),
+                      int64_t(8192), int64_t(16320), int64_t(16384), int64_t(16416), int64_t(32768),
+                      (int64_t(1) << 23) - 64, (int64_t(1) << 23) - 32, int64_t(1) << 23, (int64_t(1) << 23) + 64})
+      for (int64_t T : {int64_t(0), int64_t(1), int64_t(63), int64_t(64), int64_t(65), int64_t(128), int64_t(256),
+                        int64_t(320), int64_t(1024), int64_t(1088), int64_t(2048), int64_t(2112), int64_t(1) << 20,
+                        (int64_t(1) << 30) - 64})
+        for (int streams : {1, 2, 3, 5})
+          for (bool keep : {false, true})
+            if (!check_item(E, T, cus, streams, keep)) return 1;
   if (!check_limits()) return 1;
   std::printf("OK %lld plans\n", g_checked);
   return 0;

@@ -8,7 +8,10 @@ from 16000 to 40000 steps, lengths k*len + r (r = -8..8) up to 2^30 - 1 steps an
 several compute-unit counts: every segment must hold at least the 8 elements
 the parked pair takes in a 16-bit format, and the segments must tile the row.
 The same checks must reject the rule the launcher used before (segment count
-rounded up), whose last segment could hold a single step.
+rounded up), whose last segment could hold a single step.  The time-major item
+form's shape rule is walked too: every shape it takes has whole 64-step chunks
+(at least one) and whole blocks, so its loader and compute waves meet the same
+number of barriers.
 """
 from __future__ import annotations
 
