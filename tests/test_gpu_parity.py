@@ -120,6 +120,21 @@ def test_vtrace_clips(rho_bar, c_bar):
     _assert_ok("vtrace", compare("vtrace", d, P), "clips")
 
 
+@pytest.mark.parametrize("rho_bar,c_bar", [(1.0, 1.0), (3.0, 0.25), (2.0, 2.0)])
+@pytest.mark.parametrize("E,T", [(16, 256), (64, 256), (2048, 128)])
+def test_vtrace_extreme_log_ratios(rho_bar, c_bar, E, T):
+    # log-ratios spread over [-90, 90]: e^l from below the float32 normals
+    # (flushed or denormal) to overflow, clipped at rho_bar / c_bar; the kernel's
+    # hardware exp2 of l log2(e) must stay within the gate (with clips far above
+    # 1 the traces grow geometrically and no float32 weight keeps it)
+    d = synth.draw(E, T, seed=15 + E, p_term=0.01, p_trunc=0.01)
+    rng = np.random.default_rng(16 + E)
+    d["log_rhos"] = rng.uniform(-90.0, 90.0, size=(E, T)).astype(np.float32)
+    d["log_rhos"][:, ::7] = rng.uniform(-3.0, 3.0, size=d["log_rhos"][:, ::7].shape).astype(np.float32)
+    P = dict(rho_bar=rho_bar, c_bar=c_bar, vtrace_lam=0.9)
+    _assert_ok("vtrace", compare("vtrace", d, P), "extreme log-ratios")
+
+
 def test_misaligned_rows_use_the_scalar_path():
     """Tensors whose storage starts one element off a 16-byte boundary."""
     import torch
