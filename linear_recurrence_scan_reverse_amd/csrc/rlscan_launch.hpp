@@ -15,6 +15,7 @@
 #include "rlscan_stream.hpp"
 #include "rlscan_timemajor.hpp"
 #include "rlscan_tmitem.hpp"
+#include "rlscan_tmdma.hpp"
 
 namespace rlscan {
 
@@ -595,15 +596,12 @@ constexpr int tm_chunk() { return Traits<Est>::kStreams >= 3 ? 8 : 16; }
 //  * at columns of exactly one super-tile of tm_kernel (256 steps, 128 for
 //    V-trace), with 64-environment blocks, tm_kernel has every load of a
 //    column in flight at once and the two are close; each estimator and
-//    format takes the faster at 16384 and 32768 environments: V-trace, float32
-//    TD(lambda) and GAE, 16-bit traces and prefix sums stay with tm_kernel
-//    (V-trace 16384 x 128: 12.3 against 12.5 us; TD(lambda) 32768 x 256: 26.4
-//    against 27.1; bfloat16 traces 16384 x 256: 8.7 against 9.5), float32
-//    discounted returns, traces and prefix sums and 16-bit discounted
-//    returns, TD(lambda) and GAE take the item form (32768 x 256: float32
-//    discounted returns 22.1 -> 19.8, traces 19.2 -> 17.8; bfloat16
-//    TD(lambda) 16384 x 256 15.6 -> 13.0 before both kernels mapped blocks
-//    to XCDs by flag lines, about even after);
+//    format takes the faster at 16384 and 32768 environments: V-trace and
+//    16-bit traces and prefix sums stay with tm_kernel (V-trace 16384 x 128:
+//    12.3 against 12.5 us; bfloat16 traces 16384 x 256: 8.7 against 9.5),
+//    the others take the item form (32768 x 256: float32 discounted returns
+//    22.1 -> 19.8, traces 19.2 -> 17.8; float32 TD(lambda) and GAE 16384 x
+//    256, from its DMA form: 13.8 / 14.1 -> 13.5 / 13.4);
 //  * a block walks its columns' chunks one after another, so long columns
 //    over few blocks go to the segmented path: the item form takes columns of
 //    up to 16 chunks, or any length with at least half as many blocks as CUs
@@ -629,10 +627,34 @@ inline int tm_item_envs(const KernelArgs& a, int cus) {
   if (!al(a.r) || !al(a.v) || !al(a.aux) || !al(a.term) || !al(a.trunc) || !al(a.out0) || !al(a.out1))
     return 0;
   // one super-tile of tm_kernel: the faster kernel measured per estimator and format
-  constexpr bool keep_tm = Tr::kStreams == 3 || (__is_same(S, F32S) ? Tr::kBackwardRl && Tr::kStreams == 2
-                                                                     : !Tr::kBackwardRl);
+  constexpr bool keep_tm = Tr::kStreams == 3 || (!__is_same(S, F32S) && !Tr::kBackwardRl);
   static_assert(kTiChunkSteps == kTiChunk, "one chunk size");
   return tm_item_block_envs(a.E, a.T, cus, Tr::kStreams, (int64_t)tm_waves<Est>() * tm_chunk<Est>(), keep_tm);
+}
+
+// Data slots of the DMA item form (tm_dma_kernel) for a kernel of 64-
+// environment blocks: the most that fit, up to four, or 0 where three do not
+// (V-trace's three float32 streams with flags, Retrace), which keep the
+// register item form.  From A/B runs on one MI355X against the register form
+// (us): bfloat16 16384 x 256 V-trace 20.2 -> 17.1, TD(lambda) 13.7 -> 12.5;
+// float32 16384 x 512 TD(lambda) 24.9 -> 22.1, traces 17.7 -> 14.1; float32
+// discounted returns and traces at 16384 x 256 even (11.0 / 9.5); six slots
+// (more chunks in flight) were slower at every shape (16384 x 512 traces
+// 16.2).  With 32-environment blocks (a CU then holds two blocks) it was
+// slower (4096 x 256 traces 6.2 -> 7.3, 4096 x 512 discounted returns 11.8 ->
+// 12.7) and they keep the register form, as do columns of fewer than four
+// chunks (one chunk: float32 32768 x 64 traces 6.6 -> 8.2, its prologue
+// exposed) and float32 discounted returns (32768 x 256: 19.8 -> 21.4; one
+// stream, whose two chunks in registers already keep up).
+constexpr int kTdMaxSlots = 4;
+constexpr int64_t kTdMinSteps = 256;
+template <class Est, int OPT, class S>
+constexpr int td_slots() {
+  if (__is_same(Est, DiscountedReturn) && __is_same(S, F32S)) return 0;
+  constexpr bool flags = (OPT & 1) && Traits<Est>::kUsesFlags;
+  for (int n = kTdMaxSlots; n >= 3; --n)
+    if (td_fits(Traits<Est>::kStreams, 64, (int)sizeof(typename S::T), n, flags)) return n;
+  return 0;
 }
 
 template <class Est, int OPT, class S>
@@ -650,6 +672,12 @@ inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
     if (const int eb = tm_item_envs<Est, S>(a, cu_count())) {
       void* p1[] = {&arg};
       const dim3 grid((unsigned)(a.E / eb));
+      constexpr int nsl = Traits<Est>::kStreams <= 3 ? td_slots<Est, OPT, S>() : 0;
+      if constexpr (nsl != 0) {
+        if (eb == 64 && a.T >= kTdMinSteps)
+          return hipLaunchKernel(reinterpret_cast<const void*>(&tm_dma_kernel<Est, OPT, 64, S, nsl>), grid,
+                                 dim3(td_threads<64>()), p1, 0, s);
+      }
       if constexpr (Traits<Est>::kStreams <= 3) {
         if (eb == 64)
           return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 64, S>), grid,

@@ -107,9 +107,9 @@ def test_time_major_exact_integer_sums():
 # environments staged in LDS and scanned as rows; whole chunks, 16-byte
 # aligned arrays, one launch): one chunk, odd and even chunk counts, blocks of
 # 32 environments (fewer than 16384; 96 is no multiple of 64) and of 64
-# (16384 at 64, 256, 384 and 512 steps; at 256, one super-tile of the other
-# kernel, only discounted returns, traces and prefix sums take the item
-# form), 4096 x 1088 (columns of 17 chunks, taken since the blocks are half
+# (16384 at 64, 256, 384 and 512 steps, from 256 steps the loads moved by
+# DMA except for V-trace; at 256, one super-tile of the other kernel,
+# V-trace takes that one), 4096 x 1088 (columns of 17 chunks, taken since the blocks are half
 # as many as the CUs); dense flags; no episode ends (every row's carry
 # crosses every chunk).
 @pytest.mark.parametrize("E,T", [(64, 64), (96, 128), (128, 192), (192, 448), (256, 320), (1024, 128), (4096, 256),
@@ -136,6 +136,28 @@ def test_time_major_item_form_16bit(fmt, E, T, p):
     d = synth.draw(E, T, seed=91 + E + T, p_term=p, p_trunc=p)
     for name in SEVEN:
         check_storage(name, d, fmt, time_major=True)
+
+
+# The DMA form of 64-environment blocks (from 16384 environments, columns of
+# at least 256 steps): dense and absent flags, even and odd chunk counts,
+# 16-bit storage, and the optional inputs left out (without flags V-trace's
+# three streams fit it too).
+@pytest.mark.parametrize("fmt", ("float32", "bfloat16", "float16"))
+@pytest.mark.parametrize("T,p", [(256, 0.3), (320, 0.0), (320, 0.3)])
+def test_time_major_dma_form(fmt, T, p):
+    _say("time-major DMA form %s E=16384 T=%d p=%g" % (fmt, T, p))
+    d = synth.draw(16384, T, seed=97 + T, p_term=p, p_trunc=p)
+    for name in SEVEN:
+        check_storage(name, d, fmt, time_major=True)
+
+
+@pytest.mark.parametrize("fmt", ("float32", "bfloat16"))
+@pytest.mark.parametrize("variant", [dict(term=False, trunc=False), dict(boot=False, tboot=False),
+                                     dict(tboot=False)])
+def test_time_major_dma_form_optional_inputs(fmt, variant):
+    d = synth.draw(16384, 256, seed=98, p_term=0.03, p_trunc=0.03)
+    for name in SEVEN:
+        check_storage(name, d, fmt, time_major=True, **variant)
 
 
 @pytest.mark.parametrize("variant", [dict(term=False, trunc=False), dict(boot=False, tboot=False),
