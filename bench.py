@@ -613,7 +613,7 @@ def summarize_profiles(out):
 
     def fmt_of(k):
         s = "bf16" if "Bf16S" in k else "f16" if "F16S" in k else "f32"
-        return ("time_major_" + s) if k.startswith(("tm_kernel", "tm_carry", "tm_item_kernel")) else s
+        return ("time_major_" + s) if k.startswith(("tm_kernel", "tm_carry", "tm_item_kernel", "tm_dma_kernel")) else s
 
     rows = {}
     for k, v in runs.items():
