@@ -678,6 +678,18 @@ inline hipError_t launch_tm_opt(const KernelArgs& a, hipStream_t s) {
           return hipLaunchKernel(reinterpret_cast<const void*>(&tm_dma_kernel<Est, OPT, 64, S, nsl>), grid,
                                  dim3(td_threads<64>()), p1, 0, s);
       }
+      // V-trace's three float32 streams with flags: the flags through the
+      // storer waves' registers (three slots of one word per 4 steps, which
+      // fit beside three data slots where the raw flag bytes do not); 16384 x
+      // 256: 21.6 -> 17.9 us, 16384 x 512: 38.9 -> 35.6, 32768 x 256: 39.9 ->
+      // 37.5 against the register item form
+      constexpr bool rf = Traits<Est>::kStreams == 3 && nsl == 0 && (OPT & 1) && Traits<Est>::kUsesFlags &&
+                          td_fits(3, 64, (int)sizeof(typename S::T), 3, true, true);
+      if constexpr (rf) {
+        if (eb == 64 && a.T >= kTdMinSteps)
+          return hipLaunchKernel(reinterpret_cast<const void*>(&tm_dma_kernel<Est, OPT, 64, S, 3, true>), grid,
+                                 dim3(td_threads<64>()), p1, 0, s);
+      }
       if constexpr (Traits<Est>::kStreams <= 3) {
         if (eb == 64)
           return hipLaunchKernel(reinterpret_cast<const void*>(&tm_item_kernel<Est, OPT, 64, S>), grid,

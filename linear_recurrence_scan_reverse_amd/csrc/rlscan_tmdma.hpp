@@ -37,24 +37,31 @@ template <int EB> constexpr int td_threads() { return 64 * (td_compute<EB>() + t
 // 1 KiB groups per stream chunk (64 steps of EB values of es bytes) and per flag array chunk
 constexpr int td_groups(int eb, int es) { return eb * es * 64 / 1024; }
 constexpr int td_flag_groups(int eb) { return eb * 64 / 1024; }
-constexpr int td_lds_bytes(int ns, int eb, int es, int nsl, bool flags) {
-  return nsl * ns * td_groups(eb, es) * kTdGroup + (flags ? (nsl - 1) * 2 * td_flag_groups(eb) * kTdGroup : 0);
+// rf: flags through the storer waves' registers, combined one byte a step
+// (three slots of the register item form's words) instead of DMA
+constexpr int td_lds_bytes(int ns, int eb, int es, int nsl, bool flags, bool rf = false) {
+  return nsl * ns * td_groups(eb, es) * kTdGroup +
+         (!flags ? 0 : rf ? 3 * eb * (eb == 64 ? 17 : 18) * 4 : (nsl - 1) * 2 * td_flag_groups(eb) * kTdGroup);
 }
 // DMA requests of one DMA wave per tick
-constexpr int td_requests(int ns, int eb, int es, bool flags) {
-  return (ns * td_groups(eb, es) + (flags ? 2 * td_flag_groups(eb) : 0)) / (eb / 32);
+constexpr int td_requests(int ns, int eb, int es, bool flags, bool rf = false) {
+  return (ns * td_groups(eb, es) + (flags && !rf ? 2 * td_flag_groups(eb) : 0)) / (eb / 32);
 }
 constexpr int kTdLdsBudget = 160 * 1024;
 // Whether NSL data slots fit: the LDS, and a DMA wave's wait count (6 bits).
-constexpr bool td_fits(int ns, int eb, int es, int nsl, bool flags) {
-  return nsl >= 3 && td_lds_bytes(ns, eb, es, nsl, flags) <= kTdLdsBudget &&
-         (nsl - 2) * td_requests(ns, eb, es, flags) < 64;
+constexpr bool td_fits(int ns, int eb, int es, int nsl, bool flags, bool rf = false) {
+  return nsl >= 3 && td_lds_bytes(ns, eb, es, nsl, flags, rf) <= kTdLdsBudget &&
+         (nsl - 2) * td_requests(ns, eb, es, flags, rf) < 64;
 }
 
-// Template parameters as for tm_item_kernel, plus NSL data slots (3 or more).
+// Template parameters as for tm_item_kernel, plus NSL data slots (3 or more)
+// and RF: the flags moved by the storer waves through registers (4-byte
+// accesses, two chunks ahead, both bytes of a step folded into one, as the
+// register item form does) instead of by DMA, for three streams whose raw
+// flag bytes do not fit beside three data slots.
 // E a positive multiple of EB, T a positive multiple of 64, every per-step
 // array 16-byte aligned, 64 * E * 4 < 2^31 (checked by the launcher).
-template <class Est, int OPT, int EB, class S, int NSL>
+template <class Est, int OPT, int EB, class S, int NSL, bool RF = false>
 __global__ void __launch_bounds__(td_threads<EB>()) tm_dma_kernel(const KernelArgs p) {
   using Tr = Traits<Est>;
   constexpr int L = 16, K = 4, SPAN = kTiChunk;
@@ -64,6 +71,7 @@ __global__ void __launch_bounds__(td_threads<EB>()) tm_dma_kernel(const KernelAr
   constexpr bool OUT1 = (OPT & 2) && Tr::kHasOut1;
   constexpr int NOUT = OUT1 ? 2 : 1;
   constexpr bool GATHER_TB = USE_FLAGS && Tr::kBackwardRl;
+  constexpr bool DMAF = USE_FLAGS && !RF, RFL = USE_FLAGS && RF;  // flags by DMA / through registers
   static_assert(!Tr::kDual && NOUT <= NS, "one recurrence, outputs over streams");
   static_assert(EB == 64 || EB == 32, "blocks of 64 or 32 environments");
   constexpr int ES = (int)sizeof(typename S::T);
@@ -76,16 +84,20 @@ __global__ void __launch_bounds__(td_threads<EB>()) tm_dma_kernel(const KernelAr
   constexpr int LPF = EB / 16;    // lanes per step of a flag access
   constexpr int NFL = NSL - 1;
   constexpr int NC = td_compute<EB>(), ND = td_dma<EB>(), NST = td_storers<EB>();
-  static_assert(td_fits(NS, EB, ES, NSL, USE_FLAGS), "slots fit the LDS and the wait count");
+  static_assert(td_fits(NS, EB, ES, NSL, USE_FLAGS, RF), "slots fit the LDS and the wait count");
   static_assert(NQ % ND == 0 && NQ % NST == 0 && (2 * NQF) % ND == 0, "groups split evenly over waves");
-  constexpr int WAITN = (NSL - 3) * td_requests(NS, EB, ES, USE_FLAGS);
-  constexpr int WAIT0 = (NSL - 2) * td_requests(NS, EB, ES, USE_FLAGS);  // after chunk 0's flags
+  constexpr int WAITN = (NSL - 3) * td_requests(NS, EB, ES, USE_FLAGS, RF);
+  constexpr int WAIT0 = (NSL - 2) * td_requests(NS, EB, ES, USE_FLAGS, RF);  // after chunk 0's flags
+  constexpr int FROW = ti_flag_row<EB>();
 
   // streams (then outputs) of NSL chunks: [slot][stream][group][bytes], a
   // group holding SPI steps of EB values each
   __shared__ __attribute__((aligned(16))) unsigned char s_d[NSL][NS][NQ][kTdGroup];
   // flag bytes of NFL chunks: [slot][array: terminated, truncated][group][bytes]
-  __shared__ __attribute__((aligned(16))) unsigned char s_f[USE_FLAGS ? NFL : 1][2][USE_FLAGS ? NQF : 1][kTdGroup];
+  __shared__ __attribute__((aligned(16))) unsigned char s_f[DMAF ? NFL : 1][2][DMAF ? NQF : 1][kTdGroup];
+  // (RF) flags of three chunks, one byte a step (bit 0 terminated, bit 1
+  // truncated), four steps a word: [slot][environment][steps / 4]
+  __shared__ uint32_t s_fw[RFL ? 3 : 1][RFL ? EB : 1][FROW];
 
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -124,12 +136,62 @@ __global__ void __launch_bounds__(td_threads<EB>()) tm_dma_kernel(const KernelAr
         }
       }
     };
-    tick_barrier();  // the prologue's two
+    // (RF) flags: two passes of 4-byte accesses, each covering steps 4 fword ..
+    // + 3 of environments scol .. scol + 3; chunk k's words in register set k % 2
+    constexpr int FLPR = EB / 4;  // lanes per step row of a 4-byte flag access
+    const int scol = 4 * (lane % FLPR);
+    auto fword = [&](int i) { return (16 / NST) * sw + (64 / FLPR) * i + lane / FLPR; };
+    typedef uint32_t Flags[2][2][4];
+    auto issue_flags = [&](int c, Flags& f) {
+      if constexpr (RFL) {
+        const __amdgpu_buffer_rsrc_t rt = chunk_rs(p.term, c, 1), rr = chunk_rs(p.trunc, c, 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t off = (uint32_t)((int64_t)(4 * fword(i) + m) * E + scol);
+            f[i][0][m] = __builtin_amdgcn_raw_buffer_load_b32(rt, off, 0, 2);
+            f[i][1][m] = __builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, 2);
+          }
+      }
+    };
+    auto write_flags = [&](int c, const Flags& f) {
+      if constexpr (RFL) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) w4[m] = bytes_nonzero(f[i][0][m]) | (bytes_nonzero(f[i][1][m]) << 1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            s_fw[c % 3][scol + j][fword(i)] = ((w4[0] >> (8 * j)) & 0xffu) | (((w4[1] >> (8 * j)) & 0xffu) << 8) |
+                                              (((w4[2] >> (8 * j)) & 0xffu) << 16) |
+                                              (((w4[3] >> (8 * j)) & 0xffu) << 24);
+        }
+      }
+    };
+    Flags f0, f1;
+    issue_flags(0, f0);
+    issue_flags(1, f1);
+    write_flags(0, f0);
+    issue_flags(2, f0);
+    write_flags(1, f1);
+    issue_flags(3, f1);
+    lds_done();
+    tick_barrier();  // the prologue's two (chunks 0 and 1's flags written before the first)
     tick_barrier();
-    for (int s = 0; s < ticks; ++s) {
+    // tick s: chunk s-1's outputs stored, chunk s+2's flags written (set s % 2)
+    // and chunk s+4's requested into that set
+    auto tick = [&](int s, Flags& f) {
       store_out(s - 1);
+      write_flags(s + 2, f);
+      issue_flags(s + 4, f);
       lds_done();
       tick_barrier();
+    };
+    for (int s = 0; s < ticks; s += 2) {
+      tick(s, f0);
+      if (s + 1 < ticks) tick(s + 1, f1);
     }
     store_out(ticks - 1);
   } else if (wave >= NC) {
@@ -138,7 +200,7 @@ __global__ void __launch_bounds__(td_threads<EB>()) tm_dma_kernel(const KernelAr
     const float* srcs[5] = {p.r, p.v, p.aux, p.pi, p.mu};
     // requests of tick t: flags of chunk t + NFL, streams of chunk t + NSL - 2
     auto issue = [&](int t) {
-      if constexpr (USE_FLAGS) {
+      if constexpr (DMAF) {
         const int c = t + NFL;  // >= 0
 #pragma unroll
         for (int i = 0; i < 2 * NQF / ND; ++i) {
@@ -217,7 +279,17 @@ __global__ void __launch_bounds__(td_threads<EB>()) tm_dma_kernel(const KernelAr
 #pragma unroll
         for (int m = 0; m < K; ++m) o.boot[it][m] = 0.0f;
       }
-      if constexpr (USE_FLAGS) {
+      if constexpr (RFL) {
+        if (s < ticks) {
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const uint32_t w = s_fw[s % 3][col[it]][cs_local / 4];
+            o.tb[it] = ((w & 1u) | ((w >> 7) & 2u) | ((w >> 14) & 4u) | ((w >> 21) & 8u)) & tmask;
+            o.rb[it] = (((w >> 1) & 1u) | ((w >> 8) & 2u) | ((w >> 15) & 4u) | ((w >> 22) & 8u)) & rmask;
+          }
+        }
+      }
+      if constexpr (DMAF) {
         if (s < ticks) {
           const int fs = s % NFL;
 #pragma unroll

@@ -108,8 +108,7 @@ def test_time_major_exact_integer_sums():
 # aligned arrays, one launch): one chunk, odd and even chunk counts, blocks of
 # 32 environments (fewer than 16384; 96 is no multiple of 64) and of 64
 # (16384 at 64, 256, 384 and 512 steps, from 256 steps the loads moved by
-# DMA except for V-trace; at 256, one super-tile of the other kernel,
-# V-trace takes that one), 4096 x 1088 (columns of 17 chunks, taken since the blocks are half
+# DMA, float32 V-trace's flags through registers), 4096 x 1088 (columns of 17 chunks, taken since the blocks are half
 # as many as the CUs); dense flags; no episode ends (every row's carry
 # crosses every chunk).
 @pytest.mark.parametrize("E,T", [(64, 64), (96, 128), (128, 192), (192, 448), (256, 320), (1024, 128), (4096, 256),
